@@ -1,0 +1,346 @@
+"""Chunk-vectorised float64 oracle of LoLA's attention step for one layer.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+What is computed, and where the pages say so
+--------------------------------------------
+A *unit* is one (sequence b, KV head h).  Every memory of LoLA is per unit:
+
+* sliding window W: the most recent ``eta`` key/value pairs
+  [LoLA notes §2.1 symbol table; §2.4 step 1];
+* sparse global cache G: at most ``lam`` key/value pairs
+  [LoLA notes §2.1; §2.4, Eq. (11)];
+* linear state H (D x d_v) and s (D), which receive only the pairs that are
+  *allocated* to them [LoLA notes §2.2, Eqs. (3)-(5) and the paragraph after].
+
+Per chunk of c tokens starting at position n (chunk schedule: LoLA notes §2.6,
+Eq. (15)):
+
+1. **Read** (LoLA notes §2.5, Eq. (14)).  For query t the explicit keys are
+   G plus every local position i with max(0, n - eta) <= i <= t, and
+
+       y_t = (H^T phi(q_t) + sum_i a_ti v_i) / (phi(q_t)^T s + sum_i a_ti),
+       a_ti = exp(q_t . k_i / sqrt(d_k)),
+
+   one normaliser over all three memories, with H, s, G as at chunk start
+   (chunk queries share the existing state, LoLA notes §2.6).
+2. **Candidates** (LoLA notes §2.4 step 2; §2.6).  The tokens that leave the
+   window, L = [max(0, n - eta), max(0, n + c - eta)), joined with the current
+   cache: E = G u L.
+3. **Keep all if few** (LoLA notes §2.4, after Eq. (13)): if |E| <= lam, G <- E
+   and nothing is scored or folded.
+4. **Score before write** (LoLA notes §2.3, Eq. (10); §2.4, Eqs. (11)-(13) and
+   the before/after reading given there): each candidate's Self-Recall Error
+   against the state as it is *before* this update,
+
+       SRE(k, v | H, s) = || H^T phi(k) / (phi(k)^T s) - v ||^2 ,
+
+   squared as in the LoLA summary's SRE section (the notes print the norm
+   unsquared; the ranking is identical).  Keep the ``lam`` highest as the new
+   G; fold the rest into H += sum phi(k) v^T, s += sum phi(k).
+5. **Advance**: the window becomes the last ``eta`` positions; n += c.
+
+Readings where the pages leave a step open (each is listed in the design doc):
+eta counts past tokens kept between chunks and a query also sees its own
+chunk's causal prefix (diagonal included); z = phi(k)^T s = 0 gives prediction
+0 (the notes flag the H = 0, s = 0 division as unhandled); ties in the top-lam
+order go to the older token (lower position); the read uses the state at chunk
+start and decode is this same step with c = 1; with GQA, q-head j reads KV head
+floor(j / g); every batch sequence is at the same n.
+
+The feature map is phi(x) = [softmax(x W_h), softmax(-x W_h)] with one W_h
+(d x m) per KV head, D = 2m (learned phi, R^{d_k} -> R^D with D = 2 d_k in the
+notes §2.1 and §3.1; this fixed softmax form is the workload's).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+F64 = np.float64
+
+
+# --------------------------------------------------------------------------- phi
+def _softmax_last(u: np.ndarray) -> np.ndarray:
+    """Softmax over the last axis.  Subtracting the row max first changes
+    nothing mathematically; it only keeps exp finite."""
+    e = np.exp(u - u.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def phi(x: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """phi(x) = [softmax(x W), softmax(-x W)] for rows x (..., d), W (d, m).
+
+    Returns (..., 2m) in float64.  Each half sums to 1, so 1^T phi(x) = 2.
+    """
+    u = np.asarray(x, F64) @ np.asarray(W, F64)
+    return np.concatenate([_softmax_last(u), _softmax_last(-u)], axis=-1)
+
+
+def _phi_units(x: np.ndarray, Wu: np.ndarray) -> np.ndarray:
+    """phi for per-unit rows: x (U, ..., d), Wu (U, d, m) -> (U, ..., 2m)."""
+    U = x.shape[0]
+    flat = x.reshape(U, -1, x.shape[-1])
+    u = np.matmul(flat, Wu)                       # (U, rows, m)
+    out = np.concatenate([_softmax_last(u), _softmax_last(-u)], axis=-1)
+    return out.reshape(x.shape[:-1] + (out.shape[-1],))
+
+
+# --------------------------------------------------------------------------- SRE
+def sre(phk: np.ndarray, v: np.ndarray, H: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Self-Recall Error of candidates against a linear state.
+
+    phk (U, E, D) features of the candidate keys, v (U, E, d) their values,
+    H (U, D, d), s (U, D).  Returns (U, E):
+
+        z = phi(k)^T s;  p = H^T phi(k) / z  (p = 0 when z = 0);
+        SRE = sum_c (p_c - v_c)^2.
+
+    [LoLA notes §2.3, Eq. (10); squared per the LoLA summary; the z = 0 rule
+    is the reading of the notes' §2.6 remark that H = 0, s = 0 cannot be
+    divided.]
+    """
+    phk = np.asarray(phk, F64)
+    z = np.einsum("uef,uf->ue", phk, s)
+    num = np.matmul(phk, H)                       # (U, E, d) = phi^T H per row
+    safe = np.where(z > 0, z, 1.0)
+    p = np.where((z > 0)[..., None], num / safe[..., None], 0.0)
+    return ((p - np.asarray(v, F64)) ** 2).sum(axis=-1)
+
+
+# ------------------------------------------------------------------- selection
+def select_keep(scores: np.ndarray, pos: np.ndarray, lam: int) -> np.ndarray:
+    """Top_lam membership per unit: keep the ``lam`` candidates that come first
+    in the order (score descending, position ascending).
+
+    [LoLA notes §2.4, Eq. (11) and the note after Eq. (13): Top_lam returns the
+    highest-scoring set, capacity exactly lam; ties go to the older token.]
+    scores, pos: (U, E).  Returns a boolean keep mask (U, E).
+    """
+    U, E = scores.shape
+    keep = np.zeros((U, E), dtype=bool)
+    if lam <= 0:
+        return keep
+    for u in range(U):
+        order = np.lexsort((pos[u], -scores[u]))   # primary: -score, then pos
+        keep[u, order[:lam]] = True
+    return keep
+
+
+def boundary_gap(scores: np.ndarray, lam: int) -> np.ndarray:
+    """Relative gap (SRE_(lam) - SRE_(lam+1)) / SRE_(lam) at the capacity
+    boundary, per unit (scores sorted descending; inf if SRE_(lam) == 0)."""
+    srt = -np.sort(-scores, axis=1)
+    a, b = srt[:, lam - 1], srt[:, lam]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return np.where(a > 0, (a - b) / a, np.inf)
+
+
+# ----------------------------------------------------------------------- state
+@dataclass
+class LolaState:
+    """Per-layer state for U units (float64).
+
+    n       tokens already processed (common to every unit)
+    H, s    linear state (U, D, d) and (U, D)
+    win_k/v window pairs (U, w, d), positions [n - w, n), w = min(n, eta)
+    g_pos   cache positions (U, |G|), ascending; g_k/g_v (U, |G|, d)
+    n_fold  tokens folded into H, s so far (common to every unit)
+    """
+
+    eta: int
+    lam: int
+    n: int
+    H: np.ndarray
+    s: np.ndarray
+    win_k: np.ndarray
+    win_v: np.ndarray
+    g_pos: np.ndarray
+    g_k: np.ndarray
+    g_v: np.ndarray
+    n_fold: int = 0
+
+    def copy(self) -> "LolaState":
+        return LolaState(self.eta, self.lam, self.n, self.H.copy(), self.s.copy(),
+                         self.win_k.copy(), self.win_v.copy(), self.g_pos.copy(),
+                         self.g_k.copy(), self.g_v.copy(), self.n_fold)
+
+
+def new_state(U: int, d: int, D: int, eta: int, lam: int) -> LolaState:
+    """Empty state: n = 0, H = 0, s = 0, no window, no cache."""
+    z = np.zeros
+    return LolaState(eta, lam, 0, z((U, D, d)), z((U, D)), z((U, 0, d)), z((U, 0, d)),
+                     z((U, 0), dtype=np.int64), z((U, 0, d)), z((U, 0, d)), 0)
+
+
+def state_elements(d_k: int, d_v: int, D: int, eta: int, lam: int, t: int) -> int:
+    """Persistent attention-state element count per head after t tokens:
+    min{t (d_k + d_v), (eta + lam)(d_k + d_v) + D d_v + D}
+    [LoLA notes §2.7, memory formula of Appendix B]."""
+    return min(t * (d_k + d_v), (eta + lam) * (d_k + d_v) + D * d_v + D)
+
+
+@dataclass
+class ChunkLog:
+    """What one chunk's update did (per unit arrays; ``sre`` is None when
+    |E| <= lam and nothing was scored)."""
+
+    n: int
+    c: int
+    cand_pos: np.ndarray
+    sre: Optional[np.ndarray] = None
+    keep: Optional[np.ndarray] = None
+    gap: Optional[np.ndarray] = None
+
+
+# ------------------------------------------------------------------------ read
+def _read_chunk(st: LolaState, qc: np.ndarray, kc: np.ndarray, vc: np.ndarray,
+                Wu: np.ndarray) -> np.ndarray:
+    """Eq. (14) for every query of the chunk, with the state at chunk start.
+
+    qc (U, g, c, d); kc, vc (U, c, d).  Returns y (U, g, c, d)."""
+    U, g, c, d = qc.shape
+    keys = np.concatenate([st.g_k, st.win_k, kc], axis=1)     # (U, nk, d)
+    vals = np.concatenate([st.g_v, st.win_v, vc], axis=1)
+    n_old = st.g_k.shape[1] + st.win_k.shape[1]
+    logits = np.matmul(qc, keys[:, None].transpose(0, 1, 3, 2)) / np.sqrt(d)
+    a = np.exp(logits)                                        # unshifted, Eq. (14)
+    if not np.all(np.isfinite(a)):
+        raise FloatingPointError("exp(q.k/sqrt(d)) overflowed in float64")
+    causal = np.tril(np.ones((c, c), dtype=bool))             # t sees j <= t
+    a[..., n_old:] *= causal
+    phq = _phi_units(qc, Wu)                                  # (U, g, c, D)
+    num = np.matmul(a, vals[:, None]) + np.matmul(phq, st.H[:, None])
+    den = a.sum(axis=-1) + np.einsum("ugtf,uf->ugt", phq, st.s)
+    return num / den[..., None]
+
+
+# ---------------------------------------------------------------------- update
+def _update_chunk(st: LolaState, kc: np.ndarray, vc: np.ndarray, Wu: np.ndarray
+                  ) -> ChunkLog:
+    """Steps 2-5 of the chunk schedule (candidates, keep-all, SRE, fold,
+    advance).  Mutates ``st``."""
+    U, c, d = kc.shape
+    n, eta, lam = st.n, st.eta, st.lam
+    w = st.win_k.shape[1]
+    local_k = np.concatenate([st.win_k, kc], axis=1)          # positions n-w .. n+c-1
+    local_v = np.concatenate([st.win_v, vc], axis=1)
+    n_new = n + c
+    w_new = min(n_new, eta)
+    n_leave = w + c - w_new                                   # = |L|
+    p0 = n - w
+    leave_pos = np.broadcast_to(np.arange(p0, p0 + n_leave, dtype=np.int64), (U, n_leave))
+    E_pos = np.concatenate([st.g_pos, leave_pos], axis=1)
+    E_k = np.concatenate([st.g_k, local_k[:, :n_leave]], axis=1)
+    E_v = np.concatenate([st.g_v, local_v[:, :n_leave]], axis=1)
+    st.win_k = local_k[:, n_leave:].copy()
+    st.win_v = local_v[:, n_leave:].copy()
+    log = ChunkLog(n=n, c=c, cand_pos=E_pos.copy())
+    nE = E_pos.shape[1]
+    if nE <= lam:
+        st.g_pos, st.g_k, st.g_v = E_pos.copy(), E_k, E_v
+    else:
+        phE = _phi_units(E_k, Wu)
+        scores = sre(phE, E_v, st.H, st.s)                    # before-state
+        keep = select_keep(scores, E_pos, lam)
+        fold = (~keep).astype(F64)
+        st.H = st.H + np.matmul((phE * fold[..., None]).transpose(0, 2, 1), E_v)
+        st.s = st.s + (phE * fold[..., None]).sum(axis=1)
+        st.g_pos = E_pos[keep].reshape(U, lam)
+        st.g_k = E_k[keep].reshape(U, lam, d)
+        st.g_v = E_v[keep].reshape(U, lam, d)
+        st.n_fold += nE - lam
+        log.sre, log.keep = scores, keep
+        log.gap = boundary_gap(scores, lam) if lam > 0 else None
+    st.n = n_new
+    return log
+
+
+# ------------------------------------------------------------------ public API
+def _as_units(q, k, v, W, Hkv):
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    B, Hq, T, d = q.shape
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    g = Hq // Hkv
+    U = B * Hkv
+    qu = q.reshape(B, Hkv, g, T, d).reshape(U, g, T, d)
+    ku = k.reshape(U, T, d)
+    vu = v.reshape(U, T, d)
+    Wu = np.tile(np.asarray(W, F64), (B, 1, 1))               # unit b*Hkv+h -> W[h]
+    return qu, ku, vu, Wu, (B, Hq, T, d)
+
+
+def prefill(st: LolaState, q, k, v, W, C: int, *, outputs: bool = True,
+            logs: Optional[List[ChunkLog]] = None) -> Optional[np.ndarray]:
+    """Process T new tokens with chunk length C (the last chunk may be short).
+
+    q (B, Hq, T, d); k, v (B, Hkv, T, d); W (Hkv, d, m); ``st`` holds U = B*Hkv
+    units and is updated in place.  Returns y (B, Hq, T, d) in float64, or None
+    if ``outputs`` is False (the state trajectory does not depend on q).
+    """
+    if C < 1:
+        raise ValueError("C must be >= 1")
+    Hkv = np.asarray(W).shape[0]
+    qu, ku, vu, Wu, shape = _as_units(q, k, v, W, Hkv)
+    U, g, T, d = qu.shape
+    if st.H.shape[0] != U:
+        raise ValueError("state unit count does not match the inputs")
+    y = np.zeros(qu.shape) if outputs else None
+    t0 = 0
+    while t0 < T:
+        c = min(C, T - t0)
+        sl = slice(t0, t0 + c)
+        if outputs:
+            y[:, :, sl] = _read_chunk(st, qu[:, :, sl], ku[:, sl], vu[:, sl], Wu)
+        lg = _update_chunk(st, ku[:, sl], vu[:, sl], Wu)
+        if logs is not None:
+            logs.append(lg)
+        t0 += c
+    if not outputs:
+        return None
+    B, Hq, T, d = shape
+    return y.reshape(B, Hkv, g, T, d).reshape(B, Hq, T, d)
+
+
+def decode_step(st: LolaState, q, k, v, W, *, logs=None) -> np.ndarray:
+    """One token for every sequence: q (B, Hq, d), k, v (B, Hkv, d).
+    Defined as prefill with T = 1, C = 1 (read, then update)."""
+    y = prefill(st, np.asarray(q)[:, :, None], np.asarray(k)[:, :, None],
+                np.asarray(v)[:, :, None], W, 1, logs=logs)
+    return y[:, :, 0]
+
+
+# ------------------------------------------------------------ export / import
+def export_state(st: LolaState) -> dict:
+    """Canonical layout (per unit): n; H (U, D, d); s (U, D); window k/v oldest
+    to newest (U, w, d); cache positions ascending (U, |G|) with its k/v."""
+    return dict(n=st.n, n_fold=st.n_fold, H=st.H.copy(), s=st.s.copy(),
+                win_k=st.win_k.copy(), win_v=st.win_v.copy(),
+                g_pos=st.g_pos.copy(), g_k=st.g_k.copy(), g_v=st.g_v.copy())
+
+
+def import_state(d: dict, eta: int, lam: int) -> LolaState:
+    """Inverse of :func:`export_state`; checks the bookkeeping invariants
+    |W| = min(n, eta), |G| = min(lam, max(0, n - eta)), positions ascending
+    and older than the window."""
+    n = int(d["n"])
+    U = d["H"].shape[0]
+    w = d["win_k"].shape[1]
+    gs = d["g_pos"].shape[1]
+    if w != min(n, eta):
+        raise ValueError("window length does not match n")
+    if gs != min(lam, max(0, n - eta)):
+        raise ValueError("cache size does not match n")
+    gp = np.asarray(d["g_pos"], np.int64)
+    if gs and (np.any(np.diff(gp, axis=1) <= 0) or np.any(gp >= n - w) or np.any(gp < 0)):
+        raise ValueError("cache positions must be ascending and older than the window")
+    n_fold = int(d.get("n_fold", max(0, n - eta) - gs))
+    return LolaState(eta, lam, n, np.array(d["H"], F64), np.array(d["s"], F64),
+                     np.array(d["win_k"], F64), np.array(d["win_v"], F64), gp.copy(),
+                     np.array(d["g_k"], F64), np.array(d["g_v"], F64), n_fold)
