@@ -1,0 +1,154 @@
+/*
+ * lola.h -- C ABI of the LoLA chunkwise attention step (one layer) for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method (source: "LoLA: Low-Rank Linear Attention With Sparse Caching",
+ * close-reading notes on arXiv:2505.23666v3, cited below as "LoLA notes"):
+ * every (sequence, KV head) "unit" keeps three memories -- a sliding window
+ * of the last eta key/value pairs, a sparse cache of at most lambda pairs, and
+ * a linear-attention state H (D x d), s (D) (notes §2.1, §2.4).  Queries read
+ * all three under one softmax normaliser (notes §2.5, Eq. (14)).  Pairs that
+ * leave the window are scored, together with the cache, by the Self-Recall
+ * Error ||H^T phi(k) / (phi(k)^T s) - v||^2 (notes §2.3, Eq. (10)); the lambda
+ * highest stay cached and the rest are folded into H += phi(k) v^T,
+ * s += phi(k) (notes §2.4, Eqs. (11)-(13)).  Prefill processes chunks of C
+ * tokens that share the state at chunk start (notes §2.6, Eq. (15)).
+ *
+ * Feature map: phi(x) = [softmax(x W_h), softmax(-x W_h)], W_h a d x 64
+ * matrix per KV head, so D = 128.
+ *
+ * Conventions
+ *  - All tensor arguments are DEVICE pointers to contiguous row-major arrays,
+ *    owned by the caller, read or written only by work enqueued on `stream`
+ *    (a hipStream_t passed as void*; NULL = the null stream).  Calls return
+ *    once the work is enqueued.
+ *  - Element type of q, k, v, W and of the stored window/cache K/V is
+ *    cfg->dtype (LOLA_DTYPE_F32 or LOLA_DTYPE_BF16, bf16 as raw 16-bit
+ *    patterns).  H and s are float32.  Outputs are float32.
+ *  - Every call returns a lola_status.  Argument errors leave the state
+ *    unchanged.  A failure reported by HIP after work was enqueued marks the
+ *    state poisoned: later calls return LOLA_ERR_STATE until
+ *    lola_state_import().  lola_last_error() gives a per-thread message.
+ */
+#ifndef LOLA_H_
+#define LOLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LOLA_OK = 0,
+  LOLA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, inconsistent config */
+  LOLA_ERR_UNSUPPORTED = 2,  /* valid for the method, not for these kernels */
+  LOLA_ERR_OUT_OF_MEMORY = 3,
+  LOLA_ERR_HIP = 4,          /* a HIP runtime call failed */
+  LOLA_ERR_STATE = 5,        /* poisoned state, or an import fails invariants */
+  LOLA_ERR_WORKSPACE = 6     /* caller workspace smaller than required */
+} lola_status;
+
+typedef enum { LOLA_DTYPE_F32 = 0, LOLA_DTYPE_BF16 = 1 } lola_dtype;
+
+typedef struct {
+  int32_t batch;      /* B >= 1: sequences, all at the same position n */
+  int32_t q_heads;    /* Hq; Hq % Hkv == 0; q-head j reads KV head j / (Hq/Hkv) */
+  int32_t kv_heads;   /* Hkv >= 1 */
+  int32_t head_dim;   /* d = d_k = d_v; supported: 64, 128 */
+  int32_t feat_half;  /* m: phi has D = 2m features; supported: 64 */
+  int32_t window;     /* eta >= 0: pairs kept in the sliding window */
+  int32_t cache;      /* lambda >= 0: capacity of the sparse cache */
+  int32_t dtype;      /* lola_dtype */
+} lola_config;
+
+typedef struct lola_state lola_state;
+
+/* Create an empty state (n = 0, H = 0, s = 0, empty window and cache) on the
+ * current HIP device.  W: device array [Hkv, d, m] in cfg->dtype, COPIED into
+ * the state (the caller keeps ownership).  The library allocates and owns H
+ * [B*Hkv, D, d], s [B*Hkv, D], the window ring [B*Hkv, eta, d] x2 and the
+ * cache [B*Hkv, lambda, d] x2 plus positions (LoLA notes §2.7 state size).
+ * Errors: INVALID_ARG, UNSUPPORTED (head_dim, feat_half, Hq/Hkv not in
+ * {1,2,4}, sizes beyond the kernels' LDS budget), OUT_OF_MEMORY, HIP. */
+int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_state** out);
+
+/* Synchronise the state's last stream and release everything.  NULL: no-op. */
+int lola_state_free(lola_state* st);
+
+/* Tokens already processed (n). */
+int64_t lola_state_tokens(const lola_state* st);
+
+/* Bytes of workspace lola_prefill_chunk needs for (T, C).  0 for T == 0. */
+int lola_prefill_workspace_bytes(const lola_state* st, int T, int C, size_t* bytes);
+
+/* Process T new tokens with chunk length C (LoLA notes §2.6, Eq. (15)).
+ *   q   [B, Hq, T, d]    k, v  [B, Hkv, T, d]    (cfg->dtype)
+ *   out [B, Hq, T, d]    float32 (out_dtype must be LOLA_DTYPE_F32)
+ *   ws  device workspace of at least lola_prefill_workspace_bytes(T, C)
+ *       bytes, or NULL to use a buffer the state owns (grown on demand;
+ *       growing synchronises the stream).
+ * Chunks start at the state's n; a last partial chunk is allowed.  Each
+ * query reads the state as it was at the start of its chunk; the state is
+ * then updated in place and n += T.  C == 1 processes token by token through
+ * the decode kernel.  Other C: multiple of 32, at most 256.
+ * Errors: INVALID_ARG, UNSUPPORTED (C), WORKSPACE, STATE, HIP. */
+int lola_prefill_chunk(lola_state* st, const void* q, const void* k, const void* v, int T,
+                       int C, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* lola_prefill_chunk plus a per-chunk record, for parity diagnostics:
+ *   snap_pos  [B*Hkv, nch, lambda] int32: positions of the cache at the start
+ *             of chunk j (in the chain's order, -1 padding), nch = ceil(T/C);
+ *   cand_keys [B*Hkv, nch, lambda + C] uint64: for chunks whose candidates
+ *             were scored, key (SRE float bits << 32) | (0xFFFFFFFF - position)
+ *             of each candidate in candidate order; untouched otherwise.
+ * Either may be NULL.  C must be > 1. */
+int lola_prefill_debug(lola_state* st, const void* q, const void* k, const void* v, int T,
+                       int C, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                       int32_t* snap_pos, uint64_t* cand_keys, void* stream);
+
+/* One token for every sequence: q [B, Hq, d], k, v [B, Hkv, d], out
+ * [B, Hq, d] float32.  Exactly lola_prefill_chunk with T = 1, C = 1: the
+ * query reads the state, then the pair leaving the window (if any) is scored
+ * against the cache and the lowest-SRE candidate is folded (LoLA notes §2.4).
+ * Errors: INVALID_ARG, STATE, HIP. */
+int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v, void* out,
+                     int out_dtype, void* stream);
+
+/* Canonical state layout, all DEVICE pointers owned by the caller:
+ *   H [B*Hkv, D, d] f32, s [B*Hkv, D] f32,
+ *   win_k, win_v [B*Hkv, eta, d]: the last min(n, eta) pairs oldest first,
+ *                                  rows beyond that zero,
+ *   cache_pos [B*Hkv, lambda] int32 ascending, -1 padding; cache_k, cache_v
+ *   [B*Hkv, lambda, d] in the same order (zero padding).
+ * The cache holds min(lambda, max(0, n - eta)) pairs in every unit. */
+typedef struct {
+  int64_t n;
+  float* H;
+  float* s;
+  void* win_k;
+  void* win_v;
+  int32_t* cache_pos;
+  void* cache_k;
+  void* cache_v;
+} lola_state_view;
+
+/* Write the state into `dst` (dst->n is set on return; stream-ordered). */
+int lola_state_export(const lola_state* st, lola_state_view* dst, void* stream);
+
+/* Replace the state with `src` (n = src->n).  Checks, on the host, that cache
+ * positions are ascending, non-negative and older than the window; returns
+ * LOLA_ERR_STATE otherwise.  Clears a poisoned state.  Synchronises stream. */
+int lola_state_import(lola_state* st, const lola_state_view* src, void* stream);
+
+/* Text of a status code, and the last error detail of the calling thread. */
+const char* lola_strerror(int status);
+const char* lola_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOLA_H_ */

@@ -1,0 +1,428 @@
+// Host runtime behind include/lola.h: validation, state and workspace memory,
+// and the stream-ordered launch sequence of one prefill call:
+//   K1 phi of every candidate row  ->  K2 serial SRE/top-lam/fold chain
+//   (writes one snapshot per chunk)  ->  K3 attention of all chunks in
+//   parallel  ->  finalize (new cache rows, window ring).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "internal.h"
+#include "lola.h"
+
+using namespace lola;
+
+
+struct lola_state {
+  lola_config cfg;
+  int U, g, d, esz;
+  bool f32;
+  int64_t n;
+  int device;
+  hipStream_t last;
+  bool poisoned;
+  float* H;
+  float* s;
+  void* ring_k;
+  void* ring_v;
+  void* cache_k[2];
+  void* cache_v[2];
+  int32_t* cache_pos[2];
+  int cur;
+  void* W;
+  void* own_ws;
+  size_t own_ws_bytes;
+};
+
+namespace {
+
+thread_local std::string g_err;
+constexpr size_t kMaxLds = 160 * 1024;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(lola_state* st, hipError_t e, const char* what) {
+  if (st) st->poisoned = true;
+  return fail(LOLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t phi_hi, phi_lo, snapHT, snaps, snapG, finalG, total;
+};
+
+WsLayout ws_layout(const lola_state* st, int T, int C) {
+  const size_t U = st->U, lam = st->cfg.cache, eta = st->cfg.window, d = st->d;
+  const size_t NV = lam + eta + (size_t)T;
+  const size_t nch = ((size_t)T + C - 1) / C;
+  const size_t lam1 = lam > 0 ? lam : 1;
+  WsLayout w;
+  size_t off = 0;
+  w.phi_hi = off; off = align256(off + U * NV * kD * 2);
+  w.phi_lo = off; off = align256(off + U * NV * kD * 2);
+  w.snapHT = off; off = align256(off + U * nch * 2 * d * kD * 2);
+  w.snaps = off; off = align256(off + U * nch * kD * 4);
+  w.snapG = off; off = align256(off + U * nch * lam1 * 4);
+  w.finalG = off; off = align256(off + U * lam1 * 4);
+  w.total = off;
+  return w;
+}
+
+int check_state(const lola_state* st) {
+  if (!st) return fail(LOLA_ERR_INVALID_ARG, "state is NULL");
+  if (st->poisoned)
+    return fail(LOLA_ERR_STATE, "state is poisoned by an earlier HIP failure; import a state");
+  return LOLA_OK;
+}
+
+int supported_C(const lola_state* st, int C) {
+  if (C == 1) return LOLA_OK;
+  if (C % 32 != 0 || C > 256)
+    return fail(LOLA_ERR_UNSUPPORTED, "chunk length C=%d: need C == 1 or a multiple of 32 <= 256", C);
+  if (chain_lds_bytes(st->cfg.cache, C, st->d, st->f32) > kMaxLds)
+    return fail(LOLA_ERR_UNSUPPORTED, "lambda + C too large for the chain kernel's LDS");
+  return LOLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lola_strerror(int status) {
+  switch (status) {
+    case LOLA_OK: return "ok";
+    case LOLA_ERR_INVALID_ARG: return "invalid argument";
+    case LOLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LOLA_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case LOLA_ERR_HIP: return "HIP runtime error";
+    case LOLA_ERR_STATE: return "invalid or poisoned state";
+    case LOLA_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+const char* lola_last_error(void) { return g_err.c_str(); }
+
+int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_state** out) {
+  if (!cfg || !W || !out) return fail(LOLA_ERR_INVALID_ARG, "cfg, W and out must be non-NULL");
+  *out = nullptr;
+  const lola_config& c = *cfg;
+  if (c.batch < 1 || c.kv_heads < 1 || c.q_heads < 1 || c.q_heads % c.kv_heads ||
+      c.window < 0 || c.cache < 0 || c.head_dim < 1 || c.feat_half < 1)
+    return fail(LOLA_ERR_INVALID_ARG, "inconsistent configuration");
+  if (c.dtype != LOLA_DTYPE_F32 && c.dtype != LOLA_DTYPE_BF16)
+    return fail(LOLA_ERR_INVALID_ARG, "dtype must be LOLA_DTYPE_F32 or LOLA_DTYPE_BF16");
+  const int g = c.q_heads / c.kv_heads;
+  if (c.head_dim != 64 && c.head_dim != 128)
+    return fail(LOLA_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", c.head_dim);
+  if (c.feat_half != kM) return fail(LOLA_ERR_UNSUPPORTED, "feat_half must be %d", kM);
+  if (g != 1 && g != 2 && g != 4)
+    return fail(LOLA_ERR_UNSUPPORTED, "Hq/Hkv = %d (supported: 1, 2, 4)", g);
+  if (c.window > (1 << 20) || c.cache > (1 << 20))
+    return fail(LOLA_ERR_UNSUPPORTED, "window or cache too large");
+  if (decode_lds_bytes(c.cache, c.window, c.head_dim, g, c.dtype == LOLA_DTYPE_F32) > kMaxLds)
+    return fail(LOLA_ERR_UNSUPPORTED, "window + cache too large for the decode kernel's LDS");
+
+  lola_state* st = new lola_state();
+  memset(st, 0, sizeof *st);
+  st->cfg = c;
+  st->U = c.batch * c.kv_heads;
+  st->g = g;
+  st->d = c.head_dim;
+  st->f32 = c.dtype == LOLA_DTYPE_F32;
+  st->esz = st->f32 ? 4 : 2;
+  st->last = (hipStream_t)stream;
+  hipGetDevice(&st->device);
+  const size_t U = st->U, d = st->d, lam = c.cache, eta = c.window;
+  auto alloc = [&](void** p, size_t bytes) -> bool {
+    if (bytes == 0) bytes = 256;
+    return hipMalloc(p, bytes) == hipSuccess;
+  };
+  bool ok = alloc((void**)&st->H, U * kD * d * 4) && alloc((void**)&st->s, U * kD * 4) &&
+            alloc(&st->ring_k, U * eta * d * st->esz) && alloc(&st->ring_v, U * eta * d * st->esz) &&
+            alloc(&st->W, (size_t)c.kv_heads * d * kM * st->esz);
+  for (int b = 0; b < 2 && ok; ++b)
+    ok = alloc(&st->cache_k[b], U * lam * d * st->esz) &&
+         alloc(&st->cache_v[b], U * lam * d * st->esz) &&
+         alloc((void**)&st->cache_pos[b], U * (lam ? lam : 1) * 4);
+  if (!ok) {
+    lola_state_free(st);
+    return fail(LOLA_ERR_OUT_OF_MEMORY, "hipMalloc failed for the state");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemsetAsync(st->H, 0, U * kD * d * 4, s);
+  if (e == hipSuccess) e = hipMemsetAsync(st->s, 0, U * kD * 4, s);
+  for (int b = 0; b < 2 && e == hipSuccess; ++b)
+    e = hipMemsetAsync(st->cache_pos[b], 0xFF, U * (lam ? lam : 1) * 4, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(st->W, W, (size_t)c.kv_heads * d * kM * st->esz, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) {
+    lola_state_free(st);
+    return fail(LOLA_ERR_HIP, "state initialisation: %s", hipGetErrorString(e));
+  }
+  *out = st;
+  return LOLA_OK;
+}
+
+int lola_state_free(lola_state* st) {
+  if (!st) return LOLA_OK;
+  hipStreamSynchronize(st->last);
+  void* ps[] = {st->H, st->s, st->ring_k, st->ring_v, st->W, st->own_ws,
+                st->cache_k[0], st->cache_k[1], st->cache_v[0], st->cache_v[1],
+                st->cache_pos[0], st->cache_pos[1]};
+  for (void* p : ps)
+    if (p) hipFree(p);
+  delete st;
+  return LOLA_OK;
+}
+
+int64_t lola_state_tokens(const lola_state* st) { return st ? st->n : -1; }
+
+int lola_prefill_workspace_bytes(const lola_state* st, int T, int C, size_t* bytes) {
+  if (!st || !bytes) return fail(LOLA_ERR_INVALID_ARG, "state and bytes must be non-NULL");
+  if (T < 0 || C < 1) return fail(LOLA_ERR_INVALID_ARG, "T >= 0 and C >= 1 required");
+  *bytes = (T == 0 || C == 1) ? 0 : ws_layout(st, T, C).total;
+  return LOLA_OK;
+}
+
+int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v, void* out,
+                     int out_dtype, void* stream) {
+  int rc = check_state(st);
+  if (rc) return rc;
+  if (!q || !k || !v || !out) return fail(LOLA_ERR_INVALID_ARG, "q, k, v, out must be non-NULL");
+  if (out_dtype != LOLA_DTYPE_F32) return fail(LOLA_ERR_UNSUPPORTED, "out_dtype must be F32");
+  if (st->n > (int64_t)0x7FFFFFF0) return fail(LOLA_ERR_UNSUPPORTED, "position overflow");
+  hipStream_t s = (hipStream_t)stream;
+  DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.W = st->W;
+  a.H = st->H; a.s = st->s;
+  a.ring_k = st->ring_k; a.ring_v = st->ring_v;
+  a.cache_k = st->cache_k[st->cur]; a.cache_v = st->cache_v[st->cur];
+  a.cache_pos = st->cache_pos[st->cur];
+  a.out = (float*)out;
+  a.n = st->n;
+  a.lam = st->cfg.cache; a.eta = st->cfg.window; a.d = st->d; a.g = st->g;
+  a.Hkv = st->cfg.kv_heads;
+  a.q_su = (long long)st->g * st->d; a.q_sh = st->d; a.kv_su = st->d;
+  a.o_su = (long long)st->g * st->d; a.o_sh = st->d;
+  hipError_t e = launch_decode(a, st->U, st->f32, s);
+  if (e != hipSuccess) return hip_fail(st, e, "decode launch");
+  st->last = s;
+  st->n += 1;
+  return LOLA_OK;
+}
+
+static int prefill_impl(lola_state* st, const void* q, const void* k, const void* v, int T,
+                        int C, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                        int32_t* snap_pos, uint64_t* cand_keys, void* stream) {
+  int rc = check_state(st);
+  if (rc) return rc;
+  if (T < 0 || C < 1) return fail(LOLA_ERR_INVALID_ARG, "T >= 0 and C >= 1 required");
+  if (T == 0) return LOLA_OK;
+  if (!q || !k || !v || !out) return fail(LOLA_ERR_INVALID_ARG, "q, k, v, out must be non-NULL");
+  if (out_dtype != LOLA_DTYPE_F32) return fail(LOLA_ERR_UNSUPPORTED, "out_dtype must be F32");
+  if ((rc = supported_C(st, C))) return rc;
+  if (st->n + T > (int64_t)0x7FFFFFF0) return fail(LOLA_ERR_UNSUPPORTED, "position overflow");
+  const size_t NVs = (size_t)st->cfg.cache + st->cfg.window + T;
+  if (NVs > (size_t)0x7FFFFFF0) return fail(LOLA_ERR_UNSUPPORTED, "T too large");
+  hipStream_t s = (hipStream_t)stream;
+  const int U = st->U, d = st->d, g = st->g;
+
+  if (C == 1) {
+    // token by token through the decode kernel, reading strided slices of
+    // q [U, g, T, d], k / v [U, T, d] and writing out [U, g, T, d]
+    DecodeArgs a;
+    a.W = st->W; a.H = st->H; a.s = st->s;
+    a.ring_k = st->ring_k; a.ring_v = st->ring_v;
+    a.cache_k = st->cache_k[st->cur]; a.cache_v = st->cache_v[st->cur];
+    a.cache_pos = st->cache_pos[st->cur];
+    a.lam = st->cfg.cache; a.eta = st->cfg.window; a.d = d; a.g = g;
+    a.Hkv = st->cfg.kv_heads;
+    a.q_su = (long long)g * T * d; a.q_sh = (long long)T * d; a.kv_su = (long long)T * d;
+    a.o_su = a.q_su; a.o_sh = a.q_sh;
+    for (int t = 0; t < T; ++t) {
+      a.q = (const char*)q + (size_t)t * d * st->esz;
+      a.k = (const char*)k + (size_t)t * d * st->esz;
+      a.v = (const char*)v + (size_t)t * d * st->esz;
+      a.out = (float*)out + (size_t)t * d;
+      a.n = st->n;
+      hipError_t e = launch_decode(a, U, st->f32, s);
+      if (e != hipSuccess) return hip_fail(st, e, "decode launch");
+      st->n += 1;
+    }
+    st->last = s;
+    return LOLA_OK;
+  }
+
+  const WsLayout L = ws_layout(st, T, C);
+  char* base = (char*)ws;
+  if (!base) {
+    if (st->own_ws_bytes < L.total) {
+      hipStreamSynchronize(st->last);
+      hipStreamSynchronize(s);
+      if (st->own_ws) hipFree(st->own_ws);
+      st->own_ws = nullptr;
+      st->own_ws_bytes = 0;
+      if (hipMalloc(&st->own_ws, L.total) != hipSuccess)
+        return fail(LOLA_ERR_OUT_OF_MEMORY, "workspace of %zu bytes", L.total);
+      st->own_ws_bytes = L.total;
+    }
+    base = (char*)st->own_ws;
+  } else if (ws_bytes < L.total) {
+    return fail(LOLA_ERR_WORKSPACE, "workspace %zu < required %zu bytes", ws_bytes, L.total);
+  }
+
+  const int lam = st->cfg.cache, eta = st->cfg.window;
+  const int nch = (T + C - 1) / C;
+  VirtRows vr;
+  vr.cache_k = st->cache_k[st->cur];
+  vr.cache_v = st->cache_v[st->cur];
+  vr.cache_pos = st->cache_pos[st->cur];
+  vr.ring_k = st->ring_k;
+  vr.ring_v = st->ring_v;
+  vr.in_k = k;
+  vr.in_v = v;
+  vr.n0 = st->n;
+  vr.lam = lam;
+  vr.eta = eta;
+  vr.T = T;
+  vr.d = d;
+  const int gs0 = (int)std::min<int64_t>(lam, std::max<int64_t>(0, st->n - eta));
+  const long long nend = st->n + T;
+  const int gs_final = (int)std::min<long long>(lam, std::max<long long>(0, nend - eta));
+
+  uint16_t* phi_hi = (uint16_t*)(base + L.phi_hi);
+  uint16_t* phi_lo = (uint16_t*)(base + L.phi_lo);
+
+  PhiArgs pa;
+  pa.vr = vr; pa.W = st->W; pa.phi_hi = phi_hi; pa.phi_lo = phi_lo;
+  pa.NV = (int)NVs; pa.Hkv = st->cfg.kv_heads; pa.gs0 = gs0;
+  hipError_t e = launch_phi(pa, U, st->f32, s);
+  if (e != hipSuccess) return hip_fail(st, e, "phi launch");
+
+  ChainArgs ca;
+  ca.vr = vr; ca.phi_hi = phi_hi; ca.phi_lo = phi_lo;
+  ca.H = st->H; ca.s = st->s;
+  ca.snapHT = (uint16_t*)(base + L.snapHT);
+  ca.snaps = (float*)(base + L.snaps);
+  ca.snapG = (int32_t*)(base + L.snapG);
+  ca.finalG = (int32_t*)(base + L.finalG);
+  ca.NV = (int)NVs; ca.nch = nch; ca.C = C; ca.dbg_keys = cand_keys;
+  e = launch_chain(ca, U, st->f32, s);
+  if (e != hipSuccess) return hip_fail(st, e, "chain launch");
+  if (snap_pos) {
+    e = launch_snappos(vr, ca.snapG, snap_pos, nch, C, U, s);
+    if (e != hipSuccess) return hip_fail(st, e, "debug launch");
+  }
+
+  AttnArgs aa;
+  aa.vr = vr; aa.q = q; aa.W = st->W;
+  aa.snapHT = ca.snapHT; aa.snaps = ca.snaps; aa.snapG = ca.snapG;
+  aa.out = (float*)out;
+  aa.g = g; aa.Hkv = st->cfg.kv_heads; aa.nch = nch; aa.C = C;
+  aa.ptile = std::min(C, 128 / g);
+  aa.nblk = aa.ptile / 32;
+  e = launch_attn(aa, U, st->f32, s);
+  if (e != hipSuccess) return hip_fail(st, e, "attention launch");
+
+  FinalizeArgs fa;
+  fa.vr = vr;
+  fa.finalG = ca.finalG;
+  fa.new_cache_k = st->cache_k[1 - st->cur];
+  fa.new_cache_v = st->cache_v[1 - st->cur];
+  fa.new_cache_pos = st->cache_pos[1 - st->cur];
+  fa.ring_k = st->ring_k;
+  fa.ring_v = st->ring_v;
+  fa.gs_final = gs_final;
+  e = launch_finalize(fa, U, st->f32, s);
+  if (e != hipSuccess) return hip_fail(st, e, "finalize launch");
+  st->cur = 1 - st->cur;
+  st->n = nend;
+  st->last = s;
+  return LOLA_OK;
+}
+
+int lola_prefill_chunk(lola_state* st, const void* q, const void* k, const void* v, int T,
+                       int C, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                       void* stream) {
+  return prefill_impl(st, q, k, v, T, C, out, out_dtype, ws, ws_bytes, nullptr, nullptr, stream);
+}
+
+int lola_prefill_debug(lola_state* st, const void* q, const void* k, const void* v, int T,
+                       int C, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                       int32_t* snap_pos, uint64_t* cand_keys, void* stream) {
+  if (C == 1 && (snap_pos || cand_keys))
+    return fail(LOLA_ERR_UNSUPPORTED, "debug export needs C > 1");
+  return prefill_impl(st, q, k, v, T, C, out, out_dtype, ws, ws_bytes, snap_pos, cand_keys,
+                      stream);
+}
+
+int lola_state_export(const lola_state* st, lola_state_view* dst, void* stream) {
+  if (!st || !dst || !dst->H || !dst->s || !dst->win_k || !dst->win_v || !dst->cache_pos ||
+      !dst->cache_k || !dst->cache_v)
+    return fail(LOLA_ERR_INVALID_ARG, "state and every view pointer must be non-NULL");
+  hipStream_t s = (hipStream_t)stream;
+  const size_t U = st->U, d = st->d;
+  const int lam = st->cfg.cache, eta = st->cfg.window;
+  const int gs = (int)std::min<int64_t>(lam, std::max<int64_t>(0, st->n - eta));
+  hipError_t e = hipMemcpyAsync(dst->H, st->H, U * kD * d * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(dst->s, st->s, U * kD * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = launch_export(st->f32, st->U, st->ring_k, st->ring_v, st->cache_k[st->cur],
+                      st->cache_v[st->cur], st->cache_pos[st->cur], dst->win_k, dst->win_v,
+                      dst->cache_k, dst->cache_v, dst->cache_pos, st->n, eta, lam, gs, st->d, s);
+  if (e != hipSuccess) return fail(LOLA_ERR_HIP, "export: %s", hipGetErrorString(e));
+  dst->n = st->n;
+  return LOLA_OK;
+}
+
+int lola_state_import(lola_state* st, const lola_state_view* src, void* stream) {
+  if (!st || !src || !src->H || !src->s || !src->win_k || !src->win_v || !src->cache_pos ||
+      !src->cache_k || !src->cache_v)
+    return fail(LOLA_ERR_INVALID_ARG, "state and every view pointer must be non-NULL");
+  if (src->n < 0 || src->n > (int64_t)0x7FFFFFF0) return fail(LOLA_ERR_STATE, "bad n");
+  hipStream_t s = (hipStream_t)stream;
+  const size_t U = st->U, d = st->d;
+  const int lam = st->cfg.cache, eta = st->cfg.window;
+  const int gs = (int)std::min<int64_t>(lam, std::max<int64_t>(0, src->n - eta));
+  const int64_t w = std::min<int64_t>(eta, src->n);
+  if (lam > 0) {
+    std::vector<int32_t> pos(U * lam);
+    hipError_t e = hipMemcpyAsync(pos.data(), src->cache_pos, U * lam * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(LOLA_ERR_HIP, "import: %s", hipGetErrorString(e));
+    for (size_t u = 0; u < U; ++u)
+      for (int i = 0; i < gs; ++i) {
+        const int32_t p = pos[u * lam + i];
+        if (p < 0 || p >= src->n - w || (i > 0 && p <= pos[u * lam + i - 1]))
+          return fail(LOLA_ERR_STATE, "import: cache positions of unit %zu are not ascending "
+                      "and older than the window", u);
+      }
+  }
+  hipError_t e = hipMemcpyAsync(st->H, src->H, U * kD * d * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(st->s, src->s, U * kD * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = launch_import(st->f32, st->U, st->ring_k, st->ring_v, st->cache_k[st->cur],
+                      st->cache_v[st->cur], st->cache_pos[st->cur], src->win_k, src->win_v,
+                      src->cache_k, src->cache_v, src->cache_pos, src->n, eta, lam, gs, st->d, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(LOLA_ERR_HIP, "import: %s", hipGetErrorString(e));
+  st->n = src->n;
+  st->poisoned = false;
+  st->last = s;
+  return LOLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,351 @@
+// K3: the read of every chunk, LoLA notes §2.5, Eq. (14):
+//
+//   y_t = (H_j^T phi(q_t) + sum_{i in V(t)} a_ti v_i)
+//         / (phi(q_t)^T s_j + sum_{i in V(t)} a_ti),   a_ti = exp(q_t.k_i / sqrt(d)),
+//
+// V(t) = G_j (cache at chunk start) plus the local positions
+// max(0, n_j - eta) .. t (window and the causal prefix of the chunk).  All
+// chunks run in parallel: they only need the per-chunk snapshots (H_j, s_j,
+// G_j) written by the chain kernel.
+//
+// One workgroup = one unit, one chunk, and up to 4 waves; wave = one q-head
+// x 32 positions (the GQA heads of a unit share every K/V tile).  Scores are
+// computed transposed, S^T = K Q^T (32 keys x 32 queries), so each lane owns
+// one query and softmax statistics need a single cross-half exchange; P then
+// feeds O^T += V^T P^T straight from registers (the K index of that MFMA is
+// permuted to match the result layout, see common.h).
+//
+// Exponentials are unshifted in Eq. (14); here they are shifted by a running
+// maximum m >= 0 (log2 domain) and the linear terms are scaled by the same
+// 2^{-m}:  y = (2^-m N_lin + sum 2^{x-m} v) / (2^-m z_lin + sum 2^{x-m}),
+// which is the same quantity.  The linear read is done first with m = 0.
+//
+// Precision: q.k is exact-product bf16 MFMA with fp32 accumulation; P and V
+// go through fp16 MFMA (11-bit significand, P in [0, 1]); the linear read
+// uses the hi/lo bf16 split on both phi(q) and H.  fp32 inputs split every
+// operand into hi/lo fp16 (three passes, ~2^-22 per product).
+#include "internal.h"
+
+namespace lola {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int HTH = kM + 8;  // padded row of one half of H^T in LDS
+constexpr int KTP = 32 + 8;  // padded row of V^T tile
+
+struct AttnSmem {
+  uint16_t* WT_hi;   // [kM][d + 8]
+  uint16_t* WT_lo;
+  uint16_t* HT_hi;   // [d][HTH]   (one feature half at a time)
+  uint16_t* HT_lo;
+  float* s;          // [kD]
+  // key phase (aliases the region above)
+  uint16_t* K_hi;    // [32][d + 8]
+  uint16_t* K_lo;
+  uint16_t* VT_a;    // [d][KTP]  fp16 (bf16 inputs) or fp16 hi (fp32 inputs)
+  uint16_t* VT_b;    //           fp16 lo (fp32 inputs)
+};
+
+inline __host__ __device__ size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+// Carves both phases from the start of dynamic LDS; returns the larger size.
+__host__ __device__ inline size_t carve(int d, bool f32, unsigned char* base, AttnSmem* sm) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> unsigned char* {
+    unsigned char* p = base + off;
+    off = al16(off + bytes);
+    return p;
+  };
+  AttnSmem t;
+  t.WT_hi = (uint16_t*)take((size_t)kM * (d + 8) * 2);
+  t.WT_lo = (uint16_t*)take(f32 ? (size_t)kM * (d + 8) * 2 : 16);
+  t.HT_hi = (uint16_t*)take((size_t)d * HTH * 2);
+  t.HT_lo = (uint16_t*)take((size_t)d * HTH * 2);
+  t.s = (float*)take(kD * 4);
+  const size_t phaseA = off;
+  off = 0;
+  t.K_hi = (uint16_t*)take((size_t)32 * (d + 8) * 2);
+  t.K_lo = (uint16_t*)take(f32 ? (size_t)32 * (d + 8) * 2 : 16);
+  t.VT_a = (uint16_t*)take((size_t)d * KTP * 2);
+  t.VT_b = (uint16_t*)take(f32 ? (size_t)d * KTP * 2 : 16);
+  const size_t phaseB = off;
+  if (sm) *sm = t;
+  return phaseA > phaseB ? phaseA : phaseB;
+}
+
+__device__ __forceinline__ u32x2 ld8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// operand with K-slots sigma_h: elements [4h, 4h+4) and [8+4h, 8+4h+4) of a 16-block
+__device__ __forceinline__ u32x4 sigma_load(const uint16_t* row16, int h) {
+  u32x2 a = ld8(row16 + 4 * h), b = ld8(row16 + 8 + 4 * h);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+}  // namespace
+
+size_t attn_lds_bytes(int d, bool f32) {
+  static unsigned char dummy[1];
+  return carve(d, f32, dummy, nullptr);
+}
+
+template <class DT>
+__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
+  using T = typename DT::T;
+  const VirtRows& vr = a.vr;
+  const int d = vr.d, lam = vr.lam, eta = vr.eta;
+  const int pt = blockIdx.x, j = blockIdx.y, u = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, r = lane & 31;
+  const int kvh = u % a.Hkv;
+  const long long n0 = vr.n0;
+  const long long nj = n0 + (long long)j * a.C;
+  const int cj = min(a.C, vr.T - j * a.C);
+  const long long pbase = nj + (long long)pt * a.ptile;
+  const long long pend = min(pbase + a.ptile, nj + cj);     // exclusive
+  if (pbase >= pend) return;                                // whole block idle (uniform)
+  const int hd = wave / a.nblk, pblk = wave % a.nblk;
+  const long long p0 = pbase + 32LL * pblk;
+  const bool wactive = hd < a.g && p0 < pend;
+  const long long qpos = p0 + r;
+  const bool qvalid = wactive && qpos < pend;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  AttnSmem sm;
+  carve(d, DT::kSplit, smem, &sm);
+
+  // ---- W^T of this KV head and s_j into LDS
+  const T* W = reinterpret_cast<const T*>(a.W) + (size_t)kvh * d * kM;
+  for (int i = tid; i < d * kM; i += kThreads) {
+    const int k = i / kM, f = i % kM;
+    uint32_t hi, lo;
+    DT::split(DT::to_f32(W[i]), hi, lo);
+    sm.WT_hi[f * (d + 8) + k] = (uint16_t)hi;
+    if (DT::kSplit) sm.WT_lo[f * (d + 8) + k] = (uint16_t)lo;
+  }
+  const float* sj = a.snaps + ((size_t)u * a.nch + j) * kD;
+  for (int F = tid; F < kD; F += kThreads) sm.s[F] = sj[F];
+
+  // ---- Q operands (B of S^T = K Q^T): lane = query r, K-slots 8h .. 8h+7
+  u32x4 qh[8], ql[8];
+  {
+    const T* qrow = reinterpret_cast<const T*>(a.q) +
+                    (((size_t)u * a.g + (wactive ? hd : 0)) * vr.T + (size_t)(qvalid ? qpos - n0 : 0)) * d;
+    for (int kb = 0; kb < d / 16; ++kb) {
+      const int k0 = 16 * kb + 8 * h;
+      if constexpr (DT::kSplit) {
+        float x[8];
+        if (qvalid) load8_f32(qrow + k0, x);
+        else for (int q = 0; q < 8; ++q) x[q] = 0.f;
+        splitop<DT>(x, qh[kb], ql[kb]);
+      } else {
+        qh[kb] = qvalid ? ld16(reinterpret_cast<const uint16_t*>(qrow) + k0) : u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phi(q): u^T = W^T q^T (64 features x 32 queries)
+  float ph[2][2][16];   // [half pos/neg][mt][i]: feature 64*half + 32*mt + 8(i/4) + 4h + (i%4)
+  float zlin = 0.f;
+  {
+    f32x16 acc[2];
+    for (int mt = 0; mt < 2; ++mt) for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+    if (wactive) {
+      for (int kb = 0; kb < d / 16; ++kb) {
+        const int k0 = 16 * kb + 8 * h;
+        for (int mt = 0; mt < 2; ++mt) {
+          const int f = 32 * mt + r;
+          const u32x4 ah = ld16(sm.WT_hi + f * (d + 8) + k0);
+          acc[mt] = DT::mma(ah, qh[kb], acc[mt]);
+          if constexpr (DT::kSplit) {
+            const u32x4 al = ld16(sm.WT_lo + f * (d + 8) + k0);
+            acc[mt] = DT::mma(ah, ql[kb], acc[mt]);
+            acc[mt] = DT::mma(al, qh[kb], acc[mt]);
+          }
+        }
+      }
+    }
+    float mx = -INFINITY, mn = INFINITY;
+    for (int mt = 0; mt < 2; ++mt)
+      for (int i = 0; i < 16; ++i) { mx = fmaxf(mx, acc[mt][i]); mn = fminf(mn, acc[mt][i]); }
+    mx = fmaxf(mx, xor32(mx));
+    mn = fminf(mn, xor32(mn));
+    float sp = 0.f, sn = 0.f;
+    for (int mt = 0; mt < 2; ++mt)
+      for (int i = 0; i < 16; ++i) {
+        ph[0][mt][i] = expf(acc[mt][i] - mx);
+        ph[1][mt][i] = expf(mn - acc[mt][i]);
+        sp += ph[0][mt][i];
+        sn += ph[1][mt][i];
+      }
+    sp += xor32(sp);
+    sn += xor32(sn);
+    const float ip = 1.f / sp, in_ = 1.f / sn;
+    for (int mt = 0; mt < 2; ++mt)
+      for (int i = 0; i < 16; ++i) {
+        ph[0][mt][i] *= ip;
+        ph[1][mt][i] *= in_;
+        const int f = 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+        zlin = fmaf(ph[0][mt][i], sm.s[f], zlin);
+        zlin = fmaf(ph[1][mt][i], sm.s[kM + f], zlin);
+      }
+    zlin += xor32(zlin);
+  }
+
+  // ---- linear read N_lin^T = H_j^T phi^T into the output accumulator
+  f32x16 O[4];
+  for (int mt = 0; mt < 4; ++mt) for (int i = 0; i < 16; ++i) O[mt][i] = 0.f;
+  const int nmt = d / 32;
+  const uint16_t* snap = a.snapHT + ((size_t)u * a.nch + j) * 2 * d * kD;
+  for (int half = 0; half < 2; ++half) {
+    __syncthreads();
+    for (int i = tid; i < 2 * d * (kM / 8); i += kThreads) {
+      const int pl = i / (d * (kM / 8)), rem = i % (d * (kM / 8));
+      const int row = rem / (kM / 8), col = (rem % (kM / 8)) * 8;
+      *reinterpret_cast<u32x4*>((pl ? sm.HT_lo : sm.HT_hi) + row * HTH + col) =
+          *reinterpret_cast<const u32x4*>(snap + (size_t)pl * d * kD + (size_t)row * kD + kM * half + col);
+    }
+    __syncthreads();
+    if (wactive) {
+      for (int kb = 0; kb < kM / 16; ++kb) {
+        const int mt = kb >> 1, i0 = 8 * (kb & 1);
+        u32x4 bh, bl;
+        splitop<DT>(&ph[half][mt][i0], bh, bl);
+        for (int mo = 0; mo < nmt; ++mo) {
+          const int row = 32 * mo + r;
+          const u32x4 ah = sigma_load(sm.HT_hi + row * HTH + 16 * kb, h);
+          const u32x4 al = sigma_load(sm.HT_lo + row * HTH + 16 * kb, h);
+          O[mo] = DT::mma(ah, bh, O[mo]);
+          O[mo] = DT::mma(ah, bl, O[mo]);
+          O[mo] = DT::mma(al, bh, O[mo]);
+        }
+      }
+    }
+  }
+
+  // ---- explicit branch: cache G_j, then local positions lo_j .. pend-1
+  float m2 = 0.f, l = zlin;
+  const float scale2 = 1.4426950408889634f / sqrtf((float)d);
+  const int gsj = (int)min((long long)lam, max(0LL, nj - eta));
+  const long long lo_j = max(0LL, nj - eta);
+  const int nkeys = gsj + (int)(pend - lo_j);
+  const int32_t* Gj = a.snapG + ((size_t)u * a.nch + j) * lam;
+  for (int t0 = 0; t0 < nkeys; t0 += 32) {
+    __syncthreads();
+    for (int i = tid; i < 32 * (d / 8); i += kThreads) {
+      const int kl = i / (d / 8), cc = (i % (d / 8)) * 8;
+      const int kk = t0 + kl;
+      float kv[8], vv[8];
+      if (kk < nkeys) {
+        const int vi = kk < gsj ? Gj[kk] : lam + eta + (int)(lo_j + (kk - gsj) - n0);
+        load8_f32(reinterpret_cast<const T*>(vr.krow(u, vi, sizeof(T))) + cc, kv);
+        load8_f32(reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))) + cc, vv);
+      } else {
+        for (int q = 0; q < 8; ++q) { kv[q] = 0.f; vv[q] = 0.f; }
+      }
+      u32x4 kh, kl8;
+      splitop<DT>(kv, kh, kl8);
+      *reinterpret_cast<u32x4*>(sm.K_hi + kl * (d + 8) + cc) = kh;
+      if constexpr (DT::kSplit) {
+        *reinterpret_cast<u32x4*>(sm.K_lo + kl * (d + 8) + cc) = kl8;
+        for (int q = 0; q < 8; ++q) {
+          uint32_t hi, lo;
+          DT::split(vv[q], hi, lo);
+          sm.VT_a[(cc + q) * KTP + kl] = (uint16_t)hi;
+          sm.VT_b[(cc + q) * KTP + kl] = (uint16_t)lo;
+        }
+      } else {
+        for (int q = 0; q < 8; ++q)
+          sm.VT_a[(cc + q) * KTP + kl] = __builtin_bit_cast(uint16_t, (_Float16)vv[q]);
+      }
+    }
+    __syncthreads();
+    if (!wactive) continue;
+    f32x16 S;
+    for (int i = 0; i < 16; ++i) S[i] = 0.f;
+    for (int kb = 0; kb < d / 16; ++kb) {
+      const int k0 = 16 * kb + 8 * h;
+      const u32x4 ah = ld16(sm.K_hi + r * (d + 8) + k0);
+      S = DT::mma(ah, qh[kb], S);
+      if constexpr (DT::kSplit) {
+        const u32x4 al = ld16(sm.K_lo + r * (d + 8) + k0);
+        S = DT::mma(ah, ql[kb], S);
+        S = DT::mma(al, qh[kb], S);
+      }
+    }
+    float tmax = -INFINITY;
+    for (int i = 0; i < 16; ++i) {
+      const int kk = t0 + 8 * (i >> 2) + 4 * h + (i & 3);
+      bool ok = kk < nkeys;
+      if (ok && kk >= gsj) ok = lo_j + (kk - gsj) <= qpos;   // causal (diagonal included)
+      S[i] = ok ? S[i] * scale2 : -INFINITY;
+      tmax = fmaxf(tmax, S[i]);
+    }
+    tmax = fmaxf(tmax, xor32(tmax));
+    const float mnew = fmaxf(m2, tmax);
+    if (mnew > m2) {
+      const float alpha = exp2f(m2 - mnew);
+      for (int mt = 0; mt < nmt; ++mt) for (int i = 0; i < 16; ++i) O[mt][i] *= alpha;
+      l *= alpha;
+      m2 = mnew;
+    }
+    float rs = 0.f;
+    for (int i = 0; i < 16; ++i) { S[i] = exp2f(S[i] - m2); rs += S[i]; }
+    rs += xor32(rs);
+    l += rs;
+    for (int kb = 0; kb < 2; ++kb) {
+      if constexpr (DT::kSplit) {
+        u32x4 ph8, pl8;
+        float pv[8];
+        for (int q = 0; q < 8; ++q) pv[q] = S[8 * kb + q];
+        splitop<DT>(pv, ph8, pl8);
+        for (int mo = 0; mo < nmt; ++mo) {
+          const int row = 32 * mo + r;
+          const u32x4 vh = sigma_load(sm.VT_a + row * KTP + 16 * kb, h);
+          const u32x4 vl = sigma_load(sm.VT_b + row * KTP + 16 * kb, h);
+          O[mo] = DT::mma(vh, ph8, O[mo]);
+          O[mo] = DT::mma(vh, pl8, O[mo]);
+          O[mo] = DT::mma(vl, ph8, O[mo]);
+        }
+      } else {
+        f16x8 p8;
+        for (int q = 0; q < 8; ++q) p8[q] = (_Float16)S[8 * kb + q];
+        for (int mo = 0; mo < nmt; ++mo) {
+          const int row = 32 * mo + r;
+          f16x8 vh = __builtin_bit_cast(f16x8, sigma_load(sm.VT_a + row * KTP + 16 * kb, h));
+          O[mo] = mfma_f16(vh, p8, O[mo]);
+        }
+      }
+    }
+  }
+
+  // ---- y = O / l
+  if (!qvalid) return;
+  const float il = 1.f / l;
+  float* orow = a.out + (((size_t)u * a.g + hd) * vr.T + (size_t)(qpos - n0)) * d;
+  for (int mo = 0; mo < nmt; ++mo)
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int cc = 32 * mo + 8 * g4 + 4 * h;
+      f32x4 y;
+      for (int q = 0; q < 4; ++q) y[q] = O[mo][4 * g4 + q] * il;
+      *reinterpret_cast<f32x4*>(orow + cc) = y;
+    }
+}
+
+hipError_t launch_attn(const AttnArgs& a, int U, bool f32, hipStream_t st) {
+  if (U <= 0 || a.nch <= 0) return hipSuccess;
+  const int nptile = (a.C + a.ptile - 1) / a.ptile;
+  dim3 grid(nptile, a.nch, U);
+  size_t lds = attn_lds_bytes(a.vr.d, f32);
+  if (f32) {
+    (void)hipFuncSetAttribute((const void*)attn_kernel<F32>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(attn_kernel<F32>, grid, dim3(kThreads), lds, st, a);
+  } else {
+    (void)hipFuncSetAttribute((const void*)attn_kernel<BF16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(attn_kernel<BF16>, grid, dim3(kThreads), lds, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lola

@@ -1,0 +1,180 @@
+// Shared device helpers for the LoLA HIP kernels (gfx950 / CDNA4).
+//
+// MFMA conventions used throughout (checked on the device by a layout probe):
+//   v_mfma_f32_32x32x16_{bf16,f16}: A is 32 x 16 (M x K), B is 16 x 32 (K x N).
+//     Lane l supplies row/column (l % 32) and 8 K-values; half h = l / 32
+//     supplies the K-slots of its half.  Output lane l holds column (l % 32)
+//     and rows 8*(i/4) + 4*h + (i%4), i = 0..15.
+// Because a contraction may permute its K index freely (as long as A and B
+// agree), a C-layout result can feed the next MFMA directly: within a 16-wide
+// K-block the lane's K-slots are then
+//     sigma_h(j) = 4h + j (j < 4),  8 + 4h + (j - 4) (j >= 4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lola {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ f32x16 mfma_bf16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// ---- scalar conversions -------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+// round-to-nearest-even fp32 -> bf16 bits (finite inputs)
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ __bf16 bits_to_bf16(uint32_t b) {
+  return __builtin_bit_cast(__bf16, (uint16_t)b);
+}
+// x = hi + lo with hi, lo bf16; |x - hi - lo| <= 2^-16 |x|
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  hi = f32_to_bf16_bits(x);
+  lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+
+// Pack 8 bf16 bit patterns held as uint32 (low 16 bits) into an operand.
+__device__ __forceinline__ bf16x8 pack_bf16x8(const uint32_t* b) {
+  u32x4 w;
+  w[0] = b[0] | (b[1] << 16);
+  w[1] = b[2] | (b[3] << 16);
+  w[2] = b[4] | (b[5] << 16);
+  w[3] = b[6] | (b[7] << 16);
+  return __builtin_bit_cast(bf16x8, w);
+}
+// Split 8 floats into hi and lo bf16 operands.
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) split_bf16(x[j], h[j], l[j]);
+  hi = pack_bf16x8(h);
+  lo = pack_bf16x8(l);
+}
+
+// x = hi + lo with hi, lo fp16; |x - hi - lo| <= 2^-22 |x| for |x| in the
+// fp16 normal range (absolute error <= 2^-25 below it); |x| < 65504 required.
+__device__ __forceinline__ void split_f16(float x, uint32_t& hi, uint32_t& lo) {
+  _Float16 h = (_Float16)x;
+  _Float16 l = (_Float16)(x - (float)h);
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, l);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+__device__ __forceinline__ u32x4 pack8(const uint32_t* b) {
+  u32x4 w;
+  w[0] = b[0] | (b[1] << 16);
+  w[1] = b[2] | (b[3] << 16);
+  w[2] = b[4] | (b[5] << 16);
+  w[3] = b[6] | (b[7] << 16);
+  return w;
+}
+
+// ---- element types of the inputs --------------------------------------
+// The tag fixes the storage dtype and the 16-bit format that fp32 quantities
+// are split into for MFMA (x = hi + lo, products hi*hi + hi*lo + lo*hi):
+//  * BF16 inputs: inputs are exact in one bf16 operand; fp32 quantities
+//    (phi, H, s) split into bf16 hi/lo (full fp32 range, ~2^-16 per product).
+//  * F32 inputs: every operand splits into fp16 hi/lo (~2^-22 per product,
+//    magnitudes below 65504).
+struct BF16 {
+  using T = uint16_t;
+  static constexpr bool kSplit = false;     // inputs are exact in one pass
+  __device__ static __forceinline__ float to_f32(T x) { return bf16_bits_to_f32(x); }
+  __device__ static __forceinline__ void split(float x, uint32_t& hi, uint32_t& lo) {
+    split_bf16(x, hi, lo);
+  }
+  __device__ static __forceinline__ float from_bits(uint32_t b) { return bf16_bits_to_f32(b); }
+  __device__ static __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c);
+  }
+};
+struct F32 {
+  using T = float;
+  static constexpr bool kSplit = true;      // inputs need hi + lo
+  __device__ static __forceinline__ float to_f32(T x) { return x; }
+  __device__ static __forceinline__ void split(float x, uint32_t& hi, uint32_t& lo) {
+    split_f16(x, hi, lo);
+  }
+  __device__ static __forceinline__ float from_bits(uint32_t b) { return f16_bits_to_f32(b); }
+  __device__ static __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
+    return mfma_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c);
+  }
+};
+
+// Split 8 floats into hi and lo operands in the tag's 16-bit format.
+template <class DT>
+__device__ __forceinline__ void splitop(const float* x, u32x4& hi, u32x4& lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) DT::split(x[j], h[j], l[j]);
+  hi = pack8(h);
+  lo = pack8(l);
+}
+__device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Load 8 consecutive input elements as float.
+__device__ __forceinline__ void load8_f32(const uint16_t* p, float* o) {
+  u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o[2 * j] = __uint_as_float(w[j] << 16);
+    o[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void load8_f32(const float* p, float* o) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { o[j] = a[j]; o[4 + j] = b[j]; }
+}
+// Load 8 consecutive bf16 input elements directly as an operand.
+__device__ __forceinline__ bf16x8 load8_bf16op(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+// ---- wave reductions ---------------------------------------------------
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+// inclusive prefix sum over the wave
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+}  // namespace lola

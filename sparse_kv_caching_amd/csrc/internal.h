@@ -1,0 +1,151 @@
+// Internal interfaces between the C-ABI host runtime and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace lola {
+
+// Feature-map width: phi(x) = [softmax(x W), softmax(-x W)], W is d x kM.
+constexpr int kM = 64;
+constexpr int kD = 2 * kM;
+
+// ---------------------------------------------------------------------------
+// Virtual row space of one prefill call, per unit u = b * Hkv + h.
+//
+//   vi in [0, lam)                  slot vi of the cache at call start
+//   vi in [lam, lam + eta + T)      position p = n0 - eta + (vi - lam):
+//                                   p <  n0 -> window ring slot p % eta
+//                                   p >= n0 -> input row p - n0
+//
+// Candidate order by virtual index is not position order for cache slots
+// (decode leaves slots unordered), so every key also carries its position.
+// ---------------------------------------------------------------------------
+struct VirtRows {
+  const void* cache_k;      // [U, lam, d]  (state dtype)
+  const void* cache_v;
+  const int32_t* cache_pos; // [U, lam], -1 = empty
+  const void* ring_k;       // [U, eta, d]
+  const void* ring_v;
+  const void* in_k;         // [U, T, d]
+  const void* in_v;
+  long long n0;
+  int lam, eta, T, d;
+
+  __device__ __forceinline__ long long pos_of(int u, int vi) const {
+    if (vi < lam) return cache_pos[(size_t)u * lam + vi];
+    return n0 - eta + (vi - lam);
+  }
+  // byte offset of row vi of unit u in one of the three sources, elem = bytes
+  __device__ __forceinline__ const char* row(const void* cache, const void* ring,
+                                             const void* in, int u, int vi,
+                                             int elem) const {
+    size_t rb = (size_t)d * elem;
+    if (vi < lam) return (const char*)cache + ((size_t)u * lam + vi) * rb;
+    long long p = n0 - eta + (vi - lam);
+    if (p < n0) return (const char*)ring + ((size_t)u * eta + (size_t)(p % eta)) * rb;
+    return (const char*)in + ((size_t)u * T + (size_t)(p - n0)) * rb;
+  }
+  __device__ __forceinline__ const char* krow(int u, int vi, int elem) const {
+    return row(cache_k, ring_k, in_k, u, vi, elem);
+  }
+  __device__ __forceinline__ const char* vrow(int u, int vi, int elem) const {
+    return row(cache_v, ring_v, in_v, u, vi, elem);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// K1: phi of every candidate row of the call -> hi/lo bf16 planes.
+struct PhiArgs {
+  VirtRows vr;
+  const void* W;            // [Hkv, d, kM]
+  uint16_t* phi_hi;         // [U, NV, kD]
+  uint16_t* phi_lo;
+  int NV;                   // lam + eta + T
+  int Hkv;
+  int gs0;                  // cache entries valid at call start
+};
+
+// K2: the serial SRE / top-lam / fold chain, one step per chunk.
+struct ChainArgs {
+  VirtRows vr;
+  const uint16_t* phi_hi;
+  const uint16_t* phi_lo;
+  float* H;                 // [U, kD, d]  state in / out
+  float* s;                 // [U, kD]
+  uint16_t* snapHT;         // [U, nch, 2, d, kD]  H^T at chunk start, hi / lo
+  float* snaps;             // [U, nch, kD]        s at chunk start
+  int32_t* snapG;           // [U, nch, lam]       cache (virtual indices)
+  int32_t* finalG;          // [U, lam]
+  int NV, nch, C;
+  uint64_t* dbg_keys;       // optional [U, nch, lam + C]: candidate keys per step
+};
+
+// K3: window + cache softmax attention merged with the linear read.
+struct AttnArgs {
+  VirtRows vr;
+  const void* q;            // [B, Hq, T, d] == [U, g, T, d]
+  const void* W;            // [Hkv, d, kM]
+  const uint16_t* snapHT;
+  const float* snaps;
+  const int32_t* snapG;
+  float* out;               // [U, g, T, d]
+  int g, Hkv, nch, C, ptile, nblk;  // positions per WG, 32-position blocks per WG
+};
+
+// Finalize: new cache rows / positions and window ring after a prefill call.
+struct FinalizeArgs {
+  VirtRows vr;
+  const int32_t* finalG;    // [U, lam]
+  void* new_cache_k;        // [U, lam, d]
+  void* new_cache_v;
+  int32_t* new_cache_pos;
+  void* ring_k;             // written in place
+  void* ring_v;
+  int gs_final;
+};
+
+// Decode step (C = 1) for every unit.
+struct DecodeArgs {
+  const void* q;            // [U, g, d]
+  const void* k;            // [U, d]
+  const void* v;
+  const void* W;
+  float* H;
+  float* s;
+  void* ring_k;
+  void* ring_v;
+  void* cache_k;            // current cache buffer, updated in place
+  void* cache_v;
+  int32_t* cache_pos;
+  float* out;               // [U, g, d]
+  long long n;
+  int lam, eta, d, g, Hkv;
+  // element strides (one token): q / out [u][hd], k / v [u]
+  long long q_su, q_sh, kv_su, o_su, o_sh;
+};
+
+// launchers (return hipError_t of the launch)
+hipError_t launch_phi(const PhiArgs& a, int U, bool f32, hipStream_t st);
+hipError_t launch_chain(const ChainArgs& a, int U, bool f32, hipStream_t st);
+size_t chain_lds_bytes(int lam, int C, int d, bool f32);
+hipError_t launch_attn(const AttnArgs& a, int U, bool f32, hipStream_t st);
+size_t attn_lds_bytes(int d, bool f32);
+hipError_t launch_finalize(const FinalizeArgs& a, int U, bool f32, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int U, bool f32, hipStream_t st);
+hipError_t launch_export(bool f32, int U, const void* ring_k, const void* ring_v,
+                         const void* cache_k, const void* cache_v, const int32_t* cache_pos,
+                         void* win_k, void* win_v, void* out_ck, void* out_cv, int32_t* out_pos,
+                         long long n, int eta, int lam, int gs, int d, hipStream_t st);
+hipError_t launch_import(bool f32, int U, void* ring_k, void* ring_v, void* cache_k,
+                         void* cache_v, int32_t* cache_pos, const void* win_k,
+                         const void* win_v, const void* in_ck, const void* in_cv,
+                         const int32_t* in_pos, long long n, int eta, int lam, int gs, int d,
+                         hipStream_t st);
+size_t decode_lds_bytes(int lam, int eta, int d, int g, bool f32);
+hipError_t launch_snappos(const VirtRows& vr, const int32_t* snapG, int32_t* out, int nch,
+                          int C, int U, hipStream_t st);
+
+}  // namespace lola

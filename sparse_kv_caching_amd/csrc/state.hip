@@ -1,0 +1,175 @@
+// State maintenance after a prefill call, and the canonical export / import
+// layout of the persistent state (window oldest -> newest, cache by position).
+//
+// The persistent state per unit is the eta-token window, the lam-entry cache,
+// H and s: (eta + lam)(d_k + d_v) + D d_v + D elements (LoLA notes §2.7).
+#include "internal.h"
+
+namespace lola {
+
+namespace {
+constexpr int kThreads = 256;
+
+template <class T>
+__device__ void copy_row(T* dst, const T* src, int d) {
+  for (int c = threadIdx.x & 63; c < d; c += 64) dst[c] = src[c];
+}
+}  // namespace
+
+// New cache (compacted into the other buffer) and the window ring.
+template <class T>
+__global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeArgs a) {
+  const VirtRows& vr = a.vr;
+  const int u = blockIdx.x, d = vr.d, lam = vr.lam, eta = vr.eta;
+  const int wave = threadIdx.x >> 6;
+  for (int i = wave; i < lam; i += kThreads / 64) {
+    T* dk = reinterpret_cast<T*>(a.new_cache_k) + ((size_t)u * lam + i) * d;
+    T* dv = reinterpret_cast<T*>(a.new_cache_v) + ((size_t)u * lam + i) * d;
+    if (i < a.gs_final) {
+      const int vi = a.finalG[(size_t)u * lam + i];
+      copy_row(dk, reinterpret_cast<const T*>(vr.krow(u, vi, sizeof(T))), d);
+      copy_row(dv, reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))), d);
+      if ((threadIdx.x & 63) == 0) a.new_cache_pos[(size_t)u * lam + i] = (int32_t)vr.pos_of(u, vi);
+    } else if ((threadIdx.x & 63) == 0) {
+      a.new_cache_pos[(size_t)u * lam + i] = -1;
+    }
+  }
+  __syncthreads();   // every ring read above happens before the ring is overwritten
+  if (eta <= 0) return;
+  const long long nend = vr.n0 + vr.T;
+  const long long p_lo = max(vr.n0, nend - eta);
+  for (long long p = p_lo + wave; p < nend; p += kThreads / 64) {
+    const size_t slot = (size_t)u * eta + (size_t)(p % eta);
+    const size_t src = (size_t)u * vr.T + (size_t)(p - vr.n0);
+    copy_row(reinterpret_cast<T*>(a.ring_k) + slot * d, reinterpret_cast<const T*>(vr.in_k) + src * d, d);
+    copy_row(reinterpret_cast<T*>(a.ring_v) + slot * d, reinterpret_cast<const T*>(vr.in_v) + src * d, d);
+  }
+}
+
+hipError_t launch_finalize(const FinalizeArgs& a, int U, bool f32, hipStream_t st) {
+  if (U <= 0) return hipSuccess;
+  if (f32) hipLaunchKernelGGL(finalize_kernel<float>, dim3(U), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL(finalize_kernel<uint16_t>, dim3(U), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// export: window ring -> oldest..newest rows; cache slots -> ascending
+// positions (rank by counting), -1 padding.
+template <class T>
+__global__ __launch_bounds__(kThreads) void export_kernel(
+    const T* ring_k, const T* ring_v, const T* cache_k, const T* cache_v,
+    const int32_t* cache_pos, T* win_k, T* win_v, T* out_ck, T* out_cv,
+    int32_t* out_pos, long long n, int eta, int lam, int gs, int d) {
+  const int u = blockIdx.x, wave = threadIdx.x >> 6;
+  const int w = (int)min((long long)eta, n);
+  for (int jj = wave; jj < eta; jj += kThreads / 64) {
+    T* dk = win_k + ((size_t)u * eta + jj) * d;
+    T* dv = win_v + ((size_t)u * eta + jj) * d;
+    if (jj < w) {
+      const long long p = n - w + jj;
+      const size_t slot = (size_t)u * eta + (size_t)(p % eta);
+      copy_row(dk, ring_k + slot * d, d);
+      copy_row(dv, ring_v + slot * d, d);
+    } else {
+      for (int c = threadIdx.x & 63; c < d; c += 64) { dk[c] = T(0); dv[c] = T(0); }
+    }
+  }
+  for (int i = wave; i < lam; i += kThreads / 64) {
+    if (i >= gs) {
+      if ((threadIdx.x & 63) == 0) out_pos[(size_t)u * lam + i] = -1;
+      T* dk = out_ck + ((size_t)u * lam + i) * d;
+      T* dv = out_cv + ((size_t)u * lam + i) * d;
+      for (int c = threadIdx.x & 63; c < d; c += 64) { dk[c] = T(0); dv[c] = T(0); }
+      continue;
+    }
+    const int32_t p = cache_pos[(size_t)u * lam + i];
+    int rank = 0;
+    for (int o = threadIdx.x & 63; o < gs; o += 64) rank += cache_pos[(size_t)u * lam + o] < p;
+    rank = wave_sum_i(rank);
+    copy_row(out_ck + ((size_t)u * lam + rank) * d, cache_k + ((size_t)u * lam + i) * d, d);
+    copy_row(out_cv + ((size_t)u * lam + rank) * d, cache_v + ((size_t)u * lam + i) * d, d);
+    if ((threadIdx.x & 63) == 0) out_pos[(size_t)u * lam + rank] = p;
+  }
+}
+
+// import: canonical rows -> ring slots / cache slots (cache kept in order)
+template <class T>
+__global__ __launch_bounds__(kThreads) void import_kernel(
+    T* ring_k, T* ring_v, T* cache_k, T* cache_v, int32_t* cache_pos,
+    const T* win_k, const T* win_v, const T* in_ck, const T* in_cv,
+    const int32_t* in_pos, long long n, int eta, int lam, int gs, int d) {
+  const int u = blockIdx.x, wave = threadIdx.x >> 6;
+  const int w = (int)min((long long)eta, n);
+  for (int jj = wave; jj < w; jj += kThreads / 64) {
+    const long long p = n - w + jj;
+    const size_t slot = (size_t)u * eta + (size_t)(p % eta);
+    copy_row(ring_k + slot * d, win_k + ((size_t)u * eta + jj) * d, d);
+    copy_row(ring_v + slot * d, win_v + ((size_t)u * eta + jj) * d, d);
+  }
+  for (int i = wave; i < lam; i += kThreads / 64) {
+    copy_row(cache_k + ((size_t)u * lam + i) * d, in_ck + ((size_t)u * lam + i) * d, d);
+    copy_row(cache_v + ((size_t)u * lam + i) * d, in_cv + ((size_t)u * lam + i) * d, d);
+    if ((threadIdx.x & 63) == 0)
+      cache_pos[(size_t)u * lam + i] = i < gs ? in_pos[(size_t)u * lam + i] : -1;
+  }
+}
+
+hipError_t launch_export(bool f32, int U, const void* ring_k, const void* ring_v,
+                         const void* cache_k, const void* cache_v, const int32_t* cache_pos,
+                         void* win_k, void* win_v, void* out_ck, void* out_cv, int32_t* out_pos,
+                         long long n, int eta, int lam, int gs, int d, hipStream_t st) {
+  if (U <= 0) return hipSuccess;
+  if (f32)
+    hipLaunchKernelGGL(export_kernel<float>, dim3(U), dim3(kThreads), 0, st,
+                       (const float*)ring_k, (const float*)ring_v, (const float*)cache_k,
+                       (const float*)cache_v, cache_pos, (float*)win_k, (float*)win_v,
+                       (float*)out_ck, (float*)out_cv, out_pos, n, eta, lam, gs, d);
+  else
+    hipLaunchKernelGGL(export_kernel<uint16_t>, dim3(U), dim3(kThreads), 0, st,
+                       (const uint16_t*)ring_k, (const uint16_t*)ring_v,
+                       (const uint16_t*)cache_k, (const uint16_t*)cache_v, cache_pos,
+                       (uint16_t*)win_k, (uint16_t*)win_v, (uint16_t*)out_ck,
+                       (uint16_t*)out_cv, out_pos, n, eta, lam, gs, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_import(bool f32, int U, void* ring_k, void* ring_v, void* cache_k,
+                         void* cache_v, int32_t* cache_pos, const void* win_k,
+                         const void* win_v, const void* in_ck, const void* in_cv,
+                         const int32_t* in_pos, long long n, int eta, int lam, int gs, int d,
+                         hipStream_t st) {
+  if (U <= 0) return hipSuccess;
+  if (f32)
+    hipLaunchKernelGGL(import_kernel<float>, dim3(U), dim3(kThreads), 0, st, (float*)ring_k,
+                       (float*)ring_v, (float*)cache_k, (float*)cache_v, cache_pos,
+                       (const float*)win_k, (const float*)win_v, (const float*)in_ck,
+                       (const float*)in_cv, in_pos, n, eta, lam, gs, d);
+  else
+    hipLaunchKernelGGL(import_kernel<uint16_t>, dim3(U), dim3(kThreads), 0, st,
+                       (uint16_t*)ring_k, (uint16_t*)ring_v, (uint16_t*)cache_k,
+                       (uint16_t*)cache_v, cache_pos, (const uint16_t*)win_k,
+                       (const uint16_t*)win_v, (const uint16_t*)in_ck,
+                       (const uint16_t*)in_cv, in_pos, n, eta, lam, gs, d);
+  return hipGetLastError();
+}
+
+// positions of the cache at every chunk start (debug export)
+__global__ void snappos_kernel(VirtRows vr, const int32_t* snapG, int32_t* out, int nch, int C) {
+  const int u = blockIdx.y, j = blockIdx.x;
+  const long long nj = vr.n0 + (long long)j * C;
+  const int gs = (int)min((long long)vr.lam, max(0LL, nj - vr.eta));
+  for (int i = threadIdx.x; i < vr.lam; i += blockDim.x) {
+    const size_t o = ((size_t)u * nch + j) * vr.lam + i;
+    out[o] = i < gs ? (int32_t)vr.pos_of(u, snapG[o]) : -1;
+  }
+}
+
+hipError_t launch_snappos(const VirtRows& vr, const int32_t* snapG, int32_t* out, int nch,
+                          int C, int U, hipStream_t st) {
+  if (U <= 0 || nch <= 0 || vr.lam <= 0) return hipSuccess;
+  hipLaunchKernelGGL(snappos_kernel, dim3(nch, U), dim3(256), 0, st, vr, snapG, out, nch, C);
+  return hipGetLastError();
+}
+
+}  // namespace lola
