@@ -117,6 +117,27 @@ int lola_prefill_debug(lola_state* st, const void* q, const void* k, const void*
 int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v, void* out,
                      int out_dtype, void* stream);
 
+/* Start over: n = 0, H = 0, s = 0, empty window and cache (the memory and W
+ * are kept).  Stream-ordered.  Clears a poisoned state. */
+int lola_state_reset(lola_state* st, void* stream);
+
+/* Kernel families whose launches can be timed. */
+enum {
+  LOLA_KERNEL_PHI = 0,       /* feature map of the candidate rows */
+  LOLA_KERNEL_CHAIN = 1,     /* serial SRE / top-lambda / fold chain */
+  LOLA_KERNEL_ATTN = 2,      /* chunk attention + linear read */
+  LOLA_KERNEL_FINALIZE = 3,  /* cache / window write-back */
+  LOLA_KERNEL_DECODE = 4,    /* decode step */
+  LOLA_KERNEL_COUNT = 5
+};
+
+/* Per-kernel timing with HIP events recorded on the launch stream around
+ * every launch while enabled.  Each call synchronises the recorded events,
+ * writes the accumulated milliseconds and launch counts since the previous
+ * call into ms[LOLA_KERNEL_COUNT] and launches[LOLA_KERNEL_COUNT] (either may
+ * be NULL), resets them, and turns timing on (enable != 0) or off. */
+int lola_profile(lola_state* st, int enable, double* ms, long long* launches);
+
 /* Canonical state layout, all DEVICE pointers owned by the caller:
  *   H [B*Hkv, D, d] f32, s [B*Hkv, D] f32,
  *   win_k, win_v [B*Hkv, eta, d]: the last min(n, eta) pairs oldest first,

@@ -35,6 +35,12 @@ struct lola_state {
   void* W;
   void* own_ws;
   size_t own_ws_bytes;
+  // optional per-kernel timing with HIP events on the launch stream
+  bool prof_on;
+  struct Pending { int kind; hipEvent_t a, b; };
+  std::vector<Pending>* prof_pending;
+  double prof_ms[LOLA_KERNEL_COUNT];
+  long long prof_n[LOLA_KERNEL_COUNT];
 };
 
 namespace {
@@ -58,6 +64,25 @@ int hip_fail(lola_state* st, hipError_t e, const char* what) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Brackets one kernel launch with events when timing is on.
+struct ProfScope {
+  lola_state* st;
+  int kind;
+  hipStream_t s;
+  hipEvent_t a = nullptr, b = nullptr;
+  ProfScope(lola_state* st_, int kind_, hipStream_t s_) : st(st_), kind(kind_), s(s_) {
+    if (!st->prof_on) return;
+    hipEventCreate(&a);
+    hipEventCreate(&b);
+    hipEventRecord(a, s);
+  }
+  ~ProfScope() {
+    if (!a) return;
+    hipEventRecord(b, s);
+    st->prof_pending->push_back({kind, a, b});
+  }
+};
 
 struct WsLayout {
   size_t phi_hi, phi_lo, snapHT, snaps, snapG, finalG, total;
@@ -144,6 +169,7 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
   st->f32 = c.dtype == LOLA_DTYPE_F32;
   st->esz = st->f32 ? 4 : 2;
   st->last = (hipStream_t)stream;
+  st->prof_pending = new std::vector<lola_state::Pending>();
   hipGetDevice(&st->device);
   const size_t U = st->U, d = st->d, lam = c.cache, eta = c.window;
   auto alloc = [&](void** p, size_t bytes) -> bool {
@@ -184,6 +210,10 @@ int lola_state_free(lola_state* st) {
                 st->cache_pos[0], st->cache_pos[1]};
   for (void* p : ps)
     if (p) hipFree(p);
+  if (st->prof_pending) {
+    for (auto& pe : *st->prof_pending) { hipEventDestroy(pe.a); hipEventDestroy(pe.b); }
+    delete st->prof_pending;
+  }
   delete st;
   return LOLA_OK;
 }
@@ -217,7 +247,8 @@ int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v
   a.Hkv = st->cfg.kv_heads;
   a.q_su = (long long)st->g * st->d; a.q_sh = st->d; a.kv_su = st->d;
   a.o_su = (long long)st->g * st->d; a.o_sh = st->d;
-  hipError_t e = launch_decode(a, st->U, st->f32, s);
+  hipError_t e;
+  { ProfScope ps(st, LOLA_KERNEL_DECODE, s); e = launch_decode(a, st->U, st->f32, s); }
   if (e != hipSuccess) return hip_fail(st, e, "decode launch");
   st->last = s;
   st->n += 1;
@@ -258,7 +289,8 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
       a.v = (const char*)v + (size_t)t * d * st->esz;
       a.out = (float*)out + (size_t)t * d;
       a.n = st->n;
-      hipError_t e = launch_decode(a, U, st->f32, s);
+      hipError_t e;
+      { ProfScope ps(st, LOLA_KERNEL_DECODE, s); e = launch_decode(a, U, st->f32, s); }
       if (e != hipSuccess) return hip_fail(st, e, "decode launch");
       st->n += 1;
     }
@@ -309,7 +341,8 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   PhiArgs pa;
   pa.vr = vr; pa.W = st->W; pa.phi_hi = phi_hi; pa.phi_lo = phi_lo;
   pa.NV = (int)NVs; pa.Hkv = st->cfg.kv_heads; pa.gs0 = gs0;
-  hipError_t e = launch_phi(pa, U, st->f32, s);
+  hipError_t e;
+  { ProfScope ps(st, LOLA_KERNEL_PHI, s); e = launch_phi(pa, U, st->f32, s); }
   if (e != hipSuccess) return hip_fail(st, e, "phi launch");
 
   ChainArgs ca;
@@ -320,7 +353,7 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   ca.snapG = (int32_t*)(base + L.snapG);
   ca.finalG = (int32_t*)(base + L.finalG);
   ca.NV = (int)NVs; ca.nch = nch; ca.C = C; ca.dbg_keys = cand_keys;
-  e = launch_chain(ca, U, st->f32, s);
+  { ProfScope ps(st, LOLA_KERNEL_CHAIN, s); e = launch_chain(ca, U, st->f32, s); }
   if (e != hipSuccess) return hip_fail(st, e, "chain launch");
   if (snap_pos) {
     e = launch_snappos(vr, ca.snapG, snap_pos, nch, C, U, s);
@@ -334,7 +367,7 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   aa.g = g; aa.Hkv = st->cfg.kv_heads; aa.nch = nch; aa.C = C;
   aa.ptile = std::min(C, 128 / g);
   aa.nblk = aa.ptile / 32;
-  e = launch_attn(aa, U, st->f32, s);
+  { ProfScope ps(st, LOLA_KERNEL_ATTN, s); e = launch_attn(aa, U, st->f32, s); }
   if (e != hipSuccess) return hip_fail(st, e, "attention launch");
 
   FinalizeArgs fa;
@@ -346,7 +379,7 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   fa.ring_k = st->ring_k;
   fa.ring_v = st->ring_v;
   fa.gs_final = gs_final;
-  e = launch_finalize(fa, U, st->f32, s);
+  { ProfScope ps(st, LOLA_KERNEL_FINALIZE, s); e = launch_finalize(fa, U, st->f32, s); }
   if (e != hipSuccess) return hip_fail(st, e, "finalize launch");
   st->cur = 1 - st->cur;
   st->n = nend;
@@ -367,6 +400,44 @@ int lola_prefill_debug(lola_state* st, const void* q, const void* k, const void*
     return fail(LOLA_ERR_UNSUPPORTED, "debug export needs C > 1");
   return prefill_impl(st, q, k, v, T, C, out, out_dtype, ws, ws_bytes, snap_pos, cand_keys,
                       stream);
+}
+
+int lola_state_reset(lola_state* st, void* stream) {
+  if (!st) return fail(LOLA_ERR_INVALID_ARG, "state is NULL");
+  hipStream_t s = (hipStream_t)stream;
+  const size_t U = st->U, d = st->d, lam = st->cfg.cache;
+  hipError_t e = hipMemsetAsync(st->H, 0, U * kD * d * 4, s);
+  if (e == hipSuccess) e = hipMemsetAsync(st->s, 0, U * kD * 4, s);
+  for (int b = 0; b < 2 && e == hipSuccess; ++b)
+    e = hipMemsetAsync(st->cache_pos[b], 0xFF, U * (lam ? lam : 1) * 4, s);
+  if (e != hipSuccess) return hip_fail(st, e, "reset");
+  st->n = 0;
+  st->poisoned = false;
+  st->last = s;
+  return LOLA_OK;
+}
+
+int lola_profile(lola_state* st, int enable, double* ms, long long* launches) {
+  if (!st) return fail(LOLA_ERR_INVALID_ARG, "state is NULL");
+  for (auto& pe : *st->prof_pending) {
+    hipError_t e = hipEventSynchronize(pe.b);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, pe.a, pe.b);
+    if (e != hipSuccess) return fail(LOLA_ERR_HIP, "profile: %s", hipGetErrorString(e));
+    st->prof_ms[pe.kind] += t;
+    st->prof_n[pe.kind] += 1;
+    hipEventDestroy(pe.a);
+    hipEventDestroy(pe.b);
+  }
+  st->prof_pending->clear();
+  for (int k = 0; k < LOLA_KERNEL_COUNT; ++k) {
+    if (ms) ms[k] = st->prof_ms[k];
+    if (launches) launches[k] = st->prof_n[k];
+    st->prof_ms[k] = 0.0;
+    st->prof_n[k] = 0;
+  }
+  st->prof_on = enable != 0;
+  return LOLA_OK;
 }
 
 int lola_state_export(const lola_state* st, lola_state_view* dst, void* stream) {

@@ -25,10 +25,12 @@ LOLA_ERR_STATE = 5
 LOLA_ERR_WORKSPACE = 6
 LOLA_DTYPE_F32 = 0
 LOLA_DTYPE_BF16 = 1
+KERNELS = ("phi", "chain", "attn", "finalize", "decode")
 
 EXPORTED = [
     "lola_state_init", "lola_state_free", "lola_state_tokens", "lola_prefill_workspace_bytes",
-    "lola_prefill_chunk", "lola_prefill_debug", "lola_decode_step", "lola_state_export", "lola_state_import",
+    "lola_prefill_chunk", "lola_prefill_debug", "lola_decode_step", "lola_state_reset",
+    "lola_profile", "lola_state_export", "lola_state_import",
     "lola_strerror", "lola_last_error",
 ]
 
@@ -77,13 +79,17 @@ def library() -> ctypes.CDLL:
         lib.lola_prefill_chunk.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, sz, vp]
         lib.lola_prefill_debug.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, sz, vp, vp, vp]
         lib.lola_decode_step.argtypes = [vp, vp, vp, vp, vp, i32, vp]
+        lib.lola_state_reset.argtypes = [vp, vp]
+        lib.lola_profile.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_longlong)]
         lib.lola_state_export.argtypes = [vp, ctypes.POINTER(LolaStateView), vp]
         lib.lola_state_import.argtypes = [vp, ctypes.POINTER(LolaStateView), vp]
         lib.lola_strerror.argtypes = [i32]
         lib.lola_strerror.restype = ctypes.c_char_p
         lib.lola_last_error.restype = ctypes.c_char_p
         for f in ("lola_state_init", "lola_state_free", "lola_prefill_workspace_bytes",
-                  "lola_prefill_chunk", "lola_prefill_debug", "lola_decode_step", "lola_state_export",
+                  "lola_prefill_chunk", "lola_prefill_debug", "lola_decode_step", "lola_state_reset",
+    "lola_profile", "lola_state_export",
                   "lola_state_import"):
             getattr(lib, f).restype = i32
         _lib = lib
@@ -140,6 +146,18 @@ class LolaLayer:
             self.free()
         except Exception:
             pass
+
+    def reset(self, stream=None):
+        """Empty the state (n = 0) without reallocating."""
+        _check(self.lib.lola_state_reset(self._st, _stream(stream)), "lola_state_reset")
+
+    def profile(self, enable: bool):
+        """Return {kernel: (ms, launches)} accumulated since the last call and
+        switch per-kernel event timing on or off."""
+        ms = (ctypes.c_double * len(KERNELS))()
+        cnt = (ctypes.c_longlong * len(KERNELS))()
+        _check(self.lib.lola_profile(self._st, int(enable), ms, cnt), "lola_profile")
+        return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNELS)}
 
     @property
     def n(self) -> int:
