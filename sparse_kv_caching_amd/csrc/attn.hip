@@ -34,44 +34,33 @@ constexpr int kThreads = 256;
 constexpr int HTH = kM + 8;  // padded row of one half of H^T in LDS
 constexpr int KTP = 32 + 8;  // padded row of V^T tile
 
-struct AttnSmem {
-  uint16_t* WT_hi;   // [kM][d + 8]
-  uint16_t* WT_lo;
-  uint16_t* HT_hi;   // [d][HTH]   (one feature half at a time)
-  uint16_t* HT_lo;
-  float* s;          // [kD]
-  // key phase (aliases the region above)
-  uint16_t* K_hi;    // [32][d + 8]
-  uint16_t* K_lo;
-  uint16_t* VT_a;    // [d][KTP]  fp16 (bf16 inputs) or fp16 hi (fp32 inputs)
-  uint16_t* VT_b;    //           fp16 lo (fp32 inputs)
+// Byte offsets of the LDS arrays; the key phase reuses the region of the
+// linear-read phase.
+struct AttnLayout {
+  uint32_t WT_hi, WT_lo, HT_hi, HT_lo, s;      // linear-read phase
+  uint32_t K_hi, K_lo, VT_a, VT_b;             // key phase
+  uint32_t total;
 };
 
-inline __host__ __device__ size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
+inline __host__ __device__ uint32_t al16(uint32_t x) { return (x + 15u) & ~15u; }
 
-// Carves both phases from the start of dynamic LDS; returns the larger size.
-__host__ __device__ inline size_t carve(int d, bool f32, unsigned char* base, AttnSmem* sm) {
-  size_t off = 0;
-  auto take = [&](size_t bytes) -> unsigned char* {
-    unsigned char* p = base + off;
-    off = al16(off + bytes);
-    return p;
-  };
-  AttnSmem t;
-  t.WT_hi = (uint16_t*)take((size_t)kM * (d + 8) * 2);
-  t.WT_lo = (uint16_t*)take(f32 ? (size_t)kM * (d + 8) * 2 : 16);
-  t.HT_hi = (uint16_t*)take((size_t)d * HTH * 2);
-  t.HT_lo = (uint16_t*)take((size_t)d * HTH * 2);
-  t.s = (float*)take(kD * 4);
-  const size_t phaseA = off;
+__host__ __device__ inline AttnLayout attn_layout(int d, bool f32) {
+  AttnLayout L;
+  uint32_t off = 0;
+  auto take = [&](uint32_t b) { const uint32_t o = off; off = al16(off + b); return o; };
+  L.WT_hi = take((uint32_t)kM * (d + 8) * 2);          // [kM][d + 8]
+  L.WT_lo = take(f32 ? (uint32_t)kM * (d + 8) * 2 : 16);
+  L.HT_hi = take((uint32_t)d * HTH * 2);               // [d][HTH], one feature half
+  L.HT_lo = take((uint32_t)d * HTH * 2);
+  L.s = take(kD * 4);
+  const uint32_t phaseA = off;
   off = 0;
-  t.K_hi = (uint16_t*)take((size_t)32 * (d + 8) * 2);
-  t.K_lo = (uint16_t*)take(f32 ? (size_t)32 * (d + 8) * 2 : 16);
-  t.VT_a = (uint16_t*)take((size_t)d * KTP * 2);
-  t.VT_b = (uint16_t*)take(f32 ? (size_t)d * KTP * 2 : 16);
-  const size_t phaseB = off;
-  if (sm) *sm = t;
-  return phaseA > phaseB ? phaseA : phaseB;
+  L.K_hi = take((uint32_t)32 * (d + 8) * 2);           // [32][d + 8]
+  L.K_lo = take(f32 ? (uint32_t)32 * (d + 8) * 2 : 16);
+  L.VT_a = take((uint32_t)d * KTP * 2);                // [d][KTP] fp16 (bf16 inputs) or hi
+  L.VT_b = take(f32 ? (uint32_t)d * KTP * 2 : 16);     //          lo (fp32 inputs)
+  L.total = phaseA > off ? phaseA : off;
+  return L;
 }
 
 __device__ __forceinline__ u32x2 ld8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
@@ -84,16 +73,16 @@ __device__ __forceinline__ u32x4 sigma_load(const uint16_t* row16, int h) {
 
 }  // namespace
 
-size_t attn_lds_bytes(int d, bool f32) {
-  static unsigned char dummy[1];
-  return carve(d, f32, dummy, nullptr);
-}
+size_t attn_lds_bytes(int d, bool f32) { return attn_layout(d, f32).total; }
 
-template <class DT>
+template <class DT, int HD>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   using T = typename DT::T;
-  const VirtRows& vr = a.vr;
-  const int d = vr.d, lam = vr.lam, eta = vr.eta;
+  constexpr int d = HD;
+  constexpr int KB = HD / 16;     // 16-wide K blocks over the head dim
+  constexpr int nmt = HD / 32;    // 32-row tiles of the output
+  const VirtRows vr = a.vr;
+  const int lam = vr.lam, eta = vr.eta;
   const int pt = blockIdx.x, j = blockIdx.y, u = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, r = lane & 31;
@@ -111,8 +100,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   const bool qvalid = wactive && qpos < pend;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  AttnSmem sm;
-  carve(d, DT::kSplit, smem, &sm);
+  const AttnLayout L = attn_layout(d, DT::kSplit);
+  struct {
+    uint16_t *WT_hi, *WT_lo, *HT_hi, *HT_lo;
+    float* s;
+    uint16_t *K_hi, *K_lo, *VT_a, *VT_b;
+  } sm = {(uint16_t*)(smem + L.WT_hi), (uint16_t*)(smem + L.WT_lo), (uint16_t*)(smem + L.HT_hi),
+          (uint16_t*)(smem + L.HT_lo), (float*)(smem + L.s), (uint16_t*)(smem + L.K_hi),
+          (uint16_t*)(smem + L.K_lo), (uint16_t*)(smem + L.VT_a), (uint16_t*)(smem + L.VT_b)};
 
   // ---- W^T of this KV head and s_j into LDS
   const T* W = reinterpret_cast<const T*>(a.W) + (size_t)kvh * d * kM;
@@ -127,11 +122,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   for (int F = tid; F < kD; F += kThreads) sm.s[F] = sj[F];
 
   // ---- Q operands (B of S^T = K Q^T): lane = query r, K-slots 8h .. 8h+7
-  u32x4 qh[8], ql[8];
+  u32x4 qh[KB], ql[KB];
   {
     const T* qrow = reinterpret_cast<const T*>(a.q) +
                     (((size_t)u * a.g + (wactive ? hd : 0)) * vr.T + (size_t)(qvalid ? qpos - n0 : 0)) * d;
-    for (int kb = 0; kb < d / 16; ++kb) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
       const int k0 = 16 * kb + 8 * h;
       if constexpr (DT::kSplit) {
         float x[8];
@@ -152,8 +148,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     f32x16 acc[2];
     for (int mt = 0; mt < 2; ++mt) for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
     if (wactive) {
-      for (int kb = 0; kb < d / 16; ++kb) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
         const int k0 = 16 * kb + 8 * h;
+#pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
           const int f = 32 * mt + r;
           const u32x4 ah = ld16(sm.WT_hi + f * (d + 8) + k0);
@@ -167,11 +165,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
       }
     }
     float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
     for (int mt = 0; mt < 2; ++mt)
       for (int i = 0; i < 16; ++i) { mx = fmaxf(mx, acc[mt][i]); mn = fminf(mn, acc[mt][i]); }
     mx = fmaxf(mx, xor32(mx));
     mn = fminf(mn, xor32(mn));
     float sp = 0.f, sn = 0.f;
+#pragma unroll
     for (int mt = 0; mt < 2; ++mt)
       for (int i = 0; i < 16; ++i) {
         ph[0][mt][i] = expf(acc[mt][i] - mx);
@@ -182,6 +182,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     sp += xor32(sp);
     sn += xor32(sn);
     const float ip = 1.f / sp, in_ = 1.f / sn;
+#pragma unroll
     for (int mt = 0; mt < 2; ++mt)
       for (int i = 0; i < 16; ++i) {
         ph[0][mt][i] *= ip;
@@ -194,10 +195,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   }
 
   // ---- linear read N_lin^T = H_j^T phi^T into the output accumulator
-  f32x16 O[4];
-  for (int mt = 0; mt < 4; ++mt) for (int i = 0; i < 16; ++i) O[mt][i] = 0.f;
-  const int nmt = d / 32;
+  f32x16 O[nmt];
+#pragma unroll
+  for (int mt = 0; mt < nmt; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[mt][i] = 0.f;
   const uint16_t* snap = a.snapHT + ((size_t)u * a.nch + j) * 2 * d * kD;
+#pragma unroll
   for (int half = 0; half < 2; ++half) {
     __syncthreads();
     for (int i = tid; i < 2 * d * (kM / 8); i += kThreads) {
@@ -208,10 +212,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     }
     __syncthreads();
     if (wactive) {
+#pragma unroll
       for (int kb = 0; kb < kM / 16; ++kb) {
         const int mt = kb >> 1, i0 = 8 * (kb & 1);
         u32x4 bh, bl;
         splitop<DT>(&ph[half][mt][i0], bh, bl);
+#pragma unroll
         for (int mo = 0; mo < nmt; ++mo) {
           const int row = 32 * mo + r;
           const u32x4 ah = sigma_load(sm.HT_hi + row * HTH + 16 * kb, h);
@@ -263,8 +269,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     __syncthreads();
     if (!wactive) continue;
     f32x16 S;
+#pragma unroll
     for (int i = 0; i < 16; ++i) S[i] = 0.f;
-    for (int kb = 0; kb < d / 16; ++kb) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
       const int k0 = 16 * kb + 8 * h;
       const u32x4 ah = ld16(sm.K_hi + r * (d + 8) + k0);
       S = DT::mma(ah, qh[kb], S);
@@ -286,7 +294,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const float mnew = fmaxf(m2, tmax);
     if (mnew > m2) {
       const float alpha = exp2f(m2 - mnew);
-      for (int mt = 0; mt < nmt; ++mt) for (int i = 0; i < 16; ++i) O[mt][i] *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < nmt; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) O[mt][i] *= alpha;
       l *= alpha;
       m2 = mnew;
     }
@@ -294,12 +305,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < 16; ++i) { S[i] = exp2f(S[i] - m2); rs += S[i]; }
     rs += xor32(rs);
     l += rs;
+#pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       if constexpr (DT::kSplit) {
         u32x4 ph8, pl8;
         float pv[8];
         for (int q = 0; q < 8; ++q) pv[q] = S[8 * kb + q];
         splitop<DT>(pv, ph8, pl8);
+#pragma unroll
         for (int mo = 0; mo < nmt; ++mo) {
           const int row = 32 * mo + r;
           const u32x4 vh = sigma_load(sm.VT_a + row * KTP + 16 * kb, h);
@@ -310,7 +323,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         }
       } else {
         f16x8 p8;
+#pragma unroll
         for (int q = 0; q < 8; ++q) p8[q] = (_Float16)S[8 * kb + q];
+#pragma unroll
         for (int mo = 0; mo < nmt; ++mo) {
           const int row = 32 * mo + r;
           f16x8 vh = __builtin_bit_cast(f16x8, sigma_load(sm.VT_a + row * KTP + 16 * kb, h));
@@ -324,7 +339,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   if (!qvalid) return;
   const float il = 1.f / l;
   float* orow = a.out + (((size_t)u * a.g + hd) * vr.T + (size_t)(qpos - n0)) * d;
+#pragma unroll
   for (int mo = 0; mo < nmt; ++mo)
+#pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int cc = 32 * mo + 8 * g4 + 4 * h;
       f32x4 y;
@@ -333,19 +350,22 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     }
 }
 
-hipError_t launch_attn(const AttnArgs& a, int U, bool f32, hipStream_t st) {
-  if (U <= 0 || a.nch <= 0) return hipSuccess;
+template <class DT, int HD>
+static hipError_t launch_attn_t(const AttnArgs& a, int U, hipStream_t st) {
   const int nptile = (a.C + a.ptile - 1) / a.ptile;
   dim3 grid(nptile, a.nch, U);
-  size_t lds = attn_lds_bytes(a.vr.d, f32);
-  if (f32) {
-    (void)hipFuncSetAttribute((const void*)attn_kernel<F32>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(attn_kernel<F32>, grid, dim3(kThreads), lds, st, a);
-  } else {
-    (void)hipFuncSetAttribute((const void*)attn_kernel<BF16>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(attn_kernel<BF16>, grid, dim3(kThreads), lds, st, a);
-  }
+  const size_t lds = attn_lds_bytes(HD, DT::kSplit);
+  (void)hipFuncSetAttribute((const void*)attn_kernel<DT, HD>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((attn_kernel<DT, HD>), grid, dim3(kThreads), lds, st, a);
   return hipGetLastError();
+}
+
+hipError_t launch_attn(const AttnArgs& a, int U, bool f32, hipStream_t st) {
+  if (U <= 0 || a.nch <= 0) return hipSuccess;
+  if (a.vr.d == 64)
+    return f32 ? launch_attn_t<F32, 64>(a, U, st) : launch_attn_t<BF16, 64>(a, U, st);
+  return f32 ? launch_attn_t<F32, 128>(a, U, st) : launch_attn_t<BF16, 128>(a, U, st);
 }
 
 }  // namespace lola

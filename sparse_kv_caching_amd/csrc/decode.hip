@@ -24,44 +24,32 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int WP = 8;                // W^T row padding (bf16)
 
-struct DecSmem {
-  uint16_t* WT_hi;   // [kM][d + WP]
-  uint16_t* WT_lo;
-  float* s;          // [kD]
-  float* q;          // [g][d]
-  float* lk;         // leaving key  [d]
-  float* lv;         // leaving value [d]
-  float* nlin;       // [g][d]  linear read H^T phi(q)
-  float* zq;         // [g]
-  float* spart;      // [4][32]
-  uint64_t* keys;    // [lam + 1]
-  float* phe;        // [kD] phi of the folded row
-  float* logit;      // [g][lam + eta + 1]
-  int32_t* misc;     // [8]
+// Byte offsets of the LDS arrays.
+struct DecLayout {
+  uint32_t WT_hi, WT_lo, s, q, lk, lv, nlin, zq, spart, keys, phe, logit, misc, total;
 };
 
-inline __host__ __device__ size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
+inline __host__ __device__ uint32_t al16(uint32_t x) { return (x + 15u) & ~15u; }
 
-__host__ __device__ inline size_t carve(int lam, int eta, int d, int g, bool f32,
-                                        unsigned char* base, DecSmem* sm) {
-  size_t off = 0;
-  auto take = [&](size_t b) { unsigned char* p = base + off; off = al16(off + b); return p; };
-  DecSmem t;
-  t.WT_hi = (uint16_t*)take((size_t)kM * (d + WP) * 2);
-  t.WT_lo = (uint16_t*)take(f32 ? (size_t)kM * (d + WP) * 2 : 16);
-  t.s = (float*)take(kD * 4);
-  t.q = (float*)take((size_t)g * d * 4);
-  t.lk = (float*)take((size_t)d * 4);
-  t.lv = (float*)take((size_t)d * 4);
-  t.nlin = (float*)take((size_t)g * d * 4);
-  t.zq = (float*)take(16 * 4);
-  t.spart = (float*)take(4 * 32 * 4);
-  t.keys = (uint64_t*)take((size_t)(lam + 1) * 8);
-  t.phe = (float*)take(kD * 4);
-  t.logit = (float*)take((size_t)g * (lam + eta + 1) * 4);
-  t.misc = (int32_t*)take(8 * 4);
-  if (sm) *sm = t;
-  return off;
+__host__ __device__ inline DecLayout dec_layout(int lam, int eta, int d, int g, bool f32) {
+  DecLayout L;
+  uint32_t off = 0;
+  auto take = [&](uint32_t b) { const uint32_t o = off; off = al16(off + b); return o; };
+  L.WT_hi = take((uint32_t)kM * (d + WP) * 2);         // [kM][d + WP]
+  L.WT_lo = take(f32 ? (uint32_t)kM * (d + WP) * 2 : 16);
+  L.s = take(kD * 4);                                  // [kD]
+  L.q = take((uint32_t)g * d * 4);                     // [g][d]
+  L.lk = take((uint32_t)d * 4);                        // leaving key [d]
+  L.lv = take((uint32_t)d * 4);                        // leaving value [d]
+  L.nlin = take((uint32_t)g * d * 4);                  // [g][d] H^T phi(q)
+  L.zq = take(16 * 4);                                 // [g]
+  L.spart = take(4 * 32 * 4);                          // [4][32]
+  L.keys = take((uint32_t)(lam + 1) * 8);              // [lam + 1]
+  L.phe = take(kD * 4);                                // phi of the folded row
+  L.logit = take((uint32_t)g * (lam + eta + 1) * 4);   // [g][lam + eta + 1]
+  L.misc = take(8 * 4);
+  L.total = off;
+  return L;
 }
 
 __device__ __forceinline__ float ldx(const uint16_t* p) { return bf16_bits_to_f32(*p); }
@@ -72,8 +60,7 @@ __device__ __forceinline__ void stx(float* p, float x) { *p = x; }
 }  // namespace
 
 size_t decode_lds_bytes(int lam, int eta, int d, int g, bool f32) {
-  static unsigned char dummy[1];
-  return carve(lam, eta, d, g, f32, dummy, nullptr);
+  return dec_layout(lam, eta, d, g, f32).total;
 }
 
 template <class DT>
@@ -90,8 +77,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const int nslab = d / 32;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  DecSmem sm;
-  carve(lam, eta, d, g, DT::kSplit, smem, &sm);
+  const DecLayout L = dec_layout(lam, eta, d, g, DT::kSplit);
+  struct {
+    uint16_t *WT_hi, *WT_lo;
+    float *s, *q, *lk, *lv, *nlin, *zq, *spart;
+    uint64_t* keys;
+    float *phe, *logit;
+    int32_t* misc;
+  } sm = {(uint16_t*)(smem + L.WT_hi), (uint16_t*)(smem + L.WT_lo), (float*)(smem + L.s),
+          (float*)(smem + L.q), (float*)(smem + L.lk), (float*)(smem + L.lv),
+          (float*)(smem + L.nlin), (float*)(smem + L.zq), (float*)(smem + L.spart),
+          (uint64_t*)(smem + L.keys), (float*)(smem + L.phe), (float*)(smem + L.logit),
+          (int32_t*)(smem + L.misc)};
 
   const T* Wg = reinterpret_cast<const T*>(a.W) + (size_t)kvh * d * kM;
   for (int i = tid; i < d * kM; i += kThreads) {

@@ -3,6 +3,8 @@
 //
 // The persistent state per unit is the eta-token window, the lam-entry cache,
 // H and s: (eta + lam)(d_k + d_v) + D d_v + D elements (LoLA notes §2.7).
+#include <algorithm>
+
 #include "internal.h"
 
 namespace lola {
@@ -16,40 +18,66 @@ __device__ void copy_row(T* dst, const T* src, int d) {
 }
 }  // namespace
 
-// New cache (compacted into the other buffer) and the window ring.
-template <class T>
-__global__ __launch_bounds__(kThreads) void finalize_kernel(FinalizeArgs a) {
-  const VirtRows& vr = a.vr;
-  const int u = blockIdx.x, d = vr.d, lam = vr.lam, eta = vr.eta;
-  const int wave = threadIdx.x >> 6;
-  for (int i = wave; i < lam; i += kThreads / 64) {
-    T* dk = reinterpret_cast<T*>(a.new_cache_k) + ((size_t)u * lam + i) * d;
-    T* dv = reinterpret_cast<T*>(a.new_cache_v) + ((size_t)u * lam + i) * d;
-    if (i < a.gs_final) {
-      const int vi = a.finalG[(size_t)u * lam + i];
-      copy_row(dk, reinterpret_cast<const T*>(vr.krow(u, vi, sizeof(T))), d);
-      copy_row(dv, reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))), d);
-      if ((threadIdx.x & 63) == 0) a.new_cache_pos[(size_t)u * lam + i] = (int32_t)vr.pos_of(u, vi);
-    } else if ((threadIdx.x & 63) == 0) {
-      a.new_cache_pos[(size_t)u * lam + i] = -1;
-    }
+// New cache (compacted into the other buffer), then the window ring, as two
+// launches so that every ring row the new cache takes is read before the
+// ring is overwritten.  Rows move as 16-byte pieces, many rows per block.
+__global__ __launch_bounds__(kThreads) void finalize_cache_kernel(FinalizeArgs a, int esz) {
+  const VirtRows vr = a.vr;
+  const int u = blockIdx.y, lam = vr.lam;
+  const int pieces = vr.d * esz / 16;                  // 16-byte pieces per row
+  const int rows_per_block = kThreads / pieces;
+  const int i = blockIdx.x * rows_per_block + threadIdx.x / pieces;
+  const int pc = threadIdx.x % pieces;
+  if (i >= lam || threadIdx.x >= rows_per_block * pieces) return;
+  const size_t dst = ((size_t)u * lam + i) * vr.d * esz + (size_t)pc * 16;
+  if (i < a.gs_final) {
+    const int vi = a.finalG[(size_t)u * lam + i];
+    *reinterpret_cast<u32x4*>((char*)a.new_cache_k + dst) =
+        *reinterpret_cast<const u32x4*>(vr.krow(u, vi, esz) + pc * 16);
+    *reinterpret_cast<u32x4*>((char*)a.new_cache_v + dst) =
+        *reinterpret_cast<const u32x4*>(vr.vrow(u, vi, esz) + pc * 16);
+    if (pc == 0) a.new_cache_pos[(size_t)u * lam + i] = (int32_t)vr.pos_of(u, vi);
+  } else if (pc == 0) {
+    a.new_cache_pos[(size_t)u * lam + i] = -1;
   }
-  __syncthreads();   // every ring read above happens before the ring is overwritten
-  if (eta <= 0) return;
+}
+
+__global__ __launch_bounds__(kThreads) void finalize_ring_kernel(FinalizeArgs a, int esz) {
+  const VirtRows vr = a.vr;
+  const int u = blockIdx.y, eta = vr.eta;
   const long long nend = vr.n0 + vr.T;
   const long long p_lo = max(vr.n0, nend - eta);
-  for (long long p = p_lo + wave; p < nend; p += kThreads / 64) {
-    const size_t slot = (size_t)u * eta + (size_t)(p % eta);
-    const size_t src = (size_t)u * vr.T + (size_t)(p - vr.n0);
-    copy_row(reinterpret_cast<T*>(a.ring_k) + slot * d, reinterpret_cast<const T*>(vr.in_k) + src * d, d);
-    copy_row(reinterpret_cast<T*>(a.ring_v) + slot * d, reinterpret_cast<const T*>(vr.in_v) + src * d, d);
-  }
+  const int pieces = vr.d * esz / 16;
+  const int rows_per_block = kThreads / pieces;
+  const long long p = p_lo + (long long)blockIdx.x * rows_per_block + threadIdx.x / pieces;
+  const int pc = threadIdx.x % pieces;
+  if (p >= nend || threadIdx.x >= rows_per_block * pieces) return;
+  const size_t row_b = (size_t)vr.d * esz;
+  const size_t slot = ((size_t)u * eta + (size_t)(p % eta)) * row_b + (size_t)pc * 16;
+  const size_t src = ((size_t)u * vr.T + (size_t)(p - vr.n0)) * row_b + (size_t)pc * 16;
+  *reinterpret_cast<u32x4*>((char*)a.ring_k + slot) =
+      *reinterpret_cast<const u32x4*>((const char*)vr.in_k + src);
+  *reinterpret_cast<u32x4*>((char*)a.ring_v + slot) =
+      *reinterpret_cast<const u32x4*>((const char*)vr.in_v + src);
 }
 
 hipError_t launch_finalize(const FinalizeArgs& a, int U, bool f32, hipStream_t st) {
   if (U <= 0) return hipSuccess;
-  if (f32) hipLaunchKernelGGL(finalize_kernel<float>, dim3(U), dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL(finalize_kernel<uint16_t>, dim3(U), dim3(kThreads), 0, st, a);
+  const int esz = f32 ? 4 : 2;
+  const int pieces = a.vr.d * esz / 16;
+  const int rpb = kThreads / pieces;
+  if (a.vr.lam > 0) {
+    dim3 g1((a.vr.lam + rpb - 1) / rpb, U);
+    hipLaunchKernelGGL(finalize_cache_kernel, g1, dim3(kThreads), 0, st, a, esz);
+  }
+  if (a.vr.eta > 0) {
+    const long long nend = a.vr.n0 + a.vr.T;
+    const long long nrows = nend - std::max<long long>(a.vr.n0, nend - a.vr.eta);
+    if (nrows > 0) {
+      dim3 g2((unsigned)((nrows + rpb - 1) / rpb), U);
+      hipLaunchKernelGGL(finalize_ring_kernel, g2, dim3(kThreads), 0, st, a, esz);
+    }
+  }
   return hipGetLastError();
 }
 
