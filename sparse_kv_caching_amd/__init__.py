@@ -6,14 +6,12 @@ binding is imported lazily so that :mod:`sparse_kv_caching_amd.workloads` (the
 seeded input generators) can be used without the library.
 """
 
+import importlib
+
 __all__ = ["lola", "workloads"]
 
 
 def __getattr__(name):
-    if name == "lola":
-        from . import lola as _l
-        return _l
-    if name == "workloads":
-        from . import workloads as _w
-        return _w
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

@@ -32,7 +32,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int HTH = kM + 8;  // padded row of one half of H^T in LDS
-constexpr int KTP = 32 + 8;  // padded row of V^T tile
+constexpr int KTP = 36;      // row of the V^T tile: 32 keys + 4 (conflict-free pitch)
 
 // Byte offsets of the LDS arrays; the key phase reuses the region of the
 // linear-read phase.
@@ -239,31 +239,56 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   const int32_t* Gj = a.snapG + ((size_t)u * a.nch + j) * lam;
   for (int t0 = 0; t0 < nkeys; t0 += 32) {
     __syncthreads();
+    // K tile, row-major [key][d]: 16-byte pieces (raw copy for bf16)
     for (int i = tid; i < 32 * (d / 8); i += kThreads) {
       const int kl = i / (d / 8), cc = (i % (d / 8)) * 8;
       const int kk = t0 + kl;
-      float kv[8], vv[8];
-      if (kk < nkeys) {
-        const int vi = kk < gsj ? Gj[kk] : lam + eta + (int)(lo_j + (kk - gsj) - n0);
-        load8_f32(reinterpret_cast<const T*>(vr.krow(u, vi, sizeof(T))) + cc, kv);
-        load8_f32(reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))) + cc, vv);
-      } else {
-        for (int q = 0; q < 8; ++q) { kv[q] = 0.f; vv[q] = 0.f; }
-      }
-      u32x4 kh, kl8;
-      splitop<DT>(kv, kh, kl8);
-      *reinterpret_cast<u32x4*>(sm.K_hi + kl * (d + 8) + cc) = kh;
+      const int vi = kk < nkeys ? (kk < gsj ? Gj[kk] : lam + eta + (int)(lo_j + (kk - gsj) - n0)) : -1;
       if constexpr (DT::kSplit) {
+        float kv[8];
+        if (vi >= 0) load8_f32(reinterpret_cast<const T*>(vr.krow(u, vi, sizeof(T))) + cc, kv);
+        else for (int q = 0; q < 8; ++q) kv[q] = 0.f;
+        u32x4 kh, kl8;
+        splitop<DT>(kv, kh, kl8);
+        *reinterpret_cast<u32x4*>(sm.K_hi + kl * (d + 8) + cc) = kh;
         *reinterpret_cast<u32x4*>(sm.K_lo + kl * (d + 8) + cc) = kl8;
-        for (int q = 0; q < 8; ++q) {
-          uint32_t hi, lo;
-          DT::split(vv[q], hi, lo);
-          sm.VT_a[(cc + q) * KTP + kl] = (uint16_t)hi;
-          sm.VT_b[(cc + q) * KTP + kl] = (uint16_t)lo;
-        }
       } else {
-        for (int q = 0; q < 8; ++q)
-          sm.VT_a[(cc + q) * KTP + kl] = __builtin_bit_cast(uint16_t, (_Float16)vv[q]);
+        *reinterpret_cast<u32x4*>(sm.K_hi + kl * (d + 8) + cc) =
+            vi >= 0 ? *reinterpret_cast<const u32x4*>(vr.krow(u, vi, sizeof(T)) + cc * sizeof(T))
+                    : u32x4{0, 0, 0, 0};
+      }
+    }
+    // V^T tile [d][KTP]: a thread takes two consecutive keys x 8 columns and
+    // writes 8 dwords (the key pair) -- 16 threads fill 16 consecutive dwords
+    // of one row, and the row pitch puts the four row groups of a wave on
+    // disjoint banks.
+    for (int i = tid; i < 16 * (d / 8); i += kThreads) {
+      const int pr = i % 16, cc = (i / 16) * 8;
+      float v0[8], v1[8];
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        const int kk = t0 + 2 * pr + kq;
+        float* dst = kq ? v1 : v0;
+        if (kk < nkeys) {
+          const int vi = kk < gsj ? Gj[kk] : lam + eta + (int)(lo_j + (kk - gsj) - n0);
+          load8_f32(reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))) + cc, dst);
+        } else {
+          for (int q = 0; q < 8; ++q) dst[q] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        uint32_t* row = reinterpret_cast<uint32_t*>(sm.VT_a + (cc + q) * KTP) + pr;
+        if constexpr (DT::kSplit) {
+          uint32_t h0, l0, h1, l1;
+          DT::split(v0[q], h0, l0);
+          DT::split(v1[q], h1, l1);
+          *row = h0 | (h1 << 16);
+          *(reinterpret_cast<uint32_t*>(sm.VT_b + (cc + q) * KTP) + pr) = l0 | (l1 << 16);
+        } else {
+          *row = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0[q]) |
+                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1[q]) << 16);
+        }
       }
     }
     __syncthreads();
