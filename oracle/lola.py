@@ -40,7 +40,7 @@ Eq. (15)):
    G; fold the rest into H += sum phi(k) v^T, s += sum phi(k).
 5. **Advance**: the window becomes the last ``eta`` positions; n += c.
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
 eta counts past tokens kept between chunks and a query also sees its own
 chunk's causal prefix (diagonal included); z = phi(k)^T s = 0 gives prediction
 0 (the notes flag the H = 0, s = 0 division as unhandled); ties in the top-lam

@@ -5,7 +5,7 @@ numbers, rounds them to the storage dtype and plants repeated keys.  Both the
 HIP path (through tests and the benchmark) and the CPU oracle receive the
 arrays it returns, bit for bit.
 
-Recipe (also stated in the design doc):
+Recipe:
 
 * ``numpy.random.default_rng(seed)`` (PCG64) draws q, k, v ~ N(0, 1) in float32,
   in that order, shapes q (B, Hq, T, d), k and v (B, Hkv, T, d).  bf16
