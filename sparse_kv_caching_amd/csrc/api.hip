@@ -33,6 +33,7 @@ struct lola_state {
   int32_t* cache_pos[2];
   int cur;
   void* W;
+  void* WT;                 // W transposed [Hkv, kM, d] (decode operands)
   void* own_ws;
   size_t own_ws_bytes;
   // optional per-kernel timing with HIP events on the launch stream
@@ -178,7 +179,8 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
   };
   bool ok = alloc((void**)&st->H, U * kD * d * 4) && alloc((void**)&st->s, U * kD * 4) &&
             alloc(&st->ring_k, U * eta * d * st->esz) && alloc(&st->ring_v, U * eta * d * st->esz) &&
-            alloc(&st->W, (size_t)c.kv_heads * d * kM * st->esz);
+            alloc(&st->W, (size_t)c.kv_heads * d * kM * st->esz) &&
+            alloc(&st->WT, (size_t)c.kv_heads * d * kM * st->esz);
   for (int b = 0; b < 2 && ok; ++b)
     ok = alloc(&st->cache_k[b], U * lam * d * st->esz) &&
          alloc(&st->cache_v[b], U * lam * d * st->esz) &&
@@ -194,6 +196,7 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
     e = hipMemsetAsync(st->cache_pos[b], 0xFF, U * (lam ? lam : 1) * 4, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(st->W, W, (size_t)c.kv_heads * d * kM * st->esz, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = launch_transpose_w(st->W, st->WT, c.kv_heads, (int)d, st->f32, s);
   if (e != hipSuccess) {
     lola_state_free(st);
     return fail(LOLA_ERR_HIP, "state initialisation: %s", hipGetErrorString(e));
@@ -205,7 +208,7 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
 int lola_state_free(lola_state* st) {
   if (!st) return LOLA_OK;
   hipStreamSynchronize(st->last);
-  void* ps[] = {st->H, st->s, st->ring_k, st->ring_v, st->W, st->own_ws,
+  void* ps[] = {st->H, st->s, st->ring_k, st->ring_v, st->W, st->WT, st->own_ws,
                 st->cache_k[0], st->cache_k[1], st->cache_v[0], st->cache_v[1],
                 st->cache_pos[0], st->cache_pos[1]};
   for (void* p : ps)
@@ -236,7 +239,7 @@ int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v
   if (st->n > (int64_t)0x7FFFFFF0) return fail(LOLA_ERR_UNSUPPORTED, "position overflow");
   hipStream_t s = (hipStream_t)stream;
   DecodeArgs a;
-  a.q = q; a.k = k; a.v = v; a.W = st->W;
+  a.q = q; a.k = k; a.v = v; a.WT = st->WT;
   a.H = st->H; a.s = st->s;
   a.ring_k = st->ring_k; a.ring_v = st->ring_v;
   a.cache_k = st->cache_k[st->cur]; a.cache_v = st->cache_v[st->cur];
@@ -245,6 +248,7 @@ int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v
   a.n = st->n;
   a.lam = st->cfg.cache; a.eta = st->cfg.window; a.d = st->d; a.g = st->g;
   a.Hkv = st->cfg.kv_heads;
+  decode_plan(a.lam, a.eta, st->d, st->g, st->f32, &a.kc, &a.nslot);
   a.q_su = (long long)st->g * st->d; a.q_sh = st->d; a.kv_su = st->d;
   a.o_su = (long long)st->g * st->d; a.o_sh = st->d;
   hipError_t e;
@@ -275,12 +279,13 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
     // token by token through the decode kernel, reading strided slices of
     // q [U, g, T, d], k / v [U, T, d] and writing out [U, g, T, d]
     DecodeArgs a;
-    a.W = st->W; a.H = st->H; a.s = st->s;
+    a.WT = st->WT; a.H = st->H; a.s = st->s;
     a.ring_k = st->ring_k; a.ring_v = st->ring_v;
     a.cache_k = st->cache_k[st->cur]; a.cache_v = st->cache_v[st->cur];
     a.cache_pos = st->cache_pos[st->cur];
     a.lam = st->cfg.cache; a.eta = st->cfg.window; a.d = d; a.g = g;
     a.Hkv = st->cfg.kv_heads;
+    decode_plan(a.lam, a.eta, d, g, st->f32, &a.kc, &a.nslot);
     a.q_su = (long long)g * T * d; a.q_sh = (long long)T * d; a.kv_su = (long long)T * d;
     a.o_su = a.q_su; a.o_sh = a.q_sh;
     for (int t = 0; t < T; ++t) {

@@ -36,10 +36,16 @@ __device__ __forceinline__ f32x16 mfma_f16(f16x8 a, f16x8 b, f32x16 c) {
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
   return __uint_as_float(b16 << 16);
 }
-// round-to-nearest-even fp32 -> bf16 bits (finite inputs)
+// round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32 on gfx950), two at
+// a time: a in the low half, b in the high half
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return cvt_pk_bf16(x, 0.f) & 0xFFFFu;
 }
 __device__ __forceinline__ __bf16 bits_to_bf16(uint32_t b) {
   return __builtin_bit_cast(__bf16, (uint16_t)b);
@@ -123,11 +129,22 @@ struct F32 {
 // Split 8 floats into hi and lo operands in the tag's 16-bit format.
 template <class DT>
 __device__ __forceinline__ void splitop(const float* x, u32x4& hi, u32x4& lo) {
-  uint32_t h[8], l[8];
+  if constexpr (DT::kSplit) {
+    uint32_t h[8], l[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) DT::split(x[j], h[j], l[j]);
-  hi = pack8(h);
-  lo = pack8(l);
+    for (int j = 0; j < 8; ++j) DT::split(x[j], h[j], l[j]);
+    hi = pack8(h);
+    lo = pack8(l);
+  } else {
+    // bf16 pairs: hi = RNE(x), lo = RNE(x - hi), both exact RNE as split_bf16
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t hp = cvt_pk_bf16(x[2 * j], x[2 * j + 1]);
+      hi[j] = hp;
+      lo[j] = cvt_pk_bf16(x[2 * j] - __uint_as_float(hp << 16),
+                          x[2 * j + 1] - __uint_as_float(hp & 0xFFFF0000u));
+    }
+  }
 }
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);

@@ -112,7 +112,7 @@ struct DecodeArgs {
   const void* q;            // [U, g, d]
   const void* k;            // [U, d]
   const void* v;
-  const void* W;
+  const void* WT;           // [Hkv, kM, d]  W transposed, state dtype
   float* H;
   float* s;
   void* ring_k;
@@ -123,6 +123,7 @@ struct DecodeArgs {
   float* out;               // [U, g, d]
   long long n;
   int lam, eta, d, g, Hkv;
+  int kc, nslot;            // rows per staged key chunk, phi slots (decode_plan)
   // element strides (one token): q / out [u][hd], k / v [u]
   long long q_su, q_sh, kv_su, o_su, o_sh;
 };
@@ -145,6 +146,8 @@ hipError_t launch_import(bool f32, int U, void* ring_k, void* ring_v, void* cach
                          const int32_t* in_pos, long long n, int eta, int lam, int gs, int d,
                          hipStream_t st);
 size_t decode_lds_bytes(int lam, int eta, int d, int g, bool f32);
+void decode_plan(int lam, int eta, int d, int g, bool f32, int* kc, int* nslot);
+hipError_t launch_transpose_w(const void* W, void* WT, int Hkv, int d, bool f32, hipStream_t st);
 hipError_t launch_snappos(const VirtRows& vr, const int32_t* snapG, int32_t* out, int nch,
                           int C, int U, hipStream_t st);
 
