@@ -121,6 +121,12 @@ int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v
  * are kept).  Stream-ordered.  Clears a poisoned state. */
 int lola_state_reset(lola_state* st, void* stream);
 
+/* Wait for the state's work on `stream` and report faults the kernels
+ * recorded on the device (an SRE exchange between the workgroups of a unit
+ * that did not complete: LOLA_ERR_STATE, and the state is poisoned until
+ * reset or import).  Errors: INVALID_ARG, HIP, STATE. */
+int lola_state_check(lola_state* st, void* stream);
+
 /* Kernel families whose launches can be timed. */
 enum {
   LOLA_KERNEL_PHI = 0,       /* feature map of the candidate rows */

@@ -34,6 +34,8 @@ struct lola_state {
   int cur;
   void* W;
   void* WT;                 // W transposed [Hkv, kM, d] (decode operands)
+  int* dev_err;             // device error flags (exchange timeouts)
+  int ncu;                  // compute units of the device
   void* own_ws;
   size_t own_ws_bytes;
   // optional per-kernel timing with HIP events on the launch stream
@@ -86,7 +88,7 @@ struct ProfScope {
 };
 
 struct WsLayout {
-  size_t phi_hi, phi_lo, snapHT, snaps, snapG, finalG, total;
+  size_t phi_hi, phi_lo, snapHT, snaps, snapG, finalG, xbuf, total;
 };
 
 WsLayout ws_layout(const lola_state* st, int T, int C) {
@@ -102,8 +104,24 @@ WsLayout ws_layout(const lola_state* st, int T, int C) {
   w.snaps = off; off = align256(off + U * nch * kD * 4);
   w.snapG = off; off = align256(off + U * nch * lam1 * 4);
   w.finalG = off; off = align256(off + U * lam1 * 4);
+  w.xbuf = off; off = align256(off + U * 2 * (d / 32) * (lam + (size_t)C) * 8);
   w.total = off;
   return w;
+}
+
+// Workgroups per unit for the chain: the whole grid must be resident (one
+// workgroup per compute unit).  First split the columns into slabs (k = d / 32),
+// then split the candidate tiles into CS groups until every wave of a
+// workgroup has at most one tile per step (or the device is full).
+int chain_workgroups(int U, int ncu, int d, int lam, int C) {
+  const int nslab = d / 32;
+  const long long cap = ncu / std::max(U, 1);
+  if (cap < 2) return 1;
+  if (cap < nslab) return nslab >= 4 && cap >= 2 ? 2 : 1;
+  const int tiles = (lam + C + 31) / 32;
+  int cs = 1;
+  while ((tiles + cs - 1) / cs > 8 && nslab * cs * 2 <= cap && cs < 16) cs *= 2;
+  return nslab * cs;
 }
 
 int check_state(const lola_state* st) {
@@ -172,6 +190,10 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
   st->last = (hipStream_t)stream;
   st->prof_pending = new std::vector<lola_state::Pending>();
   hipGetDevice(&st->device);
+  st->ncu = 0;
+  if (hipDeviceGetAttribute(&st->ncu, hipDeviceAttributeMultiprocessorCount, st->device) != hipSuccess ||
+      st->ncu < 1)
+    st->ncu = 1;
   const size_t U = st->U, d = st->d, lam = c.cache, eta = c.window;
   auto alloc = [&](void** p, size_t bytes) -> bool {
     if (bytes == 0) bytes = 256;
@@ -180,7 +202,8 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
   bool ok = alloc((void**)&st->H, U * kD * d * 4) && alloc((void**)&st->s, U * kD * 4) &&
             alloc(&st->ring_k, U * eta * d * st->esz) && alloc(&st->ring_v, U * eta * d * st->esz) &&
             alloc(&st->W, (size_t)c.kv_heads * d * kM * st->esz) &&
-            alloc(&st->WT, (size_t)c.kv_heads * d * kM * st->esz);
+            alloc(&st->WT, (size_t)c.kv_heads * d * kM * st->esz) &&
+            alloc((void**)&st->dev_err, sizeof(int));
   for (int b = 0; b < 2 && ok; ++b)
     ok = alloc(&st->cache_k[b], U * lam * d * st->esz) &&
          alloc(&st->cache_v[b], U * lam * d * st->esz) &&
@@ -197,6 +220,7 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
   if (e == hipSuccess)
     e = hipMemcpyAsync(st->W, W, (size_t)c.kv_heads * d * kM * st->esz, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess) e = launch_transpose_w(st->W, st->WT, c.kv_heads, (int)d, st->f32, s);
+  if (e == hipSuccess) e = launch_zero_u32((unsigned*)st->dev_err, 1, s);
   if (e != hipSuccess) {
     lola_state_free(st);
     return fail(LOLA_ERR_HIP, "state initialisation: %s", hipGetErrorString(e));
@@ -208,7 +232,7 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
 int lola_state_free(lola_state* st) {
   if (!st) return LOLA_OK;
   hipStreamSynchronize(st->last);
-  void* ps[] = {st->H, st->s, st->ring_k, st->ring_v, st->W, st->WT, st->own_ws,
+  void* ps[] = {st->H, st->s, st->ring_k, st->ring_v, st->W, st->WT, st->dev_err, st->own_ws,
                 st->cache_k[0], st->cache_k[1], st->cache_v[0], st->cache_v[1],
                 st->cache_pos[0], st->cache_pos[1]};
   for (void* p : ps)
@@ -358,6 +382,14 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   ca.snapG = (int32_t*)(base + L.snapG);
   ca.finalG = (int32_t*)(base + L.finalG);
   ca.NV = (int)NVs; ca.nch = nch; ca.C = C; ca.dbg_keys = cand_keys;
+  ca.k = chain_workgroups(U, st->ncu, d, lam, C);
+  ca.xcd_group = (U % 8 == 0) ? 1 : 0;
+  ca.xbuf = (uint64_t*)(base + L.xbuf);
+  ca.err = st->dev_err;
+  if (ca.k > 1) {
+    e = launch_zero_u32((unsigned*)ca.xbuf, (size_t)U * 2 * (d / 32) * (lam + C) * 2, s);
+    if (e != hipSuccess) return hip_fail(st, e, "exchange reset");
+  }
   { ProfScope ps(st, LOLA_KERNEL_CHAIN, s); e = launch_chain(ca, U, st->f32, s); }
   if (e != hipSuccess) return hip_fail(st, e, "chain launch");
   if (snap_pos) {
@@ -415,11 +447,26 @@ int lola_state_reset(lola_state* st, void* stream) {
   if (e == hipSuccess) e = hipMemsetAsync(st->s, 0, U * kD * 4, s);
   for (int b = 0; b < 2 && e == hipSuccess; ++b)
     e = hipMemsetAsync(st->cache_pos[b], 0xFF, U * (lam ? lam : 1) * 4, s);
+  if (e == hipSuccess) e = launch_zero_u32((unsigned*)st->dev_err, 1, s);
   if (e != hipSuccess) return hip_fail(st, e, "reset");
   st->n = 0;
   st->poisoned = false;
   st->last = s;
   return LOLA_OK;
+}
+
+int lola_state_check(lola_state* st, void* stream) {
+  if (!st) return fail(LOLA_ERR_INVALID_ARG, "state is NULL");
+  int flag = 0;
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e == hipSuccess) e = hipMemcpy(&flag, st->dev_err, sizeof(int), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(st, e, "check");
+  if (flag) {
+    st->poisoned = true;
+    return fail(LOLA_ERR_STATE, "device fault flags 0x%x (an SRE exchange between the "
+                "workgroups of a unit did not complete)", flag);
+  }
+  return st->poisoned ? fail(LOLA_ERR_STATE, "state is poisoned") : LOLA_OK;
 }
 
 int lola_profile(lola_state* st, int enable, double* ms, long long* launches) {

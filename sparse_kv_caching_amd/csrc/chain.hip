@@ -1,28 +1,53 @@
-// K2: LoLA's serial memory-allocation chain, one step per chunk, one
-// workgroup (8 waves) per unit (b, KV head).
+// K2: LoLA's serial memory-allocation chain, one step per chunk.  A unit
+// (b, KV head) is processed by k cooperating workgroups (k = 1, 2 or 4, so
+// that every workgroup of the grid is resident at once); workgroup r owns
+// SPW = (d / 32) / k column slabs of H.
 //
 // Per chunk j (LoLA notes §2.6, Eq. (15); §2.4, Eqs. (11)-(13)):
-//   1. snapshot (H_j, s_j, G_j): the state the chunk's queries read;
+//   1. snapshot (H_j, s_j, G_j): the state the chunk's queries read (each
+//      workgroup writes its columns of H_j^T);
 //   2. candidates E = G_j ++ L_j, L_j = positions leaving the window;
 //   3. if |E| <= lam: G_{j+1} = E (keep all);
-//   4. else SRE of every candidate against (H_j, s_j) (notes §2.3, Eq. (10),
-//      squared), exact top-lam by (SRE desc, position asc), stable compaction,
-//      and the fold H += Phi_S^T V_S, s += sum phi over the rest.
+//   4. else the SRE of every candidate against (H_j, s_j) (notes §2.3,
+//      Eq. (10), squared): each workgroup computes the part of the squared
+//      error over its own columns, the parts are exchanged through global
+//      memory, and every workgroup forms the same keys and runs the same
+//      exact top-lam selection (SRE desc, position asc) and stable
+//      compaction; each folds the rest into its own columns of H
+//      (H += Phi_S^T V_S) and updates s += sum phi (all of s, everywhere).
 //
-// Precision.  SRE decides an integer (cache membership), so its GEMM
+// The SRE of a candidate is the sum of its per-slab parts, always added in
+// slab order, so the keys (and the whole chain) are bitwise the same for
+// every k.
+//
+// Precision.  SRE decides an integer (cache membership), so the GEMM
 // p = H^T phi runs as a three-pass 16-bit split (hi*hi + hi*lo + lo*hi, fp32
-// accumulation; bf16 halves for bf16 inputs, fp16 for fp32 inputs): relative
-// error ~1e-8 on these data, far inside the 1e-5 ranking band.  z = phi^T s
-// uses the same split on MFMA (s replicated over the 32 rows of a tile).
-// The fold multiplies phi (hi + lo) by V (exact in one bf16 operand, or split
-// for fp32 inputs) and accumulates into fp32 H.
+// accumulation; bf16 halves for bf16 inputs, fp16 for fp32 inputs) with
+// relative error ~1e-6 or better, inside the 1e-5 ranking band; z = phi^T s
+// is an fp32 dot product of the same split phi.  The fold multiplies phi
+// (hi + lo) by V (exact in one bf16 operand, or split for fp32 inputs) and
+// accumulates into fp32 H.
 //
-// Layout.  H (D x d, fp32) lives in registers for the whole call in MFMA
-// result layout: 32 x 32 tiles (feature block mt, column slab cs), two tiles
-// per wave; folds accumulate into them in place.  After each fold H^T is
-// rebuilt in LDS as hi/lo planes, the A operand of the next step's SRE GEMM,
-// whose (32-candidate tile, column half) work units are spread over the
-// eight waves.
+// Layout.  A workgroup's H columns live in registers for the whole call in
+// MFMA result layout (32 x 32 tiles (feature block mt, slab)); folds
+// accumulate into them in place.  After each fold the columns are written to
+// LDS as H^T hi/lo rows, from which every wave loads its slab's A operands of
+// the next SRE GEMM once per step.
+//
+// Work split.  A unit's k workgroups form NG = (d / 32) / SPW slab groups
+// times CS candidate groups: workgroup (g, ch) owns the columns of slab group
+// g and scores the candidate tiles t with t % CS == ch.  The CS workgroups of
+// one slab group hold the same columns and apply the same fold.
+//
+// Exchange.  Every (slab, candidate) part is written as one 64-bit word
+// (value, step tag) with an agent-scope relaxed atomic store (it bypasses the
+// non-coherent caches); a reader polls each word with agent-scope atomic
+// loads until its tag is the current step's, bounded (a lost partner sets an
+// error flag and ends the chain instead of hanging).  Tags are the step
+// number + 1 and the buffer is zeroed before every call; parts are
+// double-buffered by the parity of the exchange step (a workgroup can only
+// write step x + 2 after every partner has published step x + 1, which each
+// does after reading step x).
 #include <type_traits>
 
 #include "internal.h"
@@ -35,52 +60,54 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int HTP = kD + 8;   // padded LDS row of H^T (16-bit elements)
 constexpr int STP = 64 + 8;   // padded LDS row of fold staging tiles (64 tokens)
+constexpr int kSpinLimit = 1 << 22;   // counter polls before an exchange is declared lost
 
 // Byte offsets of the LDS arrays (computed by value so that the kernel's
-// pointers stay plain LDS pointers).  The candidate list, keys and radix
-// histogram of the selection phase share one region with the fold's staging
-// tiles, which are live only after the selection.
+// pointers stay plain LDS pointers).  The candidate list, parts, keys and
+// radix histogram of the selection phase share one region with the fold's
+// staging tiles, which are live only after the selection.
 struct ChainLayout {
-  uint32_t HT_hi, HT_lo, s32, s_hi, s_lo, spart, G, Gp, S, misc, kred;
-  uint32_t E, keys, hist;                      // selection phase
+  uint32_t HT_hi, HT_lo, s32, spart, G, Gp, S, misc, kred;
+  uint32_t E, part, keys, hist;                // selection phase
   uint32_t phT_hi, phT_lo, VT_hi, VT_lo;       // fold phase (same region)
   uint32_t total;
 };
 
 __host__ __device__ inline uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
 
-__host__ __device__ inline ChainLayout chain_layout(int lam, int C, int d, bool f32) {
+__host__ __device__ inline ChainLayout chain_layout(int lam, int C, int spw, bool f32) {
   ChainLayout L;
   uint32_t off = 0;
   auto take = [&](uint32_t bytes) { const uint32_t o = off; off = align16(off + bytes); return o; };
   const uint32_t lam1 = lam > 0 ? (uint32_t)lam : 1u;
-  L.HT_hi = take((uint32_t)d * HTP * 2);   // [d][HTP]
-  L.HT_lo = take((uint32_t)d * HTP * 2);
+  const uint32_t ncol = 32u * (uint32_t)spw;   // H columns of the workgroup
+  const uint32_t le = (uint32_t)(lam + C);     // candidates per step, at most
+  L.HT_hi = take(ncol * HTP * 2);          // [ncol][HTP]
+  L.HT_lo = take(ncol * HTP * 2);
   L.s32 = take(kD * 4);                    // [kD]
-  L.s_hi = take(kD * 2);                   // s split into 16-bit hi / lo
-  L.s_lo = take(kD * 2);
   L.spart = take((kThreads / kD) * kD * 4);
   L.G = take(lam1 * 4);                    // cache (virtual indices)
   L.Gp = take(lam1 * 4);                   // cache positions
   L.S = take((uint32_t)C * 4);             // folded list (<= C per step)
-  L.misc = take(16 * 4);
+  L.misc = take(20 * 4);                   // [0..2] selection, [8..15] per wave, [16] abort
   L.kred = take(2 * kWaves * 8);           // per-wave key min / max
   const uint32_t region = off;
-  L.E = take((uint32_t)(lam + C) * 4);     // candidates (virtual indices)
-  L.keys = take((uint32_t)(lam + C) * 8);  // SRE partials, then keys
+  L.E = take(le * 4);                      // candidates (virtual indices)
+  L.part = take((uint32_t)spw * le * 4);   // [slab][candidate] SRE parts
+  L.keys = take(le * 8);
   L.hist = take(2048 * 4);                 // radix histogram
   const uint32_t sel_end = off;
   off = region;
   L.phT_hi = take(kD * STP * 2);           // [kD][STP]
   L.phT_lo = take(kD * STP * 2);
-  L.VT_hi = take((uint32_t)d * STP * 2);   // [d][STP]
-  L.VT_lo = take(f32 ? (uint32_t)d * STP * 2 : 16);
+  L.VT_hi = take(ncol * STP * 2);          // [ncol][STP]
+  L.VT_lo = take(f32 ? ncol * STP * 2 : 16);
   L.total = off > sel_end ? off : sel_end;
   return L;
 }
 
-// Workgroup barrier that orders LDS only.  Inside this kernel no thread reads
-// global memory written by another thread, so pending global stores (the
+// Workgroup barrier that orders LDS only.  No thread reads global memory
+// written by another thread of the workgroup, so pending global stores (the
 // per-chunk snapshots) need not drain at every barrier.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -88,53 +115,74 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+
 }  // namespace
 
 size_t chain_lds_bytes(int lam, int C, int d, bool f32) {
-  return chain_layout(lam, C, d, f32).total;
+  return chain_layout(lam, C, d / 32, f32).total;   // the largest case, k = 1
 }
 
-template <class DT, int HD>
+template <class DT, int HD, int SPW>
 __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
   using T = typename DT::T;
   constexpr int NSLAB = HD / 32;                  // column slabs of H
-  constexpr int NPW = NSLAB * 4 / kWaves;         // H tiles per wave (2 or 4)
+  constexpr int NTILE = 4 * SPW;                  // own H tiles (feature block, slab)
+  constexpr int NPW = (NTILE + kWaves - 1) / kWaves;   // H tiles per wave (1 or 2)
+  constexpr int NG = NSLAB / SPW;                 // slab groups
   const VirtRows vr = a.vr;
-  const int lam = vr.lam, eta = vr.eta;
-  const int u = blockIdx.x;
+  const int lam = vr.lam, eta = vr.eta, k = a.k, CS = a.k / NG;
+  const int LE = lam + a.C;                       // candidates per step, at most
+  // workgroup -> (unit, rank); with U a multiple of 8 the k workgroups of a
+  // unit get blocks of one residue mod 8 (blocks are dealt to the 8 XCDs
+  // round-robin, so they share an L2)
+  int u, rank;
+  if (a.xcd_group) {
+    const int b = blockIdx.x, m = b >> 3;
+    u = 8 * (m / k) + (b & 7);
+    rank = m % k;
+  } else {
+    u = blockIdx.x / k;
+    rank = blockIdx.x % k;
+  }
+  const int grp = rank % NG, ch = rank / NG;      // slab group, candidate group
+  const bool writer = ch == 0;                    // writes this slab group's columns
+  const int col0 = 32 * SPW * grp;                // first H column of this workgroup
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, r = lane & 31;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const ChainLayout L = chain_layout(lam, a.C, HD, DT::kSplit);
+  const ChainLayout L = chain_layout(lam, a.C, SPW, DT::kSplit);
   struct {
     uint16_t *HT_hi, *HT_lo;
-    float* s32;
-    uint16_t *s_hi, *s_lo;
-    float* spart;
+    float *s32, *spart;
     int32_t *G, *Gp, *S, *misc;
     uint64_t* kred;
     int32_t* E;
+    float* part;
     uint64_t* keys;
     int32_t* hist;
     uint16_t *phT_hi, *phT_lo, *VT_hi, *VT_lo;
   } sm = {(uint16_t*)(smem + L.HT_hi), (uint16_t*)(smem + L.HT_lo), (float*)(smem + L.s32),
-          (uint16_t*)(smem + L.s_hi), (uint16_t*)(smem + L.s_lo), (float*)(smem + L.spart),
-          (int32_t*)(smem + L.G), (int32_t*)(smem + L.Gp), (int32_t*)(smem + L.S),
-          (int32_t*)(smem + L.misc), (uint64_t*)(smem + L.kred), (int32_t*)(smem + L.E),
-          (uint64_t*)(smem + L.keys), (int32_t*)(smem + L.hist), (uint16_t*)(smem + L.phT_hi),
-          (uint16_t*)(smem + L.phT_lo), (uint16_t*)(smem + L.VT_hi), (uint16_t*)(smem + L.VT_lo)};
+          (float*)(smem + L.spart), (int32_t*)(smem + L.G), (int32_t*)(smem + L.Gp),
+          (int32_t*)(smem + L.S), (int32_t*)(smem + L.misc), (uint64_t*)(smem + L.kred),
+          (int32_t*)(smem + L.E), (float*)(smem + L.part), (uint64_t*)(smem + L.keys),
+          (int32_t*)(smem + L.hist), (uint16_t*)(smem + L.phT_hi), (uint16_t*)(smem + L.phT_lo),
+          (uint16_t*)(smem + L.VT_hi), (uint16_t*)(smem + L.VT_lo)};
 
-  // ---- H tiles of this wave: pair p = wave + kWaves * i -> (slab p / 4, mt p % 4)
+  // ---- own H tiles: tile p = wave + kWaves * i (p < NTILE) -> slab p / 4, mt p % 4
   f32x16 Hreg[NPW];
   const float* Hg = a.H + (size_t)u * kD * HD;
 #pragma unroll
   for (int i = 0; i < NPW; ++i) {
-    const int p = wave + kWaves * i, cs = p >> 2, mt = p & 3;
+    const int p = wave + kWaves * i, sw = p >> 2, mt = p & 3;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int F = 32 * mt + 8 * (q >> 2) + 4 * h + (q & 3);
-      Hreg[i][q] = Hg[(size_t)F * HD + 32 * cs + r];
+    for (int q = 0; q < 16; ++q) Hreg[i][q] = 0.f;
+    if (p < NTILE) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int F = 32 * mt + 8 * (q >> 2) + 4 * h + (q & 3);
+        Hreg[i][q] = Hg[(size_t)F * HD + col0 + 32 * sw + r];
+      }
     }
   }
   for (int F = tid; F < kD; F += kThreads) sm.s32[F] = a.s[(size_t)u * kD + F];
@@ -144,28 +192,25 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     sm.G[i] = i;
     sm.Gp[i] = vr.cache_pos[(size_t)u * lam + i];
   }
+  if (tid == 0) sm.misc[16] = 0;
 
+  // own columns of H^T as hi / lo rows (row = column - col0)
   auto rebuild_HT = [&]() {
-    for (int F = tid; F < kD; F += kThreads) {
-      uint32_t hi, lo;
-      DT::split(sm.s32[F], hi, lo);
-      sm.s_hi[F] = (uint16_t)hi;
-      sm.s_lo[F] = (uint16_t)lo;
-    }
 #pragma unroll
     for (int i = 0; i < NPW; ++i) {
-      const int p = wave + kWaves * i, cs = p >> 2, mt = p & 3;
-      const int c = 32 * cs + r;
+      const int p = wave + kWaves * i, sw = p >> 2, mt = p & 3;
+      if (p < NTILE) {
+        const int cl = 32 * sw + r;
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int F = 32 * mt + 8 * g4 + 4 * h;
-        uint32_t hi[4], lo[4];
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int F = 32 * mt + 8 * g4 + 4 * h;
+          float x[4] = {Hreg[i][4 * g4], Hreg[i][4 * g4 + 1], Hreg[i][4 * g4 + 2], Hreg[i][4 * g4 + 3]};
+          uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) DT::split(Hreg[i][4 * g4 + q], hi[q], lo[q]);
-        *reinterpret_cast<u32x2*>(sm.HT_hi + c * HTP + F) =
-            u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
-        *reinterpret_cast<u32x2*>(sm.HT_lo + c * HTP + F) =
-            u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+          for (int q = 0; q < 4; ++q) DT::split(x[q], hi[q], lo[q]);
+          *reinterpret_cast<u32x2*>(sm.HT_hi + cl * HTP + F) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+          *reinterpret_cast<u32x2*>(sm.HT_lo + cl * HTP + F) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+        }
       }
     }
   };
@@ -173,26 +218,29 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
   lds_barrier();
 
   int gs = gs0;
+  int xstep = 0;                                  // exchange steps so far
   const size_t phi_unit = (size_t)u * a.NV * kD;
   for (int j = 0; j < a.nch; ++j) {
     const long long nj = n0 + (long long)j * a.C;
     const int c = min(a.C, vr.T - j * a.C);
 
-    // ---- 1. snapshot (H_j^T hi/lo, s_j, G_j)
-    {
+    // ---- 1. snapshot (own rows of H_j^T hi/lo; rank 0: s_j, G_j)
+    if (writer) {
       uint16_t* dst = a.snapHT + ((size_t)u * a.nch + j) * 2 * HD * kD;
-      constexpr int chunks = HD * (kD / 8);  // 16-byte pieces per plane
+      constexpr int chunks = 32 * SPW * (kD / 8);   // 16-byte pieces per plane
       for (int i = tid; i < 2 * chunks; i += kThreads) {
         const int pl = i / chunks, rem = i % chunks;
         const int row = rem / (kD / 8), col = (rem % (kD / 8)) * 8;
         const uint16_t* src = (pl ? sm.HT_lo : sm.HT_hi) + row * HTP + col;
-        *reinterpret_cast<u32x4*>(dst + (size_t)pl * HD * kD + row * kD + col) =
+        *reinterpret_cast<u32x4*>(dst + (size_t)pl * HD * kD + (size_t)(col0 + row) * kD + col) =
             *reinterpret_cast<const u32x4*>(src);
       }
-      float* sdst = a.snaps + ((size_t)u * a.nch + j) * kD;
-      for (int F = tid; F < kD; F += kThreads) sdst[F] = sm.s32[F];
-      int32_t* gdst = a.snapG + ((size_t)u * a.nch + j) * lam;
-      for (int i = tid; i < gs; i += kThreads) gdst[i] = sm.G[i];
+      if (rank == 0) {
+        float* sdst = a.snaps + ((size_t)u * a.nch + j) * kD;
+        for (int F = tid; F < kD; F += kThreads) sdst[F] = sm.s32[F];
+        int32_t* gdst = a.snapG + ((size_t)u * a.nch + j) * lam;
+        for (int i = tid; i < gs; i += kThreads) gdst[i] = sm.G[i];
+      }
     }
 
     // ---- 2. candidates
@@ -213,95 +261,109 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     for (int i = tid; i < 2048; i += kThreads) sm.hist[i] = 0;
     lds_barrier();
 
-    // ---- 4a. SRE of every candidate, 32-row tiles over the waves.  All of a
-    // tile's operand loads are issued first (one memory latency per tile);
-    // the output columns are done in two halves to bound registers.
-    // Work unit = (32-candidate tile, half of the d columns): partial SRE of
-    // the half, z recomputed per unit.  Two waves per SIMD hide each other's
-    // load latency.  The two partials meet in the 64-bit key slot of e.
-    constexpr int NH = NSLAB / 2;                  // 32-column tiles per half
-    const int nunits = lam > 0 ? ((nE + 31) / 32) * 2 : 0;
-    for (int wu = wave; wu < nunits; wu += kWaves) {
-      const int t = wu >> 1, half = wu & 1;
-      const int e = t * 32 + r;
-      const bool ev = e < nE;
-      const int vi = ev ? sm.E[e] : sm.E[0];
-      const T* vrow = reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))) + 4 * h + 32 * NH * half;
-      const uint16_t* ph = a.phi_hi + phi_unit + (size_t)vi * kD + 8 * h;
-      const uint16_t* pl = a.phi_lo + phi_unit + (size_t)vi * kD + 8 * h;
-      u32x4 bh[8], bl[8];
+    // ---- 4a. SRE parts over this workgroup's columns.  Wave w takes slab
+    // w % SPW (A operands from its H^T rows in LDS) and the
+    // candidate tiles t = w / SPW, w / SPW + kWaves / SPW, ...; per tile the
+    // phi rows (B operands) and V columns come from global memory.
+    const int ntile = lam > 0 ? (nE + 31) / 32 : 0;
+    const int ntile_own = ntile > ch ? (ntile - ch + CS - 1) / CS : 0;
+    const uint32_t tag = (uint32_t)(xstep + 1);
+    uint64_t* xb = a.xbuf + ((size_t)u * 2 + (xstep & 1)) * NSLAB * LE;
+    {
+      const int sw = wave % SPW;
+      const int t_first = wave / SPW;
+      constexpr int TSTEP = kWaves / SPW;
+      if (t_first < ntile_own) {
+        const uint16_t* Ahi = sm.HT_hi + (32 * sw + r) * HTP + 8 * h;
+        const uint16_t* Alo = sm.HT_lo + (32 * sw + r) * HTP + 8 * h;
+        for (int lt = t_first; lt < ntile_own; lt += TSTEP) {
+          const int e = 32 * (ch + CS * lt) + r;
+          const bool ev = e < nE;
+          const int vi = ev ? sm.E[e] : sm.E[0];
+          const uint16_t* ph = a.phi_hi + phi_unit + (size_t)vi * kD + 8 * h;
+          const uint16_t* pl = a.phi_lo + phi_unit + (size_t)vi * kD + 8 * h;
+          u32x4 bh[8], bl[8];
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) { bh[kb] = ld16(ph + 16 * kb); bl[kb] = ld16(pl + 16 * kb); }
-      using VRaw = typename std::conditional<DT::kSplit, f32x4, u32x2>::type;
-      VRaw vraw[NH][4];
+          for (int kb = 0; kb < 8; ++kb) { bh[kb] = ld16(ph + 16 * kb); bl[kb] = ld16(pl + 16 * kb); }
+          const T* vrow = reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))) + col0 + 32 * sw + 4 * h;
+          float vv[4][4];
 #pragma unroll
-      for (int mt = 0; mt < NH; ++mt)
+          for (int g4 = 0; g4 < 4; ++g4) load4_f32(vrow + 8 * g4, vv[g4]);
+          // z = phi^T s with phi = hi + lo, as the GEMM sees it
+          float z = 0.f;
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          vraw[mt][g4] = *reinterpret_cast<const VRaw*>(vrow + 32 * mt + 8 * g4);
-      // P^T (this half's columns) and z = phi^T s (s replicated over the 32
-      // rows of an A operand): NH + 1 independent accumulators, pass-major.
-      f32x16 P[NH], Z;
+          for (int kb = 0; kb < 8; ++kb) {
+            const f32x4 s0 = *reinterpret_cast<const f32x4*>(sm.s32 + 16 * kb + 8 * h);
+            const f32x4 s1 = *reinterpret_cast<const f32x4*>(sm.s32 + 16 * kb + 8 * h + 4);
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        Z[q] = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < NH; ++mt) P[mt][q] = 0.f;
-      }
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        const int k0 = kb * 16 + 8 * h;
-        u32x4 ah[NH], al[NH];
-#pragma unroll
-        for (int mt = 0; mt < NH; ++mt) {
-          const int row = 32 * (NH * half + mt) + r;
-          ah[mt] = ld16(sm.HT_hi + row * HTP + k0);
-          al[mt] = ld16(sm.HT_lo + row * HTP + k0);
-        }
-        const u32x4 zh = ld16(sm.s_hi + k0), zl = ld16(sm.s_lo + k0);
-#pragma unroll
-        for (int mt = 0; mt < NH; ++mt) P[mt] = DT::mma(ah[mt], bh[kb], P[mt]);
-        Z = DT::mma(zh, bh[kb], Z);
-#pragma unroll
-        for (int mt = 0; mt < NH; ++mt) P[mt] = DT::mma(al[mt], bh[kb], P[mt]);
-        Z = DT::mma(zl, bh[kb], Z);
-#pragma unroll
-        for (int mt = 0; mt < NH; ++mt) P[mt] = DT::mma(ah[mt], bl[kb], P[mt]);
-        Z = DT::mma(zh, bl[kb], Z);
-      }
-      const float z = Z[0];
-      const float iz = z > 0.f ? 1.f / z : 0.f;   // z == 0: prediction 0
-      float acc = 0.f;
-#pragma unroll
-      for (int mt = 0; mt < NH; ++mt)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          float vv[4];
-          if constexpr (DT::kSplit) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) vv[q] = vraw[mt][g4][q];
-          } else {
-            const u32x2 x = vraw[mt][g4];
-            vv[0] = __uint_as_float(x[0] << 16);
-            vv[1] = __uint_as_float(x[0] & 0xFFFF0000u);
-            vv[2] = __uint_as_float(x[1] << 16);
-            vv[3] = __uint_as_float(x[1] & 0xFFFF0000u);
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t wh = bh[kb][q], wl = bl[kb][q];
+              const float f0 = DT::from_bits(wh & 0xFFFFu) + DT::from_bits(wl & 0xFFFFu);
+              const float f1 = DT::from_bits(wh >> 16) + DT::from_bits(wl >> 16);
+              z = fmaf(f0, q < 2 ? s0[2 * q] : s1[2 * q - 4], z);
+              z = fmaf(f1, q < 2 ? s0[2 * q + 1] : s1[2 * q - 3], z);
+            }
           }
+          z += xor32(z);
+          // P^T (this slab's 32 columns x 32 candidates), two accumulators
+          f32x16 P0, P1;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float df = P[mt][4 * g4 + q] * iz - vv[q];
-            acc = fmaf(df, df, acc);
+          for (int q = 0; q < 16; ++q) { P0[q] = 0.f; P1[q] = 0.f; }
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) {
+            const u32x4 ah = ld16(Ahi + 16 * kb), al = ld16(Alo + 16 * kb);
+            f32x16& P = (kb & 1) ? P1 : P0;
+            P = DT::mma(ah, bh[kb], P);
+            P = DT::mma(al, bh[kb], P);
+            P = DT::mma(ah, bl[kb], P);
+          }
+          const float iz = z > 0.f ? 1.f / z : 0.f;   // z == 0: prediction 0
+          float acc = 0.f;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float df = (P0[4 * g4 + q] + P1[4 * g4 + q]) * iz - vv[g4][q];
+              acc = fmaf(df, df, acc);
+            }
+          acc += xor32(acc);
+          if (ev && h == 0) {
+            if (k == 1) sm.part[sw * LE + e] = acc;
+            else __hip_atomic_store(xb + (size_t)(grp * SPW + sw) * LE + e,
+                                    ((uint64_t)tag << 32) | __float_as_uint(acc),
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
-      acc += xor32(acc);
-      if (ev && h == 0) reinterpret_cast<float*>(sm.keys)[2 * e + 1 - half] = acc;
+      }
     }
     lds_barrier();
-    // keys = (SRE bits << 32) | (0xFFFFFFFF - position); SRE = half 0 + half 1
+
+    ++xstep;
+
+    // keys = (SRE bits << 32) | (0xFFFFFFFF - position); SRE = slab parts in
+    // order (k > 1: read back from the exchange, waiting for each tag)
     uint64_t kmin = ~0ull, kmax = 0;
+    bool lost = false;
     for (int e = tid; lam > 0 && e < nE; e += kThreads) {
-      const float* pp = reinterpret_cast<const float*>(sm.keys) + 2 * e;
-      const float sre = pp[1] + pp[0];             // column halves 0 and 1
+      float sre = 0.f;
+      if (k > 1) {
+        uint64_t w[NSLAB];
+#pragma unroll
+        for (int q = 0; q < NSLAB; ++q)
+          w[q] = __hip_atomic_load(xb + (size_t)q * LE + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int q = 0; q < NSLAB; ++q) {
+          int spins = 0;
+          while ((uint32_t)(w[q] >> 32) != tag && !lost) {
+            if (++spins > kSpinLimit) lost = true;
+            w[q] = __hip_atomic_load(xb + (size_t)q * LE + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          sre += __uint_as_float((uint32_t)w[q]);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < NSLAB; ++q) sre += sm.part[q * LE + e];
+      }
       const uint32_t pos = e < gs ? (uint32_t)sm.Gp[e] : (uint32_t)(lo_p + (e - gs));
       const uint64_t key = ((uint64_t)__float_as_uint(sre) << 32) | (uint64_t)(0xFFFFFFFFu - pos);
       sm.keys[e] = key;
@@ -315,8 +377,13 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
       kmax = a2 > kmax ? a2 : kmax;
     }
     if (lane == 0) { sm.kred[2 * wave] = kmin; sm.kred[2 * wave + 1] = kmax; }
+    if (lost) sm.misc[16] = 1;
     lds_barrier();
-    if (a.dbg_keys) {
+    if (sm.misc[16]) {           // a partner is lost: stop (the error flag is set)
+      if (tid == 0) atomicOr(a.err, 1);
+      return;
+    }
+    if (a.dbg_keys && rank == 0) {
       uint64_t* dk = a.dbg_keys + ((size_t)u * a.nch + j) * (lam + a.C);
       for (int e = tid; e < nE; e += kThreads) dk[e] = sm.keys[e];
     }
@@ -421,10 +488,10 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     gs = lam;
     lds_barrier();
 
-    // ---- 4d. fold the rest into H (MFMA) and s, 64 tokens per block.  The
-    // gather is by rows: lane = token, wave = feature / column chunks, with
-    // 16-byte loads; the tiles are written transposed (token-contiguous) for
-    // the MFMA operands.
+    // ---- 4d. fold the rest into own columns of H (MFMA) and into s, 64
+    // tokens per block.  The gather is by rows: lane = token, wave = feature
+    // / column chunks, with 16-byte loads where possible; the tiles are
+    // written transposed (token-contiguous) for the MFMA operands.
     const int nS = nE - lam;
     float sacc = 0.f;
     for (int sb = 0; sb < nS; sb += 64) {
@@ -441,18 +508,18 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
           xh[q] = tv ? ld16(a.phi_hi + phi_unit + (size_t)vi * kD + f0) : u32x4{0, 0, 0, 0};
           xl[q] = tv ? ld16(a.phi_lo + phi_unit + (size_t)vi * kD + f0) : u32x4{0, 0, 0, 0};
         }
-        // V: HD / 8 columns per wave
-        constexpr int VC = HD / kWaves;                  // 16 or 8 columns
+        // V: own columns, VC per wave
+        constexpr int VC = 32 * SPW / kWaves;            // 4, 8 or 16 columns
         float vx[VC];
         {
-          const T* vrow = reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))) + VC * wave;
+          const T* vrow = reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))) + col0 + VC * wave;
 #pragma unroll
-          for (int q8 = 0; q8 < VC; q8 += 8) {
-            float x[8];
-            if (tv) load8_f32(vrow + q8, x);
-            else for (int q = 0; q < 8; ++q) x[q] = 0.f;
+          for (int q4 = 0; q4 < VC; q4 += 4) {
+            float x[4];
+            if (tv) load4_f32(vrow + q4, x);
+            else for (int q = 0; q < 4; ++q) x[q] = 0.f;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) vx[q8 + q] = x[q];
+            for (int q = 0; q < 4; ++q) vx[q4 + q] = x[q];
           }
         }
 #pragma unroll
@@ -489,23 +556,17 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
       const int nkb = min(4, (nS - sb + 15) / 16);
       for (int kb = 0; kb < nkb; ++kb) {
         const int k0 = 16 * kb + 8 * h;
-        u32x4 bv[NPW], ah[NPW], al[NPW];
 #pragma unroll
         for (int i = 0; i < NPW; ++i) {
-          const int p = wave + kWaves * i, cs = p >> 2, mt = p & 3;
-          bv[i] = ld16(sm.VT_hi + (32 * cs + r) * STP + k0);
-          ah[i] = ld16(sm.phT_hi + (32 * mt + r) * STP + k0);
-          al[i] = ld16(sm.phT_lo + (32 * mt + r) * STP + k0);
-        }
-#pragma unroll
-        for (int i = 0; i < NPW; ++i) Hreg[i] = DT::mma(ah[i], bv[i], Hreg[i]);
-#pragma unroll
-        for (int i = 0; i < NPW; ++i) Hreg[i] = DT::mma(al[i], bv[i], Hreg[i]);
-        if constexpr (DT::kSplit) {
-#pragma unroll
-          for (int i = 0; i < NPW; ++i) {
-            const int p = wave + kWaves * i, cs = p >> 2;
-            Hreg[i] = DT::mma(ah[i], ld16(sm.VT_lo + (32 * cs + r) * STP + k0), Hreg[i]);
+          const int p = wave + kWaves * i, sw = p >> 2, mt = p & 3;
+          if (p < NTILE) {
+            const u32x4 bv = ld16(sm.VT_hi + (32 * sw + r) * STP + k0);
+            const u32x4 ah = ld16(sm.phT_hi + (32 * mt + r) * STP + k0);
+            const u32x4 al = ld16(sm.phT_lo + (32 * mt + r) * STP + k0);
+            Hreg[i] = DT::mma(ah, bv, Hreg[i]);
+            Hreg[i] = DT::mma(al, bv, Hreg[i]);
+            if constexpr (DT::kSplit)
+              Hreg[i] = DT::mma(ah, ld16(sm.VT_lo + (32 * sw + r) * STP + k0), Hreg[i]);
           }
         }
       }
@@ -523,35 +584,51 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     lds_barrier();
   }
 
-  // ---- final state
+  // ---- final state: own columns of H (candidate group 0); rank 0: s, the cache list
   float* Ho = a.H + (size_t)u * kD * HD;
 #pragma unroll
   for (int i = 0; i < NPW; ++i) {
-    const int p = wave + kWaves * i, cs = p >> 2, mt = p & 3;
+    const int p = wave + kWaves * i, sw = p >> 2, mt = p & 3;
+    if (p < NTILE && writer) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int F = 32 * mt + 8 * (q >> 2) + 4 * h + (q & 3);
-      Ho[(size_t)F * HD + 32 * cs + r] = Hreg[i][q];
+      for (int q = 0; q < 16; ++q) {
+        const int F = 32 * mt + 8 * (q >> 2) + 4 * h + (q & 3);
+        Ho[(size_t)F * HD + col0 + 32 * sw + r] = Hreg[i][q];
+      }
     }
   }
-  for (int F = tid; F < kD; F += kThreads) a.s[(size_t)u * kD + F] = sm.s32[F];
-  for (int i = tid; i < gs; i += kThreads) a.finalG[(size_t)u * lam + i] = sm.G[i];
+  if (rank == 0) {
+    for (int F = tid; F < kD; F += kThreads) a.s[(size_t)u * kD + F] = sm.s32[F];
+    for (int i = tid; i < gs; i += kThreads) a.finalG[(size_t)u * lam + i] = sm.G[i];
+  }
+}
+
+template <class DT, int HD, int SPW>
+static hipError_t launch_chain_t(const ChainArgs& a, int U, hipStream_t st) {
+  const size_t lds = chain_layout(a.vr.lam, a.C, SPW, DT::kSplit).total;
+  const void* fn = (const void*)chain_kernel<DT, HD, SPW>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((chain_kernel<DT, HD, SPW>), dim3(U * a.k), dim3(kThreads), lds, st, a);
+  return hipGetLastError();
 }
 
 template <class DT, int HD>
-static hipError_t launch_chain_t(const ChainArgs& a, int U, hipStream_t st) {
-  const size_t lds = chain_lds_bytes(a.vr.lam, a.C, HD, DT::kSplit);
-  (void)hipFuncSetAttribute((const void*)chain_kernel<DT, HD>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((chain_kernel<DT, HD>), dim3(U), dim3(kThreads), lds, st, a);
-  return hipGetLastError();
+static hipError_t launch_chain_k(const ChainArgs& a, int U, hipStream_t st) {
+  constexpr int NSLAB = HD / 32;
+  if (a.k >= NSLAB) return launch_chain_t<DT, HD, 1>(a, U, st);   // k = NSLAB * CS
+  if (a.k == 1) return launch_chain_t<DT, HD, NSLAB>(a, U, st);
+  if constexpr (NSLAB == 4) {
+    if (a.k == 2) return launch_chain_t<DT, HD, 2>(a, U, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_chain(const ChainArgs& a, int U, bool f32, hipStream_t st) {
   if (U <= 0) return hipSuccess;
   if (a.vr.d == 64)
-    return f32 ? launch_chain_t<F32, 64>(a, U, st) : launch_chain_t<BF16, 64>(a, U, st);
-  return f32 ? launch_chain_t<F32, 128>(a, U, st) : launch_chain_t<BF16, 128>(a, U, st);
+    return f32 ? launch_chain_k<F32, 64>(a, U, st) : launch_chain_k<BF16, 64>(a, U, st);
+  return f32 ? launch_chain_k<F32, 128>(a, U, st) : launch_chain_k<BF16, 128>(a, U, st);
 }
 
 }  // namespace lola

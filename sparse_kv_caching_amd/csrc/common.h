@@ -165,6 +165,16 @@ __device__ __forceinline__ void load8_f32(const float* p, float* o) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) { o[j] = a[j]; o[4 + j] = b[j]; }
 }
+// Load 4 consecutive input elements as float.
+__device__ __forceinline__ void load4_f32(const uint16_t* p, float* o) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  o[0] = __uint_as_float(w[0] << 16); o[1] = __uint_as_float(w[0] & 0xFFFF0000u);
+  o[2] = __uint_as_float(w[1] << 16); o[3] = __uint_as_float(w[1] & 0xFFFF0000u);
+}
+__device__ __forceinline__ void load4_f32(const float* p, float* o) {
+  const f32x4 w = *reinterpret_cast<const f32x4*>(p);
+  o[0] = w[0]; o[1] = w[1]; o[2] = w[2]; o[3] = w[3];
+}
 // Load 8 consecutive bf16 input elements directly as an operand.
 __device__ __forceinline__ bf16x8 load8_bf16op(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));

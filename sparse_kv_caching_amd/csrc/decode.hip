@@ -212,16 +212,6 @@ __device__ __forceinline__ f32x16 slab_product(const u32x4* slot, const u32x4 (&
   return P0;
 }
 
-// 4 consecutive elements as float
-__device__ __forceinline__ void load4_f32(const uint16_t* p, float* o) {
-  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
-  o[0] = __uint_as_float(w[0] << 16); o[1] = __uint_as_float(w[0] & 0xFFFF0000u);
-  o[2] = __uint_as_float(w[1] << 16); o[3] = __uint_as_float(w[1] & 0xFFFF0000u);
-}
-__device__ __forceinline__ void load4_f32(const float* p, float* o) {
-  const f32x4 w = *reinterpret_cast<const f32x4*>(p);
-  o[0] = w[0]; o[1] = w[1]; o[2] = w[2]; o[3] = w[3];
-}
 // N consecutive elements (N = 1 or 2) as float
 template <int N>
 __device__ __forceinline__ void load_cols(const uint16_t* p, float* o) {

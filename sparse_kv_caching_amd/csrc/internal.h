@@ -81,6 +81,12 @@ struct ChainArgs {
   int32_t* finalG;          // [U, lam]
   int NV, nch, C;
   uint64_t* dbg_keys;       // optional [U, nch, lam + C]: candidate keys per step
+  // k workgroups per unit: 1, 2, or (d / 32) x CS with CS candidate groups;
+  // every workgroup of the grid resident at once
+  int k;
+  int xcd_group;            // U % 8 == 0: a unit's workgroups share a block residue mod 8
+  uint64_t* xbuf;           // [U, 2, d / 32, lam + C]  tagged SRE parts per slab (k > 1), zeroed
+  int* err;                 // device error flag: bit 0 = an exchange partner was lost
 };
 
 // K3: window + cache softmax attention merged with the linear read.
@@ -148,6 +154,7 @@ hipError_t launch_import(bool f32, int U, void* ring_k, void* ring_v, void* cach
 size_t decode_lds_bytes(int lam, int eta, int d, int g, bool f32);
 void decode_plan(int lam, int eta, int d, int g, bool f32, int* kc, int* nslot);
 hipError_t launch_transpose_w(const void* W, void* WT, int Hkv, int d, bool f32, hipStream_t st);
+hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st);
 hipError_t launch_snappos(const VirtRows& vr, const int32_t* snapG, int32_t* out, int nch,
                           int C, int U, hipStream_t st);
 

@@ -200,4 +200,16 @@ hipError_t launch_snappos(const VirtRows& vr, const int32_t* snapG, int32_t* out
   return hipGetLastError();
 }
 
+// fill n 32-bit words with 0 (a kernel, so that the call is safe to capture)
+__global__ void zero_u32_kernel(unsigned* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, p, n);
+  return hipGetLastError();
+}
+
 }  // namespace lola

@@ -30,7 +30,7 @@ KERNELS = ("phi", "chain", "attn", "finalize", "decode")
 EXPORTED = [
     "lola_state_init", "lola_state_free", "lola_state_tokens", "lola_prefill_workspace_bytes",
     "lola_prefill_chunk", "lola_prefill_debug", "lola_decode_step", "lola_state_reset",
-    "lola_profile", "lola_state_export", "lola_state_import",
+    "lola_state_check", "lola_profile", "lola_state_export", "lola_state_import",
     "lola_strerror", "lola_last_error",
 ]
 
@@ -80,6 +80,7 @@ def library() -> ctypes.CDLL:
         lib.lola_prefill_debug.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, sz, vp, vp, vp]
         lib.lola_decode_step.argtypes = [vp, vp, vp, vp, vp, i32, vp]
         lib.lola_state_reset.argtypes = [vp, vp]
+        lib.lola_state_check.argtypes = [vp, vp]
         lib.lola_profile.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(ctypes.c_longlong)]
         lib.lola_state_export.argtypes = [vp, ctypes.POINTER(LolaStateView), vp]
@@ -88,8 +89,8 @@ def library() -> ctypes.CDLL:
         lib.lola_strerror.restype = ctypes.c_char_p
         lib.lola_last_error.restype = ctypes.c_char_p
         for f in ("lola_state_init", "lola_state_free", "lola_prefill_workspace_bytes",
-                  "lola_prefill_chunk", "lola_prefill_debug", "lola_decode_step", "lola_state_reset",
-    "lola_profile", "lola_state_export",
+                  "lola_prefill_chunk", "lola_prefill_debug", "lola_decode_step",
+                  "lola_state_reset", "lola_state_check", "lola_profile", "lola_state_export",
                   "lola_state_import"):
             getattr(lib, f).restype = i32
         _lib = lib
@@ -146,6 +147,10 @@ class LolaLayer:
             self.free()
         except Exception:
             pass
+
+    def check(self, stream=None):
+        """Synchronise and raise if a kernel recorded a device-side fault."""
+        _check(self.lib.lola_state_check(self._st, _stream(stream)), "lola_state_check")
 
     def reset(self, stream=None):
         """Empty the state (n = 0) without reallocating."""
@@ -219,7 +224,9 @@ class LolaLayer:
 
     def export(self, stream=None) -> Dict[str, torch.Tensor]:
         """Canonical state: H (U, D, d), s (U, D), win_k/v (U, eta, d) oldest
-        first, cache_pos (U, lam) ascending (-1 padding), cache_k/v."""
+        first, cache_pos (U, lam) ascending (-1 padding), cache_k/v.  Raises if
+        a kernel recorded a device-side fault (lola_state_check)."""
+        self.check(stream)
         t = self._view_tensors(torch.device("cuda", torch.cuda.current_device()))
         view = LolaStateView(0, *[t[k].data_ptr() for k in
                                   ("H", "s", "win_k", "win_v", "cache_pos", "cache_k", "cache_v")])
