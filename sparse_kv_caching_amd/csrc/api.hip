@@ -111,8 +111,8 @@ WsLayout ws_layout(const lola_state* st, int T, int C) {
 
 // Workgroups per unit for the chain: the whole grid must be resident (one
 // workgroup per compute unit).  First split the columns into slabs (k = d / 32),
-// then split the candidate tiles into CS groups until every wave of a
-// workgroup has at most one tile per step (or the device is full).
+// then split the candidate tiles into CS groups until a workgroup has at most
+// one tile per SIMD per step (or the device is full).
 int chain_workgroups(int U, int ncu, int d, int lam, int C) {
   const int nslab = d / 32;
   const long long cap = ncu / std::max(U, 1);
@@ -120,7 +120,7 @@ int chain_workgroups(int U, int ncu, int d, int lam, int C) {
   if (cap < nslab) return nslab >= 4 && cap >= 2 ? 2 : 1;
   const int tiles = (lam + C + 31) / 32;
   int cs = 1;
-  while ((tiles + cs - 1) / cs > 8 && nslab * cs * 2 <= cap && cs < 16) cs *= 2;
+  while ((tiles + cs - 1) / cs > 4 && nslab * cs * 2 <= cap && cs < 32) cs *= 2;
   return nslab * cs;
 }
 

@@ -95,7 +95,7 @@ __host__ __device__ inline ChainLayout chain_layout(int lam, int C, int spw, boo
   L.E = take(le * 4);                      // candidates (virtual indices)
   L.part = take((uint32_t)spw * le * 4);   // [slab][candidate] SRE parts
   L.keys = take(le * 8);
-  L.hist = take(2048 * 4);                 // radix histogram
+  L.hist = take(512 * 4);                  // two radix histograms
   const uint32_t sel_end = off;
   off = region;
   L.phT_hi = take(kD * STP * 2);           // [kD][STP]
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
       continue;
     }
     for (int i = tid; i < nE; i += kThreads) sm.E[i] = i < gs ? sm.G[i] : vi_L0 + (i - gs);
-    for (int i = tid; i < 2048; i += kThreads) sm.hist[i] = 0;
+    for (int i = tid; i < 512; i += kThreads) sm.hist[i] = 0;
     lds_barrier();
 
     // ---- 4a. SRE parts over this workgroup's columns.  Wave w takes slab
@@ -389,9 +389,9 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     }
 
     // ---- 4b. exact top-lam: radix select of the lam-th largest key with
-    // 11-bit digits, starting at the highest bit where the keys differ (one
-    // pass separates a few hundred keys in most steps).  lam == 0: nothing
-    // is kept.  Thread t owns 2048 / kThreads bins.
+    // 8-bit digits, from the highest bit where the keys differ down; one wave
+    // scans the 256 bins, and two histograms alternate so that a pass needs
+    // two barriers.  lam == 0: nothing is kept.
     uint64_t prefix = 0, mask = 0;
     if (lam > 0) {
       kmin = sm.kred[0];
@@ -405,47 +405,44 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
       const int top = 63 - __clzll((long long)(kmin ^ kmax));
       mask = top >= 63 ? 0 : (~0ull << (top + 1));
       prefix = kmin & mask;
-      int shift = top - 10 > 0 ? top - 10 : 0;
+      int hi_bit = top + 1;          // the digit covers bits [lo, hi_bit)
       int need = lam;
+      int buf = 0;
       for (;;) {
+        const int lo = hi_bit > 8 ? hi_bit - 8 : 0;
+        const uint32_t dmask = (1u << (hi_bit - lo)) - 1u;
+        int32_t* H = sm.hist + 256 * buf;
         for (int e = tid; e < nE; e += kThreads) {
           const uint64_t k = sm.keys[e];
-          if ((k & mask) == prefix) atomicAdd(&sm.hist[(k >> shift) & 2047], 1);
+          if ((k & mask) == prefix) atomicAdd(&H[(uint32_t)(k >> lo) & dmask], 1);
         }
+        for (int i = tid; i < 256; i += kThreads) sm.hist[256 * (buf ^ 1) + i] = 0;
         lds_barrier();
-        // thread t owns bins [BPT (T-1-t), BPT (T-1-t) + BPT): scanning the
-        // threads in order walks the bins from the top down
-        constexpr int BPT = 2048 / kThreads;
-        const int b0 = BPT * (kThreads - 1 - tid);
-        int cnt[BPT], tot = 0;
+        if (wave == 0) {
+          // lane l owns bins 255 - 4 l - q: the lanes in order walk the bins
+          // from the top down
+          int cnt[4], tot = 0;
 #pragma unroll
-        for (int q = 0; q < BPT; ++q) { cnt[q] = sm.hist[b0 + q]; tot += cnt[q]; }
-        const int incl = wave_incl_scan(tot);
-        if (lane == 63) sm.misc[8 + wave] = incl;
-        lds_barrier();
-        int above = incl - tot;
+          for (int q = 0; q < 4; ++q) { cnt[q] = H[255 - 4 * lane - q]; tot += cnt[q]; }
+          int above = wave_incl_scan(tot) - tot;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-          if (w < wave) above += sm.misc[8 + w];
-#pragma unroll
-        for (int q = BPT - 1; q >= 0; --q) {
-          if (above < need && need <= above + cnt[q]) {
-            sm.misc[0] = b0 + q;
-            sm.misc[1] = need - above;
-            sm.misc[2] = cnt[q];
+          for (int q = 0; q < 4; ++q) {
+            if (above < need && need <= above + cnt[q]) {
+              sm.misc[0] = 255 - 4 * lane - q;
+              sm.misc[1] = need - above;
+              sm.misc[2] = cnt[q];
+            }
+            above += cnt[q];
           }
-          above += cnt[q];
         }
         lds_barrier();
         const int bsel = sm.misc[0], cb = sm.misc[2];
         need = sm.misc[1];
-        prefix |= (uint64_t)bsel << shift;
-        mask |= (uint64_t)2047 << shift;
-        if (cb == need || shift == 0) break;
-        shift = shift >= 11 ? shift - 11 : 0;
-        lds_barrier();   // every thread has read misc before it changes
-        for (int i = tid; i < 2048; i += kThreads) sm.hist[i] = 0;
-        lds_barrier();
+        prefix |= (uint64_t)bsel << lo;
+        mask |= (uint64_t)dmask << lo;
+        if (cb == need || lo == 0) break;
+        hi_bit = lo;
+        buf ^= 1;
       }
     }
 
