@@ -137,6 +137,8 @@ int supported_C(const lola_state* st, int C) {
     return fail(LOLA_ERR_UNSUPPORTED, "chunk length C=%d: need C == 1 or a multiple of 32 <= 256", C);
   if (chain_lds_bytes(st->cfg.cache, C, st->d, st->f32) > kMaxLds)
     return fail(LOLA_ERR_UNSUPPORTED, "lambda + C too large for the chain kernel's LDS");
+  if (attn_lds_bytes(st->d, st->cfg.cache, st->f32) > kMaxLds)
+    return fail(LOLA_ERR_UNSUPPORTED, "lambda too large for the attention kernel's LDS");
   return LOLA_OK;
 }
 
@@ -398,11 +400,11 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   }
 
   AttnArgs aa;
-  aa.vr = vr; aa.q = q; aa.W = st->W;
+  aa.vr = vr; aa.q = q; aa.WT = st->WT;
   aa.snapHT = ca.snapHT; aa.snaps = ca.snaps; aa.snapG = ca.snapG;
   aa.out = (float*)out;
   aa.g = g; aa.Hkv = st->cfg.kv_heads; aa.nch = nch; aa.C = C;
-  aa.ptile = std::min(C, 128 / g);
+  aa.ptile = attn_positions_per_block(C, g);
   aa.nblk = aa.ptile / 32;
   { ProfScope ps(st, LOLA_KERNEL_ATTN, s); e = launch_attn(aa, U, st->f32, s); }
   if (e != hipSuccess) return hip_fail(st, e, "attention launch");

@@ -8,12 +8,16 @@
 // chunks run in parallel: they only need the per-chunk snapshots (H_j, s_j,
 // G_j) written by the chain kernel.
 //
-// One workgroup = one unit, one chunk, and up to 4 waves; wave = one q-head
-// x 32 positions (the GQA heads of a unit share every K/V tile).  Scores are
-// computed transposed, S^T = K Q^T (32 keys x 32 queries), so each lane owns
+// One workgroup = one unit, one chunk, one tile of up to 256 / g positions,
+// and 8 waves; wave = one q-head x 32 positions, so the GQA heads of a unit
+// share every staged K/V tile.  Keys are staged 64 at a time, double-buffered:
+// the global loads of tile t + 1 are in flight while tile t is multiplied,
+// and one barrier per tile separates the buffers.  Scores are computed
+// transposed, S^T = K Q^T (32 keys x 32 queries per MFMA), so each lane owns
 // one query and softmax statistics need a single cross-half exchange; P then
 // feeds O^T += V^T P^T straight from registers (the K index of that MFMA is
-// permuted to match the result layout, see common.h).
+// permuted to match the result layout, see common.h), with V staged
+// transposed (key pairs packed per dword).
 //
 // Exponentials are unshifted in Eq. (14); here they are shifted by a running
 // maximum m >= 0 (log2 domain) and the linear terms are scaled by the same
@@ -30,35 +34,42 @@ namespace lola {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int HTH = kM + 8;  // padded row of one half of H^T in LDS
-constexpr int KTP = 36;      // row of the V^T tile: 32 keys + 4 (conflict-free pitch)
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int KT = 64;        // keys per staged tile
+constexpr int HTS = kD + 8;   // LDS row of H^T (16-bit elements)
+constexpr int VTS = KT + 8;   // LDS row of the V^T tile (keys)
 
 // Byte offsets of the LDS arrays; the key phase reuses the region of the
 // linear-read phase.
 struct AttnLayout {
-  uint32_t WT_hi, WT_lo, HT_hi, HT_lo, s;      // linear-read phase
-  uint32_t K_hi, K_lo, VT_a, VT_b;             // key phase
+  uint32_t G;                                  // both phases
+  uint32_t WT, HT_hi, HT_lo, s;                // linear-read phase
+  uint32_t K[2], KL[2], VT[2], VTL[2];         // key phase, two buffers
   uint32_t total;
 };
 
 inline __host__ __device__ uint32_t al16(uint32_t x) { return (x + 15u) & ~15u; }
 
-__host__ __device__ inline AttnLayout attn_layout(int d, bool f32) {
+__host__ __device__ inline AttnLayout attn_layout(int d, int lam, bool f32) {
   AttnLayout L;
   uint32_t off = 0;
   auto take = [&](uint32_t b) { const uint32_t o = off; off = al16(off + b); return o; };
-  L.WT_hi = take((uint32_t)kM * (d + 8) * 2);          // [kM][d + 8]
-  L.WT_lo = take(f32 ? (uint32_t)kM * (d + 8) * 2 : 16);
-  L.HT_hi = take((uint32_t)d * HTH * 2);               // [d][HTH], one feature half
-  L.HT_lo = take((uint32_t)d * HTH * 2);
+  const uint32_t esz = f32 ? 4 : 2;
+  L.G = take((uint32_t)(lam > 0 ? lam : 1) * 4);      // cache at chunk start (virtual indices)
+  const uint32_t base = off;
+  L.WT = take((uint32_t)kM * (d + 8) * esz);          // [kM][d + 8] W^T, input dtype
+  L.HT_hi = take((uint32_t)d * HTS * 2);               // [d][HTS]
+  L.HT_lo = take((uint32_t)d * HTS * 2);
   L.s = take(kD * 4);
   const uint32_t phaseA = off;
-  off = 0;
-  L.K_hi = take((uint32_t)32 * (d + 8) * 2);           // [32][d + 8]
-  L.K_lo = take(f32 ? (uint32_t)32 * (d + 8) * 2 : 16);
-  L.VT_a = take((uint32_t)d * KTP * 2);                // [d][KTP] fp16 (bf16 inputs) or hi
-  L.VT_b = take(f32 ? (uint32_t)d * KTP * 2 : 16);     //          lo (fp32 inputs)
+  off = base;
+  for (int b = 0; b < 2; ++b) {
+    L.K[b] = take((uint32_t)KT * (d + 8) * 2);         // [KT][d + 8] bf16 (fp32 inputs: fp16 hi)
+    L.KL[b] = take(f32 ? (uint32_t)KT * (d + 8) * 2 : 16);   //                  fp16 lo
+    L.VT[b] = take((uint32_t)d * VTS * 2);             // [d][VTS] fp16 (fp32 inputs: hi)
+    L.VTL[b] = take(f32 ? (uint32_t)d * VTS * 2 : 16); //                       lo
+  }
   L.total = phaseA > off ? phaseA : off;
   return L;
 }
@@ -71,16 +82,23 @@ __device__ __forceinline__ u32x4 sigma_load(const uint16_t* row16, int h) {
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
+__device__ __forceinline__ uint32_t f16_bits(float x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
 }  // namespace
 
-size_t attn_lds_bytes(int d, bool f32) { return attn_layout(d, f32).total; }
+size_t attn_lds_bytes(int d, int lam, bool f32) { return attn_layout(d, lam, f32).total; }
 
 template <class DT, int HD>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   using T = typename DT::T;
-  constexpr int d = HD;
   constexpr int KB = HD / 16;     // 16-wide K blocks over the head dim
-  constexpr int nmt = HD / 32;    // 32-row tiles of the output
+  constexpr int NMT = HD / 32;    // 32-row tiles of the output
+  constexpr int KRS = HD + 8;     // LDS row of a staged key (elements)
+  constexpr int PER = 16 / (int)sizeof(T);       // input elements per 16-byte piece
+  constexpr int KPT = KT * HD / PER / kThreads;  // key pieces per thread and tile
+  constexpr int VITEMS = (KT / 2) * (HD / 8);    // (key pair, 8 columns) items per tile
   const VirtRows vr = a.vr;
   const int lam = vr.lam, eta = vr.eta;
   const int pt = blockIdx.x, j = blockIdx.y, u = blockIdx.z;
@@ -98,34 +116,69 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   const bool wactive = hd < a.g && p0 < pend;
   const long long qpos = p0 + r;
   const bool qvalid = wactive && qpos < pend;
+  const int gsj = (int)min((long long)lam, max(0LL, nj - eta));
+  const long long lo_j = max(0LL, nj - eta);
+  const int nkeys = gsj + (int)(pend - lo_j);
+  // last key any query of this wave sees (wave-uniform)
+  const int wlast = gsj + (int)(min(p0 + 31, pend - 1) - lo_j);
+  const int n0e = eta > 0 ? (int)(n0 % eta) : 0;            // ring slot of position n0 - eta
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const AttnLayout L = attn_layout(d, DT::kSplit);
-  struct {
-    uint16_t *WT_hi, *WT_lo, *HT_hi, *HT_lo;
-    float* s;
-    uint16_t *K_hi, *K_lo, *VT_a, *VT_b;
-  } sm = {(uint16_t*)(smem + L.WT_hi), (uint16_t*)(smem + L.WT_lo), (uint16_t*)(smem + L.HT_hi),
-          (uint16_t*)(smem + L.HT_lo), (float*)(smem + L.s), (uint16_t*)(smem + L.K_hi),
-          (uint16_t*)(smem + L.K_lo), (uint16_t*)(smem + L.VT_a), (uint16_t*)(smem + L.VT_b)};
+  const AttnLayout L = attn_layout(HD, lam, DT::kSplit);
+  int32_t* sm_G = (int32_t*)(smem + L.G);
+  T* sm_WT = (T*)(smem + L.WT);
+  uint16_t* sm_HT_hi = (uint16_t*)(smem + L.HT_hi);
+  uint16_t* sm_HT_lo = (uint16_t*)(smem + L.HT_lo);
+  float* sm_s = (float*)(smem + L.s);
 
-  // ---- W^T of this KV head and s_j into LDS
-  const T* W = reinterpret_cast<const T*>(a.W) + (size_t)kvh * d * kM;
-  for (int i = tid; i < d * kM; i += kThreads) {
-    const int k = i / kM, f = i % kM;
-    uint32_t hi, lo;
-    DT::split(DT::to_f32(W[i]), hi, lo);
-    sm.WT_hi[f * (d + 8) + k] = (uint16_t)hi;
-    if (DT::kSplit) sm.WT_lo[f * (d + 8) + k] = (uint16_t)lo;
+  // row of virtual index vi (cache slot, ring slot or input row), 32-bit math
+  const T* ck = reinterpret_cast<const T*>(vr.cache_k) + (size_t)u * lam * HD;
+  const T* cv = reinterpret_cast<const T*>(vr.cache_v) + (size_t)u * lam * HD;
+  const T* rk = reinterpret_cast<const T*>(vr.ring_k) + (size_t)u * eta * HD;
+  const T* rv = reinterpret_cast<const T*>(vr.ring_v) + (size_t)u * eta * HD;
+  const T* ik = reinterpret_cast<const T*>(vr.in_k) + (size_t)u * vr.T * HD;
+  const T* iv = reinterpret_cast<const T*>(vr.in_v) + (size_t)u * vr.T * HD;
+  auto vrow = [&](int vi, bool val) -> const T* {
+    if (vi < lam) return (val ? cv : ck) + (size_t)vi * HD;
+    const int off = vi - lam;                       // position n0 - eta + off
+    if (off < eta) {
+      int slot = n0e + off;
+      if (slot >= eta) slot -= eta;
+      return (val ? rv : rk) + (size_t)slot * HD;
+    }
+    return (val ? iv : ik) + (size_t)(off - eta) * HD;
+  };
+  // virtual index of key kk: cache G_j, then local positions lo_j ..
+  const int vi_loc0 = lam + eta + (int)(lo_j - n0);
+  auto key_vi = [&](int kk) -> int { return kk < gsj ? sm_G[kk] : vi_loc0 + (kk - gsj); };
+
+  // ---- stage W^T (this KV head), H_j^T hi / lo, s_j and G_j
+  {
+    const T* WT = reinterpret_cast<const T*>(a.WT) + (size_t)kvh * kM * HD;
+    constexpr int WPIECES = kM * HD / PER;
+    for (int i = tid; i < WPIECES; i += kThreads) {
+      const int f = i / (HD / PER), c = (i % (HD / PER)) * PER;
+      *reinterpret_cast<u32x4*>(sm_WT + f * KRS + c) = *reinterpret_cast<const u32x4*>(WT + (size_t)f * HD + c);
+    }
+    const uint16_t* snap = a.snapHT + ((size_t)u * a.nch + j) * 2 * HD * kD;
+    constexpr int HPIECES = HD * (kD / 8);
+    for (int i = tid; i < 2 * HPIECES; i += kThreads) {
+      const int pl = i / HPIECES, rem = i % HPIECES;
+      const int row = rem / (kD / 8), col = (rem % (kD / 8)) * 8;
+      *reinterpret_cast<u32x4*>((pl ? sm_HT_lo : sm_HT_hi) + row * HTS + col) =
+          *reinterpret_cast<const u32x4*>(snap + (size_t)pl * HD * kD + (size_t)row * kD + col);
+    }
+    const float* sj = a.snaps + ((size_t)u * a.nch + j) * kD;
+    for (int F = tid; F < kD; F += kThreads) sm_s[F] = sj[F];
+    const int32_t* Gj = a.snapG + ((size_t)u * a.nch + j) * lam;
+    for (int i = tid; i < gsj; i += kThreads) sm_G[i] = Gj[i];
   }
-  const float* sj = a.snaps + ((size_t)u * a.nch + j) * kD;
-  for (int F = tid; F < kD; F += kThreads) sm.s[F] = sj[F];
 
   // ---- Q operands (B of S^T = K Q^T): lane = query r, K-slots 8h .. 8h+7
   u32x4 qh[KB], ql[KB];
   {
     const T* qrow = reinterpret_cast<const T*>(a.q) +
-                    (((size_t)u * a.g + (wactive ? hd : 0)) * vr.T + (size_t)(qvalid ? qpos - n0 : 0)) * d;
+                    (((size_t)u * a.g + (wactive ? hd : 0)) * vr.T + (size_t)(qvalid ? qpos - n0 : 0)) * HD;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int k0 = 16 * kb + 8 * h;
@@ -136,12 +189,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         splitop<DT>(x, qh[kb], ql[kb]);
       } else {
         qh[kb] = qvalid ? ld16(reinterpret_cast<const uint16_t*>(qrow) + k0) : u32x4{0, 0, 0, 0};
+        ql[kb] = u32x4{0, 0, 0, 0};
       }
     }
   }
   __syncthreads();
 
-  // ---- phi(q): u^T = W^T q^T (64 features x 32 queries)
+  // ---- phi(q): u^T = W^T q^T (64 features x 32 queries), softmax halves
   float ph[2][2][16];   // [half pos/neg][mt][i]: feature 64*half + 32*mt + 8(i/4) + 4h + (i%4)
   float zlin = 0.f;
   {
@@ -153,13 +207,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         const int k0 = 16 * kb + 8 * h;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const int f = 32 * mt + r;
-          const u32x4 ah = ld16(sm.WT_hi + f * (d + 8) + k0);
-          acc[mt] = DT::mma(ah, qh[kb], acc[mt]);
+          const T* wrow = sm_WT + (32 * mt + r) * KRS + k0;
           if constexpr (DT::kSplit) {
-            const u32x4 al = ld16(sm.WT_lo + f * (d + 8) + k0);
+            float x[8];
+            load8_f32(wrow, x);
+            u32x4 ah, al;
+            splitop<DT>(x, ah, al);
+            acc[mt] = DT::mma(ah, qh[kb], acc[mt]);
             acc[mt] = DT::mma(ah, ql[kb], acc[mt]);
             acc[mt] = DT::mma(al, qh[kb], acc[mt]);
+          } else {
+            acc[mt] = DT::mma(ld16(reinterpret_cast<const uint16_t*>(wrow)), qh[kb], acc[mt]);
           }
         }
       }
@@ -170,12 +228,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
       for (int i = 0; i < 16; ++i) { mx = fmaxf(mx, acc[mt][i]); mn = fminf(mn, acc[mt][i]); }
     mx = fmaxf(mx, xor32(mx));
     mn = fminf(mn, xor32(mn));
+    constexpr float kL2E = 1.4426950408889634f;
+    const float mxl = mx * kL2E, mnl = mn * kL2E;
     float sp = 0.f, sn = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
       for (int i = 0; i < 16; ++i) {
-        ph[0][mt][i] = expf(acc[mt][i] - mx);
-        ph[1][mt][i] = expf(mn - acc[mt][i]);
+        ph[0][mt][i] = __builtin_amdgcn_exp2f(fmaf(acc[mt][i], kL2E, -mxl));
+        ph[1][mt][i] = __builtin_amdgcn_exp2f(fmaf(-acc[mt][i], kL2E, mnl));
         sp += ph[0][mt][i];
         sn += ph[1][mt][i];
       }
@@ -188,184 +248,202 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         ph[0][mt][i] *= ip;
         ph[1][mt][i] *= in_;
         const int f = 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-        zlin = fmaf(ph[0][mt][i], sm.s[f], zlin);
-        zlin = fmaf(ph[1][mt][i], sm.s[kM + f], zlin);
+        zlin = fmaf(ph[0][mt][i], sm_s[f], zlin);
+        zlin = fmaf(ph[1][mt][i], sm_s[kM + f], zlin);
       }
     zlin += xor32(zlin);
   }
 
   // ---- linear read N_lin^T = H_j^T phi^T into the output accumulator
-  f32x16 O[nmt];
+  f32x16 O[NMT];
 #pragma unroll
-  for (int mt = 0; mt < nmt; ++mt)
+  for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) O[mt][i] = 0.f;
-  const uint16_t* snap = a.snapHT + ((size_t)u * a.nch + j) * 2 * d * kD;
+  if (wactive) {
 #pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    __syncthreads();
-    for (int i = tid; i < 2 * d * (kM / 8); i += kThreads) {
-      const int pl = i / (d * (kM / 8)), rem = i % (d * (kM / 8));
-      const int row = rem / (kM / 8), col = (rem % (kM / 8)) * 8;
-      *reinterpret_cast<u32x4*>((pl ? sm.HT_lo : sm.HT_hi) + row * HTH + col) =
-          *reinterpret_cast<const u32x4*>(snap + (size_t)pl * d * kD + (size_t)row * kD + kM * half + col);
-    }
-    __syncthreads();
-    if (wactive) {
+    for (int kb = 0; kb < kD / 16; ++kb) {
+      const int half = kb >> 2, mt = (kb >> 1) & 1, i0 = 8 * (kb & 1);
+      u32x4 bh, bl;
+      splitop<DT>(&ph[half][mt][i0], bh, bl);
 #pragma unroll
-      for (int kb = 0; kb < kM / 16; ++kb) {
-        const int mt = kb >> 1, i0 = 8 * (kb & 1);
-        u32x4 bh, bl;
-        splitop<DT>(&ph[half][mt][i0], bh, bl);
-#pragma unroll
-        for (int mo = 0; mo < nmt; ++mo) {
-          const int row = 32 * mo + r;
-          const u32x4 ah = sigma_load(sm.HT_hi + row * HTH + 16 * kb, h);
-          const u32x4 al = sigma_load(sm.HT_lo + row * HTH + 16 * kb, h);
-          O[mo] = DT::mma(ah, bh, O[mo]);
-          O[mo] = DT::mma(ah, bl, O[mo]);
-          O[mo] = DT::mma(al, bh, O[mo]);
-        }
+      for (int mo = 0; mo < NMT; ++mo) {
+        const int row = 32 * mo + r;
+        const u32x4 ah = sigma_load(sm_HT_hi + row * HTS + 16 * kb, h);
+        const u32x4 al = sigma_load(sm_HT_lo + row * HTS + 16 * kb, h);
+        O[mo] = DT::mma(ah, bh, O[mo]);
+        O[mo] = DT::mma(ah, bl, O[mo]);
+        O[mo] = DT::mma(al, bh, O[mo]);
       }
     }
   }
+  __syncthreads();   // the key tiles reuse the linear-read region
 
-  // ---- explicit branch: cache G_j, then local positions lo_j .. pend-1
+  // ---- explicit branch: key tiles of KT, double-buffered
   float m2 = 0.f, l = zlin;
-  const float scale2 = 1.4426950408889634f / sqrtf((float)d);
-  const int gsj = (int)min((long long)lam, max(0LL, nj - eta));
-  const long long lo_j = max(0LL, nj - eta);
-  const int nkeys = gsj + (int)(pend - lo_j);
-  const int32_t* Gj = a.snapG + ((size_t)u * a.nch + j) * lam;
-  for (int t0 = 0; t0 < nkeys; t0 += 32) {
-    __syncthreads();
-    // K tile, row-major [key][d]: 16-byte pieces (raw copy for bf16)
-    for (int i = tid; i < 32 * (d / 8); i += kThreads) {
-      const int kl = i / (d / 8), cc = (i % (d / 8)) * 8;
+  const float scale2 = 1.4426950408889634f / sqrtf((float)HD);
+  const int ntiles = (nkeys + KT - 1) / KT;
+  // one tile's pieces in registers: keys (KPT pieces of 16 bytes) and one
+  // (key pair, 8 columns) item of V
+  u32x4 kreg[KPT];
+  float vreg[2][8];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      const int pc = q * kThreads + tid, kl = pc / (HD / PER), c = (pc % (HD / PER)) * PER;
       const int kk = t0 + kl;
-      const int vi = kk < nkeys ? (kk < gsj ? Gj[kk] : lam + eta + (int)(lo_j + (kk - gsj) - n0)) : -1;
-      if constexpr (DT::kSplit) {
-        float kv[8];
-        if (vi >= 0) load8_f32(reinterpret_cast<const T*>(vr.krow(u, vi, sizeof(T))) + cc, kv);
-        else for (int q = 0; q < 8; ++q) kv[q] = 0.f;
-        u32x4 kh, kl8;
-        splitop<DT>(kv, kh, kl8);
-        *reinterpret_cast<u32x4*>(sm.K_hi + kl * (d + 8) + cc) = kh;
-        *reinterpret_cast<u32x4*>(sm.K_lo + kl * (d + 8) + cc) = kl8;
-      } else {
-        *reinterpret_cast<u32x4*>(sm.K_hi + kl * (d + 8) + cc) =
-            vi >= 0 ? *reinterpret_cast<const u32x4*>(vr.krow(u, vi, sizeof(T)) + cc * sizeof(T))
-                    : u32x4{0, 0, 0, 0};
-      }
+      kreg[q] = kk < nkeys ? *reinterpret_cast<const u32x4*>(vrow(key_vi(kk), false) + c)
+                           : u32x4{0, 0, 0, 0};
     }
-    // V^T tile [d][KTP]: a thread takes two consecutive keys x 8 columns and
-    // writes 8 dwords (the key pair) -- 16 threads fill 16 consecutive dwords
-    // of one row, and the row pitch puts the four row groups of a wave on
-    // disjoint banks.
-    for (int i = tid; i < 16 * (d / 8); i += kThreads) {
-      const int pr = i % 16, cc = (i / 16) * 8;
-      float v0[8], v1[8];
+    if (tid < VITEMS) {
+      const int pr = tid % (KT / 2), c = (tid / (KT / 2)) * 8;
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq) {
         const int kk = t0 + 2 * pr + kq;
-        float* dst = kq ? v1 : v0;
-        if (kk < nkeys) {
-          const int vi = kk < gsj ? Gj[kk] : lam + eta + (int)(lo_j + (kk - gsj) - n0);
-          load8_f32(reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))) + cc, dst);
-        } else {
-          for (int q = 0; q < 8; ++q) dst[q] = 0.f;
-        }
+        if (kk < nkeys) load8_f32(vrow(key_vi(kk), true) + c, vreg[kq]);
+        else for (int q = 0; q < 8; ++q) vreg[kq][q] = 0.f;
       }
+    }
+  };
+  // buffer b's arrays (selects, so that the offsets stay in registers)
+  auto buf_off = [&](const uint32_t (&o)[2], int b) -> uint32_t { return b ? o[1] : o[0]; };
+  auto store_tile = [&](int b) {
+    uint16_t* Kb = (uint16_t*)(smem + buf_off(L.K, b));
+    uint16_t* KLb = (uint16_t*)(smem + buf_off(L.KL, b));
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      const int pc = q * kThreads + tid, kl = pc / (HD / PER), c = (pc % (HD / PER)) * PER;
+      if constexpr (DT::kSplit) {
+        float x[4] = {__uint_as_float(kreg[q][0]), __uint_as_float(kreg[q][1]),
+                      __uint_as_float(kreg[q][2]), __uint_as_float(kreg[q][3])};
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) DT::split(x[e], hi[e], lo[e]);
+        *reinterpret_cast<u32x2*>(Kb + kl * KRS + c) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+        *reinterpret_cast<u32x2*>(KLb + kl * KRS + c) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+      } else {
+        *reinterpret_cast<u32x4*>(Kb + kl * KRS + c) = kreg[q];
+      }
+    }
+    if (tid < VITEMS) {
+      const int pr = tid % (KT / 2), c = (tid / (KT / 2)) * 8;
+      uint16_t* VTb = (uint16_t*)(smem + buf_off(L.VT, b));
+      uint16_t* VTLb = (uint16_t*)(smem + buf_off(L.VTL, b));
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        uint32_t* row = reinterpret_cast<uint32_t*>(sm.VT_a + (cc + q) * KTP) + pr;
+        uint32_t* row = reinterpret_cast<uint32_t*>(VTb + (c + q) * VTS) + pr;
         if constexpr (DT::kSplit) {
           uint32_t h0, l0, h1, l1;
-          DT::split(v0[q], h0, l0);
-          DT::split(v1[q], h1, l1);
+          DT::split(vreg[0][q], h0, l0);
+          DT::split(vreg[1][q], h1, l1);
           *row = h0 | (h1 << 16);
-          *(reinterpret_cast<uint32_t*>(sm.VT_b + (cc + q) * KTP) + pr) = l0 | (l1 << 16);
+          *(reinterpret_cast<uint32_t*>(VTLb + (c + q) * VTS) + pr) = l0 | (l1 << 16);
         } else {
-          *row = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v0[q]) |
-                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v1[q]) << 16);
+          *row = f16_bits(vreg[0][q]) | (f16_bits(vreg[1][q]) << 16);
         }
       }
     }
+  };
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int t0 = t * KT, b = t & 1;
+    if (t + 1 < ntiles) load_tile(t0 + KT);       // in flight during this tile's products
+    if (wactive && t0 <= wlast) {
+      const uint16_t* Kb = (const uint16_t*)(smem + buf_off(L.K, b));
+      const uint16_t* KLb = (const uint16_t*)(smem + buf_off(L.KL, b));
+      const uint16_t* VTb = (const uint16_t*)(smem + buf_off(L.VT, b));
+      const uint16_t* VTLb = (const uint16_t*)(smem + buf_off(L.VTL, b));
+      f32x16 S[2];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[kh][i] = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int k0 = 16 * kb + 8 * h;
+          const u32x4 ah = ld16(Kb + (32 * kh + r) * KRS + k0);
+          S[kh] = DT::mma(ah, qh[kb], S[kh]);
+          if constexpr (DT::kSplit) {
+            const u32x4 al = ld16(KLb + (32 * kh + r) * KRS + k0);
+            S[kh] = DT::mma(ah, ql[kb], S[kh]);
+            S[kh] = DT::mma(al, qh[kb], S[kh]);
+          }
+        }
+      }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kk = t0 + 32 * kh + 8 * (i >> 2) + 4 * h + (i & 3);
+          bool ok = kk < nkeys;
+          if (ok && kk >= gsj) ok = lo_j + (kk - gsj) <= qpos;   // causal (diagonal included)
+          S[kh][i] = ok ? S[kh][i] * scale2 : -INFINITY;
+          tmax = fmaxf(tmax, S[kh][i]);
+        }
+      tmax = fmaxf(tmax, xor32(tmax));
+      const float mnew = fmaxf(m2, tmax);
+      if (mnew > m2) {
+        const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) O[mt][i] *= alpha;
+        l *= alpha;
+        m2 = mnew;
+      }
+      float rs = 0.f;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { S[kh][i] = __builtin_amdgcn_exp2f(S[kh][i] - m2); rs += S[kh][i]; }
+      rs += xor32(rs);
+      l += rs;
+#pragma unroll
+      for (int kb = 0; kb < KT / 16; ++kb) {
+        const int kh = kb >> 1, i0 = 8 * (kb & 1);
+        if constexpr (DT::kSplit) {
+          u32x4 ph8, pl8;
+          float pv[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) pv[q] = S[kh][i0 + q];
+          splitop<DT>(pv, ph8, pl8);
+#pragma unroll
+          for (int mo = 0; mo < NMT; ++mo) {
+            const int row = 32 * mo + r;
+            const u32x4 vh = sigma_load(VTb + row * VTS + 16 * kb, h);
+            const u32x4 vl = sigma_load(VTLb + row * VTS + 16 * kb, h);
+            O[mo] = DT::mma(vh, ph8, O[mo]);
+            O[mo] = DT::mma(vh, pl8, O[mo]);
+            O[mo] = DT::mma(vl, ph8, O[mo]);
+          }
+        } else {
+          f16x8 p8;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) p8[q] = (_Float16)S[kh][i0 + q];
+#pragma unroll
+          for (int mo = 0; mo < NMT; ++mo) {
+            const int row = 32 * mo + r;
+            const f16x8 vh = __builtin_bit_cast(f16x8, sigma_load(VTb + row * VTS + 16 * kb, h));
+            O[mo] = mfma_f16(vh, p8, O[mo]);
+          }
+        }
+      }
+    }
+    if (t + 1 < ntiles) store_tile(b ^ 1);
     __syncthreads();
-    if (!wactive) continue;
-    f32x16 S;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) S[i] = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int k0 = 16 * kb + 8 * h;
-      const u32x4 ah = ld16(sm.K_hi + r * (d + 8) + k0);
-      S = DT::mma(ah, qh[kb], S);
-      if constexpr (DT::kSplit) {
-        const u32x4 al = ld16(sm.K_lo + r * (d + 8) + k0);
-        S = DT::mma(ah, ql[kb], S);
-        S = DT::mma(al, qh[kb], S);
-      }
-    }
-    float tmax = -INFINITY;
-    for (int i = 0; i < 16; ++i) {
-      const int kk = t0 + 8 * (i >> 2) + 4 * h + (i & 3);
-      bool ok = kk < nkeys;
-      if (ok && kk >= gsj) ok = lo_j + (kk - gsj) <= qpos;   // causal (diagonal included)
-      S[i] = ok ? S[i] * scale2 : -INFINITY;
-      tmax = fmaxf(tmax, S[i]);
-    }
-    tmax = fmaxf(tmax, xor32(tmax));
-    const float mnew = fmaxf(m2, tmax);
-    if (mnew > m2) {
-      const float alpha = exp2f(m2 - mnew);
-#pragma unroll
-      for (int mt = 0; mt < nmt; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) O[mt][i] *= alpha;
-      l *= alpha;
-      m2 = mnew;
-    }
-    float rs = 0.f;
-    for (int i = 0; i < 16; ++i) { S[i] = exp2f(S[i] - m2); rs += S[i]; }
-    rs += xor32(rs);
-    l += rs;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if constexpr (DT::kSplit) {
-        u32x4 ph8, pl8;
-        float pv[8];
-        for (int q = 0; q < 8; ++q) pv[q] = S[8 * kb + q];
-        splitop<DT>(pv, ph8, pl8);
-#pragma unroll
-        for (int mo = 0; mo < nmt; ++mo) {
-          const int row = 32 * mo + r;
-          const u32x4 vh = sigma_load(sm.VT_a + row * KTP + 16 * kb, h);
-          const u32x4 vl = sigma_load(sm.VT_b + row * KTP + 16 * kb, h);
-          O[mo] = DT::mma(vh, ph8, O[mo]);
-          O[mo] = DT::mma(vh, pl8, O[mo]);
-          O[mo] = DT::mma(vl, ph8, O[mo]);
-        }
-      } else {
-        f16x8 p8;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) p8[q] = (_Float16)S[8 * kb + q];
-#pragma unroll
-        for (int mo = 0; mo < nmt; ++mo) {
-          const int row = 32 * mo + r;
-          f16x8 vh = __builtin_bit_cast(f16x8, sigma_load(sm.VT_a + row * KTP + 16 * kb, h));
-          O[mo] = mfma_f16(vh, p8, O[mo]);
-        }
-      }
-    }
   }
 
   // ---- y = O / l
   if (!qvalid) return;
   const float il = 1.f / l;
-  float* orow = a.out + (((size_t)u * a.g + hd) * vr.T + (size_t)(qpos - n0)) * d;
+  float* orow = a.out + (((size_t)u * a.g + hd) * vr.T + (size_t)(qpos - n0)) * HD;
 #pragma unroll
-  for (int mo = 0; mo < nmt; ++mo)
+  for (int mo = 0; mo < NMT; ++mo)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int cc = 32 * mo + 8 * g4 + 4 * h;
@@ -379,11 +457,17 @@ template <class DT, int HD>
 static hipError_t launch_attn_t(const AttnArgs& a, int U, hipStream_t st) {
   const int nptile = (a.C + a.ptile - 1) / a.ptile;
   dim3 grid(nptile, a.nch, U);
-  const size_t lds = attn_lds_bytes(HD, DT::kSplit);
-  (void)hipFuncSetAttribute((const void*)attn_kernel<DT, HD>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const size_t lds = attn_lds_bytes(HD, a.vr.lam, DT::kSplit);
+  const void* fn = (const void*)attn_kernel<DT, HD>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_kernel<DT, HD>), grid, dim3(kThreads), lds, st, a);
   return hipGetLastError();
+}
+
+int attn_positions_per_block(int C, int g) {
+  const int p = 32 * kWaves / g;
+  return C < p ? (C + 31) / 32 * 32 : p;
 }
 
 hipError_t launch_attn(const AttnArgs& a, int U, bool f32, hipStream_t st) {

@@ -93,7 +93,7 @@ struct ChainArgs {
 struct AttnArgs {
   VirtRows vr;
   const void* q;            // [B, Hq, T, d] == [U, g, T, d]
-  const void* W;            // [Hkv, d, kM]
+  const void* WT;           // [Hkv, kM, d]  W transposed
   const uint16_t* snapHT;
   const float* snaps;
   const int32_t* snapG;
@@ -139,7 +139,8 @@ hipError_t launch_phi(const PhiArgs& a, int U, bool f32, hipStream_t st);
 hipError_t launch_chain(const ChainArgs& a, int U, bool f32, hipStream_t st);
 size_t chain_lds_bytes(int lam, int C, int d, bool f32);
 hipError_t launch_attn(const AttnArgs& a, int U, bool f32, hipStream_t st);
-size_t attn_lds_bytes(int d, bool f32);
+size_t attn_lds_bytes(int d, int lam, bool f32);
+int attn_positions_per_block(int C, int g);
 hipError_t launch_finalize(const FinalizeArgs& a, int U, bool f32, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int U, bool f32, hipStream_t st);
 hipError_t launch_export(bool f32, int U, const void* ring_k, const void* ring_v,
