@@ -1,0 +1,198 @@
+"""HBM traffic of the library's kernels from rocprofv3 counters.
+
+Two modes:
+
+``run``       executes one workload's kernels for counter collection (run it
+              under ``rocprofv3 --pmc FETCH_SIZE`` and again under
+              ``--pmc WRITE_SIZE``, one counter per run):
+
+                python3 -m sparse_kv_caching_amd.traffic run --workload llama8b_4k
+                python3 -m sparse_kv_caching_amd.traffic run --workload decode_b64
+
+              A prefill workload runs two prefill calls (the second is the one
+              measured); the decode workload runs its 4096-token prefill and
+              then decode steps.  Both end with an elementwise copy of
+              256 MiB (``torch.neg`` into a preallocated tensor), whose
+              counters calibrate the scale: bytes = counter * 1024 * factor
+              with factor = copy bytes / (copy counter * 1024).
+
+``summarize`` reads the two rocprofv3 output folders and writes
+              ``profiles/traffic_<kernel>_<workload>.txt`` with the measured
+              bytes per launch (the average over the measured launches), the
+              calibration factors, the algorithmic bytes where they are
+              defined, and the hash of the kernel's sources (``bench.py``
+              only uses a summary whose hash matches the current sources).
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "sparse_kv_caching_amd", "csrc")
+COPY_BYTES = 256 << 20
+
+# kernel -> (source file, symbol prefix in the rocprofv3 kernel name)
+KERNELS = {
+    "phi": ("phi.hip", "lola::phi_kernel"),
+    "chain": ("chain.hip", "lola::chain_kernel"),
+    "attn": ("attn.hip", "lola::attn_kernel"),
+    "decode": ("decode.hip", "lola::decode_kernel"),
+}
+
+
+def kernel_source_hash(fname: str) -> str:
+    h = hashlib.sha256()
+    for f in (fname, "common.h", "internal.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------- run
+def _run(args):
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, ROOT)
+    from sparse_kv_caching_amd.lola import LolaLayer
+    from sparse_kv_caching_amd.workloads import WORKLOADS, make_inputs
+
+    def to_dev(arr):
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).cuda().view(torch.bfloat16)
+
+    torch.cuda.set_device(0)
+    wl = WORKLOADS[args.workload]
+    print("[traffic] %s" % wl.name, flush=True)
+    if wl.decode_steps:
+        inp = make_inputs(wl, with_q=False)
+        layer = LolaLayer(batch=wl.B, q_heads=wl.Hq, kv_heads=wl.Hkv, head_dim=wl.d,
+                          window=wl.eta, cache=wl.lam, W=to_dev(inp.W), dtype=torch.bfloat16)
+        q0 = torch.zeros((wl.B, wl.Hq, wl.T, wl.d), dtype=torch.bfloat16, device="cuda")
+        layer.prefill(q0, to_dev(inp.k), to_dev(inp.v), wl.C)
+        gen = torch.Generator(device="cuda").manual_seed(wl.seed)
+        out = torch.empty((wl.B, wl.Hq, wl.d), dtype=torch.float32, device="cuda")
+        for _ in range(args.steps):
+            q = torch.randn((wl.B, wl.Hq, wl.d), generator=gen, device="cuda").to(torch.bfloat16)
+            k = torch.randn((wl.B, wl.Hkv, wl.d), generator=gen, device="cuda").to(torch.bfloat16)
+            v = torch.randn((wl.B, wl.Hkv, wl.d), generator=gen, device="cuda").to(torch.bfloat16)
+            layer.decode(q, k, v, out=out)
+    else:
+        inp = make_inputs(wl)
+        layer = LolaLayer(batch=wl.B, q_heads=wl.Hq, kv_heads=wl.Hkv, head_dim=wl.d,
+                          window=wl.eta, cache=wl.lam, W=to_dev(inp.W), dtype=torch.bfloat16)
+        q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+        for _ in range(2):
+            layer.reset()
+            layer.prefill(q, k, v, wl.C)
+    torch.cuda.synchronize()
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    layer.free()
+    print("[traffic] done", flush=True)
+
+
+# ------------------------------------------------------------- summarize
+def _read_counter(folder: str, counter: str):
+    """{kernel name: [value per dispatch in dispatch order]} from a rocprofv3
+    counter_collection.csv (values in KiB for FETCH_SIZE / WRITE_SIZE)."""
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % folder)
+    per = defaultdict(dict)
+    for path in files:
+        with open(path) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                did = int(row.get("Dispatch_Id") or row.get("Correlation_Id") or 0)
+                name = row.get("Kernel_Name", "")
+                per[name][did] = per[name].get(did, 0.0) + float(row["Counter_Value"])
+    return {k: [v[i] for i in sorted(v)] for k, v in per.items()}
+
+
+def _pick(counts, prefix):
+    vals = []
+    for name, v in counts.items():
+        if name.startswith(prefix) or ("%s<" % prefix) in name or prefix in name:
+            vals.extend(v)
+    return vals
+
+
+def _summarize(args):
+    fetch = _read_counter(args.fetch, "FETCH_SIZE")
+    write = _read_counter(args.write, "WRITE_SIZE")
+    fname, prefix = KERNELS[args.kernel]
+    fv, wv = _pick(fetch, prefix), _pick(write, prefix)
+    if not fv or not wv:
+        raise SystemExit("kernel %s not found in the counter files" % prefix)
+    # measured launches: the last `--last` dispatches of the kernel
+    fv, wv = fv[-args.last:], wv[-args.last:]
+    cf = [v for k, vs in fetch.items() if "neg" in k.lower() for v in vs]
+    cw = [v for k, vs in write.items() if "neg" in k.lower() for v in vs]
+    if not cf or not cw:
+        raise SystemExit("calibration copy kernel not found")
+    f_fac = COPY_BYTES / (cf[-1] * 1024.0)
+    w_fac = COPY_BYTES / (cw[-1] * 1024.0)
+    fb = sum(fv) / len(fv) * 1024.0 * f_fac
+    wb = sum(wv) / len(wv) * 1024.0 * w_fac
+    out = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (args.kernel, args.workload))
+    with open(out, "w") as fh:
+        fh.write("# HBM traffic of %s on the %s workload (rocprofv3 PMC, MI355X)\n"
+                 % (prefix, args.workload))
+        fh.write("# commands (repository root, one counter per run):\n")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            fh.write("#   cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc %s "
+                     "--output-format csv -d $REPO/gpurun_out/<dir> -o run -- python3 -m "
+                     "sparse_kv_caching_amd.traffic run --workload %s\n" % (c, args.workload))
+        fh.write("#   python3 -m sparse_kv_caching_amd.traffic summarize --workload %s --kernel %s "
+                 "--fetch <fetch dir> --write <write dir> --last %d\n"
+                 % (args.workload, args.kernel, args.last))
+        fh.write("# calibration: torch.neg over %d bytes reads %.1f KiB and writes %.1f KiB\n"
+                 % (COPY_BYTES, cf[-1], cw[-1]))
+        fh.write("kernel = %s\n" % args.kernel)
+        fh.write("workload = %s\n" % args.workload)
+        fh.write("src_sha = %s\n" % kernel_source_hash(fname))
+        fh.write("launches = %d\n" % len(fv))
+        fh.write("fetch_kib_per_launch = %.1f\n" % (sum(fv) / len(fv)))
+        fh.write("write_kib_per_launch = %.1f\n" % (sum(wv) / len(wv)))
+        fh.write("fetch_factor = %.4f\n" % f_fac)
+        fh.write("write_factor = %.4f\n" % w_fac)
+        fh.write("fetch_bytes_per_launch = %.0f\n" % fb)
+        fh.write("write_bytes_per_launch = %.0f\n" % wb)
+        fh.write("bytes_per_launch = %.0f\n" % (fb + wb))
+        if args.algorithmic:
+            fh.write("algorithmic_bytes_per_launch = %d\n" % args.algorithmic)
+    print(open(out).read())
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("--workload", required=True)
+    r.add_argument("--steps", type=int, default=16)
+    s = sub.add_parser("summarize")
+    s.add_argument("--workload", required=True)
+    s.add_argument("--kernel", required=True, choices=sorted(KERNELS))
+    s.add_argument("--fetch", required=True)
+    s.add_argument("--write", required=True)
+    s.add_argument("--last", type=int, default=1)
+    s.add_argument("--algorithmic", type=int, default=0)
+    args = ap.parse_args()
+    if args.mode == "run":
+        _run(args)
+    else:
+        _summarize(args)
+
+
+if __name__ == "__main__":
+    main()
