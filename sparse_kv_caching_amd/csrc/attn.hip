@@ -101,7 +101,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   constexpr int VITEMS = (KT / 2) * (HD / 8);    // (key pair, 8 columns) items per tile
   const VirtRows vr = a.vr;
   const int lam = vr.lam, eta = vr.eta;
-  const int pt = blockIdx.x, j = blockIdx.y, u = blockIdx.z;
+  // unit fastest: with the unit count a multiple of 8, a unit's chunks share
+  // an XCD (blocks are dealt to the 8 XCDs round-robin) and its K/V rows,
+  // re-read by every chunk, stay in that XCD's L2
+  const int u = blockIdx.x, j = blockIdx.y, pt = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, r = lane & 31;
   const int kvh = u % a.Hkv;
@@ -456,7 +459,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 template <class DT, int HD>
 static hipError_t launch_attn_t(const AttnArgs& a, int U, hipStream_t st) {
   const int nptile = (a.C + a.ptile - 1) / a.ptile;
-  dim3 grid(nptile, a.nch, U);
+  dim3 grid(U, a.nch, nptile);
   const size_t lds = attn_lds_bytes(HD, a.vr.lam, DT::kSplit);
   const void* fn = (const void*)attn_kernel<DT, HD>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
