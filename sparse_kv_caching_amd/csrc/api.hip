@@ -274,7 +274,7 @@ int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v
   a.n = st->n;
   a.lam = st->cfg.cache; a.eta = st->cfg.window; a.d = st->d; a.g = st->g;
   a.Hkv = st->cfg.kv_heads;
-  decode_plan(a.lam, a.eta, st->d, st->g, st->f32, &a.kc, &a.nslot);
+  decode_plan(a.lam, a.eta, st->d, st->g, st->f32, &a.kc);
   a.q_su = (long long)st->g * st->d; a.q_sh = st->d; a.kv_su = st->d;
   a.o_su = (long long)st->g * st->d; a.o_sh = st->d;
   hipError_t e;
@@ -311,7 +311,7 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
     a.cache_pos = st->cache_pos[st->cur];
     a.lam = st->cfg.cache; a.eta = st->cfg.window; a.d = d; a.g = g;
     a.Hkv = st->cfg.kv_heads;
-    decode_plan(a.lam, a.eta, d, g, st->f32, &a.kc, &a.nslot);
+    decode_plan(a.lam, a.eta, d, g, st->f32, &a.kc);
     a.q_su = (long long)g * T * d; a.q_sh = (long long)T * d; a.kv_su = (long long)T * d;
     a.o_su = a.q_su; a.o_sh = a.q_sh;
     for (int t = 0; t < T; ++t) {
@@ -502,7 +502,8 @@ int lola_state_export(const lola_state* st, lola_state_view* dst, void* stream) 
   const size_t U = st->U, d = st->d;
   const int lam = st->cfg.cache, eta = st->cfg.window;
   const int gs = (int)std::min<int64_t>(lam, std::max<int64_t>(0, st->n - eta));
-  hipError_t e = hipMemcpyAsync(dst->H, st->H, U * kD * d * 4, hipMemcpyDeviceToDevice, s);
+  // the device keeps H^T [U, d, D]; the view holds H [U, D, d]
+  hipError_t e = launch_transpose_f32(st->H, dst->H, (int)U, (int)d, kD, s);
   if (e == hipSuccess) e = hipMemcpyAsync(dst->s, st->s, U * kD * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
     e = launch_export(st->f32, st->U, st->ring_k, st->ring_v, st->cache_k[st->cur],
@@ -536,7 +537,7 @@ int lola_state_import(lola_state* st, const lola_state_view* src, void* stream) 
                       "and older than the window", u);
       }
   }
-  hipError_t e = hipMemcpyAsync(st->H, src->H, U * kD * d * 4, hipMemcpyDeviceToDevice, s);
+  hipError_t e = launch_transpose_f32(src->H, st->H, (int)U, kD, (int)d, s);
   if (e == hipSuccess) e = hipMemcpyAsync(st->s, src->s, U * kD * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
     e = launch_import(st->f32, st->U, st->ring_k, st->ring_v, st->cache_k[st->cur],

@@ -170,6 +170,8 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
           (uint16_t*)(smem + L.VT_hi), (uint16_t*)(smem + L.VT_lo)};
 
   // ---- own H tiles: tile p = wave + kWaves * i (p < NTILE) -> slab p / 4, mt p % 4
+  // (H is stored transposed, H^T [d][kD]: the lane's four consecutive
+  // features of a column are one 16-byte load)
   f32x16 Hreg[NPW];
   const float* Hg = a.H + (size_t)u * kD * HD;
 #pragma unroll
@@ -178,10 +180,12 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) Hreg[i][q] = 0.f;
     if (p < NTILE) {
+      const float* hc = Hg + (size_t)(col0 + 32 * sw + r) * kD + 32 * mt + 4 * h;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int F = 32 * mt + 8 * (q >> 2) + 4 * h + (q & 3);
-        Hreg[i][q] = Hg[(size_t)F * HD + col0 + 32 * sw + r];
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(hc + 8 * g4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Hreg[i][4 * g4 + q] = x[q];
       }
     }
   }
@@ -587,11 +591,11 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
   for (int i = 0; i < NPW; ++i) {
     const int p = wave + kWaves * i, sw = p >> 2, mt = p & 3;
     if (p < NTILE && writer) {
+      float* hc = Ho + (size_t)(col0 + 32 * sw + r) * kD + 32 * mt + 4 * h;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int F = 32 * mt + 8 * (q >> 2) + 4 * h + (q & 3);
-        Ho[(size_t)F * HD + col0 + 32 * sw + r] = Hreg[i][q];
-      }
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<f32x4*>(hc + 8 * g4) =
+            f32x4{Hreg[i][4 * g4], Hreg[i][4 * g4 + 1], Hreg[i][4 * g4 + 2], Hreg[i][4 * g4 + 3]};
     }
   }
   if (rank == 0) {

@@ -10,26 +10,29 @@
 //          s; if that was a cache entry, the leaving pair takes its slot
 //          (Eqs. (10)-(13)).  The new pair enters the ring slot n % eta.
 //
-// The step is bound by HBM traffic: H and s are read and written once, the
-// window and cache K/V read once.  One workgroup (4 waves) per unit.
+// The step is bound by HBM traffic (H and s read and written once, the window
+// and cache K / V read once), so the kernel is shaped for every unit to be
+// resident at once with all of its reads in flight from the start:
 //
-//   * Every wave owns a 32-column slab of H, loaded at the start (buffer
-//     loads, all in flight together) and held in registers in MFMA operand
-//     layout: lane (c, h) holds H[16 kb + sigma_h(j)][c].
-//   * The keys a query sees, in the order cache 0..gs-1, window (oldest
-//     first), new pair, are streamed through LDS in chunks of kc rows (one
-//     chunk for the decode shapes here), every load of a chunk issued before
-//     the first is waited for.  The leaving pair is key gs, so the candidate
-//     rows of the SRE are exactly keys 0..gs.
-//   * Per chunk: logits S^T = K Q^T on MFMA; phi of the chunk's candidate rows
-//     (x W^T on MFMA, W transposed once at state creation) computed by every
-//     wave for itself, so that the phi registers feed P^T = H_slab^T phi (hi/lo
-//     16-bit split, three passes) directly, giving the wave's columns of the
-//     SRE predictions; online softmax (running max starting at 0); P V on the
-//     VALU with every V row read once per workgroup.
-//   * The query rows get phi(q) and the linear read H^T phi(q), phi(q)^T s the
-//     same way.  Then the argmin key, the output, and the rank-1 fold of the
-//     evicted pair into the register-resident H, written back once.
+//   * One workgroup of 4 waves per unit.  For bf16 state it needs at most
+//     80 KB of LDS and 256 registers per lane, so two workgroups share a CU.
+//   * Wave w owns the 32-column slab w of H.  H lives on the device as H^T
+//     [d][D], so the slab arrives in the MFMA operand layout with 16-byte
+//     loads: lane (c, h) holds H[16 kb + sigma_h(j)][32 w + c].
+//   * The keys a query sees (cache 0..gs-1, window oldest first, the new
+//     pair) go through LDS in chunks (one chunk for the decode shapes here).
+//     Key tiles of 32 are dealt to the waves; each wave loads its tiles' V
+//     rows into registers at the start.  The leaving pair is key gs, so the
+//     SRE candidates are exactly keys 0..gs.
+//   * Per wave: logits S^T = K Q^T of its tiles (MFMA), a softmax with a
+//     wave-local running max, and P V on the VALU.  The partials of the four
+//     waves are merged once; the linear read enters as the term with logit 0.
+//   * Every slab wave computes phi of the candidate and query rows itself
+//     (x W^T on MFMA, W transposed once at state creation) and multiplies it
+//     by its slab (P^T = H_slab^T phi, 16-bit hi/lo split, three passes):
+//     its columns of the SRE parts and of H^T phi(q).
+//   * Wave 0 picks the argmin and recomputes phi of the folded row; every
+//     slab wave adds the rank-1 term to its registers and writes them back.
 #include "internal.h"
 
 namespace lola {
@@ -37,41 +40,45 @@ namespace lola {
 namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int WP = 8;   // row padding (elements) of W^T, K and q in LDS (bank spread)
+constexpr size_t kLdsPair = 80 * 1024;    // two workgroups per CU
+constexpr size_t kLdsOne = 160 * 1024;
 
 // Byte offsets of the LDS arrays.
 struct DecLayout {
-  uint32_t wt, kst, vst, q, lk, lv, slot, slotz, logit, spart, phe, nlin, zq, ml, pv, red, total;
+  uint32_t wt, k, q, lk, lv, nk, nv, ve, s, cpos, spart, logit, nlin, pv, phe, wst, zq, red, total;
 };
-constexpr int WP = 8;   // row padding (elements) of W^T, K, V and q in LDS (bank spread)
-constexpr uint32_t kSlotBytes = 8 * 2 * 64 * 16;   // B operands of one 32-row phi tile
 
 inline __host__ __device__ uint32_t al16(uint32_t x) { return (x + 15u) & ~15u; }
 
-__host__ __device__ inline DecLayout dec_layout(int lam, int d, int g, int esz, int kc, int nslot) {
+// krows: cache / window key rows staged per chunk
+__host__ __device__ inline DecLayout dec_layout(int lam, int d, int esz, int krows) {
   DecLayout L;
   uint32_t off = 0;
   auto take = [&](uint32_t b) { const uint32_t o = off; off = al16(off + b); return o; };
   const uint32_t row = (uint32_t)(d + WP) * esz;
+  const uint32_t lrows = (uint32_t)(krows + 31) / 32 * 32;
   L.wt = take(kM * row);                               // [kM][d + WP] W^T of this KV head
-  L.kst = take((uint32_t)kc * row);                    // [kc][d + WP] key chunk
-  L.vst = take((uint32_t)kc * row);                    // [kc][d + WP] value chunk
+  L.k = take((uint32_t)krows * row);                   // [krows][d + WP] key chunk
   L.q = take(4 * row);                                 // [g][d + WP] queries
-  L.lk = take((uint32_t)d * esz);                      // leaving key
-  L.lv = take((uint32_t)d * esz);                      // leaving value
-  L.slot = take((uint32_t)nslot * kSlotBytes);         // [slot][kb][hi, lo][lane] phi operands
-  L.slotz = take((uint32_t)nslot * 32 * 4);            // [slot][row] phi^T s
-  L.logit = take((uint32_t)4 * kc * 4);                // [kc][4] logits, then weights
-  L.spart = take((uint32_t)(d / 32) * (lam + 1) * 4);  // [slab][candidate] partial SRE
-  L.phe = take(kD * 4);                                // phi of the folded row
-  L.nlin = take((uint32_t)g * d * 4);                  // [g][d] H^T phi(q)
-  L.zq = take(4 * 4);                                  // [g] phi(q)^T s
-  L.ml = take(3 * 4 * 4);                              // [4] running max, sum, rescale
+  L.lk = take((uint32_t)d * esz);                      // leaving pair
+  L.lv = take((uint32_t)d * esz);
+  L.nk = take((uint32_t)d * esz);                      // new pair
+  L.nv = take((uint32_t)d * esz);
+  L.ve = take((uint32_t)d * 4);                        // value of the folded row
+  L.s = take(kD * 4);                                  // s
+  L.cpos = take((uint32_t)lam * 4);                    // cache positions
+  L.spart = take((uint32_t)(d / 32) * (lam + 1) * 4);  // [slab][candidate] SRE parts
+  L.logit = take(lrows * 16);                          // [key][4] softmax weights
+  L.nlin = take((uint32_t)4 * d * 4);                  // [g][d] H^T phi(q)
   L.pv = take((uint32_t)kWaves * 4 * d * 4);           // [wave][4][d] P V partials
-  L.red = take(kWaves * 16);                           // the folded row
+  L.phe = take(kD * 4);                                // phi of the folded row
+  L.wst = take(kWaves * 8 * 4);                        // [wave][max 4, sum 4]
+  L.zq = take(4 * 4);                                  // [g] phi(q)^T s
+  L.red = take(16);                                    // the folded row
   L.total = off;
   return L;
 }
-constexpr size_t kDecLdsBudget = 160 * 1024;
 
 // 8 consecutive input elements as a 16-bit MFMA operand (hi; lo for split types)
 __device__ __forceinline__ void xop(const BF16&, const uint16_t* p, u32x4& hi, u32x4& lo) {
@@ -83,194 +90,243 @@ __device__ __forceinline__ void xop(const F32&, const float* p, u32x4& hi, u32x4
   load8_f32(p, x);
   splitop<F32>(x, hi, lo);
 }
+
+// v_mfma_f32_16x16x32_{bf16,f16}: A is 16 x 32 (M x K), B is 32 x 16 (K x N).
+// Lane l supplies row / column (l % 16) and the 8 K-values 8 (l / 16) + j;
+// the output lane l holds column (l % 16), rows 4 (l / 16) + i, i = 0..3.
+// Because a contraction may permute its K index freely (A and B agreeing), a
+// C-layout result feeds the next product directly; within a 32-wide K-block
+// kb the lane group q = l / 16 then holds the K-slots
+//     sigma(kb, q, j) = 32 kb + 16 (j / 4) + 4 q + (j % 4),  j = 0..7.
+__device__ __forceinline__ f32x4 mma16(const BF16&, u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(const F32&, u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+// a b with the split passes of the type (hi hi + hi lo + lo hi for fp32 inputs)
 template <class DT>
-__device__ __forceinline__ f32x16 mma_x(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x16 c) {
-  c = DT::mma(ah, bh, c);
+__device__ __forceinline__ f32x4 mma16x(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, f32x4 c) {
+  const DT dt{};
+  c = mma16(dt, ah, bh, c);
   if constexpr (DT::kSplit) {
-    c = DT::mma(ah, bl, c);
-    c = DT::mma(al, bh, c);
+    c = mma16(dt, ah, bl, c);
+    c = mma16(dt, al, bh, c);
   }
   return c;
 }
 
 __device__ __forceinline__ float ldf(const uint16_t* p) { return bf16_bits_to_f32(*p); }
 __device__ __forceinline__ float ldf(const float* p) { return *p; }
+__device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16, 64); }
+// sum / max / min over the four lane groups q of a 16-lane column
+__device__ __forceinline__ float qsum(float x) { x += xor16(x); return x + xor32(x); }
+__device__ __forceinline__ float qmax(float x) { x = fmaxf(x, xor16(x)); return fmaxf(x, xor32(x)); }
+__device__ __forceinline__ float qmin(float x) { x = fminf(x, xor16(x)); return fminf(x, xor32(x)); }
 
-// phi of 32 rows (lane (r, h) supplies row r); W^T rows f = 32 mt + r, row
-// stride HD + WP elements (LDS).
-// Result: ph[half][mt][i] = phi[64 half + 32 mt + 8 (i/4) + 4 h + (i%4)] of row r.
+constexpr float kL2E = 1.4426950408889634f;
+
+// Pre-activations of phi for 16 rows: U^T = W x^T, lane (n, q) supplying row
+// n (xrow, any valid row); W^T rows f = 16 mt + n, row stride HD + WP
+// elements (LDS).  U[mt][i] is feature 16 mt + 4 q + i of row n.  The
+// operands of k-block kb + 1 are read while kb's products run; the
+// scheduling barriers keep the compiler from hoisting every block's reads.
 template <class DT, int HD>
-__device__ __forceinline__ void phi_tile(const DT& dt, const typename DT::T* xrow,
-                                         const typename DT::T* WT, int h, int r,
-                                         float (&ph)[2][2][16]) {
-  constexpr int KB = HD / 16;
-  f32x16 U2[2];
+__device__ __forceinline__ void pre16(const typename DT::T* xrow, const typename DT::T* WT,
+                                      int n, int q, f32x4 (&U)[4]) {
+  constexpr int KB = HD / 32;
+  const DT dt{};
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 4; ++mt) U[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 bh, bl, ah[4], al[4];
+  auto ops = [&](int kb) {
+    const int k0 = 32 * kb + 8 * q;
+    xop(dt, xrow + k0, bh, bl);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) U2[mt][i] = 0.f;
+    for (int mt = 0; mt < 4; ++mt) xop(dt, WT + (16 * mt + n) * (HD + WP) + k0, ah[mt], al[mt]);
+  };
+  ops(0);
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    const int k0 = 16 * kb + 8 * h;
-    u32x4 bh, bl;
-    if (xrow) xop(dt, xrow + k0, bh, bl);
-    else bh = bl = u32x4{0, 0, 0, 0};
+    u32x4 cah[4], cal[4];
+    const u32x4 cbh = bh, cbl = bl;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      u32x4 ah, al;
-      xop(dt, WT + (32 * mt + r) * (HD + WP) + k0, ah, al);
-      U2[mt] = mma_x<DT>(ah, al, bh, bl, U2[mt]);
-    }
+    for (int mt = 0; mt < 4; ++mt) { cah[mt] = ah[mt]; cal[mt] = al[mt]; }
+    if (kb + 1 < KB) ops(kb + 1);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) U[mt] = mma16x<DT>(cah[mt], cal[mt], cbh, cbl, U[mt]);
+    __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// phi from the pre-activations: ph[half][mt][i] = phi[64 half + 16 mt + 4 q + i]
+// of the lane's row.
+__device__ __forceinline__ void phi16(const f32x4 (&U)[4], float (&ph)[2][4][4]) {
   float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { mx = fmaxf(mx, U2[mt][i]); mn = fminf(mn, U2[mt][i]); }
-  mx = fmaxf(mx, xor32(mx));
-  mn = fminf(mn, xor32(mn));
+    for (int i = 0; i < 4; ++i) { mx = fmaxf(mx, U[mt][i]); mn = fminf(mn, U[mt][i]); }
+  mx = qmax(mx);
+  mn = qmin(mn);
   // e^(u - max) = 2^(u log2 e - max log2 e)
-  constexpr float kL2E = 1.4426950408889634f;
   const float mxl = mx * kL2E, mnl = mn * kL2E;
   float sp = 0.f, sn = 0.f;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      ph[0][mt][i] = __builtin_amdgcn_exp2f(fmaf(U2[mt][i], kL2E, -mxl));
-      ph[1][mt][i] = __builtin_amdgcn_exp2f(fmaf(-U2[mt][i], kL2E, mnl));
+    for (int i = 0; i < 4; ++i) {
+      ph[0][mt][i] = __builtin_amdgcn_exp2f(fmaf(U[mt][i], kL2E, -mxl));
+      ph[1][mt][i] = __builtin_amdgcn_exp2f(fmaf(-U[mt][i], kL2E, mnl));
       sp += ph[0][mt][i];
       sn += ph[1][mt][i];
     }
-  sp += xor32(sp);
-  sn += xor32(sn);
-  const float ip = 1.f / sp, in_ = 1.f / sn;
+  const float ip = 1.f / qsum(sp), in_ = 1.f / qsum(sn);
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { ph[0][mt][i] *= ip; ph[1][mt][i] *= in_; }
+    for (int i = 0; i < 4; ++i) { ph[0][mt][i] *= ip; ph[1][mt][i] *= in_; }
 }
 
-// feature of K-slot j of k-block kb for lane half h (the sigma_h permutation)
-__device__ __forceinline__ int sigma_feat(int kb, int h, int j) {
-  return 16 * kb + (j < 4 ? 4 * h + j : 8 + 4 * h + (j - 4));
-}
-// byte offset of H row sigma_feat(kb, 0, j) (the lane part 4 h rows is separate)
-__device__ __forceinline__ int h_soff(int kb, int j, int hd) {
-  return (16 * kb + (j < 4 ? j : 8 + (j - 4))) * hd * 4;
-}
-// buffer resource word 3 for gfx9-class raw (untyped) dword access
-constexpr int kBufWord3 = 0x00020000;
-
-// phi of a 32-row tile into an LDS slot: B operands of the H product in
-// sigma order ([kb][hi, lo][lane] 16-byte pieces, the lane's own layout) and
-// z = phi^T s per row (fp32 phi; the split operands differ from it by less
-// than 2^-17 relative).
-template <class DT, int HD>
-__device__ __forceinline__ void phi_to_slot(const DT& dt, const typename DT::T* xrow,
-                                            const typename DT::T* WT, const float (&sv)[8][8],
-                                            int lane, int h, int r, u32x4* slot, float* slotz) {
-  float ph[2][2][16];
-  phi_tile<DT, HD>(dt, xrow, WT, h, r, ph);
-  float zz = 0.f;
+// For the 16 rows of a tile: P^T = H_slab^T phi^T and z = phi^T s, with phi
+// never held whole.  phi = [e+ / S+, e- / S-] (e+- the exponentials of +-u
+// less their max, S+- their sums), so P^T = P+ / S+ + P- / S- with P+- the
+// products of the unnormalised halves.  K-block kb (features sigma(kb, q, j),
+// half kb / 2) makes its 8 exponentials from the lane's pre-activations,
+// splits them and H into 16-bit hi / lo, and runs three passes for each of
+// the slab's two 16-column blocks.  Hs[mb][kb][j] = H[sigma(kb, q, j)][16 mb + n].
+// Lane (n, q) gets P[mb][i] = P^T[16 mb + 4 q + i][row n] and z of row n.
+template <class DT>
+__device__ __forceinline__ void phi_slab(const f32x4 (&U)[4], const float (&Hs)[2][4][8],
+                                         const float* s, int q, f32x4 (&P)[2], float& z) {
+  float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb) {
-    const int half = kb >> 2, mt = (kb & 3) >> 1, i0 = 8 * (kb & 1);
-    float x[8];
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { mx = fmaxf(mx, U[mt][i]); mn = fminf(mn, U[mt][i]); }
+  mx = qmax(mx);
+  mn = qmin(mn);
+  const float mxl = mx * kL2E, mnl = mn * kL2E;
+  const DT dt{};
+  f32x4 Pp[2], Pn[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) { Pp[mb] = f32x4{0.f, 0.f, 0.f, 0.f}; Pn[mb] = Pp[mb]; }
+  float sum[2] = {0.f, 0.f}, zs[2] = {0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int half = kb >> 1, mt0 = 2 * (kb & 1);
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(s + 32 * kb + 4 * q);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(s + 32 * kb + 16 + 4 * q);
+    float e[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      x[j] = ph[half][mt][i0 + j];
-      zz = fmaf(x[j], sv[kb][j], zz);
+      const float uu = U[mt0 + (j >> 2)][j & 3];
+      e[j] = __builtin_amdgcn_exp2f(half ? fmaf(-uu, kL2E, mnl) : fmaf(uu, kL2E, -mxl));
+      sum[half] += e[j];
+      zs[half] = fmaf(e[j], j < 4 ? s0[j] : s1[j - 4], zs[half]);
     }
     u32x4 Bh, Bl;
-    splitop<DT>(x, Bh, Bl);
-    slot[(2 * kb) * 64 + lane] = Bh;
-    slot[(2 * kb + 1) * 64 + lane] = Bl;
+    splitop<DT>(e, Bh, Bl);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      u32x4 Ah, Al;
+      splitop<DT>(Hs[mb][kb], Ah, Al);
+      f32x4& A = half ? Pn[mb] : Pp[mb];
+      A = mma16(dt, Ah, Bh, A);
+      A = mma16(dt, Ah, Bl, A);
+      A = mma16(dt, Al, Bh, A);
+    }
   }
-  zz += xor32(zz);
-  if (h == 0) slotz[r] = zz;
+  const float ip = 1.f / qsum(sum[0]), in_ = 1.f / qsum(sum[1]);
+  z = qsum(zs[0]) * ip + qsum(zs[1]) * in_;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) P[mb][i] = Pp[mb][i] * ip + Pn[mb][i] * in_;
 }
 
-// P^T = H_slab^T phi for the 32 rows of a slot, three split passes with the
-// slab's pre-split operands.  Lane (r, h) gets P^T[32 slab + 8 (i/4) + 4 h + (i%4)][r].
-template <class DT>
-__device__ __forceinline__ f32x16 slab_product(const u32x4* slot, const u32x4 (&Ah)[8],
-                                              const u32x4 (&Al)[8], int lane) {
-  f32x16 P0, P1;
+// 16 bytes of input elements as floats
+__device__ __forceinline__ void cvt_piece(const BF16&, u32x4 w, float* o) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) { P0[i] = 0.f; P1[i] = 0.f; }
-#pragma unroll
-  for (int kb = 0; kb < 8; ++kb) {
-    const u32x4 Bh = slot[(2 * kb) * 64 + lane], Bl = slot[(2 * kb + 1) * 64 + lane];
-    f32x16& P = (kb & 1) ? P1 : P0;
-    P = DT::mma(Ah[kb], Bh, P);
-    P = DT::mma(Ah[kb], Bl, P);
-    P = DT::mma(Al[kb], Bh, P);
+  for (int e = 0; e < 4; ++e) {
+    o[2 * e] = __uint_as_float(w[e] << 16);
+    o[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
   }
+}
+__device__ __forceinline__ void cvt_piece(const F32&, u32x4 w, float* o) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) P0[i] += P1[i];
-  return P0;
+  for (int e = 0; e < 4; ++e) o[e] = __uint_as_float(w[e]);
 }
 
-// N consecutive elements (N = 1 or 2) as float
-template <int N>
-__device__ __forceinline__ void load_cols(const uint16_t* p, float* o) {
-  if constexpr (N == 2) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
-    o[0] = __uint_as_float(w << 16);
-    o[1] = __uint_as_float(w & 0xFFFF0000u);
-  } else {
-    o[0] = bf16_bits_to_f32(*p);
+// four consecutive values of a V row (the SRE operand of one lane and block)
+template <class DT> struct VQuad;
+template <> struct VQuad<BF16> {
+  u32x2 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = *reinterpret_cast<const u32x2*>(p); }
+  __device__ __forceinline__ float get(int i) const {
+    const uint32_t x = w[i >> 1];
+    return __uint_as_float((i & 1) ? (x & 0xFFFF0000u) : (x << 16));
   }
-}
-template <int N>
-__device__ __forceinline__ void load_cols(const float* p, float* o) {
-#pragma unroll
-  for (int j = 0; j < N; ++j) o[j] = p[j];
-}
+};
+template <> struct VQuad<F32> {
+  f32x4 w;
+  __device__ __forceinline__ void load(const float* p) { w = *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ float get(int i) const { return w[i]; }
+};
 
 }  // namespace
 
-// Rows per staged key chunk and phi slots: all lam + eta + 1 keys if they fit
-// (rows rounded up to 8), with as many slots (<= 4) as the phi rows need and
-// the LDS holds; else fewer rows.  kc = 0: nothing fits.
-void decode_plan(int lam, int eta, int d, int g, bool f32, int* kc_out, int* nslot_out) {
+// Cache / window key rows per staged chunk: a multiple of 32, at most 128
+// (one 32-key tile per wave); kc >= lam + eta means one chunk.  Two
+// workgroups per CU when a chunk of at least min(lam + eta, 128) rows fits
+// 80 KB of LDS, else one per CU; kc = 0: nothing fits.
+void decode_plan(int lam, int eta, int d, int g, bool f32, int* kc_out) {
+  (void)g;
   const int esz = f32 ? 4 : 2;
-  const int nk = lam + eta + 1;
-  const int tiles = (lam + 1 + g + 31) / 32;
-  const int want_slots = tiles < 4 ? tiles : 4;
-  for (int kc = (nk + 7) / 8 * 8; kc >= 32; kc -= 8) {
-    for (int ns = want_slots; ns >= 1; --ns)
-      if (dec_layout(lam, d, g, esz, kc, ns).total <= kDecLdsBudget) {
+  const int nomax = lam + eta;
+  const size_t budgets[2] = {kLdsPair, kLdsOne};
+  for (int b = 0; b < 2; ++b) {
+    for (int kc = 32 * kWaves; kc >= 32; kc -= 32) {
+      if (b == 0 && kc < (nomax < 128 ? nomax : 128)) break;
+      if (dec_layout(lam, d, esz, kc < nomax ? kc : nomax).total <= budgets[b]) {
         *kc_out = kc;
-        *nslot_out = ns;
         return;
       }
+    }
   }
   *kc_out = 0;
-  *nslot_out = 0;
 }
 
 size_t decode_lds_bytes(int lam, int eta, int d, int g, bool f32) {
-  int kc, ns;
-  decode_plan(lam, eta, d, g, f32, &kc, &ns);
-  if (kc == 0) return kDecLdsBudget + 1;
-  return dec_layout(lam, d, g, f32 ? 4 : 2, kc, ns).total;
+  int kc;
+  decode_plan(lam, eta, d, g, f32, &kc);
+  if (kc == 0) return kLdsOne + 1;
+  return dec_layout(lam, d, f32 ? 4 : 2, kc < lam + eta ? kc : lam + eta).total;
 }
 
-template <class DT, int HD>
-__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+// MULTI: more than one key chunk (lam + eta > kc); the one-chunk instance has
+// no chunk loop at all.
+template <class DT, int HD, bool MULTI>
+__global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(DecodeArgs a) {
   using T = typename DT::T;
-  constexpr int NS = HD / 32;        // column slabs of H (one per wave)
-  constexpr int KB = HD / 16;        // k-blocks of a d-long contraction
+  constexpr int NS = HD / 32;                // column slabs of H (one per wave)
+  constexpr int KB = HD / 32;                // 32-wide k-blocks of a d-long contraction
   constexpr int PER = 16 / (int)sizeof(T);   // elements per 16-byte piece
   constexpr int PPR = HD / PER;              // pieces per row
   constexpr int RS = HD + WP;                // LDS row stride (elements)
-  constexpr int NB = 24;                     // staged pieces in flight per thread
+  constexpr int KGR = 64 / PPR;              // key groups of the P V layout
+  constexpr int KPL = 32 / KGR;              // keys per lane of a tile
+  constexpr int KPT = 32 * kWaves * PPR / kThreads;   // staged K pieces per thread
+  constexpr int WPT = kM * PPR / kThreads;            // W^T pieces per thread
+  constexpr int MISC = 8 * PPR + kD / 4;     // queries (4 rows), leaving and new pair, s
+  constexpr int MPT = (MISC + kThreads - 1) / kThreads;
   const DT dt{};
-  const int u = blockIdx.x, lam = a.lam, eta = a.eta, g = a.g, KC = a.kc, NSLOT = a.nslot;
+  const int u = blockIdx.x, lam = a.lam, eta = a.eta, g = a.g, KC = a.kc;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = lane >> 5, r = lane & 31;
+  const int n16 = lane & 15, q4 = lane >> 4;       // 16 x 16 MFMA layout: row / column, K group
+  const int kg = lane / PPR, cp = lane % PPR;      // P V layout: key group, piece
   const int kvh = u % a.Hkv;
   const long long n = a.n;
   const int gs = (int)min((long long)lam, max(0LL, n - eta));
@@ -278,28 +334,33 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   const bool full = has_leave && gs + 1 > lam;     // score and fold
   const int ncand = full ? gs + 1 : 0;             // candidate rows = keys 0..gs
   const int w_len = (int)min((long long)eta, n);   // window positions n - w_len .. n - 1
-  const int nk = gs + w_len + 1;                   // keys a query sees (cache, window, itself)
+  const int nko = gs + w_len;                      // cache and window keys; the new pair is key nko
   const int ring0 = eta > 0 ? (int)((n - w_len) % eta) : 0;   // ring slot of the oldest window row
   const int ringn = eta > 0 ? (int)(n % eta) : 0;             // ring slot of position n (and n - eta)
+  const bool has_slab = wave < NS;
+  const int krows = min(KC, lam + eta);
+  const int nch = MULTI ? max(1, (nko + KC - 1) / KC) : 1;   // key chunks (at least one)
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const DecLayout L = dec_layout(lam, HD, g, (int)sizeof(T), KC, NSLOT);
+  const DecLayout L = dec_layout(lam, HD, (int)sizeof(T), krows);
   T* sm_wt = (T*)(smem + L.wt);
-  T* sm_k = (T*)(smem + L.kst);
-  T* sm_v = (T*)(smem + L.vst);
+  T* sm_k = (T*)(smem + L.k);
   T* sm_q = (T*)(smem + L.q);
   T* sm_lk = (T*)(smem + L.lk);
   T* sm_lv = (T*)(smem + L.lv);
-  u32x4* sm_slot = (u32x4*)(smem + L.slot);
-  float* sm_slotz = (float*)(smem + L.slotz);
-  float* sm_logit = (float*)(smem + L.logit);
+  T* sm_nk = (T*)(smem + L.nk);
+  T* sm_nv = (T*)(smem + L.nv);
+  float* sm_ve = (float*)(smem + L.ve);
+  float* sm_s = (float*)(smem + L.s);
+  int32_t* sm_cpos = (int32_t*)(smem + L.cpos);
   float* sm_spart = (float*)(smem + L.spart);
-  float* sm_phe = (float*)(smem + L.phe);
+  float* sm_logit = (float*)(smem + L.logit);
   float* sm_nlin = (float*)(smem + L.nlin);
-  float* sm_zq = (float*)(smem + L.zq);
-  float* sm_ml = (float*)(smem + L.ml);            // [0..3] max, [4..7] sum, [8..11] rescale
   float* sm_pv = (float*)(smem + L.pv);
-  int32_t* sm_redi = (int32_t*)(smem + L.red);
+  float* sm_phe = (float*)(smem + L.phe);
+  float* sm_wst = (float*)(smem + L.wst);
+  float* sm_zq = (float*)(smem + L.zq);
+  int32_t* sm_red = (int32_t*)(smem + L.red);
 
   const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)u * a.q_su;
   const T* kin = reinterpret_cast<const T*>(a.k) + (size_t)u * a.kv_su;
@@ -310,338 +371,422 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   T* cv = reinterpret_cast<T*>(a.cache_v) + (size_t)u * lam * HD;
   const T* WT = reinterpret_cast<const T*>(a.WT) + (size_t)kvh * kM * HD;
   const float* sg = a.s + (size_t)u * kD;
+  float* HT = a.H + (size_t)u * kD * HD;          // H^T [HD][kD] of this unit
   // the leaving pair (position n - eta): ring slot n % eta, or the new pair
   const T* leave_k = eta > 0 ? ringk + (size_t)ringn * HD : kin;
   const T* leave_v = eta > 0 ? ringv + (size_t)ringn * HD : vin;
-  // global rows of key kk
+  // global row of key kk (kk == nko: the new pair)
   auto key_row = [&](int kk, bool val) -> const T* {
     if (kk < gs) return (val ? cv : ck) + (size_t)kk * HD;
-    if (kk < gs + w_len) {
+    if (kk < nko) {
       int slot = ring0 + (kk - gs);
       if (slot >= eta) slot -= eta;
       return (val ? ringv : ringk) + (size_t)slot * HD;
     }
     return val ? vin : kin;
   };
-  // Stage K and V rows k0 .. k0 + kn into LDS, NB 16-byte loads in flight
-  // per thread before the first is written.
-  auto stage_chunk = [&](int k0, int kn) {
-    const int total = 2 * kn * PPR;
-    for (int b0 = 0; b0 < total; b0 += NB * kThreads) {
-      u32x4 buf[NB];
+  // V rows of the wave's key tile (keys 32 wave .. of chunk k0): lane (kg, cp)
+  // takes piece cp of keys 32 wave + KGR j + kg (clamped to the chunk; the
+  // weights of absent keys are 0)
+  u32x4 Vpv[KPL];
+  auto load_vpv = [&](int k0, int kn, int ln) {
+    if (32 * wave < kn) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int i = b0 + j * kThreads + tid;
-        if (i < total) {
-          const bool isv = i >= kn * PPR;
-          const int ii = isv ? i - kn * PPR : i;
-          buf[j] = *reinterpret_cast<const u32x4*>(key_row(k0 + ii / PPR, isv) + (ii % PPR) * PER);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int i = b0 + j * kThreads + tid;
-        if (i < total) {
-          const bool isv = i >= kn * PPR;
-          const int ii = isv ? i - kn * PPR : i;
-          *reinterpret_cast<u32x4*>((isv ? sm_v : sm_k) + (ii / PPR) * RS + (ii % PPR) * PER) = buf[j];
-        }
+      for (int j = 0; j < KPL; ++j) {
+        const int key = min(32 * wave + KGR * j + ln / PPR, kn - 1);
+        Vpv[j] = *reinterpret_cast<const u32x4*>(key_row(k0 + key, true) + (ln % PPR) * PER);
       }
     }
   };
+  // V values of candidate row row0 + rr at the lane's SRE columns
+  // 32 wave + 16 mb + 4 q4 + (0..3)
+  VQuad<DT> vs[2];
+  auto load_vs = [&](int row0, int rr) {
+    const T* p = key_row(min(row0 + rr, ncand - 1), true) + 32 * wave + 4 * q4;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) vs[mb].load(p + 16 * mb);
+  };
+  // K rows k0 .. k0 + kn (piece i = j * kThreads + t)
+  u32x4 kbuf[KPT];
+  auto load_keys = [&](int k0, int kn, int t) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int i = j * kThreads + t;
+      if (i < kn * PPR) kbuf[j] = *reinterpret_cast<const u32x4*>(key_row(k0 + i / PPR, false) + (i % PPR) * PER);
+    }
+  };
+  auto store_keys = [&](int kn, int t) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int i = j * kThreads + t;
+      if (i < kn * PPR) *reinterpret_cast<u32x4*>(sm_k + (i / PPR) * RS + (i % PPR) * PER) = kbuf[j];
+    }
+  };
+  // the small pieces: queries, leaving pair, new pair, s
+  auto misc_src = [&](int i) -> const u32x4* {
+    if (i < 4 * PPR) return i / PPR < g ? reinterpret_cast<const u32x4*>(qg + (size_t)(i / PPR) * a.q_sh + (i % PPR) * PER) : nullptr;
+    if (i < 6 * PPR) return has_leave ? reinterpret_cast<const u32x4*>((i < 5 * PPR ? leave_k : leave_v) + (i % PPR) * PER) : nullptr;
+    if (i < 8 * PPR) return reinterpret_cast<const u32x4*>((i < 7 * PPR ? kin : vin) + (i % PPR) * PER);
+    if (i < MISC) return reinterpret_cast<const u32x4*>(sg + 4 * (i - 8 * PPR));
+    return nullptr;
+  };
+  auto misc_dst = [&](int i) -> u32x4* {
+    if (i < 4 * PPR) return reinterpret_cast<u32x4*>(sm_q + (i / PPR) * RS + (i % PPR) * PER);
+    if (i < 6 * PPR) return reinterpret_cast<u32x4*>((i < 5 * PPR ? sm_lk : sm_lv) + (i % PPR) * PER);
+    if (i < 8 * PPR) return reinterpret_cast<u32x4*>((i < 7 * PPR ? sm_nk : sm_nv) + (i % PPR) * PER);
+    return reinterpret_cast<u32x4*>(sm_s + 4 * (i - 8 * PPR));
+  };
 
   // ---- every read of the step that does not depend on the argmin, in flight together
-  // H slab through a buffer resource: one lane offset plus a uniform offset per
-  // element (waves without a slab, d = 64, read a valid column they never use)
-  const bool has_slab = NS >= kWaves || wave < NS;
-  const int cc = 32 * wave + r;                    // this lane's H column
-  const __amdgpu_buffer_rsrc_t Hrs =
-      __builtin_amdgcn_make_buffer_rsrc(a.H + (size_t)u * kD * HD, 0, kD * HD * 4, kBufWord3);
-  const int hoff = (4 * h * HD + (cc & (HD - 1))) * 4;
-  float Hs[8][8];
+  const int kn0 = min(KC, nko);
+  load_keys(0, kn0, tid);
+  u32x4 wbuf[WPT], mbuf[MPT];
 #pragma unroll
-  for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      Hs[kb][j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(Hrs, hoff, h_soff(kb, j, HD), 0));
-  // s at this lane's features (the same sigma pattern as its H rows)
-  float sv[8][8];
-#pragma unroll
-  for (int kb = 0; kb < 8; ++kb) {
-    const f32x4 s0 = *reinterpret_cast<const f32x4*>(sg + 16 * kb + 4 * h);
-    const f32x4 s1 = *reinterpret_cast<const f32x4*>(sg + 16 * kb + 8 + 4 * h);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { sv[kb][j] = s0[j]; sv[kb][4 + j] = s1[j]; }
+  for (int j = 0; j < WPT; ++j) {
+    const int i = j * kThreads + tid;
+    wbuf[j] = *reinterpret_cast<const u32x4*>(WT + (size_t)(i / PPR) * HD + (i % PPR) * PER);
   }
-  {
-    constexpr int WPT = kM * PPR / kThreads;       // W^T pieces per thread
-    u32x4 wb[WPT], qb, lb;
 #pragma unroll
-    for (int j = 0; j < WPT; ++j) {
-      const int i = j * kThreads + tid;
-      wb[j] = *reinterpret_cast<const u32x4*>(WT + (size_t)(i / PPR) * HD + (i % PPR) * PER);
-    }
-    const bool hq = tid < g * PPR, hl = has_leave && tid < 2 * PPR;
-    if (hq) qb = *reinterpret_cast<const u32x4*>(qg + (size_t)(tid / PPR) * a.q_sh + (tid % PPR) * PER);
-    if (hl) lb = *reinterpret_cast<const u32x4*>((tid < PPR ? leave_k : leave_v) + (tid % PPR) * PER);
-    stage_chunk(0, min(KC, nk));
-#pragma unroll
-    for (int j = 0; j < WPT; ++j) {
-      const int i = j * kThreads + tid;
-      *reinterpret_cast<u32x4*>(sm_wt + (i / PPR) * RS + (i % PPR) * PER) = wb[j];
-    }
-    if (hq) *reinterpret_cast<u32x4*>(sm_q + (tid / PPR) * RS + (tid % PPR) * PER) = qb;
-    if (hl) *reinterpret_cast<u32x4*>((tid < PPR ? sm_lk : sm_lv) + (tid % PPR) * PER) = lb;
+  for (int j = 0; j < MPT; ++j) {
+    const u32x4* p = misc_src(j * kThreads + tid);
+    if (p) mbuf[j] = *p;
   }
-  if (tid < 4) { sm_ml[tid] = 0.f; sm_ml[4 + tid] = 0.f; sm_ml[8 + tid] = 1.f; }
+  load_vpv(0, kn0, lane);
+  // the H slab: lane (n16, q4) holds H[sigma(kb, q4, j)][32 wave + 16 mb + n16],
+  // two 16-byte pieces of an H^T row per block
+  float Hs[2][4][8];
+  if (has_slab) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const float* hrow = HT + (size_t)(32 * wave + 16 * mb + n16) * kD + 4 * q4;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(hrow + 32 * kb);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(hrow + 32 * kb + 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { Hs[mb][kb][j] = x0[j]; Hs[mb][kb][4 + j] = x1[j]; }
+      }
+    }
+  }
+  if (has_slab && ncand > 0) load_vs(0, n16);
+  for (int i = tid; i < gs; i += kThreads) sm_cpos[i] = a.cache_pos[(size_t)u * lam + i];
+  store_keys(kn0, tid);
+#pragma unroll
+  for (int j = 0; j < WPT; ++j) {
+    const int i = j * kThreads + tid;
+    *reinterpret_cast<u32x4*>(sm_wt + (i / PPR) * RS + (i % PPR) * PER) = wbuf[j];
+  }
+#pragma unroll
+  for (int j = 0; j < MPT; ++j) {
+    const int i = j * kThreads + tid;
+    if (misc_src(i)) *misc_dst(i) = mbuf[j];
+  }
   __syncthreads();
 
-  constexpr float kL2E = 1.4426950408889634f;
   const float scale2 = kL2E / sqrtf((float)HD);   // logits in the log2 domain
-  constexpr int CPL = HD / 64;                     // P V columns per lane
-  float acc[4][CPL];
+  // the wave's running max and sum per head (the same in every lane); its
+  // P V partials live in sm_pv[wave], rescaled when the max moves
+  float mrun[4], lrun[4];
 #pragma unroll
-  for (int hd = 0; hd < 4; ++hd)
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) acc[hd][j] = 0.f;
-  bool phe_in_slot = false;                        // the folded row's phi is still in a slot
+  for (int hd = 0; hd < 4; ++hd) { mrun[hd] = -INFINITY; lrun[hd] = 0.f; }
 
   // ---- key chunks (one for the decode shapes here)
-  for (int k0 = 0; k0 < nk; k0 += KC) {
-    const int kn = min(KC, nk - k0);
-    const bool last = k0 + KC >= nk;
-    if (k0 > 0) {
-      __syncthreads();                             // the previous chunk's readers are done
-      stage_chunk(k0, kn);
+  for (int c = 0; c < nch; ++c) {
+    const int k0 = c * KC;
+    const int kn = max(0, min(KC, nko - k0));
+    const bool last = c == nch - 1;
+    if (MULTI && c > 0) {
+      __syncthreads();                             // the previous chunk's K rows are consumed
+      // (the thread index made opaque here: the addresses of a later chunk's
+      // staging are not hoisted out of the chunk loop, where they would stay
+      // live through the whole kernel)
+      int t = tid;
+      __asm__ volatile("" : "+v"(t));
+      load_keys(k0, kn, t);
+      load_vpv(k0, kn, t & 63);
+      if (has_slab && k0 < ncand) load_vs(k0, t & 15);
+      store_keys(kn, t);
       __syncthreads();
     }
-    // phi rows of the chunk: its candidate rows, then (last chunk) the queries
-    const int cn = max(0, min(kn, ncand - k0));
-    const int nr = cn + (last ? g : 0);
-    const int nt = (nr + 31) / 32;
-    const int nrounds = max(1, (nt + NSLOT - 1) / NSLOT);
-    phe_in_slot = k0 == 0 && last && nt <= NSLOT;
-    for (int R = 0; R < nrounds; ++R) {
-      const int t_lo = R * NSLOT, t_n = max(0, min(NSLOT, nt - t_lo));
-      if (R > 0) __syncthreads();                  // the previous round's slots are consumed
-      // phase A: wave w < t_n computes phi of tile t_lo + w into slot w; the
-      // other waves (then all) compute the chunk's logits S^T = K Q^T
-      if (wave < t_n) {
-        const int row = 32 * (t_lo + wave) + r;
-        const T* xrow = row < cn ? sm_k + row * RS : (row < nr ? sm_q + (row - cn) * RS : nullptr);
-        phi_to_slot<DT, HD>(dt, xrow, sm_wt, sv, lane, h, r, sm_slot + wave * (kSlotBytes / 16),
-                            sm_slotz + wave * 32);
-      }
-      if (R == 0) {
-        for (int kt = (wave - t_n + kWaves) % kWaves; 32 * kt < kn; kt += kWaves) {
-          const int row = 32 * kt + r;
-          f32x16 S;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) S[i] = 0.f;
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            u32x4 kh, kl, qh, ql;
-            if (row < kn) xop(dt, sm_k + row * RS + 16 * kb + 8 * h, kh, kl);
-            else kh = kl = u32x4{0, 0, 0, 0};
-            if (r < g) xop(dt, sm_q + r * RS + 16 * kb + 8 * h, qh, ql);
-            else qh = ql = u32x4{0, 0, 0, 0};
-            S = mma_x<DT>(kh, kl, qh, ql, S);
-          }
-          if (r < g) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int j = 32 * kt + 8 * (i / 4) + 4 * h + (i % 4);
-              if (j < kn) sm_logit[4 * j + r] = S[i] * scale2;
-            }
-          }
-        }
-      }
-      __syncthreads();                             // slots (and logits)
-      // phase B: every slab wave, its columns of the SRE parts / linear read,
-      // with the slab's split operands
-      if (has_slab) {
-        u32x4 Ah[8], Al[8];
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb) splitop<DT>(Hs[kb], Ah[kb], Al[kb]);
-        for (int t = 0; t < t_n; ++t) {
-          const f32x16 P = slab_product<DT>(sm_slot + t * (kSlotBytes / 16), Ah, Al, lane);
-          const int row = 32 * (t_lo + t) + r;
-          const float z = sm_slotz[t * 32 + r];
-          if (row < cn) {
-            const float iz = z > 0.f ? 1.f / z : 0.f;
-            float part = 0.f;
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-              float vv[4];
-              load4_f32(sm_v + row * RS + 32 * wave + 8 * g4 + 4 * h, vv);
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const float p = P[4 * g4 + q] * iz;
-                part = fmaf(p - vv[q], p - vv[q], part);
-              }
-            }
-            part += xor32(part);
-            if (h == 0) sm_spart[wave * (lam + 1) + k0 + row] = part;
-          } else if (row < nr) {
-            const int hd = row - cn;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sm_nlin[hd * HD + 32 * wave + 8 * (i / 4) + 4 * h + (i % 4)] = P[i];
-            if (wave == 0 && h == 0) sm_zq[hd] = z;
-          }
-        }
-      }
-    }
-
-    // online softmax per head (wave = head), log2 domain; running max starts at 0
-    if (wave < g) {
-      float* lg = sm_logit + wave;
-      const float m_old = sm_ml[wave];
-      float m = m_old;
-      for (int j = lane; j < kn; j += 64) m = fmaxf(m, lg[4 * j]);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-      float l = 0.f;
-      for (int j = lane; j < kn; j += 64) {
-        const float p = __builtin_amdgcn_exp2f(lg[4 * j] - m);
-        lg[4 * j] = p;
-        l += p;
-      }
-      l = wave_sum(l);
-      if (lane == 0) {
-        const float alpha = __builtin_amdgcn_exp2f(m_old - m);
-        sm_ml[wave] = m;
-        sm_ml[4 + wave] = sm_ml[4 + wave] * alpha + l;
-        sm_ml[8 + wave] = alpha;
-      }
-    }
-    __syncthreads();                               // weights, rescale factors
-
-    // P V: wave w takes rows w, w + 4, ... of the chunk; four heads always
-    // (rows of absent heads are never read back)
-#pragma unroll
-    for (int hd = 0; hd < 4; ++hd) {
-      const float alpha = sm_ml[8 + hd];
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) acc[hd][j] *= alpha;
-    }
-    int j0 = wave;
-    for (; j0 + 3 * kWaves < kn; j0 += 4 * kWaves) {
-      float vv[4][CPL];
-      f32x4 pp[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        load_cols<CPL>(sm_v + (j0 + e * kWaves) * RS + CPL * lane, vv[e]);
-        pp[e] = *reinterpret_cast<const f32x4*>(sm_logit + 4 * (j0 + e * kWaves));
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int hd = 0; hd < 4; ++hd)
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) acc[hd][c] = fmaf(pp[e][hd], vv[e][c], acc[hd][c]);
-    }
-    for (; j0 < kn; j0 += kWaves) {
-      float vv[CPL];
-      load_cols<CPL>(sm_v + j0 * RS + CPL * lane, vv);
-      const f32x4 pp = *reinterpret_cast<const f32x4*>(sm_logit + 4 * j0);
+    {
+      float acc[4][PER];
 #pragma unroll
       for (int hd = 0; hd < 4; ++hd)
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[hd][c] = fmaf(pp[hd], vv[c], acc[hd][c]);
-    }
-  }
+        for (int e = 0; e < PER; ++e) acc[hd][e] = 0.f;
+      float alpha[4] = {1.f, 1.f, 1.f, 1.f};       // rescale of the earlier chunks' partials
+      // logits of the wave's tile: S^T = K Q^T in two 16-key blocks, lane
+      // (n16, q4) = query n16, keys 32 wave + 16 kt + 4 q4 + i; softmax
+      // weights with the running max
+      if (32 * wave < kn) {
+        // (keys past the chunk and queries past g read a valid row; masked below)
+        const T* qrow = sm_q + min(n16, g - 1) * RS + 8 * q4;
+        f32x4 St[2];
 #pragma unroll
-  for (int hd = 0; hd < 4; ++hd)
+        for (int kt = 0; kt < 2; ++kt) {
+          const T* krow = sm_k + min(32 * wave + 16 * kt + n16, kn - 1) * RS + 8 * q4;
+          St[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) sm_pv[(wave * 4 + hd) * HD + CPL * lane + j] = acc[hd][j];
-
-  // ---- the candidate to fold: lowest SRE, ties to the newer position
-  // (the lowest key (SRE, 0xFFFFFFFF - pos)); candidates are few, one wave
-  int fold_row = -1;   // < gs: cache slot; == gs: the leaving pair
-  if (full && wave == 0) {
-    float best = INFINITY;
-    int bpos = -1, bi = 0;
-    for (int e = lane; e < ncand; e += 64) {
-      float sre = 0.f;
+          for (int kb = 0; kb < KB; ++kb) {
+            u32x4 kh, kl, qh, ql;
+            xop(dt, krow + 32 * kb, kh, kl);
+            xop(dt, qrow + 32 * kb, qh, ql);
+            St[kt] = mma16x<DT>(kh, kl, qh, ql, St[kt]);
+          }
+        }
+        float S[2][4], mx = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < NS; ++w) sre += sm_spart[w * (lam + 1) + e];
-      const int pos = e < gs ? a.cache_pos[(size_t)u * lam + e] : (int)(n - eta);
-      if (sre < best || (sre == best && pos > bpos)) { best = sre; bpos = pos; bi = e; }
-    }
-    float m = best;
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fminf(m, __shfl_xor(m, o, 64));
-    int p = best == m ? bpos : -1;
+          for (int i = 0; i < 4; ++i) {
+            const int j = 32 * wave + 16 * kt + 4 * q4 + i;
+            S[kt][i] = j < kn ? St[kt][i] * scale2 : -INFINITY;
+            mx = fmaxf(mx, S[kt][i]);
+          }
+        mx = qmax(mx);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) p = max(p, __shfl_xor(p, o, 64));
-    const uint64_t win = __ballot(best == m && bpos == p);
-    const int wl = (int)__builtin_ctzll(win);
-    bi = __shfl(bi, wl, 64);
-    if (lane == 0) sm_redi[0] = bi;
-  }
-  __syncthreads();                                 // pv partials, the folded row
-  if (full) fold_row = sm_redi[0];
-
-  // ---- phi of the folded row (last wave): hi + lo from its slot as the
-  // products above saw it, else recomputed (MFMA); the others write y
-  if (fold_row >= 0 && wave == kWaves - 1) {
-    if (phe_in_slot) {
-      if (r == (fold_row & 31)) {
-        const u32x4* sl = sm_slot + (fold_row >> 5) * (kSlotBytes / 16);
+        for (int hd = 0; hd < 4; ++hd) {
+          const float mn = fmaxf(mrun[hd], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), hd)));
+          alpha[hd] = __builtin_amdgcn_exp2f(mrun[hd] - mn);
+          mrun[hd] = mn;
+        }
+        const float mr = n16 == 0 ? mrun[0] : (n16 == 1 ? mrun[1] : (n16 == 2 ? mrun[2] : mrun[3]));
+        float ls = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-          const u32x4 bh = sl[(2 * kb) * 64 + lane], bl = sl[(2 * kb + 1) * 64 + lane];
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const uint32_t hw = bh[j >> 1] >> (16 * (j & 1)), lw = bl[j >> 1] >> (16 * (j & 1));
-            sm_phe[sigma_feat(kb, h, j)] = DT::from_bits(hw & 0xFFFFu) + DT::from_bits(lw & 0xFFFFu);
+          for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(S[kt][i] - mr);
+            ls += p;
+            if (n16 < 4) sm_logit[4 * (32 * wave + 16 * kt + 4 * q4 + i) + n16] = n16 < g ? p : 0.f;
+          }
+        ls = qsum(ls);
+#pragma unroll
+        for (int hd = 0; hd < 4; ++hd)
+          lrun[hd] = fmaf(lrun[hd], alpha[hd], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), hd)));
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // weights written above
+        // P V: lane (kg, cp) over its keys, PER columns, four heads
+#pragma unroll
+        for (int j = 0; j < KPL; ++j) {
+          const f32x4 p4 = *reinterpret_cast<const f32x4*>(sm_logit + 4 * (32 * wave + KGR * j + kg));
+          float v[PER];
+          cvt_piece(dt, Vpv[j], v);
+#pragma unroll
+          for (int hd = 0; hd < 4; ++hd)
+#pragma unroll
+            for (int e = 0; e < PER; ++e) acc[hd][e] = fmaf(p4[hd], v[e], acc[hd][e]);
+        }
+      }
+      if (last && wave == kWaves - 1) {
+        // the new pair (key nko): logits q . k on the VALU, lane (kg, cp) a
+        // piece of head hd0 + kg
+        float snew[4];
+#pragma unroll
+        for (int hd0 = 0; hd0 < 4; hd0 += KGR) {
+          const int hd = hd0 + kg;
+          float part = 0.f;
+          if (hd < g) {
+            float qv[PER], kv[PER];
+            cvt_piece(dt, *reinterpret_cast<const u32x4*>(sm_q + hd * RS + cp * PER), qv);
+            cvt_piece(dt, *reinterpret_cast<const u32x4*>(sm_nk + cp * PER), kv);
+#pragma unroll
+            for (int e = 0; e < PER; ++e) part = fmaf(qv[e], kv[e], part);
+          }
+#pragma unroll
+          for (int o = 1; o < PPR; o <<= 1) part += __shfl_xor(part, o, 64);
+#pragma unroll
+          for (int hh = 0; hh < KGR; ++hh)
+            if (hd0 + hh < 4)
+              snew[hd0 + hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(part), hh * PPR)) * scale2;
+        }
+        float v[PER];
+        cvt_piece(dt, *reinterpret_cast<const u32x4*>(sm_nv + cp * PER), v);
+#pragma unroll
+        for (int hd = 0; hd < 4; ++hd) {
+          const float mn = fmaxf(mrun[hd], snew[hd]);
+          const float al = __builtin_amdgcn_exp2f(mrun[hd] - mn);
+          const float p = __builtin_amdgcn_exp2f(snew[hd] - mn);
+          lrun[hd] = fmaf(lrun[hd], al, p);
+          mrun[hd] = mn;
+          alpha[hd] *= al;
+          const float pk = kg == 0 ? p : 0.f;      // added once over the key groups
+#pragma unroll
+          for (int e = 0; e < PER; ++e) acc[hd][e] = fmaf(acc[hd][e], al, pk * v[e]);
+        }
+      }
+      // into the wave's partials: sum over the key groups, rescale the earlier chunks
+#pragma unroll
+      for (int o = PPR; o < 64; o <<= 1)
+#pragma unroll
+        for (int hd = 0; hd < 4; ++hd)
+#pragma unroll
+          for (int e = 0; e < PER; ++e) acc[hd][e] += __shfl_xor(acc[hd][e], o, 64);
+#pragma unroll
+      for (int hd = 0; hd < 4; ++hd) {
+        if (hd % KGR == kg) {                      // lane (kg, cp) writes the heads = kg mod KGR
+          float* dst = sm_pv + (wave * 4 + hd) * HD + cp * PER;
+#pragma unroll
+          for (int e = 0; e < PER; e += 4) {
+            f32x4 x = f32x4{acc[hd][e], acc[hd][e + 1], acc[hd][e + 2], acc[hd][e + 3]};
+            if (MULTI && c > 0) {
+              const f32x4 o = *reinterpret_cast<const f32x4*>(dst + e);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) x[k] = fmaf(o[k], alpha[hd], x[k]);
+            }
+            *reinterpret_cast<f32x4*>(dst + e) = x;
           }
         }
       }
-    } else {
-      const T* xrow = r == 0 ? (fold_row < gs ? ck + (size_t)fold_row * HD : sm_lk) : nullptr;
-      float ph[2][2][16];
-      phi_tile<DT, HD>(dt, xrow, sm_wt, h, r, ph);
-      if (r == 0) {
+      if (last) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
+        for (int hd = 0; hd < 4; ++hd)
+          if (lane == hd) {
+            sm_wst[wave * 8 + hd] = mrun[hd];
+            sm_wst[wave * 8 + 4 + hd] = lrun[hd];
+          }
+      }
+    }
+
+    // phi of the chunk's candidate rows (and the new pair when it is one),
+    // then (last chunk) the queries, in tiles of 16 rows; per slab wave: its
+    // columns of the SRE parts and of H^T phi(q)
+    if (has_slab) {
+      const int cno = max(0, min(kn, ncand - k0));
+      const int cn = cno + (last && ncand > nko ? 1 : 0);
+      const int nr = cn + (last ? g : 0);
+      const int nt = (nr + 15) / 16;
+      for (int t = 0; t < nt; ++t) {
+        VQuad<DT> vcur[2];
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt)
+        for (int mb = 0; mb < 2; ++mb) vcur[mb] = vs[mb];
+        if (16 * (t + 1) < cn) load_vs(k0 + 16 * (t + 1), n16);   // the next tile's rows
+        const int row = 16 * t + n16;
+        // (rows past the last are a copy of a query row, never read back)
+        const T* xrow = row < cno ? sm_k + row * RS
+                                  : (row < cn ? sm_nk : sm_q + min(row - cn, g - 1) * RS);
+        f32x4 U[4];
+        pre16<DT, HD>(xrow, sm_wt, n16, q4, U);
+        f32x4 P[2];
+        float z;
+        phi_slab<DT>(U, Hs, sm_s, q4, P, z);
+        if (row < cn) {
+          const float iz = z > 0.f ? 1.f / z : 0.f;
+          float part = 0.f;
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-              sm_phe[64 * half + 32 * mt + 8 * (i / 4) + 4 * h + (i % 4)] = ph[half][mt][i];
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float e = fmaf(P[mb][i], iz, -vcur[mb].get(i));
+              part = fmaf(e, e, part);
+            }
+          part = qsum(part);
+          if (q4 == 0) sm_spart[wave * (lam + 1) + k0 + row] = part;
+        } else if (row < nr) {
+          const int hd = row - cn;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            *reinterpret_cast<f32x4*>(sm_nlin + hd * HD + 32 * wave + 16 * mb + 4 * q4) = P[mb];
+          if (wave == 0 && q4 == 0) sm_zq[hd] = z;
+        }
       }
     }
   }
-  for (int i = tid; i < g * HD; i += kThreads) {
-    const int hd = i / HD, c = i % HD;
-    const float em = __builtin_amdgcn_exp2f(-sm_ml[hd]);
-    float num = em * sm_nlin[i];
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) num += sm_pv[(w * 4 + hd) * HD + c];
-    const float den = sm_ml[4 + hd] + em * sm_zq[hd];
-    a.out[(size_t)u * a.o_su + (size_t)hd * a.o_sh + c] = num / den;
-  }
-  __syncthreads();   // phe; every read of the cache and ring is done
+  __syncthreads();                                 // SRE parts, partials, linear read
 
-  // ---- update: fold, cache slot, ring slot
+  if (wave == 0) {
+    if (full) {
+      // ---- the candidate to fold: lowest SRE, ties to the newer position
+      float best = INFINITY;
+      int bpos = -1, bi = 0;
+      for (int e = lane; e < ncand; e += 64) {
+        float sre = 0.f;
+#pragma unroll
+        for (int w = 0; w < NS; ++w) sre += sm_spart[w * (lam + 1) + e];
+        const int pos = e < gs ? sm_cpos[e] : (int)(n - eta);
+        if (sre < best || (sre == best && pos > bpos)) { best = sre; bpos = pos; bi = e; }
+      }
+      float m = best;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) m = fminf(m, __shfl_xor(m, o, 64));
+      int p = best == m ? bpos : -1;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) p = max(p, __shfl_xor(p, o, 64));
+      const uint64_t win = __ballot(best == m && bpos == p);
+      bi = __shfl(bi, (int)__builtin_ctzll(win), 64);
+      if (lane == 0) sm_red[0] = bi;
+      // its value row and phi (the key row from LDS while it is staged; every
+      // lane supplies the same row)
+      const T* vrow = bi == gs ? sm_lv : cv + (size_t)bi * HD;
+      for (int e = lane; e < HD; e += 64) sm_ve[e] = ldf(vrow + e);
+      const T* xrow = bi == gs ? sm_lk : (nko <= KC ? sm_k + bi * RS : ck + (size_t)bi * HD);
+      f32x4 U[4];
+      pre16<DT, HD>(xrow, sm_wt, n16, q4, U);
+      float ph[2][4][4];
+      phi16(U, ph);
+      if (n16 == 0) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt)
+            *reinterpret_cast<f32x4*>(sm_phe + 64 * half + 16 * mt + 4 * q4) =
+                f32x4{ph[half][mt][0], ph[half][mt][1], ph[half][mt][2], ph[half][mt][3]};
+      }
+    }
+  } else {
+    // ---- the outputs: the four waves' partials and the linear read (logit 0)
+    for (int i = tid - 64; i < g * HD; i += kThreads - 64) {
+      const int hd = i / HD, e = i % HD;
+      float m = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) m = fmaxf(m, sm_wst[w * 8 + hd]);
+      const float em = __builtin_amdgcn_exp2f(-m);
+      float num = em * sm_nlin[hd * HD + e], den = em * sm_zq[hd];
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(sm_wst[w * 8 + hd] - m);
+        num = fmaf(f, sm_pv[(w * 4 + hd) * HD + e], num);
+        den = fmaf(f, sm_wst[w * 8 + 4 + hd], den);
+      }
+      a.out[(size_t)u * a.o_su + (size_t)hd * a.o_sh + e] = num / den;
+    }
+    // ---- the new pair enters the ring slot n % eta (every read of the ring is done)
+    if (eta > 0) {
+      T* dk = ringk + (size_t)ringn * HD;
+      T* dv = ringv + (size_t)ringn * HD;
+      for (int i = tid - 64; i < 2 * PPR; i += kThreads - 64) {
+        const int k = (i % PPR) * PER;
+        if (i < PPR) *reinterpret_cast<u32x4*>(dk + k) = *reinterpret_cast<const u32x4*>(sm_nk + k);
+        else *reinterpret_cast<u32x4*>(dv + k) = *reinterpret_cast<const u32x4*>(sm_nv + k);
+      }
+    }
+  }
+  __syncthreads();                                 // the folded row, its phi and value
+
+  // ---- update: fold into the slab and s, cache slot
+  const int fold_row = full ? sm_red[0] : -1;      // < gs: cache slot; == gs: the leaving pair
   if (fold_row >= 0) {
     if (has_slab) {
-      // v of the folded row: staged V row (single chunk), else the cache
-      const float ve = ldf(fold_row == gs ? sm_lv + cc
-                                          : (nk <= KC ? sm_v + fold_row * RS + cc
-                                                      : cv + (size_t)fold_row * HD + cc));
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
+      for (int mb = 0; mb < 2; ++mb) {
+        const float ve = sm_ve[32 * wave + 16 * mb + n16];
+        float* hrow = HT + (size_t)(32 * wave + 16 * mb + n16) * kD + 4 * q4;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float hv = fmaf(sm_phe[sigma_feat(kb, h, j)], ve, Hs[kb][j]);
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(hv), Hrs, hoff, h_soff(kb, j, HD), 0);
+        for (int kb = 0; kb < 4; ++kb) {
+          const f32x4 p0 = *reinterpret_cast<const f32x4*>(sm_phe + 32 * kb + 4 * q4);
+          const f32x4 p1 = *reinterpret_cast<const f32x4*>(sm_phe + 32 * kb + 16 + 4 * q4);
+          f32x4 x0, x1;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            x0[j] = fmaf(p0[j], ve, Hs[mb][kb][j]);
+            x1[j] = fmaf(p1[j], ve, Hs[mb][kb][4 + j]);
+          }
+          *reinterpret_cast<f32x4*>(hrow + 32 * kb) = x0;
+          *reinterpret_cast<f32x4*>(hrow + 32 * kb + 16) = x1;
         }
+      }
     }
-    for (int F = tid; F < kD; F += kThreads) a.s[(size_t)u * kD + F] = sg[F] + sm_phe[F];
+    for (int F = tid; F < kD; F += kThreads) a.s[(size_t)u * kD + F] = sm_s[F] + sm_phe[F];
   }
-  __syncthreads();   // the folded cache row has been read
   if (has_leave) {
     const int slot_in = !full ? gs : (fold_row < gs ? fold_row : -1);
     if (slot_in >= 0) {
@@ -651,15 +796,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
         else *reinterpret_cast<u32x4*>(cv + (size_t)slot_in * HD + k) = *reinterpret_cast<const u32x4*>(sm_lv + k);
       }
       if (tid == 0) a.cache_pos[(size_t)u * lam + slot_in] = (int32_t)(n - eta);
-    }
-  }
-  if (eta > 0) {
-    T* dk = ringk + (size_t)ringn * HD;
-    T* dv = ringv + (size_t)ringn * HD;
-    for (int i = tid; i < 2 * PPR; i += kThreads) {
-      const int k = (i % PPR) * PER;
-      if (i < PPR) *reinterpret_cast<u32x4*>(dk + k) = *reinterpret_cast<const u32x4*>(kin + k);
-      else *reinterpret_cast<u32x4*>(dv + k) = *reinterpret_cast<const u32x4*>(vin + k);
     }
   }
 }
@@ -688,12 +824,17 @@ hipError_t launch_transpose_w(const void* W, void* WT, int Hkv, int d, bool f32,
 
 template <class DT, int HD>
 static hipError_t launch_decode_t(const DecodeArgs& a, int U, hipStream_t st) {
-  if (a.kc < 32 || a.nslot < 1) return hipErrorInvalidValue;
-  const size_t lds = dec_layout(a.lam, HD, a.g, (int)sizeof(typename DT::T), a.kc, a.nslot).total;
-  const void* fn = (const void*)decode_kernel<DT, HD>;
+  if (a.kc < 32 || a.kc % 32 || a.kc > 32 * kWaves || a.g < 1 || a.g > 4) return hipErrorInvalidValue;
+  const int nomax = a.lam + a.eta;
+  const size_t lds = dec_layout(a.lam, HD, (int)sizeof(typename DT::T), a.kc < nomax ? a.kc : nomax).total;
+  const bool multi = nomax > a.kc;
+  const void* fn = multi ? (const void*)decode_kernel<DT, HD, true> : (const void*)decode_kernel<DT, HD, false>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_kernel<DT, HD>), dim3(U), dim3(kThreads), lds, st, a);
+  if (multi)
+    hipLaunchKernelGGL((decode_kernel<DT, HD, true>), dim3(U), dim3(kThreads), lds, st, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<DT, HD, false>), dim3(U), dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }
 

@@ -73,7 +73,7 @@ struct ChainArgs {
   VirtRows vr;
   const uint16_t* phi_hi;
   const uint16_t* phi_lo;
-  float* H;                 // [U, kD, d]  state in / out
+  float* H;                 // [U, d, kD]  H^T (the device layout of H), in / out
   float* s;                 // [U, kD]
   uint16_t* snapHT;         // [U, nch, 2, d, kD]  H^T at chunk start, hi / lo
   float* snaps;             // [U, nch, kD]        s at chunk start
@@ -119,8 +119,8 @@ struct DecodeArgs {
   const void* k;            // [U, d]
   const void* v;
   const void* WT;           // [Hkv, kM, d]  W transposed, state dtype
-  float* H;
-  float* s;
+  float* H;                 // [U, d, kD]  H^T
+  float* s;                 // [U, kD]
   void* ring_k;
   void* ring_v;
   void* cache_k;            // current cache buffer, updated in place
@@ -129,7 +129,7 @@ struct DecodeArgs {
   float* out;               // [U, g, d]
   long long n;
   int lam, eta, d, g, Hkv;
-  int kc, nslot;            // rows per staged key chunk, phi slots (decode_plan)
+  int kc;                   // key rows per staged chunk (decode_plan)
   // element strides (one token): q / out [u][hd], k / v [u]
   long long q_su, q_sh, kv_su, o_su, o_sh;
 };
@@ -153,9 +153,12 @@ hipError_t launch_import(bool f32, int U, void* ring_k, void* ring_v, void* cach
                          const int32_t* in_pos, long long n, int eta, int lam, int gs, int d,
                          hipStream_t st);
 size_t decode_lds_bytes(int lam, int eta, int d, int g, bool f32);
-void decode_plan(int lam, int eta, int d, int g, bool f32, int* kc, int* nslot);
+void decode_plan(int lam, int eta, int d, int g, bool f32, int* kc);
 hipError_t launch_transpose_w(const void* W, void* WT, int Hkv, int d, bool f32, hipStream_t st);
 hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st);
+// dst[b][c][r] = src[b][r][c] for b < batch, r < rows, c < cols (float32)
+hipError_t launch_transpose_f32(const float* src, float* dst, int batch, int rows, int cols,
+                                hipStream_t st);
 hipError_t launch_snappos(const VirtRows& vr, const int32_t* snapG, int32_t* out, int nch,
                           int C, int U, hipStream_t st);
 

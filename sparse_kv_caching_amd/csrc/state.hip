@@ -212,4 +212,28 @@ hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
+// dst[b][c][r] = src[b][r][c]: 32 x 32 tiles through LDS (export / import of
+// H, whose device layout is H^T)
+__global__ void transpose_f32_kernel(const float* src, float* dst, int rows, int cols) {
+  __shared__ float tile[32][33];
+  const int b = blockIdx.z;
+  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8 threads
+  const float* s = src + (size_t)b * rows * cols;
+  float* d = dst + (size_t)b * rows * cols;
+  for (int y = ty; y < 32; y += 8)
+    if (r0 + y < rows && c0 + tx < cols) tile[y][tx] = s[(size_t)(r0 + y) * cols + c0 + tx];
+  __syncthreads();
+  for (int y = ty; y < 32; y += 8)
+    if (c0 + y < cols && r0 + tx < rows) d[(size_t)(c0 + y) * rows + r0 + tx] = tile[tx][y];
+}
+
+hipError_t launch_transpose_f32(const float* src, float* dst, int batch, int rows, int cols,
+                                hipStream_t st) {
+  if (batch <= 0 || rows <= 0 || cols <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((cols + 31) / 32), (unsigned)((rows + 31) / 32), (unsigned)batch);
+  hipLaunchKernelGGL(transpose_f32_kernel, grid, dim3(256), 0, st, src, dst, rows, cols);
+  return hipGetLastError();
+}
+
 }  // namespace lola
