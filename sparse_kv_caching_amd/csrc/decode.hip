@@ -12,27 +12,31 @@
 //
 // The step is bound by HBM traffic (H and s read and written once, the window
 // and cache K / V read once), so the kernel is shaped for every unit to be
-// resident at once with all of its reads in flight from the start:
+// resident at once, with the reads issued up front in two waves:
 //
 //   * One workgroup of 4 waves per unit.  For bf16 state it needs at most
 //     80 KB of LDS and 256 registers per lane, so two workgroups share a CU.
-//   * Wave w owns the 32-column slab w of H.  H lives on the device as H^T
-//     [d][D], so the slab arrives in the MFMA operand layout with 16-byte
-//     loads: lane (c, h) holds H[16 kb + sigma_h(j)][32 w + c].
-//   * The keys a query sees (cache 0..gs-1, window oldest first, the new
-//     pair) go through LDS in chunks (one chunk for the decode shapes here).
-//     Key tiles of 32 are dealt to the waves; each wave loads its tiles' V
-//     rows into registers at the start.  The leaving pair is key gs, so the
-//     SRE candidates are exactly keys 0..gs.
-//   * Per wave: logits S^T = K Q^T of its tiles (MFMA), a softmax with a
-//     wave-local running max, and P V on the VALU.  The partials of the four
-//     waves are merged once; the linear read enters as the term with logit 0.
-//   * Every slab wave computes phi of the candidate and query rows itself
-//     (x W^T on MFMA, W transposed once at state creation) and multiplies it
-//     by its slab (P^T = H_slab^T phi, 16-bit hi/lo split, three passes):
-//     its columns of the SRE parts and of H^T phi(q).
-//   * Wave 0 picks the argmin and recomputes phi of the folded row; every
-//     slab wave adds the rank-1 term to its registers and writes them back.
+//   * The keys a query sees (cache 0..gs-1, window oldest first; the new pair
+//     apart) come in chunks of 128, 32 per wave, loaded straight into the
+//     registers of the wave's MFMA operands; the wave also loads its keys' V
+//     rows.  W^T, the queries, s and the leaving and new pairs go to LDS.
+//     Only when those reads have arrived does the wave issue its slab of H,
+//     so that across the GPU the keys and values come back first and the
+//     logits and phi work overlaps the stream of H.
+//   * Per wave: logits S^T = K Q^T of its keys (MFMA, 16 x 16 x 32), a
+//     softmax with a wave-local running max, and P V on the VALU.  The
+//     partials of the four waves are merged once; the linear read enters as
+//     the term with logit 0; the new pair's logits are dot products.
+//   * SRE candidates are keys 0..gs (the leaving pair is key gs).  phi of
+//     the candidate rows (and of the queries) is computed once, by the wave
+//     holding the rows, and stored in LDS as 16-bit hi / lo operands with
+//     the row's normalisers and phi^T s.  Wave w owns the 32-column slab w
+//     of H (H lives on the device as H^T [d][D], so the slab arrives in
+//     operand layout) and multiplies it by every phi tile: its columns of
+//     the SRE parts and of H^T phi(q).
+//   * Wave 0 picks the argmin and takes phi of the folded row from its
+//     tile; every slab wave adds the rank-1 term to its registers and writes
+//     the slab back once.
 #include "internal.h"
 
 namespace lola {
@@ -40,26 +44,35 @@ namespace lola {
 namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int WP = 8;   // row padding (elements) of W^T, K and q in LDS (bank spread)
+constexpr int WP = 8;   // row padding (elements) of W^T and q in LDS (bank spread)
 constexpr size_t kLdsPair = 80 * 1024;    // two workgroups per CU
 constexpr size_t kLdsOne = 160 * 1024;
 
+constexpr int kKC = 32 * kWaves;   // keys per chunk: a 32-key tile per wave
+
+// phi tiles of 16 rows per chunk: the candidate rows of the chunk, then (last
+// chunk) the new pair when it is a candidate and the g <= 4 query rows
+__host__ __device__ inline int dec_phi_tiles(int lam, int eta) {
+  const int rows = (lam + eta <= kKC ? lam + 1 : kKC + 1) + 4;
+  return (rows + 15) / 16;
+}
+
 // Byte offsets of the LDS arrays.
 struct DecLayout {
-  uint32_t wt, k, q, lk, lv, nk, nv, ve, s, cpos, spart, logit, nlin, pv, phe, wst, zq, red, total;
+  uint32_t wt, q, lk, lv, nk, nv, ve, s, cpos, spart, logit, nlin, pv, phe, wst, zq, red, slot,
+      meta, total;
+  int ntile;
 };
 
 inline __host__ __device__ uint32_t al16(uint32_t x) { return (x + 15u) & ~15u; }
 
-// krows: cache / window key rows staged per chunk
-__host__ __device__ inline DecLayout dec_layout(int lam, int d, int esz, int krows) {
+__host__ __device__ inline DecLayout dec_layout(int lam, int eta, int d, int esz) {
   DecLayout L;
   uint32_t off = 0;
   auto take = [&](uint32_t b) { const uint32_t o = off; off = al16(off + b); return o; };
   const uint32_t row = (uint32_t)(d + WP) * esz;
-  const uint32_t lrows = (uint32_t)(krows + 31) / 32 * 32;
+  L.ntile = dec_phi_tiles(lam, eta);
   L.wt = take(kM * row);                               // [kM][d + WP] W^T of this KV head
-  L.k = take((uint32_t)krows * row);                   // [krows][d + WP] key chunk
   L.q = take(4 * row);                                 // [g][d + WP] queries
   L.lk = take((uint32_t)d * esz);                      // leaving pair
   L.lv = take((uint32_t)d * esz);
@@ -69,13 +82,15 @@ __host__ __device__ inline DecLayout dec_layout(int lam, int d, int esz, int kro
   L.s = take(kD * 4);                                  // s
   L.cpos = take((uint32_t)lam * 4);                    // cache positions
   L.spart = take((uint32_t)(d / 32) * (lam + 1) * 4);  // [slab][candidate] SRE parts
-  L.logit = take(lrows * 16);                          // [key][4] softmax weights
+  L.logit = take(kKC * 16);                            // [key][4] softmax weights
   L.nlin = take((uint32_t)4 * d * 4);                  // [g][d] H^T phi(q)
   L.pv = take((uint32_t)kWaves * 4 * d * 4);           // [wave][4][d] P V partials
   L.phe = take(kD * 4);                                // phi of the folded row
   L.wst = take(kWaves * 8 * 4);                        // [wave][max 4, sum 4]
   L.zq = take(4 * 4);                                  // [g] phi(q)^T s
   L.red = take(16);                                    // the folded row
+  L.slot = take((uint32_t)L.ntile * 8 * 64 * 16);      // [tile][kb][hi, lo][lane] phi operands
+  L.meta = take((uint32_t)L.ntile * 16 * 16);          // [tile][row] 1/S+, 1/S-, phi^T s
   L.total = off;
   return L;
 }
@@ -128,24 +143,24 @@ __device__ __forceinline__ float qmin(float x) { x = fminf(x, xor16(x)); return 
 
 constexpr float kL2E = 1.4426950408889634f;
 
-// Pre-activations of phi for 16 rows: U^T = W x^T, lane (n, q) supplying row
-// n (xrow, any valid row); W^T rows f = 16 mt + n, row stride HD + WP
-// elements (LDS).  U[mt][i] is feature 16 mt + 4 q + i of row n.  The
-// operands of k-block kb + 1 are read while kb's products run; the
-// scheduling barriers keep the compiler from hoisting every block's reads.
-template <class DT, int HD>
-__device__ __forceinline__ void pre16(const typename DT::T* xrow, const typename DT::T* WT,
-                                      int n, int q, f32x4 (&U)[4]) {
+// Pre-activations of phi for 16 rows: U^T = W x^T; bop(kb, hi, lo) gives the
+// lane's x operand of k-block kb (row n, k = 32 kb + 8 q ..); W^T rows
+// f = 16 mt + n, row stride HD + WP elements (LDS).  U[mt][i] is feature
+// 16 mt + 4 q + i of row n.  The operands of k-block kb + 1 are read while
+// kb's products run; the scheduling barriers keep the compiler from
+// hoisting every block's reads.
+template <class DT, int HD, class BOp>
+__device__ __forceinline__ void pre16(BOp bop, const typename DT::T* WT, int n, int q,
+                                      f32x4 (&U)[4]) {
   constexpr int KB = HD / 32;
   const DT dt{};
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) U[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x4 bh, bl, ah[4], al[4];
   auto ops = [&](int kb) {
-    const int k0 = 32 * kb + 8 * q;
-    xop(dt, xrow + k0, bh, bl);
+    bop(kb, bh, bl);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) xop(dt, WT + (16 * mt + n) * (HD + WP) + k0, ah[mt], al[mt]);
+    for (int mt = 0; mt < 4; ++mt) xop(dt, WT + (16 * mt + n) * (HD + WP) + 32 * kb + 8 * q, ah[mt], al[mt]);
   };
   ops(0);
 #pragma unroll
@@ -190,17 +205,63 @@ __device__ __forceinline__ void phi16(const f32x4 (&U)[4], float (&ph)[2][4][4])
     for (int i = 0; i < 4; ++i) { ph[0][mt][i] *= ip; ph[1][mt][i] *= in_; }
 }
 
-// For the 16 rows of a tile: P^T = H_slab^T phi^T and z = phi^T s, with phi
-// never held whole.  phi = [e+ / S+, e- / S-] (e+- the exponentials of +-u
-// less their max, S+- their sums), so P^T = P+ / S+ + P- / S- with P+- the
-// products of the unnormalised halves.  K-block kb (features sigma(kb, q, j),
-// half kb / 2) makes its 8 exponentials from the lane's pre-activations,
-// splits them and H into 16-bit hi / lo, and runs three passes for each of
-// the slab's two 16-column blocks.  Hs[mb][kb][j] = H[sigma(kb, q, j)][16 mb + n].
-// Lane (n, q) gets P[mb][i] = P^T[16 mb + 4 q + i][row n] and z of row n.
+// The wave's slab of H in the lane's operand positions: lane (n, q) holds
+// H[sigma(kb, q, j)][16 mb + n].  For bf16 state it is kept as an exact
+// three-way bf16 split (hi + mid + lo equals the fp32 value), split once: the
+// products use hi and mid (the 16-bit pair of the three-pass scheme), the
+// fold rebuilds the fp32 value.  fp32 state keeps fp32 and splits on use.
+template <class DT> struct HSlab;
+template <> struct HSlab<BF16> {
+  u32x4 hi[2][4], mid[2][4], lo[2][4];
+  __device__ __forceinline__ void set(int mb, int kb, const float (&x)[8]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a0 = x[2 * j], a1 = x[2 * j + 1];
+      const uint32_t h = cvt_pk_bf16(a0, a1);
+      const float r0 = a0 - __uint_as_float(h << 16), r1 = a1 - __uint_as_float(h & 0xFFFF0000u);
+      const uint32_t m = cvt_pk_bf16(r0, r1);
+      hi[mb][kb][j] = h;
+      mid[mb][kb][j] = m;
+      lo[mb][kb][j] = cvt_pk_bf16(r0 - __uint_as_float(m << 16), r1 - __uint_as_float(m & 0xFFFF0000u));
+    }
+  }
+  __device__ __forceinline__ void ops(int mb, int kb, u32x4& Ah, u32x4& Al) const {
+    Ah = hi[mb][kb];
+    Al = mid[mb][kb];
+  }
+  __device__ __forceinline__ void get(int mb, int kb, float (&x)[8]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t h = hi[mb][kb][j], m = mid[mb][kb][j], l = lo[mb][kb][j];
+      x[2 * j] = (__uint_as_float(h << 16) + __uint_as_float(m << 16)) + __uint_as_float(l << 16);
+      x[2 * j + 1] = (__uint_as_float(h & 0xFFFF0000u) + __uint_as_float(m & 0xFFFF0000u)) +
+                     __uint_as_float(l & 0xFFFF0000u);
+    }
+  }
+};
+template <> struct HSlab<F32> {
+  float v[2][4][8];
+  __device__ __forceinline__ void set(int mb, int kb, const float (&x)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[mb][kb][j] = x[j];
+  }
+  __device__ __forceinline__ void ops(int mb, int kb, u32x4& Ah, u32x4& Al) const {
+    splitop<F32>(v[mb][kb], Ah, Al);
+  }
+  __device__ __forceinline__ void get(int mb, int kb, float (&x)[8]) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = v[mb][kb][j];
+  }
+};
+
+// phi of a 16-row tile into its LDS slot.  phi = [e+ / S+, e- / S-] with
+// e+- the exponentials of +-u less their max and S+- their sums: the slot
+// holds the unnormalised e as 16-bit hi / lo operands in the B layout of the
+// H product (k-block kb: features sigma(kb, q, j), half kb / 2; lane (n, q)
+// keeps its own 16 bytes), meta[n] = (1 / S+, 1 / S-, phi^T s).
 template <class DT>
-__device__ __forceinline__ void phi_slab(const f32x4 (&U)[4], const float (&Hs)[2][4][8],
-                                         const float* s, int q, f32x4 (&P)[2], float& z) {
+__device__ __forceinline__ void phi_to_slot(const f32x4 (&U)[4], const float* s, int lane, int n,
+                                            int q, u32x4* slot, float* meta) {
   float mx = -INFINITY, mn = INFINITY;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -209,10 +270,6 @@ __device__ __forceinline__ void phi_slab(const f32x4 (&U)[4], const float (&Hs)[
   mx = qmax(mx);
   mn = qmin(mn);
   const float mxl = mx * kL2E, mnl = mn * kL2E;
-  const DT dt{};
-  f32x4 Pp[2], Pn[2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) { Pp[mb] = f32x4{0.f, 0.f, 0.f, 0.f}; Pn[mb] = Pp[mb]; }
   float sum[2] = {0.f, 0.f}, zs[2] = {0.f, 0.f};
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
@@ -229,23 +286,92 @@ __device__ __forceinline__ void phi_slab(const f32x4 (&U)[4], const float (&Hs)[
     }
     u32x4 Bh, Bl;
     splitop<DT>(e, Bh, Bl);
+    slot[(2 * kb) * 64 + lane] = Bh;
+    slot[(2 * kb + 1) * 64 + lane] = Bl;
+  }
+  const float ip = 1.f / qsum(sum[0]), in_ = 1.f / qsum(sum[1]);
+  const float z = qsum(zs[0]) * ip + qsum(zs[1]) * in_;
+  if (q == 0) *reinterpret_cast<f32x4*>(meta + 4 * n) = f32x4{ip, in_, z, 0.f};
+}
+
+// P^T = H_slab^T phi^T for the 16 rows of a slot: three passes per k-block
+// (H hi / lo from the slab, phi hi / lo from the slot) into the products of
+// the two halves, normalised by the row's meta.
+// Lane (n, q) gets P[mb][i] = P^T[16 mb + 4 q + i][row n] and z of row n.
+template <class DT>
+__device__ __forceinline__ void slab_prod(const u32x4* slot, const float* meta, const HSlab<DT>& Hs,
+                                          int lane, int n, f32x4 (&P)[2], float& z) {
+  const DT dt{};
+  f32x4 Pp[2], Pn[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) { Pp[mb] = f32x4{0.f, 0.f, 0.f, 0.f}; Pn[mb] = Pp[mb]; }
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const u32x4 Bh = slot[(2 * kb) * 64 + lane], Bl = slot[(2 * kb + 1) * 64 + lane];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       u32x4 Ah, Al;
-      splitop<DT>(Hs[mb][kb], Ah, Al);
-      f32x4& A = half ? Pn[mb] : Pp[mb];
+      Hs.ops(mb, kb, Ah, Al);
+      f32x4& A = (kb >> 1) ? Pn[mb] : Pp[mb];
       A = mma16(dt, Ah, Bh, A);
       A = mma16(dt, Ah, Bl, A);
       A = mma16(dt, Al, Bh, A);
     }
   }
-  const float ip = 1.f / qsum(sum[0]), in_ = 1.f / qsum(sum[1]);
-  z = qsum(zs[0]) * ip + qsum(zs[1]) * in_;
+  const f32x4 m = *reinterpret_cast<const f32x4*>(meta + 4 * n);
+  z = m[2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) P[mb][i] = Pp[mb][i] * ip + Pn[mb][i] * in_;
+    for (int i = 0; i < 4; ++i) P[mb][i] = Pp[mb][i] * m[0] + Pn[mb][i] * m[1];
 }
+
+// The lane's 8 key elements of one k-block in registers (row n, k = 32 kb + 8 q ..)
+template <class DT> struct KOp;
+template <> struct KOp<BF16> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const uint16_t* p) { w = ld16(p); }
+  // y if c else x, register by register (no indexed copy)
+  __device__ static __forceinline__ KOp pick(bool c, const KOp& x, const KOp& y) {
+    KOp r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r.w[j] = c ? y.w[j] : x.w[j];
+    return r;
+  }
+  // the operand: these registers if use, else the 8 elements at p (LDS)
+  __device__ __forceinline__ void op(bool use, const uint16_t* p, u32x4& hi, u32x4& lo) const {
+    const u32x4 x = ld16(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hi[j] = use ? w[j] : x[j];
+    lo = u32x4{0, 0, 0, 0};
+  }
+};
+template <> struct KOp<F32> {
+  f32x4 a, b;
+  __device__ static __forceinline__ KOp pick(bool c, const KOp& x, const KOp& y) {
+    KOp r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r.a[j] = c ? y.a[j] : x.a[j];
+      r.b[j] = c ? y.b[j] : x.b[j];
+    }
+    return r;
+  }
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void op(bool use, const float* p, u32x4& hi, u32x4& lo) const {
+    float x[8];
+    load8_f32(p, x);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = use ? a[j] : x[j];
+      x[4 + j] = use ? b[j] : x[4 + j];
+    }
+    splitop<F32>(x, hi, lo);
+  }
+};
 
 // 16 bytes of input elements as floats
 __device__ __forceinline__ void cvt_piece(const BF16&, u32x4 w, float* o) {
@@ -278,36 +404,20 @@ template <> struct VQuad<F32> {
 
 }  // namespace
 
-// Cache / window key rows per staged chunk: a multiple of 32, at most 128
-// (one 32-key tile per wave); kc >= lam + eta means one chunk.  Two
-// workgroups per CU when a chunk of at least min(lam + eta, 128) rows fits
-// 80 KB of LDS, else one per CU; kc = 0: nothing fits.
+// Keys per chunk (kKC = 128); kc = 0 when the layout exceeds the LDS of a CU.
+// Two workgroups share a CU whenever the layout fits 80 KB.
 void decode_plan(int lam, int eta, int d, int g, bool f32, int* kc_out) {
   (void)g;
-  const int esz = f32 ? 4 : 2;
-  const int nomax = lam + eta;
-  const size_t budgets[2] = {kLdsPair, kLdsOne};
-  for (int b = 0; b < 2; ++b) {
-    for (int kc = 32 * kWaves; kc >= 32; kc -= 32) {
-      if (b == 0 && kc < (nomax < 128 ? nomax : 128)) break;
-      if (dec_layout(lam, d, esz, kc < nomax ? kc : nomax).total <= budgets[b]) {
-        *kc_out = kc;
-        return;
-      }
-    }
-  }
-  *kc_out = 0;
+  *kc_out = dec_layout(lam, eta, d, f32 ? 4 : 2).total <= kLdsOne ? kKC : 0;
 }
 
 size_t decode_lds_bytes(int lam, int eta, int d, int g, bool f32) {
-  int kc;
-  decode_plan(lam, eta, d, g, f32, &kc);
-  if (kc == 0) return kLdsOne + 1;
-  return dec_layout(lam, d, f32 ? 4 : 2, kc < lam + eta ? kc : lam + eta).total;
+  (void)g;
+  return dec_layout(lam, eta, d, f32 ? 4 : 2).total;
 }
 
-// MULTI: more than one key chunk (lam + eta > kc); the one-chunk instance has
-// no chunk loop at all.
+// MULTI: more than one key chunk (lam + eta > 128); the one-chunk instance
+// has no chunk loop at all.
 template <class DT, int HD, bool MULTI>
 __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(DecodeArgs a) {
   using T = typename DT::T;
@@ -318,12 +428,12 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   constexpr int RS = HD + WP;                // LDS row stride (elements)
   constexpr int KGR = 64 / PPR;              // key groups of the P V layout
   constexpr int KPL = 32 / KGR;              // keys per lane of a tile
-  constexpr int KPT = 32 * kWaves * PPR / kThreads;   // staged K pieces per thread
-  constexpr int WPT = kM * PPR / kThreads;            // W^T pieces per thread
+  constexpr int WPT = kM * PPR / kThreads;   // W^T pieces per thread
   constexpr int MISC = 8 * PPR + kD / 4;     // queries (4 rows), leaving and new pair, s
   constexpr int MPT = (MISC + kThreads - 1) / kThreads;
+  constexpr int NVS = 5;                     // phi tiles whose SRE values are loaded up front
   const DT dt{};
-  const int u = blockIdx.x, lam = a.lam, eta = a.eta, g = a.g, KC = a.kc;
+  const int u = blockIdx.x, lam = a.lam, eta = a.eta, g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, q4 = lane >> 4;       // 16 x 16 MFMA layout: row / column, K group
   const int kg = lane / PPR, cp = lane % PPR;      // P V layout: key group, piece
@@ -338,13 +448,11 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   const int ring0 = eta > 0 ? (int)((n - w_len) % eta) : 0;   // ring slot of the oldest window row
   const int ringn = eta > 0 ? (int)(n % eta) : 0;             // ring slot of position n (and n - eta)
   const bool has_slab = wave < NS;
-  const int krows = min(KC, lam + eta);
-  const int nch = MULTI ? max(1, (nko + KC - 1) / KC) : 1;   // key chunks (at least one)
+  const int nch = MULTI ? max(1, (nko + kKC - 1) / kKC) : 1;  // key chunks (at least one)
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const DecLayout L = dec_layout(lam, HD, (int)sizeof(T), krows);
+  const DecLayout L = dec_layout(lam, eta, HD, (int)sizeof(T));
   T* sm_wt = (T*)(smem + L.wt);
-  T* sm_k = (T*)(smem + L.k);
   T* sm_q = (T*)(smem + L.q);
   T* sm_lk = (T*)(smem + L.lk);
   T* sm_lv = (T*)(smem + L.lv);
@@ -361,6 +469,8 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   float* sm_wst = (float*)(smem + L.wst);
   float* sm_zq = (float*)(smem + L.zq);
   int32_t* sm_red = (int32_t*)(smem + L.red);
+  u32x4* sm_slot = (u32x4*)(smem + L.slot);
+  float* sm_meta = (float*)(smem + L.meta);
 
   const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)u * a.q_su;
   const T* kin = reinterpret_cast<const T*>(a.k) + (size_t)u * a.kv_su;
@@ -385,12 +495,20 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
     }
     return val ? vin : kin;
   };
-  // V rows of the wave's key tile (keys 32 wave .. of chunk k0): lane (kg, cp)
-  // takes piece cp of keys 32 wave + KGR j + kg (clamped to the chunk; the
-  // weights of absent keys are 0)
+  // The wave's keys of chunk k0 (keys k0 + 32 wave + 16 kt + n16, clamped to
+  // the chunk) as MFMA operands, and their V rows in the P V layout: lane
+  // (kg, cp) takes piece cp of keys 32 wave + KGR j + kg (the weights of
+  // absent keys are 0).
+  KOp<DT> Kr[2][KB];
   u32x4 Vpv[KPL];
-  auto load_vpv = [&](int k0, int kn, int ln) {
+  auto load_tile = [&](int k0, int kn, int ln) {
     if (32 * wave < kn) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const T* kr = key_row(k0 + min(32 * wave + 16 * kt + (ln & 15), kn - 1), false) + 8 * (ln >> 4);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) Kr[kt][kb].load(kr + 32 * kb);
+      }
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
         const int key = min(32 * wave + KGR * j + ln / PPR, kn - 1);
@@ -400,27 +518,10 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   };
   // V values of candidate row row0 + rr at the lane's SRE columns
   // 32 wave + 16 mb + 4 q4 + (0..3)
-  VQuad<DT> vs[2];
-  auto load_vs = [&](int row0, int rr) {
+  auto load_vs = [&](VQuad<DT> (&v)[2], int row0, int rr) {
     const T* p = key_row(min(row0 + rr, ncand - 1), true) + 32 * wave + 4 * q4;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) vs[mb].load(p + 16 * mb);
-  };
-  // K rows k0 .. k0 + kn (piece i = j * kThreads + t)
-  u32x4 kbuf[KPT];
-  auto load_keys = [&](int k0, int kn, int t) {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int i = j * kThreads + t;
-      if (i < kn * PPR) kbuf[j] = *reinterpret_cast<const u32x4*>(key_row(k0 + i / PPR, false) + (i % PPR) * PER);
-    }
-  };
-  auto store_keys = [&](int kn, int t) {
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int i = j * kThreads + t;
-      if (i < kn * PPR) *reinterpret_cast<u32x4*>(sm_k + (i / PPR) * RS + (i % PPR) * PER) = kbuf[j];
-    }
+    for (int mb = 0; mb < 2; ++mb) v[mb].load(p + 16 * mb);
   };
   // the small pieces: queries, leaving pair, new pair, s
   auto misc_src = [&](int i) -> const u32x4* {
@@ -437,9 +538,8 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
     return reinterpret_cast<u32x4*>(sm_s + 4 * (i - 8 * PPR));
   };
 
-  // ---- every read of the step that does not depend on the argmin, in flight together
-  const int kn0 = min(KC, nko);
-  load_keys(0, kn0, tid);
+  // ---- first wave of reads: W^T and the small pieces (to LDS), the wave's
+  // keys and values, the SRE values of the first phi tiles
   u32x4 wbuf[WPT], mbuf[MPT];
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
@@ -451,26 +551,12 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
     const u32x4* p = misc_src(j * kThreads + tid);
     if (p) mbuf[j] = *p;
   }
-  load_vpv(0, kn0, lane);
-  // the H slab: lane (n16, q4) holds H[sigma(kb, q4, j)][32 wave + 16 mb + n16],
-  // two 16-byte pieces of an H^T row per block
-  float Hs[2][4][8];
-  if (has_slab) {
+  const int kn0 = min(kKC, nko);
+  load_tile(0, kn0, lane);
+  VQuad<DT> vs[NVS][2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const float* hrow = HT + (size_t)(32 * wave + 16 * mb + n16) * kD + 4 * q4;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const f32x4 x0 = *reinterpret_cast<const f32x4*>(hrow + 32 * kb);
-        const f32x4 x1 = *reinterpret_cast<const f32x4*>(hrow + 32 * kb + 16);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) { Hs[mb][kb][j] = x0[j]; Hs[mb][kb][4 + j] = x1[j]; }
-      }
-    }
-  }
-  if (has_slab && ncand > 0) load_vs(0, n16);
-  for (int i = tid; i < gs; i += kThreads) sm_cpos[i] = a.cache_pos[(size_t)u * lam + i];
-  store_keys(kn0, tid);
+  for (int t = 0; t < NVS; ++t)
+    if (has_slab && 16 * t < ncand) load_vs(vs[t], 16 * t, n16);
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
     const int i = j * kThreads + tid;
@@ -481,6 +567,23 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
     const int i = j * kThreads + tid;
     if (misc_src(i)) *misc_dst(i) = mbuf[j];
   }
+  // ---- second wave: the H slab, issued once the first wave's LDS data has
+  // arrived.  Lane (n16, q4) holds H[sigma(kb, q4, j)][32 wave + 16 mb + n16]:
+  // two 16-byte pieces of an H^T row per block.
+  __builtin_amdgcn_sched_barrier(0);
+  f32x4 Hraw[2][4][2];
+  if (has_slab) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const float* hrow = HT + (size_t)(32 * wave + 16 * mb + n16) * kD + 4 * q4;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        Hraw[mb][kb][0] = *reinterpret_cast<const f32x4*>(hrow + 32 * kb);
+        Hraw[mb][kb][1] = *reinterpret_cast<const f32x4*>(hrow + 32 * kb + 16);
+      }
+    }
+  }
+  for (int i = tid; i < gs; i += kThreads) sm_cpos[i] = a.cache_pos[(size_t)u * lam + i];
   __syncthreads();
 
   const float scale2 = kL2E / sqrtf((float)HD);   // logits in the log2 domain
@@ -489,24 +592,24 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   float mrun[4], lrun[4];
 #pragma unroll
   for (int hd = 0; hd < 4; ++hd) { mrun[hd] = -INFINITY; lrun[hd] = 0.f; }
+  HSlab<DT> Hs;
 
   // ---- key chunks (one for the decode shapes here)
   for (int c = 0; c < nch; ++c) {
-    const int k0 = c * KC;
-    const int kn = max(0, min(KC, nko - k0));
+    const int k0 = c * kKC;
+    const int kn = max(0, min(kKC, nko - k0));
     const bool last = c == nch - 1;
     if (MULTI && c > 0) {
-      __syncthreads();                             // the previous chunk's K rows are consumed
-      // (the thread index made opaque here: the addresses of a later chunk's
-      // staging are not hoisted out of the chunk loop, where they would stay
+      __syncthreads();                             // the previous chunk's phi tiles are consumed
+      // (the lane index made opaque here: the addresses of a later chunk's
+      // reads are not hoisted out of the chunk loop, where they would stay
       // live through the whole kernel)
-      int t = tid;
+      int t = lane;
       __asm__ volatile("" : "+v"(t));
-      load_keys(k0, kn, t);
-      load_vpv(k0, kn, t & 63);
-      if (has_slab && k0 < ncand) load_vs(k0, t & 15);
-      store_keys(kn, t);
-      __syncthreads();
+      load_tile(k0, kn, t);
+#pragma unroll
+      for (int tt = 0; tt < NVS; ++tt)
+        if (has_slab && k0 + 16 * tt < ncand) load_vs(vs[tt], k0 + 16 * tt, t & 15);
     }
     {
       float acc[4][PER];
@@ -515,22 +618,23 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
 #pragma unroll
         for (int e = 0; e < PER; ++e) acc[hd][e] = 0.f;
       float alpha[4] = {1.f, 1.f, 1.f, 1.f};       // rescale of the earlier chunks' partials
-      // logits of the wave's tile: S^T = K Q^T in two 16-key blocks, lane
+      // logits of the wave's keys: S^T = K Q^T in two 16-key blocks, lane
       // (n16, q4) = query n16, keys 32 wave + 16 kt + 4 q4 + i; softmax
       // weights with the running max
       if (32 * wave < kn) {
-        // (keys past the chunk and queries past g read a valid row; masked below)
+        // (queries past g read a valid row; never read back)
         const T* qrow = sm_q + min(n16, g - 1) * RS + 8 * q4;
         f32x4 St[2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const T* krow = sm_k + min(32 * wave + 16 * kt + n16, kn - 1) * RS + 8 * q4;
-          St[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kt = 0; kt < 2; ++kt) St[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            u32x4 kh, kl, qh, ql;
-            xop(dt, krow + 32 * kb, kh, kl);
-            xop(dt, qrow + 32 * kb, qh, ql);
+        for (int kb = 0; kb < KB; ++kb) {
+          u32x4 qh, ql;
+          xop(dt, qrow + 32 * kb, qh, ql);
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            u32x4 kh, kl;
+            Kr[kt][kb].op(true, qrow, kh, kl);
             St[kt] = mma16x<DT>(kh, kl, qh, ql, St[kt]);
           }
         }
@@ -647,28 +751,49 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
       }
     }
 
-    // phi of the chunk's candidate rows (and the new pair when it is one),
-    // then (last chunk) the queries, in tiles of 16 rows; per slab wave: its
-    // columns of the SRE parts and of H^T phi(q)
+    // phi rows of the chunk: its candidate keys (cno), the new pair when it is
+    // a candidate (eta = 0), then (last chunk) the queries.  Tile t (rows
+    // 16 t ..) is computed by wave t / 2, whose key block t % 2 holds its key
+    // rows; tiles past the keys by the last wave.
+    const int cno = max(0, min(kn, ncand - k0));
+    const int cn = cno + (last && ncand > nko ? 1 : 0);
+    const int nr = cn + (last ? g : 0);
+    const int nt = (nr + 15) / 16;
+    for (int t = 0; t < nt; ++t) {
+      if (min(t >> 1, kWaves - 1) != wave) continue;
+      const int row = 16 * t + n16;
+      // rows past the keys: the new pair, a query, else a copy of a query (never read back)
+      const T* xr = row < cn ? sm_nk : sm_q + min(max(row - cn, 0), g - 1) * RS;
+      const bool use = row < cno;
+      const bool odd = (t & 1) != 0;               // key block t % 2 (selected, not indexed)
+      f32x4 U[4];
+      pre16<DT, HD>([&](int kb, u32x4& hi, u32x4& lo) {
+                      const KOp<DT> kr = KOp<DT>::pick(odd, Kr[0][kb], Kr[1][kb]);
+                      kr.op(use, xr + 32 * kb + 8 * q4, hi, lo);
+                    },
+                    sm_wt, n16, q4, U);
+      phi_to_slot<DT>(U, sm_s, lane, n16, q4, sm_slot + t * (8 * 64), sm_meta + t * 64);
+    }
+    __syncthreads();                               // phi tiles
+
+    // per slab wave: its columns of the SRE parts and of H^T phi(q)
     if (has_slab) {
-      const int cno = max(0, min(kn, ncand - k0));
-      const int cn = cno + (last && ncand > nko ? 1 : 0);
-      const int nr = cn + (last ? g : 0);
-      const int nt = (nr + 15) / 16;
-      for (int t = 0; t < nt; ++t) {
-        VQuad<DT> vcur[2];
+      if (c == 0) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) vcur[mb] = vs[mb];
-        if (16 * (t + 1) < cn) load_vs(k0 + 16 * (t + 1), n16);   // the next tile's rows
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            float x[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { x[j] = Hraw[mb][kb][0][j]; x[4 + j] = Hraw[mb][kb][1][j]; }
+            Hs.set(mb, kb, x);
+          }
+      }
+      auto tile = [&](int t, const VQuad<DT> (&v)[2]) {
         const int row = 16 * t + n16;
-        // (rows past the last are a copy of a query row, never read back)
-        const T* xrow = row < cno ? sm_k + row * RS
-                                  : (row < cn ? sm_nk : sm_q + min(row - cn, g - 1) * RS);
-        f32x4 U[4];
-        pre16<DT, HD>(xrow, sm_wt, n16, q4, U);
         f32x4 P[2];
         float z;
-        phi_slab<DT>(U, Hs, sm_s, q4, P, z);
+        slab_prod<DT>(sm_slot + t * (8 * 64), sm_meta + t * 64, Hs, lane, n16, P, z);
         if (row < cn) {
           const float iz = z > 0.f ? 1.f / z : 0.f;
           float part = 0.f;
@@ -676,7 +801,7 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
           for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const float e = fmaf(P[mb][i], iz, -vcur[mb].get(i));
+              const float e = fmaf(P[mb][i], iz, -v[mb].get(i));
               part = fmaf(e, e, part);
             }
           part = qsum(part);
@@ -688,6 +813,14 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
             *reinterpret_cast<f32x4*>(sm_nlin + hd * HD + 32 * wave + 16 * mb + 4 * q4) = P[mb];
           if (wave == 0 && q4 == 0) sm_zq[hd] = z;
         }
+      };
+#pragma unroll
+      for (int t = 0; t < NVS; ++t)
+        if (t < nt) tile(t, vs[t]);
+      for (int t = NVS; t < nt; ++t) {
+        VQuad<DT> v[2];
+        if (16 * t < cn) load_vs(v, k0 + 16 * t, n16);
+        tile(t, v);
       }
     }
   }
@@ -714,22 +847,47 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
       const uint64_t win = __ballot(best == m && bpos == p);
       bi = __shfl(bi, (int)__builtin_ctzll(win), 64);
       if (lane == 0) sm_red[0] = bi;
-      // its value row and phi (the key row from LDS while it is staged; every
-      // lane supplies the same row)
       const T* vrow = bi == gs ? sm_lv : cv + (size_t)bi * HD;
       for (int e = lane; e < HD; e += 64) sm_ve[e] = ldf(vrow + e);
-      const T* xrow = bi == gs ? sm_lk : (nko <= KC ? sm_k + bi * RS : ck + (size_t)bi * HD);
-      f32x4 U[4];
-      pre16<DT, HD>(xrow, sm_wt, n16, q4, U);
-      float ph[2][4][4];
-      phi16(U, ph);
-      if (n16 == 0) {
+      if constexpr (!MULTI) {
+        // phi of the folded row from its tile (hi + lo, normalised)
+        const int t = bi >> 4;
+        if (n16 == (bi & 15)) {
+          const u32x4* sl = sm_slot + t * (8 * 64);
+          const f32x4 mt = *reinterpret_cast<const f32x4*>(sm_meta + t * 64 + 4 * n16);
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
+          for (int kb = 0; kb < 4; ++kb) {
+            const u32x4 bh = sl[(2 * kb) * 64 + lane], bl = sl[(2 * kb + 1) * 64 + lane];
+            const float sc = kb < 2 ? mt[0] : mt[1];
+            f32x4 o0, o1;
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-            *reinterpret_cast<f32x4*>(sm_phe + 64 * half + 16 * mt + 4 * q4) =
-                f32x4{ph[half][mt][0], ph[half][mt][1], ph[half][mt][2], ph[half][mt][3]};
+            for (int j = 0; j < 8; ++j) {
+              const uint32_t hw = (bh[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+              const uint32_t lw = (bl[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+              const float x = (DT::from_bits(hw) + DT::from_bits(lw)) * sc;
+              if (j < 4) o0[j] = x; else o1[j - 4] = x;
+            }
+            *reinterpret_cast<f32x4*>(sm_phe + 32 * kb + 4 * q4) = o0;
+            *reinterpret_cast<f32x4*>(sm_phe + 32 * kb + 16 + 4 * q4) = o1;
+          }
+        }
+      } else {
+        // (chunks of earlier keys are gone) phi of the folded row again, every
+        // lane supplying the same row
+        const T* xrow = bi == gs ? sm_lk : ck + (size_t)bi * HD;
+        f32x4 U[4];
+        pre16<DT, HD>([&](int kb, u32x4& hi, u32x4& lo) { xop(dt, xrow + 32 * kb + 8 * q4, hi, lo); },
+                      sm_wt, n16, q4, U);
+        float ph[2][4][4];
+        phi16(U, ph);
+        if (n16 == 0) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+              *reinterpret_cast<f32x4*>(sm_phe + 64 * half + 16 * mt + 4 * q4) =
+                  f32x4{ph[half][mt][0], ph[half][mt][1], ph[half][mt][2], ph[half][mt][3]};
+        }
       }
     }
   } else {
@@ -774,11 +932,13 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
         for (int kb = 0; kb < 4; ++kb) {
           const f32x4 p0 = *reinterpret_cast<const f32x4*>(sm_phe + 32 * kb + 4 * q4);
           const f32x4 p1 = *reinterpret_cast<const f32x4*>(sm_phe + 32 * kb + 16 + 4 * q4);
+          float hv[8];
+          Hs.get(mb, kb, hv);
           f32x4 x0, x1;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            x0[j] = fmaf(p0[j], ve, Hs[mb][kb][j]);
-            x1[j] = fmaf(p1[j], ve, Hs[mb][kb][4 + j]);
+            x0[j] = fmaf(p0[j], ve, hv[j]);
+            x1[j] = fmaf(p1[j], ve, hv[4 + j]);
           }
           *reinterpret_cast<f32x4*>(hrow + 32 * kb) = x0;
           *reinterpret_cast<f32x4*>(hrow + 32 * kb + 16) = x1;
@@ -824,10 +984,10 @@ hipError_t launch_transpose_w(const void* W, void* WT, int Hkv, int d, bool f32,
 
 template <class DT, int HD>
 static hipError_t launch_decode_t(const DecodeArgs& a, int U, hipStream_t st) {
-  if (a.kc < 32 || a.kc % 32 || a.kc > 32 * kWaves || a.g < 1 || a.g > 4) return hipErrorInvalidValue;
-  const int nomax = a.lam + a.eta;
-  const size_t lds = dec_layout(a.lam, HD, (int)sizeof(typename DT::T), a.kc < nomax ? a.kc : nomax).total;
-  const bool multi = nomax > a.kc;
+  if (a.kc != kKC || a.g < 1 || a.g > 4) return hipErrorInvalidValue;
+  const size_t lds = dec_layout(a.lam, a.eta, HD, (int)sizeof(typename DT::T)).total;
+  if (lds > kLdsOne) return hipErrorInvalidValue;
+  const bool multi = a.lam + a.eta > kKC;
   const void* fn = multi ? (const void*)decode_kernel<DT, HD, true> : (const void*)decode_kernel<DT, HD, false>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
