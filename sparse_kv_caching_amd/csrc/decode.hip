@@ -402,6 +402,35 @@ template <> struct VQuad<F32> {
   __device__ __forceinline__ float get(int i) const { return w[i]; }
 };
 
+// CPL consecutive elements of a V row (the lane's P V columns) in registers
+template <class DT, int CPL> struct VCols;
+template <> struct VCols<BF16, 2> {
+  using W = uint32_t;
+  __device__ static __forceinline__ W load(const uint16_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+  __device__ static __forceinline__ void cvt(W w, float* o) {
+    o[0] = __uint_as_float(w << 16);
+    o[1] = __uint_as_float(w & 0xFFFF0000u);
+  }
+};
+template <> struct VCols<BF16, 1> {
+  using W = uint32_t;
+  __device__ static __forceinline__ W load(const uint16_t* p) { return *p; }
+  __device__ static __forceinline__ void cvt(W w, float* o) { o[0] = __uint_as_float(w << 16); }
+};
+template <> struct VCols<F32, 2> {
+  using W = u32x2;
+  __device__ static __forceinline__ W load(const float* p) { return *reinterpret_cast<const u32x2*>(p); }
+  __device__ static __forceinline__ void cvt(W w, float* o) {
+    o[0] = __uint_as_float(w[0]);
+    o[1] = __uint_as_float(w[1]);
+  }
+};
+template <> struct VCols<F32, 1> {
+  using W = uint32_t;
+  __device__ static __forceinline__ W load(const float* p) { return __float_as_uint(*p); }
+  __device__ static __forceinline__ void cvt(W w, float* o) { o[0] = __uint_as_float(w); }
+};
+
 }  // namespace
 
 // Keys per chunk (kKC = 128); kc = 0 when the layout exceeds the LDS of a CU.
@@ -426,8 +455,7 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   constexpr int PER = 16 / (int)sizeof(T);   // elements per 16-byte piece
   constexpr int PPR = HD / PER;              // pieces per row
   constexpr int RS = HD + WP;                // LDS row stride (elements)
-  constexpr int KGR = 64 / PPR;              // key groups of the P V layout
-  constexpr int KPL = 32 / KGR;              // keys per lane of a tile
+  constexpr int CPL = HD / 64;               // P V columns per lane
   constexpr int WPT = kM * PPR / kThreads;   // W^T pieces per thread
   constexpr int MISC = 8 * PPR + kD / 4;     // queries (4 rows), leaving and new pair, s
   constexpr int MPT = (MISC + kThreads - 1) / kThreads;
@@ -436,7 +464,7 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   const int u = blockIdx.x, lam = a.lam, eta = a.eta, g = a.g;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n16 = lane & 15, q4 = lane >> 4;       // 16 x 16 MFMA layout: row / column, K group
-  const int kg = lane / PPR, cp = lane % PPR;      // P V layout: key group, piece
+  const int kg = lane / PPR, cp = lane % PPR;      // a lane's piece of a row: row group, piece
   const int kvh = u % a.Hkv;
   const long long n = a.n;
   const int gs = (int)min((long long)lam, max(0LL, n - eta));
@@ -496,11 +524,10 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
     return val ? vin : kin;
   };
   // The wave's keys of chunk k0 (keys k0 + 32 wave + 16 kt + n16, clamped to
-  // the chunk) as MFMA operands, and their V rows in the P V layout: lane
-  // (kg, cp) takes piece cp of keys 32 wave + KGR j + kg (the weights of
-  // absent keys are 0).
+  // the chunk) as MFMA operands, and their V rows for P V: lane l takes the
+  // columns CPL l .. of every key (the weights of absent keys are 0).
   KOp<DT> Kr[2][KB];
-  u32x4 Vpv[KPL];
+  typename VCols<DT, CPL>::W Vpv[32];
   auto load_tile = [&](int k0, int kn, int ln) {
     if (32 * wave < kn) {
 #pragma unroll
@@ -510,10 +537,8 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
         for (int kb = 0; kb < KB; ++kb) Kr[kt][kb].load(kr + 32 * kb);
       }
 #pragma unroll
-      for (int j = 0; j < KPL; ++j) {
-        const int key = min(32 * wave + KGR * j + ln / PPR, kn - 1);
-        Vpv[j] = *reinterpret_cast<const u32x4*>(key_row(k0 + key, true) + (ln % PPR) * PER);
-      }
+      for (int j = 0; j < 32; ++j)
+        Vpv[j] = VCols<DT, CPL>::load(key_row(k0 + min(32 * wave + j, kn - 1), true) + CPL * ln);
     }
   };
   // V values of candidate row row0 + rr at the lane's SRE columns
@@ -557,6 +582,7 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
 #pragma unroll
   for (int t = 0; t < NVS; ++t)
     if (has_slab && 16 * t < ncand) load_vs(vs[t], 16 * t, n16);
+  for (int i = tid; i < gs; i += kThreads) sm_cpos[i] = a.cache_pos[(size_t)u * lam + i];
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
     const int i = j * kThreads + tid;
@@ -583,7 +609,6 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
       }
     }
   }
-  for (int i = tid; i < gs; i += kThreads) sm_cpos[i] = a.cache_pos[(size_t)u * lam + i];
   __syncthreads();
 
   const float scale2 = kL2E / sqrtf((float)HD);   // logits in the log2 domain
@@ -612,11 +637,11 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
         if (has_slab && k0 + 16 * tt < ncand) load_vs(vs[tt], k0 + 16 * tt, t & 15);
     }
     {
-      float acc[4][PER];
+      float acc[4][CPL];
 #pragma unroll
       for (int hd = 0; hd < 4; ++hd)
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[hd][e] = 0.f;
+        for (int e = 0; e < CPL; ++e) acc[hd][e] = 0.f;
       float alpha[4] = {1.f, 1.f, 1.f, 1.f};       // rescale of the earlier chunks' partials
       // logits of the wave's keys: S^T = K Q^T in two 16-key blocks, lane
       // (n16, q4) = query n16, keys 32 wave + 16 kt + 4 q4 + i; softmax
@@ -669,24 +694,25 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
         for (int hd = 0; hd < 4; ++hd)
           lrun[hd] = fmaf(lrun[hd], alpha[hd], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), hd)));
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // weights written above
-        // P V: lane (kg, cp) over its keys, PER columns, four heads
+        // P V: lane l over the 32 keys, its CPL columns, four heads
 #pragma unroll
-        for (int j = 0; j < KPL; ++j) {
-          const f32x4 p4 = *reinterpret_cast<const f32x4*>(sm_logit + 4 * (32 * wave + KGR * j + kg));
-          float v[PER];
-          cvt_piece(dt, Vpv[j], v);
+        for (int j = 0; j < 32; ++j) {
+          const f32x4 p4 = *reinterpret_cast<const f32x4*>(sm_logit + 4 * (32 * wave + j));
+          float v[CPL];
+          VCols<DT, CPL>::cvt(Vpv[j], v);
 #pragma unroll
           for (int hd = 0; hd < 4; ++hd)
 #pragma unroll
-            for (int e = 0; e < PER; ++e) acc[hd][e] = fmaf(p4[hd], v[e], acc[hd][e]);
+            for (int e = 0; e < CPL; ++e) acc[hd][e] = fmaf(p4[hd], v[e], acc[hd][e]);
         }
       }
       if (last && wave == kWaves - 1) {
         // the new pair (key nko): logits q . k on the VALU, lane (kg, cp) a
-        // piece of head hd0 + kg
+        // piece of head hd0 + kg (RG row groups of PPR lanes)
+        constexpr int RG = 64 / PPR;
         float snew[4];
 #pragma unroll
-        for (int hd0 = 0; hd0 < 4; hd0 += KGR) {
+        for (int hd0 = 0; hd0 < 4; hd0 += RG) {
           const int hd = hd0 + kg;
           float part = 0.f;
           if (hd < g) {
@@ -699,12 +725,13 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
 #pragma unroll
           for (int o = 1; o < PPR; o <<= 1) part += __shfl_xor(part, o, 64);
 #pragma unroll
-          for (int hh = 0; hh < KGR; ++hh)
+          for (int hh = 0; hh < RG; ++hh)
             if (hd0 + hh < 4)
               snew[hd0 + hh] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(part), hh * PPR)) * scale2;
         }
-        float v[PER];
-        cvt_piece(dt, *reinterpret_cast<const u32x4*>(sm_nv + cp * PER), v);
+        float v[CPL];
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) v[e] = DT::to_f32(sm_nv[CPL * lane + e]);
 #pragma unroll
         for (int hd = 0; hd < 4; ++hd) {
           const float mn = fmaxf(mrun[hd], snew[hd]);
@@ -713,32 +740,19 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
           lrun[hd] = fmaf(lrun[hd], al, p);
           mrun[hd] = mn;
           alpha[hd] *= al;
-          const float pk = kg == 0 ? p : 0.f;      // added once over the key groups
 #pragma unroll
-          for (int e = 0; e < PER; ++e) acc[hd][e] = fmaf(acc[hd][e], al, pk * v[e]);
+          for (int e = 0; e < CPL; ++e) acc[hd][e] = fmaf(acc[hd][e], al, p * v[e]);
         }
       }
-      // into the wave's partials: sum over the key groups, rescale the earlier chunks
-#pragma unroll
-      for (int o = PPR; o < 64; o <<= 1)
-#pragma unroll
-        for (int hd = 0; hd < 4; ++hd)
-#pragma unroll
-          for (int e = 0; e < PER; ++e) acc[hd][e] += __shfl_xor(acc[hd][e], o, 64);
+      // into the wave's partials, rescaling the earlier chunks'
 #pragma unroll
       for (int hd = 0; hd < 4; ++hd) {
-        if (hd % KGR == kg) {                      // lane (kg, cp) writes the heads = kg mod KGR
-          float* dst = sm_pv + (wave * 4 + hd) * HD + cp * PER;
+        float* dst = sm_pv + (wave * 4 + hd) * HD + CPL * lane;
 #pragma unroll
-          for (int e = 0; e < PER; e += 4) {
-            f32x4 x = f32x4{acc[hd][e], acc[hd][e + 1], acc[hd][e + 2], acc[hd][e + 3]};
-            if (MULTI && c > 0) {
-              const f32x4 o = *reinterpret_cast<const f32x4*>(dst + e);
-#pragma unroll
-              for (int k = 0; k < 4; ++k) x[k] = fmaf(o[k], alpha[hd], x[k]);
-            }
-            *reinterpret_cast<f32x4*>(dst + e) = x;
-          }
+        for (int e = 0; e < CPL; ++e) {
+          float x = acc[hd][e];
+          if (MULTI && c > 0) x = fmaf(dst[e], alpha[hd], x);
+          dst[e] = x;
         }
       }
       if (last) {
