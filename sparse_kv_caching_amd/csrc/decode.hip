@@ -462,7 +462,8 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   constexpr int NVS = 5;                     // phi tiles whose SRE values are loaded up front
   const DT dt{};
   const int u = blockIdx.x, lam = a.lam, eta = a.eta, g = a.g;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // (the wave index is uniform: scalar registers and scalar address math)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n16 = lane & 15, q4 = lane >> 4;       // 16 x 16 MFMA layout: row / column, K group
   const int kg = lane / PPR, cp = lane % PPR;      // a lane's piece of a row: row group, piece
   const int kvh = u % a.Hkv;
