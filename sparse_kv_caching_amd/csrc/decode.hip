@@ -529,7 +529,7 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   // columns CPL l .. of every key (the weights of absent keys are 0).
   KOp<DT> Kr[2][KB];
   typename VCols<DT, CPL>::W Vpv[32];
-  auto load_tile = [&](int k0, int kn, int ln) {
+  auto load_keys = [&](int k0, int kn, int ln) {
     if (32 * wave < kn) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -537,6 +537,10 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) Kr[kt][kb].load(kr + 32 * kb);
       }
+    }
+  };
+  auto load_vals = [&](int k0, int kn, int ln) {
+    if (32 * wave < kn) {
 #pragma unroll
       for (int j = 0; j < 32; ++j)
         Vpv[j] = VCols<DT, CPL>::load(key_row(k0 + min(32 * wave + j, kn - 1), true) + CPL * ln);
@@ -564,8 +568,7 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
     return reinterpret_cast<u32x4*>(sm_s + 4 * (i - 8 * PPR));
   };
 
-  // ---- first wave of reads: W^T and the small pieces (to LDS), the wave's
-  // keys and values, the SRE values of the first phi tiles
+  // ---- first wave of reads: W^T and the small pieces (to LDS), the wave's keys
   u32x4 wbuf[WPT], mbuf[MPT];
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
@@ -577,13 +580,9 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
     const u32x4* p = misc_src(j * kThreads + tid);
     if (p) mbuf[j] = *p;
   }
-  const int kn0 = min(kKC, nko);
-  load_tile(0, kn0, lane);
-  VQuad<DT> vs[NVS][2];
-#pragma unroll
-  for (int t = 0; t < NVS; ++t)
-    if (has_slab && 16 * t < ncand) load_vs(vs[t], 16 * t, n16);
   for (int i = tid; i < gs; i += kThreads) sm_cpos[i] = a.cache_pos[(size_t)u * lam + i];
+  const int kn0 = min(kKC, nko);
+  load_keys(0, kn0, lane);
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
     const int i = j * kThreads + tid;
@@ -594,10 +593,17 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
     const int i = j * kThreads + tid;
     if (misc_src(i)) *misc_dst(i) = mbuf[j];
   }
-  // ---- second wave: the H slab, issued once the first wave's LDS data has
-  // arrived.  Lane (n16, q4) holds H[sigma(kb, q4, j)][32 wave + 16 mb + n16]:
-  // two 16-byte pieces of an H^T row per block.
+  // ---- second wave, issued once the first wave's LDS data has arrived: the
+  // values of the wave's keys, the SRE values of the first phi tiles, the H
+  // slab (lane (n16, q4) holds H[sigma(kb, q4, j)][32 wave + 16 mb + n16]:
+  // two 16-byte pieces of an H^T row per block).  Logits and phi run while
+  // these stream in.
   __builtin_amdgcn_sched_barrier(0);
+  load_vals(0, kn0, lane);
+  VQuad<DT> vs[NVS][2];
+#pragma unroll
+  for (int t = 0; t < NVS; ++t)
+    if (has_slab && 16 * t < ncand) load_vs(vs[t], 16 * t, n16);
   f32x4 Hraw[2][4][2];
   if (has_slab) {
 #pragma unroll
@@ -632,18 +638,14 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
       // live through the whole kernel)
       int t = lane;
       __asm__ volatile("" : "+v"(t));
-      load_tile(k0, kn, t);
+      load_keys(k0, kn, t);
+      load_vals(k0, kn, t);
 #pragma unroll
       for (int tt = 0; tt < NVS; ++tt)
         if (has_slab && k0 + 16 * tt < ncand) load_vs(vs[tt], k0 + 16 * tt, t & 15);
     }
+    float alpha[4] = {1.f, 1.f, 1.f, 1.f};         // rescale of the earlier chunks' partials
     {
-      float acc[4][CPL];
-#pragma unroll
-      for (int hd = 0; hd < 4; ++hd)
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) acc[hd][e] = 0.f;
-      float alpha[4] = {1.f, 1.f, 1.f, 1.f};       // rescale of the earlier chunks' partials
       // logits of the wave's keys: S^T = K Q^T in two 16-key blocks, lane
       // (n16, q4) = query n16, keys 32 wave + 16 kt + 4 q4 + i; softmax
       // weights with the running max
@@ -694,8 +696,43 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
 #pragma unroll
         for (int hd = 0; hd < 4; ++hd)
           lrun[hd] = fmaf(lrun[hd], alpha[hd], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ls), hd)));
+      }
+    }
+
+    // phi rows of the chunk: its candidate keys (cno), the new pair when it is
+    // a candidate (eta = 0), then (last chunk) the queries.  Tile t (rows
+    // 16 t ..) is computed by wave t / 2, whose key block t % 2 holds its key
+    // rows; tiles past the keys by the last wave.
+    const int cno = max(0, min(kn, ncand - k0));
+    const int cn = cno + (last && ncand > nko ? 1 : 0);
+    const int nr = cn + (last ? g : 0);
+    const int nt = (nr + 15) / 16;
+    for (int t = 0; t < nt; ++t) {
+      if (min(t >> 1, kWaves - 1) != wave) continue;
+      const int row = 16 * t + n16;
+      // rows past the keys: the new pair, a query, else a copy of a query (never read back)
+      const T* xr = row < cn ? sm_nk : sm_q + min(max(row - cn, 0), g - 1) * RS;
+      const bool use = row < cno;
+      const bool odd = (t & 1) != 0;               // key block t % 2 (selected, not indexed)
+      f32x4 U[4];
+      pre16<DT, HD>([&](int kb, u32x4& hi, u32x4& lo) {
+                      const KOp<DT> kr = KOp<DT>::pick(odd, Kr[0][kb], Kr[1][kb]);
+                      kr.op(use, xr + 32 * kb + 8 * q4, hi, lo);
+                    },
+                    sm_wt, n16, q4, U);
+      phi_to_slot<DT>(U, sm_s, lane, n16, q4, sm_slot + t * (8 * 64), sm_meta + t * 64);
+    }
+    // P V of the wave's keys (their values arrive while the logits and phi
+    // tiles run), the new pair, into the wave's partials
+    {
+      float acc[4][CPL];
+#pragma unroll
+      for (int hd = 0; hd < 4; ++hd)
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) acc[hd][e] = 0.f;
+      if (32 * wave < kn) {
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // weights written above
-        // P V: lane l over the 32 keys, its CPL columns, four heads
+        // lane l over the 32 keys, its CPL columns, four heads
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
           const f32x4 p4 = *reinterpret_cast<const f32x4*>(sm_logit + 4 * (32 * wave + j));
@@ -766,29 +803,6 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
       }
     }
 
-    // phi rows of the chunk: its candidate keys (cno), the new pair when it is
-    // a candidate (eta = 0), then (last chunk) the queries.  Tile t (rows
-    // 16 t ..) is computed by wave t / 2, whose key block t % 2 holds its key
-    // rows; tiles past the keys by the last wave.
-    const int cno = max(0, min(kn, ncand - k0));
-    const int cn = cno + (last && ncand > nko ? 1 : 0);
-    const int nr = cn + (last ? g : 0);
-    const int nt = (nr + 15) / 16;
-    for (int t = 0; t < nt; ++t) {
-      if (min(t >> 1, kWaves - 1) != wave) continue;
-      const int row = 16 * t + n16;
-      // rows past the keys: the new pair, a query, else a copy of a query (never read back)
-      const T* xr = row < cn ? sm_nk : sm_q + min(max(row - cn, 0), g - 1) * RS;
-      const bool use = row < cno;
-      const bool odd = (t & 1) != 0;               // key block t % 2 (selected, not indexed)
-      f32x4 U[4];
-      pre16<DT, HD>([&](int kb, u32x4& hi, u32x4& lo) {
-                      const KOp<DT> kr = KOp<DT>::pick(odd, Kr[0][kb], Kr[1][kb]);
-                      kr.op(use, xr + 32 * kb + 8 * q4, hi, lo);
-                    },
-                    sm_wt, n16, q4, U);
-      phi_to_slot<DT>(U, sm_s, lane, n16, q4, sm_slot + t * (8 * 64), sm_meta + t * 64);
-    }
     __syncthreads();                               // phi tiles
 
     // per slab wave: its columns of the SRE parts and of H^T phi(q)
