@@ -388,6 +388,9 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   ca.xcd_group = (U % 8 == 0) ? 1 : 0;
   ca.xbuf = (uint64_t*)(base + L.xbuf);
   ca.err = st->dev_err;
+  ca.j0 = 0;
+  ca.j1 = nch;
+  ca.xstep0 = 0;
   if (ca.k > 1) {
     e = launch_zero_u32((unsigned*)ca.xbuf, (size_t)U * 2 * (d / 32) * (lam + C) * 2, s);
     if (e != hipSuccess) return hip_fail(st, e, "exchange reset");
@@ -406,6 +409,8 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   aa.g = g; aa.Hkv = st->cfg.kv_heads; aa.nch = nch; aa.C = C;
   aa.ptile = attn_positions_per_block(C, g);
   aa.nblk = aa.ptile / 32;
+  aa.ch0 = 0;
+  aa.nch_launch = nch;
   { ProfScope ps(st, LOLA_KERNEL_ATTN, s); e = launch_attn(aa, U, st->f32, s); }
   if (e != hipSuccess) return hip_fail(st, e, "attention launch");
 

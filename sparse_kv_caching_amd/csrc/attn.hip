@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   // unit fastest: with the unit count a multiple of 8, a unit's chunks share
   // an XCD (blocks are dealt to the 8 XCDs round-robin) and its K/V rows,
   // re-read by every chunk, stay in that XCD's L2
-  const int u = blockIdx.x, j = blockIdx.y, pt = blockIdx.z;
+  const int u = blockIdx.x, j = a.ch0 + blockIdx.y, pt = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, r = lane & 31;
   const int kvh = u % a.Hkv;
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 template <class DT, int HD>
 static hipError_t launch_attn_t(const AttnArgs& a, int U, hipStream_t st) {
   const int nptile = (a.C + a.ptile - 1) / a.ptile;
-  dim3 grid(U, a.nch, nptile);
+  dim3 grid(U, a.nch_launch, nptile);
   const size_t lds = attn_lds_bytes(HD, a.vr.lam, DT::kSplit);
   const void* fn = (const void*)attn_kernel<DT, HD>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -474,7 +474,8 @@ int attn_positions_per_block(int C, int g) {
 }
 
 hipError_t launch_attn(const AttnArgs& a, int U, bool f32, hipStream_t st) {
-  if (U <= 0 || a.nch <= 0) return hipSuccess;
+  if (U <= 0 || a.nch_launch <= 0) return hipSuccess;
+  if (a.ch0 < 0 || a.ch0 + a.nch_launch > a.nch) return hipErrorInvalidValue;
   if (a.vr.d == 64)
     return f32 ? launch_attn_t<F32, 64>(a, U, st) : launch_attn_t<BF16, 64>(a, U, st);
   return f32 ? launch_attn_t<F32, 128>(a, U, st) : launch_attn_t<BF16, 128>(a, U, st);

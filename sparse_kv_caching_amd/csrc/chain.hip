@@ -39,6 +39,11 @@
 // g and scores the candidate tiles t with t % CS == ch.  The CS workgroups of
 // one slab group hold the same columns and apply the same fold.
 //
+// Segments.  A launch runs steps j0 .. j1 - 1; the state between segments
+// is H and s in global memory and the cache list (virtual rows) in finalG,
+// and the exchange tags continue over the call (xstep0), so that the
+// attention of finished chunks can run beside the rest of the chain.
+//
 // Exchange.  Every (slab, candidate) part is written as one 64-bit word
 // (value, step tag) with an agent-scope relaxed atomic store (it bypasses the
 // non-coherent caches); a reader polls each word with agent-scope atomic
@@ -191,10 +196,14 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
   }
   for (int F = tid; F < kD; F += kThreads) sm.s32[F] = a.s[(size_t)u * kD + F];
   const long long n0 = vr.n0;
-  const int gs0 = (int)min((long long)lam, max(0LL, n0 - eta));
+  // the cache at the first step j0: at the call start, cache slots 0..gs0-1;
+  // a later segment resumes from the list the previous one wrote to finalG
+  // (gs entries: every position that left the window is cached or folded)
+  const int gs0 = (int)min((long long)lam, max(0LL, n0 + (long long)a.j0 * a.C - eta));
   for (int i = tid; i < gs0; i += kThreads) {
-    sm.G[i] = i;
-    sm.Gp[i] = vr.cache_pos[(size_t)u * lam + i];
+    const int vi = a.j0 == 0 ? i : a.finalG[(size_t)u * lam + i];
+    sm.G[i] = vi;
+    sm.Gp[i] = (int32_t)vr.pos_of(u, vi);
   }
   if (tid == 0) sm.misc[16] = 0;
 
@@ -222,9 +231,9 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
   lds_barrier();
 
   int gs = gs0;
-  int xstep = 0;                                  // exchange steps so far
+  int xstep = a.xstep0;                           // exchange steps so far (over the call)
   const size_t phi_unit = (size_t)u * a.NV * kD;
-  for (int j = 0; j < a.nch; ++j) {
+  for (int j = a.j0; j < a.j1; ++j) {
     const long long nj = n0 + (long long)j * a.C;
     const int c = min(a.C, vr.T - j * a.C);
 

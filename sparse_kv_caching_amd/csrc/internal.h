@@ -87,6 +87,8 @@ struct ChainArgs {
   int xcd_group;            // U % 8 == 0: a unit's workgroups share a block residue mod 8
   uint64_t* xbuf;           // [U, 2, d / 32, lam + C]  tagged SRE parts per slab (k > 1), zeroed
   int* err;                 // device error flag: bit 0 = an exchange partner was lost
+  int j0, j1;               // steps of this launch (a segment of the call's nch)
+  int xstep0;               // exchange steps of the call before j0 (tags continue)
 };
 
 // K3: window + cache softmax attention merged with the linear read.
@@ -99,6 +101,7 @@ struct AttnArgs {
   const int32_t* snapG;
   float* out;               // [U, g, T, d]
   int g, Hkv, nch, C, ptile, nblk;  // positions per WG, 32-position blocks per WG
+  int ch0, nch_launch;      // chunks ch0 .. ch0 + nch_launch - 1 in this launch
 };
 
 // Finalize: new cache rows / positions and window ring after a prefill call.
