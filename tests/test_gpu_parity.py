@@ -215,23 +215,20 @@ def _full_size_single_call(wl, units=None):
         assert np.linalg.norm(gst.s[u] - s) / np.linalg.norm(s) <= tol
 
 
-def test_decode_lockstep():
-    """Token-by-token decode after a prefill: every step's outputs, cache
+def _decode_lockstep(wl, steps):
+    """Prefill, then token-by-token decode: every step's outputs, cache
     membership (argmin rule) and state against the oracle (resync per step)."""
-    wl = WORKLOADS["decode_b64"].scaled(B=3, Hq=8, Hkv=2, T=96, eta=16, lam=24, C=32)
+    print("decode lockstep", wl, flush=True)
     inp = make_inputs(wl)
     layer = make_layer(wl, inp.W)
     layer.prefill(dev(wl, inp.q), dev(wl, inp.k), dev(wl, inp.v), wl.C)
     st = gpu_state(layer, wl)
     Wf = inp.f64("W")
-    rng = np.random.default_rng(7)
     tol = _tol(wl)
     stats = dict(exact=0, allowed=0)
-    from sparse_kv_caching_amd.workloads import bf16_bits
-    for step in range(60):
-        q = bf16_bits(rng.standard_normal((wl.B, wl.Hq, wl.d)).astype(np.float32))
-        k = bf16_bits(rng.standard_normal((wl.B, wl.Hkv, wl.d)).astype(np.float32))
-        v = bf16_bits(rng.standard_normal((wl.B, wl.Hkv, wl.d)).astype(np.float32))
+    from sparse_kv_caching_amd.workloads import decode_inputs
+    for step in range(steps):
+        q, k, v = decode_inputs(wl, step)
         yg = layer.decode(dev(wl, q), dev(wl, k), dev(wl, v)).cpu().numpy().astype(np.float64)
         logs = []
         yo = O.decode_step(st, to_f64(wl, q), to_f64(wl, k), to_f64(wl, v), Wf, logs=logs)
@@ -241,11 +238,36 @@ def test_decode_lockstep():
         assert bad == 0, (step, msgs[:3])
         stats["exact"] += ex
         stats["allowed"] += al
-        assert rel_fro(gst.H, st.H) <= tol and rel_fro(gst.s, st.s) <= tol
+        assert rel_fro(gst.H, st.H) <= tol and rel_fro(gst.s, st.s) <= tol, step
         np.testing.assert_array_equal(gst.win_k, st.win_k)
         st = gst
     print(stats)
     layer.free()
+    return stats
+
+
+def test_decode_lockstep():
+    """Token-by-token decode after a prefill, 60 steps (one key chunk)."""
+    wl = WORKLOADS["decode_b64"].scaled(B=3, Hq=8, Hkv=2, T=96, eta=16, lam=24, C=32)
+    _decode_lockstep(wl, 60)
+
+
+@pytest.mark.parametrize("name,eta,lam,T", [
+    ("decode_b64", 96, 64, 192),     # lam + eta = 160 > 128: the chunked decode kernel
+    ("decode_b64", 0, 24, 64),       # eta = 0: the new pair leaves at once
+    ("decode_b64", 16, 0, 64),       # lam = 0: every leaving pair is folded
+    ("decode_b64", 64, 64, 32),      # the window and cache still filling
+    ("tiny_fp32", 100, 40, 160),     # fp32, d = 64, chunked
+])
+def test_decode_lockstep_shapes(name, eta, lam, T):
+    """Decode through the chunked kernel instance and the degenerate cases."""
+    base = WORKLOADS[name]
+    kw = dict(B=2, T=T, eta=eta, lam=lam, C=32)
+    if name == "decode_b64":
+        kw.update(Hq=8, Hkv=2)
+    else:
+        kw.update(planted=0)
+    _decode_lockstep(base.scaled(**kw), 40)
 
 
 def test_decode_equals_prefill_c1_and_fp32_decode():
