@@ -193,14 +193,18 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
 }
-// inclusive prefix sum over the wave
+// inclusive prefix sum over the wave, with DPP moves (no LDS round trips):
+// shifts by 1, 2, 4, 8 within each row of 16 lanes (lanes shifted in from
+// outside the row add 0), then the last lane of row 0 is added to row 1 and
+// that of row 2 to row 3 (row_bcast:15), then lane 31 to rows 2 and 3
+// (row_bcast:31)
 __device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
   return x;
 }
 
