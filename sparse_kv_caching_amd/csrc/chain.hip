@@ -383,13 +383,8 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
       kmin = key < kmin ? key : kmin;
       kmax = key > kmax ? key : kmax;
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const uint64_t a1 = __shfl_xor(kmin, o, 64), a2 = __shfl_xor(kmax, o, 64);
-      kmin = a1 < kmin ? a1 : kmin;
-      kmax = a2 > kmax ? a2 : kmax;
-    }
-    if (lane == 0) { sm.kred[2 * wave] = kmin; sm.kred[2 * wave + 1] = kmax; }
+    wave_minmax_u64(kmin, kmax);
+    if (lane == 63) { sm.kred[2 * wave] = kmin; sm.kred[2 * wave + 1] = kmax; }
     if (lost) sm.misc[16] = 1;
     lds_barrier();
     if (sm.misc[16]) {           // a partner is lost: stop (the error flag is set)
@@ -556,11 +551,19 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
         // s partial sums: feature F, 64 / NPART tokens per part, fixed order
         const int F = tid % kD, qt = tid / kD;
         constexpr int TPP = 64 / (kThreads / kD);
+        static_assert(TPP % 8 == 0, "parts are read as 8-token pieces");
         float part = 0.f;
 #pragma unroll
-        for (int q = 0; q < TPP; ++q)
-          part += DT::from_bits(sm.phT_hi[F * STP + TPP * qt + q]) +
-                  DT::from_bits(sm.phT_lo[F * STP + TPP * qt + q]);
+        for (int q8 = 0; q8 < TPP / 8; ++q8) {
+          const u32x4 wh = ld16(sm.phT_hi + F * STP + TPP * qt + 8 * q8);
+          const u32x4 wl = ld16(sm.phT_lo + F * STP + TPP * qt + 8 * q8);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const uint32_t bh = (q & 1) ? wh[q >> 1] >> 16 : wh[q >> 1] & 0xFFFFu;
+            const uint32_t bl = (q & 1) ? wl[q >> 1] >> 16 : wl[q >> 1] & 0xFFFFu;
+            part += DT::from_bits(bh) + DT::from_bits(bl);
+          }
+        }
         sacc += part;
       }
       const int nkb = min(4, (nS - sb + 15) / 16);

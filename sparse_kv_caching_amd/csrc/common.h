@@ -193,6 +193,26 @@ __device__ __forceinline__ int wave_sum_i(int x) {
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
   return x;
 }
+// One DPP move of a 64-bit value (both halves); lanes without a source (or
+// in rows outside ROWMASK) get `ident`.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x, uint64_t ident) {
+  const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)ident, (int)(uint32_t)x, CTRL, ROWMASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(ident >> 32), (int)(uint32_t)(x >> 32), CTRL, ROWMASK, 0xf, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+// Wave minimum and maximum of 64-bit keys, valid in lane 63 (the scan steps
+// of wave_incl_scan below with min / max in place of +).
+__device__ __forceinline__ void wave_minmax_u64(uint64_t& mn, uint64_t& mx) {
+  auto step = [&](uint64_t a, uint64_t b) { mn = a < mn ? a : mn; mx = b > mx ? b : mx; };
+  step(dpp_u64<0x111, 0xf>(mn, ~0ull), dpp_u64<0x111, 0xf>(mx, 0ull));
+  step(dpp_u64<0x112, 0xf>(mn, ~0ull), dpp_u64<0x112, 0xf>(mx, 0ull));
+  step(dpp_u64<0x114, 0xf>(mn, ~0ull), dpp_u64<0x114, 0xf>(mx, 0ull));
+  step(dpp_u64<0x118, 0xf>(mn, ~0ull), dpp_u64<0x118, 0xf>(mx, 0ull));
+  step(dpp_u64<0x142, 0xa>(mn, ~0ull), dpp_u64<0x142, 0xa>(mx, 0ull));
+  step(dpp_u64<0x143, 0xc>(mn, ~0ull), dpp_u64<0x143, 0xc>(mx, 0ull));
+}
+
 // inclusive prefix sum over the wave, with DPP moves (no LDS round trips):
 // shifts by 1, 2, 4, 8 within each row of 16 lanes (lanes shifted in from
 // outside the row add 0), then the last lane of row 0 is added to row 1 and
