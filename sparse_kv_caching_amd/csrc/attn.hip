@@ -38,7 +38,8 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int KT = 64;        // keys per staged tile
 constexpr int HTS = kD + 8;   // LDS row of H^T (16-bit elements)
-constexpr int VTS = KT + 8;   // LDS row of the V^T tile (keys)
+constexpr int VTS = KT + 4;   // LDS row of the V^T tile (keys): 34 dwords, so that the 32 rows of a
+                              // 64-bit operand read fall on distinct bank pairs
 
 // Byte offsets of the LDS arrays; the key phase reuses the region of the
 // linear-read phase.
