@@ -47,13 +47,20 @@ class BruteUnit:
         self.s = [0.0] * self.D
         self.folded: List[int] = []
 
-    # -- Eq. (14), state at chunk start
-    def read(self, q: Sequence[float], t: int, n: int) -> List[float]:
+    # -- Eq. (14), state at chunk start; `branches` (bit 1 state, 2 cache,
+    # 4 window) leaves out the hidden memories (LoLA notes §4.8, Table 12)
+    def read(self, q: Sequence[float], t: int, n: int, branches: int = 7) -> List[float]:
         d, D = self.d, self.D
-        fq = _phi_row(q, self.W)
-        num = [sum(fq[i] * self.H[i][c] for i in range(D)) for c in range(d)]
-        den = sum(fq[i] * self.s[i] for i in range(D))
-        visible = list(self.cache) + list(range(max(0, n - self.eta), t + 1))
+        num, den = [0.0] * d, 0.0
+        if branches & 1:
+            fq = _phi_row(q, self.W)
+            num = [sum(fq[i] * self.H[i][c] for i in range(D)) for c in range(d)]
+            den = sum(fq[i] * self.s[i] for i in range(D))
+        visible = []
+        if branches & 2:
+            visible += list(self.cache)
+        if branches & 4:
+            visible += list(range(max(0, n - self.eta), t + 1))
         for p in visible:
             a = math.exp(sum(q[i] * self.hist_k[p][i] for i in range(d)) / math.sqrt(d))
             den += a
@@ -94,13 +101,13 @@ class BruteUnit:
         self.cache = kept
 
 
-def brute_prefill(units: List[BruteUnit], q, k, v, C: int, n0: int = 0):
+def brute_prefill(units: List[BruteUnit], q, k, v, C: int, n0: int = 0, branches: int = 7):
     """Run T tokens through every unit with chunk length C.
 
     units: B*Hkv BruteUnit, unit b*Hkv + h for sequence b, KV head h.
     q (B, Hq, T, d), k, v (B, Hkv, T, d) as nested sequences or arrays.
     n0: tokens the units have already seen.  Returns y as nested lists
-    [B][Hq][T][d].
+    [B][Hq][T][d].  ``branches``: read mask (see BruteUnit.read).
     """
     B, Hq, T = len(q), len(q[0]), len(q[0][0])
     Hkv = len(k[0])
@@ -119,7 +126,7 @@ def brute_prefill(units: List[BruteUnit], q, k, v, C: int, n0: int = 0):
                 for t in range(t0, t0 + c):
                     for j in range(g):
                         y[b][h * g + j][t] = u.read([float(x) for x in q[b][h * g + j][t]],
-                                                    n0 + t, n)
+                                                    n0 + t, n, branches)
                 u.update(n, c)
                 t0 += c
     return y

@@ -62,6 +62,23 @@ import numpy as np
 
 F64 = np.float64
 
+# Read branches of Eq. (14) (LoLA notes §4.8, Table 12: the ablation hides
+# some memories from the queries while every update runs as before).  The
+# window branch (local keys, including the chunk's causal prefix) is always
+# read, as in every row of that table; it also keeps the normaliser positive.
+BRANCH_STATE = 1      # H^T phi(q) and phi(q)^T s
+BRANCH_SPARSE = 2     # the cache G
+BRANCH_WINDOW = 4     # local positions max(0, n - eta) .. t
+BRANCH_ALL = 7
+
+
+def check_branches(branches: int) -> int:
+    """A read-branch mask: bits BRANCH_*, with the window bit set."""
+    b = int(branches)
+    if b & ~BRANCH_ALL or not b & BRANCH_WINDOW:
+        raise ValueError("read branches must be a subset of 7 that includes the window (4)")
+    return b
+
 
 # --------------------------------------------------------------------------- phi
 def _softmax_last(u: np.ndarray) -> np.ndarray:
@@ -198,10 +215,12 @@ class ChunkLog:
 
 # ------------------------------------------------------------------------ read
 def _read_chunk(st: LolaState, qc: np.ndarray, kc: np.ndarray, vc: np.ndarray,
-                Wu: np.ndarray) -> np.ndarray:
+                Wu: np.ndarray, branches: int = BRANCH_ALL) -> np.ndarray:
     """Eq. (14) for every query of the chunk, with the state at chunk start.
 
-    qc (U, g, c, d); kc, vc (U, c, d).  Returns y (U, g, c, d)."""
+    qc (U, g, c, d); kc, vc (U, c, d).  Returns y (U, g, c, d).  ``branches``
+    drops the terms of hidden memories from both numerator and denominator
+    (LoLA notes §4.8, Table 12)."""
     U, g, c, d = qc.shape
     keys = np.concatenate([st.g_k, st.win_k, kc], axis=1)     # (U, nk, d)
     vals = np.concatenate([st.g_v, st.win_v, vc], axis=1)
@@ -212,9 +231,14 @@ def _read_chunk(st: LolaState, qc: np.ndarray, kc: np.ndarray, vc: np.ndarray,
         raise FloatingPointError("exp(q.k/sqrt(d)) overflowed in float64")
     causal = np.tril(np.ones((c, c), dtype=bool))             # t sees j <= t
     a[..., n_old:] *= causal
-    phq = _phi_units(qc, Wu)                                  # (U, g, c, D)
-    num = np.matmul(a, vals[:, None]) + np.matmul(phq, st.H[:, None])
-    den = a.sum(axis=-1) + np.einsum("ugtf,uf->ugt", phq, st.s)
+    if not branches & BRANCH_SPARSE:
+        a[..., :st.g_k.shape[1]] = 0.0
+    num = np.matmul(a, vals[:, None])
+    den = a.sum(axis=-1)
+    if branches & BRANCH_STATE:
+        phq = _phi_units(qc, Wu)                              # (U, g, c, D)
+        num = num + np.matmul(phq, st.H[:, None])
+        den = den + np.einsum("ugtf,uf->ugt", phq, st.s)
     return num / den[..., None]
 
 
@@ -277,15 +301,19 @@ def _as_units(q, k, v, W, Hkv):
 
 
 def prefill(st: LolaState, q, k, v, W, C: int, *, outputs: bool = True,
-            logs: Optional[List[ChunkLog]] = None) -> Optional[np.ndarray]:
+            logs: Optional[List[ChunkLog]] = None,
+            branches: int = BRANCH_ALL) -> Optional[np.ndarray]:
     """Process T new tokens with chunk length C (the last chunk may be short).
 
     q (B, Hq, T, d); k, v (B, Hkv, T, d); W (Hkv, d, m); ``st`` holds U = B*Hkv
     units and is updated in place.  Returns y (B, Hq, T, d) in float64, or None
     if ``outputs`` is False (the state trajectory does not depend on q).
+    ``branches`` masks the read only (see check_branches); the state update is
+    the same for every mask.
     """
     if C < 1:
         raise ValueError("C must be >= 1")
+    branches = check_branches(branches)
     Hkv = np.asarray(W).shape[0]
     qu, ku, vu, Wu, shape = _as_units(q, k, v, W, Hkv)
     U, g, T, d = qu.shape
@@ -297,7 +325,7 @@ def prefill(st: LolaState, q, k, v, W, C: int, *, outputs: bool = True,
         c = min(C, T - t0)
         sl = slice(t0, t0 + c)
         if outputs:
-            y[:, :, sl] = _read_chunk(st, qu[:, :, sl], ku[:, sl], vu[:, sl], Wu)
+            y[:, :, sl] = _read_chunk(st, qu[:, :, sl], ku[:, sl], vu[:, sl], Wu, branches)
         lg = _update_chunk(st, ku[:, sl], vu[:, sl], Wu)
         if logs is not None:
             logs.append(lg)
@@ -308,11 +336,12 @@ def prefill(st: LolaState, q, k, v, W, C: int, *, outputs: bool = True,
     return y.reshape(B, Hkv, g, T, d).reshape(B, Hq, T, d)
 
 
-def decode_step(st: LolaState, q, k, v, W, *, logs=None) -> np.ndarray:
+def decode_step(st: LolaState, q, k, v, W, *, logs=None,
+                branches: int = BRANCH_ALL) -> np.ndarray:
     """One token for every sequence: q (B, Hq, d), k, v (B, Hkv, d).
     Defined as prefill with T = 1, C = 1 (read, then update)."""
     y = prefill(st, np.asarray(q)[:, :, None], np.asarray(k)[:, :, None],
-                np.asarray(v)[:, :, None], W, 1, logs=logs)
+                np.asarray(v)[:, :, None], W, 1, logs=logs, branches=branches)
     return y[:, :, 0]
 
 
