@@ -117,6 +117,24 @@ int lola_prefill_debug(lola_state* st, const void* q, const void* k, const void*
 int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v, void* out,
                      int out_dtype, void* stream);
 
+/* Read branches (LoLA notes §4.8, Table 12: an ablation that hides memories
+ * from the queries while the window, the cache, H and s are updated exactly
+ * as before).  The read of Eq. (14) keeps the numerator and denominator terms
+ * of the chosen memories only. */
+enum {
+  LOLA_READ_STATE = 1,    /* linear read H^T phi(q), phi(q)^T s */
+  LOLA_READ_CACHE = 2,    /* keys of the sparse cache */
+  LOLA_READ_WINDOW = 4,   /* local keys: window and the chunk's causal prefix */
+  LOLA_READ_ALL = 7
+};
+
+/* Set the read-branch mask of the following prefill and decode calls
+ * (default LOLA_READ_ALL).  The window bit must be set (every read then has
+ * a positive normaliser).  Host-side only, takes effect at the next launch;
+ * kept across lola_state_reset, not part of an exported state.
+ * Errors: INVALID_ARG (NULL state, unknown bits, window bit clear). */
+int lola_set_read_branches(lola_state* st, int branches);
+
 /* Start over: n = 0, H = 0, s = 0, empty window and cache (the memory and W
  * are kept).  Stream-ordered.  Clears a poisoned state. */
 int lola_state_reset(lola_state* st, void* stream);

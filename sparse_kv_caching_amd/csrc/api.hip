@@ -24,6 +24,7 @@ struct lola_state {
   int device;
   hipStream_t last;
   bool poisoned;
+  int branches;             // read mask (LOLA_READ_*)
   float* H;
   float* s;
   void* ring_k;
@@ -186,6 +187,7 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
   lola_state* st = new lola_state();
   memset(st, 0, sizeof *st);
   st->cfg = c;
+  st->branches = LOLA_READ_ALL;
   st->U = c.batch * c.kv_heads;
   st->g = g;
   st->d = c.head_dim;
@@ -277,6 +279,7 @@ int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v
   a.lam = st->cfg.cache; a.eta = st->cfg.window; a.d = st->d; a.g = st->g;
   a.Hkv = st->cfg.kv_heads;
   decode_plan(a.lam, a.eta, st->d, st->g, st->f32, &a.kc);
+  a.branches = st->branches;
   a.q_su = (long long)st->g * st->d; a.q_sh = st->d; a.kv_su = st->d;
   a.o_su = (long long)st->g * st->d; a.o_sh = st->d;
   hipError_t e;
@@ -314,6 +317,7 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
     a.lam = st->cfg.cache; a.eta = st->cfg.window; a.d = d; a.g = g;
     a.Hkv = st->cfg.kv_heads;
     decode_plan(a.lam, a.eta, d, g, st->f32, &a.kc);
+    a.branches = st->branches;
     a.q_su = (long long)g * T * d; a.q_sh = (long long)T * d; a.kv_su = (long long)T * d;
     a.o_su = a.q_su; a.o_sh = a.q_sh;
     for (int t = 0; t < T; ++t) {
@@ -413,6 +417,7 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   aa.nblk = aa.ptile / 32;
   aa.ch0 = 0;
   aa.nch_launch = nch;
+  aa.branches = st->branches;
   { ProfScope ps(st, LOLA_KERNEL_ATTN, s); e = launch_attn(aa, U, st->f32, s); }
   if (e != hipSuccess) return hip_fail(st, e, "attention launch");
 
@@ -446,6 +451,15 @@ int lola_prefill_debug(lola_state* st, const void* q, const void* k, const void*
     return fail(LOLA_ERR_UNSUPPORTED, "debug export needs C > 1");
   return prefill_impl(st, q, k, v, T, C, out, out_dtype, ws, ws_bytes, snap_pos, cand_keys,
                       stream);
+}
+
+int lola_set_read_branches(lola_state* st, int branches) {
+  if (!st) return fail(LOLA_ERR_INVALID_ARG, "state must be non-NULL");
+  if ((branches & ~LOLA_READ_ALL) || !(branches & LOLA_READ_WINDOW))
+    return fail(LOLA_ERR_INVALID_ARG, "read branches %d: need a subset of %d with the window bit %d",
+                branches, LOLA_READ_ALL, LOLA_READ_WINDOW);
+  st->branches = branches;
+  return LOLA_OK;
 }
 
 int lola_state_reset(lola_state* st, void* stream) {

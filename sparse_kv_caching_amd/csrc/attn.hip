@@ -256,6 +256,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         zlin = fmaf(ph[1][mt][i], sm_s[kM + f], zlin);
       }
     zlin += xor32(zlin);
+    if (!(a.branches & LOLA_READ_STATE)) zlin = 0.f;   // state hidden from the read
   }
 
   // ---- linear read N_lin^T = H_j^T phi^T into the output accumulator
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) O[mt][i] = 0.f;
-  if (wactive) {
+  if (wactive && (a.branches & LOLA_READ_STATE)) {
 #pragma unroll
     for (int kb = 0; kb < kD / 16; ++kb) {
       const int half = kb >> 2, mt = (kb >> 1) & 1, i0 = 8 * (kb & 1);
@@ -286,7 +287,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   // ---- explicit branch: key tiles of KT, double-buffered
   float m2 = 0.f, l = zlin;
   const float scale2 = 1.4426950408889634f / sqrtf((float)HD);
-  const int ntiles = (nkeys + KT - 1) / KT;
+  // cache keys hidden from the read: the key loop starts past them
+  const int kbase = (a.branches & LOLA_READ_CACHE) ? 0 : gsj;
+  const int ntiles = (nkeys - kbase + KT - 1) / KT;
   // one tile's pieces in registers: keys (KPT pieces of 16 bytes) and one
   // (key pair, 8 columns) item of V
   u32x4 kreg[KPT];
@@ -349,12 +352,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     }
   };
   if (ntiles > 0) {
-    load_tile(0);
+    load_tile(kbase);
     store_tile(0);
   }
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
-    const int t0 = t * KT, b = t & 1;
+    const int t0 = kbase + t * KT, b = t & 1;
     if (t + 1 < ntiles) load_tile(t0 + KT);       // in flight during this tile's products
     if (wactive && t0 <= wlast) {
       const uint16_t* Kb = (const uint16_t*)(smem + buf_off(L.K, b));

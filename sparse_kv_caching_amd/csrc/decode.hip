@@ -672,7 +672,8 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int j = 32 * wave + 16 * kt + 4 * q4 + i;
-            S[kt][i] = j < kn ? St[kt][i] * scale2 : -INFINITY;
+            const bool vis = j < kn && (k0 + j >= gs || (a.branches & LOLA_READ_CACHE));   // cache keys unless hidden
+            S[kt][i] = vis ? St[kt][i] * scale2 : -INFINITY;
             mx = fmaxf(mx, S[kt][i]);
           }
         mx = qmax(mx);
@@ -926,7 +927,8 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
       float m = 0.f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) m = fmaxf(m, sm_wst[w * 8 + hd]);
-      const float em = __builtin_amdgcn_exp2f(-m);
+      // the linear read (logit 0), unless the state is hidden from the read
+      const float em = (a.branches & LOLA_READ_STATE) ? __builtin_amdgcn_exp2f(-m) : 0.f;
       float num = em * sm_nlin[hd * HD + e], den = em * sm_zq[hd];
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "common.h"
+#include "lola.h"
 
 namespace lola {
 
@@ -102,6 +103,7 @@ struct AttnArgs {
   float* out;               // [U, g, T, d]
   int g, Hkv, nch, C, ptile, nblk;  // positions per WG, 32-position blocks per WG
   int ch0, nch_launch;      // chunks ch0 .. ch0 + nch_launch - 1 in this launch
+  int branches;             // read mask, LOLA_READ_* bits (window always set)
 };
 
 // Finalize: new cache rows / positions and window ring after a prefill call.
@@ -133,6 +135,7 @@ struct DecodeArgs {
   long long n;
   int lam, eta, d, g, Hkv;
   int kc;                   // key rows per staged chunk (decode_plan)
+  int branches;             // read mask, LOLA_READ_* bits (window always set)
   // element strides (one token): q / out [u][hd], k / v [u]
   long long q_su, q_sh, kv_su, o_su, o_sh;
 };
