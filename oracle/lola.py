@@ -242,6 +242,35 @@ def _read_chunk(st: LolaState, qc: np.ndarray, kc: np.ndarray, vc: np.ndarray,
     return num / den[..., None]
 
 
+def _read_after(st: LolaState, qc: np.ndarray, Wu: np.ndarray,
+                branches: int = BRANCH_ALL) -> np.ndarray:
+    """Eq. (14) as the notes write it for one token (LoLA notes §2.5): the
+    query of token t reads H_t, s_t, G_t and the window W_t *after* token t's
+    update, so every key in W_t and G_t is visible (no causal part).
+    qc (U, g, 1, d).  Returns y (U, g, 1, d)."""
+    U, g, c, d = qc.shape
+    nk = 0
+    parts_k, parts_v = [], []
+    if branches & BRANCH_SPARSE:
+        parts_k.append(st.g_k)
+        parts_v.append(st.g_v)
+    parts_k.append(st.win_k)
+    parts_v.append(st.win_v)
+    keys = np.concatenate(parts_k, axis=1)
+    vals = np.concatenate(parts_v, axis=1)
+    logits = np.matmul(qc, keys[:, None].transpose(0, 1, 3, 2)) / np.sqrt(d)
+    a = np.exp(logits)
+    if not np.all(np.isfinite(a)):
+        raise FloatingPointError("exp(q.k/sqrt(d)) overflowed in float64")
+    num = np.matmul(a, vals[:, None])
+    den = a.sum(axis=-1)
+    if branches & BRANCH_STATE:
+        phq = _phi_units(qc, Wu)
+        num = num + np.matmul(phq, st.H[:, None])
+        den = den + np.einsum("ugtf,uf->ugt", phq, st.s)
+    return num / den[..., None]
+
+
 # ---------------------------------------------------------------------- update
 def _update_chunk(st: LolaState, kc: np.ndarray, vc: np.ndarray, Wu: np.ndarray
                   ) -> ChunkLog:
@@ -302,18 +331,29 @@ def _as_units(q, k, v, W, Hkv):
 
 def prefill(st: LolaState, q, k, v, W, C: int, *, outputs: bool = True,
             logs: Optional[List[ChunkLog]] = None,
-            branches: int = BRANCH_ALL) -> Optional[np.ndarray]:
+            branches: int = BRANCH_ALL, order: str = "before") -> Optional[np.ndarray]:
     """Process T new tokens with chunk length C (the last chunk may be short).
 
     q (B, Hq, T, d); k, v (B, Hkv, T, d); W (Hkv, d, m); ``st`` holds U = B*Hkv
     units and is updated in place.  Returns y (B, Hq, T, d) in float64, or None
     if ``outputs`` is False (the state trajectory does not depend on q).
     ``branches`` masks the read only (see check_branches); the state update is
-    the same for every mask.
+    the same for every mask.  ``order``: "before" (the chunk schedule, LoLA
+    notes §2.6: the chunk's queries read the state at chunk start) or "after"
+    (the literal token recurrence, §2.4-§2.5: with C = 1, token t's query
+    reads the state after token t's update).
     """
     if C < 1:
         raise ValueError("C must be >= 1")
     branches = check_branches(branches)
+    if order not in ("before", "after"):
+        raise ValueError("order must be 'before' or 'after'")
+    if order == "after" and C != 1:
+        raise ValueError("the read-after-update order is defined token by token (C = 1)")
+    if order == "after" and outputs and st.eta == 0 and not (
+            (st.lam > 0 and branches & BRANCH_SPARSE) or (st.lam == 0 and branches & BRANCH_STATE)):
+        raise ValueError("eta = 0 reads no window after the update: keep a memory that is "
+                         "never empty (the cache if lam > 0, else the state)")
     Hkv = np.asarray(W).shape[0]
     qu, ku, vu, Wu, shape = _as_units(q, k, v, W, Hkv)
     U, g, T, d = qu.shape
@@ -324,9 +364,11 @@ def prefill(st: LolaState, q, k, v, W, C: int, *, outputs: bool = True,
     while t0 < T:
         c = min(C, T - t0)
         sl = slice(t0, t0 + c)
-        if outputs:
+        if outputs and order == "before":
             y[:, :, sl] = _read_chunk(st, qu[:, :, sl], ku[:, sl], vu[:, sl], Wu, branches)
         lg = _update_chunk(st, ku[:, sl], vu[:, sl], Wu)
+        if outputs and order == "after":
+            y[:, :, sl] = _read_after(st, qu[:, :, sl], Wu, branches)
         if logs is not None:
             logs.append(lg)
         t0 += c
@@ -337,11 +379,12 @@ def prefill(st: LolaState, q, k, v, W, C: int, *, outputs: bool = True,
 
 
 def decode_step(st: LolaState, q, k, v, W, *, logs=None,
-                branches: int = BRANCH_ALL) -> np.ndarray:
+                branches: int = BRANCH_ALL, order: str = "before") -> np.ndarray:
     """One token for every sequence: q (B, Hq, d), k, v (B, Hkv, d).
-    Defined as prefill with T = 1, C = 1 (read, then update)."""
+    Defined as prefill with T = 1, C = 1 (read, then update; or update, then
+    read with order="after")."""
     y = prefill(st, np.asarray(q)[:, :, None], np.asarray(k)[:, :, None],
-                np.asarray(v)[:, :, None], W, 1, logs=logs, branches=branches)
+                np.asarray(v)[:, :, None], W, 1, logs=logs, branches=branches, order=order)
     return y[:, :, 0]
 
 

@@ -9,14 +9,17 @@ state *before* the update and the lam highest form G_t (all kept when there are
 fewer than lam); the rest, S_t = E_t \\ G_t, are written into H and s
 (Eqs. (11)-(13)).
 
-Only the state trajectory is produced here; it is used to pin that the chunk
-schedule with C = 1 follows this recurrence exactly.  The window is a deque of
+The state trajectory pins that the chunk schedule with C = 1 follows this
+recurrence exactly; the outputs of the literal token mode (each query reads
+the memories after its own token's update, LoLA notes §2.5) pin the
+read-after-update order of the vectorised form.  The window is a deque of
 positions and the scores come from a direct transcription of Eq. (10) with
 numpy float64 vectors, independent of the other two forms.
 """
 
 from __future__ import annotations
 
+import math
 from collections import deque
 from typing import List, Tuple
 
@@ -30,10 +33,9 @@ def _phi(x: np.ndarray, W: np.ndarray) -> np.ndarray:
     return np.concatenate([a / a.sum(), b / b.sum()])
 
 
-def token_trajectory(k: np.ndarray, v: np.ndarray, W: np.ndarray, eta: int, lam: int
-                     ) -> List[Tuple[frozenset, np.ndarray, np.ndarray]]:
-    """k, v (T, d); W (d, m).  Returns, after each token t, the tuple
-    (cache positions, H copy, s copy)."""
+def _token_steps(k: np.ndarray, v: np.ndarray, W: np.ndarray, eta: int, lam: int):
+    """The recurrence token by token; yields (t, G, window, H, s) after the
+    update of token t (G and the window as positions)."""
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     W = np.asarray(W, np.float64)
@@ -43,7 +45,6 @@ def token_trajectory(k: np.ndarray, v: np.ndarray, W: np.ndarray, eta: int, lam:
     s = np.zeros(D)
     window: deque = deque()
     G: set = set()
-    out = []
     for t in range(T):
         window.append(t)                          # step 1: enter the window
         if len(window) > eta:
@@ -63,5 +64,38 @@ def token_trajectory(k: np.ndarray, v: np.ndarray, W: np.ndarray, eta: int, lam:
                     f = _phi(k[p], W)
                     H = H + np.outer(f, v[p])
                     s = s + f
-        out.append((frozenset(G), H.copy(), s.copy()))
-    return out
+        yield t, G, tuple(window), H, s
+
+
+def token_trajectory(k: np.ndarray, v: np.ndarray, W: np.ndarray, eta: int, lam: int
+                     ) -> List[Tuple[frozenset, np.ndarray, np.ndarray]]:
+    """k, v (T, d); W (d, m).  Returns, after each token t, the tuple
+    (cache positions, H copy, s copy)."""
+    return [(frozenset(G), H.copy(), s.copy()) for _, G, _, H, s in _token_steps(k, v, W, eta, lam)]
+
+
+def token_outputs(q: np.ndarray, k: np.ndarray, v: np.ndarray, W: np.ndarray, eta: int,
+                  lam: int, branches: int = 7) -> np.ndarray:
+    """The literal token mode: every query reads the memories *after* its
+    own token's update, LoLA notes §2.5 (y_t with H_t, s_t, G_t and W_t, the
+    window holding positions t - eta + 1 .. t).  q (g, T, d) for the q-heads
+    of one unit; k, v (T, d).  ``branches`` hides memories as in the
+    read-branch ablation (LoLA notes §4.8): bit 1 H and s, bit 2 G, bit 4 the
+    window.  Returns y (g, T, d)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    g, T, d = q.shape
+    y = np.zeros((g, T, d))
+    for t, G, window, H, s in _token_steps(k, v, W, eta, lam):
+        keys = (sorted(G) if branches & 2 else []) + (list(window) if branches & 4 else [])
+        for j in range(g):
+            a = np.array([math.exp(float(q[j, t] @ k[p]) / math.sqrt(d)) for p in keys])
+            num = (a @ v[keys]) if keys else np.zeros(d)
+            den = float(a.sum()) if keys else 0.0
+            if branches & 1:
+                f = _phi(q[j, t], np.asarray(W, np.float64))
+                num = num + f @ H
+                den = den + float(f @ s)
+            y[j, t] = num / den
+    return y
