@@ -135,6 +135,26 @@ enum {
  * Errors: INVALID_ARG (NULL state, unknown bits, window bit clear). */
 int lola_set_read_branches(lola_state* st, int branches);
 
+/* Order of read and update for one token (LoLA notes §2.4-§2.6). */
+enum {
+  LOLA_READ_BEFORE_UPDATE = 0,  /* the chunk schedule: queries read the state as
+                                   it is at chunk start (decode = C = 1) */
+  LOLA_READ_AFTER_UPDATE = 1    /* the literal token recurrence: token t's query
+                                   reads H_t, s_t, G_t and the window t-eta+1..t,
+                                   after token t's pair has entered the window and
+                                   the leaving pair was kept or folded (§2.5) */
+};
+
+/* Set the read order of the following decode calls and prefill calls with
+ * C = 1 (default LOLA_READ_BEFORE_UPDATE).  With LOLA_READ_AFTER_UPDATE a
+ * prefill with C > 1 returns UNSUPPORTED, and every token costs two decode
+ * launches (update, then read).  With eta = 0 the window is empty after the
+ * update; a call then needs a memory that is never empty (read branches with
+ * the cache if lambda > 0, with the state if lambda = 0), else INVALID_ARG.
+ * Host-side only; kept across lola_state_reset, not exported.
+ * Errors: INVALID_ARG (NULL state, unknown order). */
+int lola_set_read_order(lola_state* st, int order);
+
 /* Start over: n = 0, H = 0, s = 0, empty window and cache (the memory and W
  * are kept).  Stream-ordered.  Clears a poisoned state. */
 int lola_state_reset(lola_state* st, void* stream);

@@ -25,6 +25,7 @@ struct lola_state {
   hipStream_t last;
   bool poisoned;
   int branches;             // read mask (LOLA_READ_*)
+  int order;                // LOLA_READ_BEFORE_UPDATE / LOLA_READ_AFTER_UPDATE
   float* H;
   float* s;
   void* ring_k;
@@ -145,6 +146,37 @@ int supported_C(const lola_state* st, int C) {
   return LOLA_OK;
 }
 
+// A read after the update with eta = 0 sees no window: it needs a memory
+// that is never empty then (the cache if lambda > 0, else the state).
+int check_read_config(const lola_state* st) {
+  if (st->order != LOLA_READ_AFTER_UPDATE || st->cfg.window > 0) return LOLA_OK;
+  const bool ok = st->cfg.cache > 0 ? (st->branches & LOLA_READ_CACHE) != 0
+                                    : (st->branches & LOLA_READ_STATE) != 0;
+  if (!ok)
+    return fail(LOLA_ERR_INVALID_ARG, "read after update with window 0: the read branches "
+                "must include the %s", st->cfg.cache > 0 ? "cache" : "state");
+  return LOLA_OK;
+}
+
+// One token through the decode kernel at position a.n: read, then update;
+// or (read after update) an update launch, then a read launch of the
+// updated state at a.n + 1.
+hipError_t decode_token(lola_state* st, DecodeArgs a, hipStream_t s) {
+  hipError_t e;
+  if (st->order != LOLA_READ_AFTER_UPDATE) {
+    a.phase = 0;
+    ProfScope ps(st, LOLA_KERNEL_DECODE, s);
+    return launch_decode(a, st->U, st->f32, s);
+  }
+  a.phase = 1;
+  { ProfScope ps(st, LOLA_KERNEL_DECODE, s); e = launch_decode(a, st->U, st->f32, s); }
+  if (e != hipSuccess) return e;
+  a.phase = 2;
+  a.n += 1;
+  ProfScope ps(st, LOLA_KERNEL_DECODE, s);
+  return launch_decode(a, st->U, st->f32, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -188,6 +220,7 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
   memset(st, 0, sizeof *st);
   st->cfg = c;
   st->branches = LOLA_READ_ALL;
+  st->order = LOLA_READ_BEFORE_UPDATE;
   st->U = c.batch * c.kv_heads;
   st->g = g;
   st->d = c.head_dim;
@@ -267,6 +300,7 @@ int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v
   if (!q || !k || !v || !out) return fail(LOLA_ERR_INVALID_ARG, "q, k, v, out must be non-NULL");
   if (out_dtype != LOLA_DTYPE_F32) return fail(LOLA_ERR_UNSUPPORTED, "out_dtype must be F32");
   if (st->n > (int64_t)0x7FFFFFF0) return fail(LOLA_ERR_UNSUPPORTED, "position overflow");
+  if ((rc = check_read_config(st))) return rc;
   hipStream_t s = (hipStream_t)stream;
   DecodeArgs a;
   a.q = q; a.k = k; a.v = v; a.WT = st->WT;
@@ -282,8 +316,7 @@ int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v
   a.branches = st->branches;
   a.q_su = (long long)st->g * st->d; a.q_sh = st->d; a.kv_su = st->d;
   a.o_su = (long long)st->g * st->d; a.o_sh = st->d;
-  hipError_t e;
-  { ProfScope ps(st, LOLA_KERNEL_DECODE, s); e = launch_decode(a, st->U, st->f32, s); }
+  const hipError_t e = decode_token(st, a, s);
   if (e != hipSuccess) return hip_fail(st, e, "decode launch");
   st->last = s;
   st->n += 1;
@@ -300,6 +333,9 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   if (!q || !k || !v || !out) return fail(LOLA_ERR_INVALID_ARG, "q, k, v, out must be non-NULL");
   if (out_dtype != LOLA_DTYPE_F32) return fail(LOLA_ERR_UNSUPPORTED, "out_dtype must be F32");
   if ((rc = supported_C(st, C))) return rc;
+  if (st->order == LOLA_READ_AFTER_UPDATE && C != 1)
+    return fail(LOLA_ERR_UNSUPPORTED, "read after update is token by token: C must be 1");
+  if ((rc = check_read_config(st))) return rc;
   if (st->n + T > (int64_t)0x7FFFFFF0) return fail(LOLA_ERR_UNSUPPORTED, "position overflow");
   const size_t NVs = (size_t)st->cfg.cache + st->cfg.window + T;
   if (NVs > (size_t)0x7FFFFFF0) return fail(LOLA_ERR_UNSUPPORTED, "T too large");
@@ -326,8 +362,7 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
       a.v = (const char*)v + (size_t)t * d * st->esz;
       a.out = (float*)out + (size_t)t * d;
       a.n = st->n;
-      hipError_t e;
-      { ProfScope ps(st, LOLA_KERNEL_DECODE, s); e = launch_decode(a, U, st->f32, s); }
+      const hipError_t e = decode_token(st, a, s);
       if (e != hipSuccess) return hip_fail(st, e, "decode launch");
       st->n += 1;
     }
@@ -459,6 +494,15 @@ int lola_set_read_branches(lola_state* st, int branches) {
     return fail(LOLA_ERR_INVALID_ARG, "read branches %d: need a subset of %d with the window bit %d",
                 branches, LOLA_READ_ALL, LOLA_READ_WINDOW);
   st->branches = branches;
+  return LOLA_OK;
+}
+
+int lola_set_read_order(lola_state* st, int order) {
+  if (!st) return fail(LOLA_ERR_INVALID_ARG, "state must be non-NULL");
+  if (order != LOLA_READ_BEFORE_UPDATE && order != LOLA_READ_AFTER_UPDATE)
+    return fail(LOLA_ERR_INVALID_ARG, "read order %d: need %d or %d", order,
+                LOLA_READ_BEFORE_UPDATE, LOLA_READ_AFTER_UPDATE);
+  st->order = order;
   return LOLA_OK;
 }
 

@@ -468,8 +468,9 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   const int kg = lane / PPR, cp = lane % PPR;      // a lane's piece of a row: row group, piece
   const int kvh = u % a.Hkv;
   const long long n = a.n;
+  const bool up = a.phase != 2, rd = a.phase != 1; // update the state / write the outputs
   const int gs = (int)min((long long)lam, max(0LL, n - eta));
-  const bool has_leave = n >= eta;                 // eta == 0: the new pair leaves at once
+  const bool has_leave = up && n >= eta;           // eta == 0: the new pair leaves at once
   const bool full = has_leave && gs + 1 > lam;     // score and fold
   const int ncand = full ? gs + 1 : 0;             // candidate rows = keys 0..gs
   const int w_len = (int)min((long long)eta, n);   // window positions n - w_len .. n - 1
@@ -745,7 +746,7 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
             for (int e = 0; e < CPL; ++e) acc[hd][e] = fmaf(p4[hd], v[e], acc[hd][e]);
         }
       }
-      if (last && wave == kWaves - 1) {
+      if (up && last && wave == kWaves - 1) {
         // the new pair (key nko): logits q . k on the VALU, lane (kg, cp) a
         // piece of head hd0 + kg (RG row groups of PPR lanes)
         constexpr int RG = 64 / PPR;
@@ -936,10 +937,10 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
         num = fmaf(f, sm_pv[(w * 4 + hd) * HD + e], num);
         den = fmaf(f, sm_wst[w * 8 + 4 + hd], den);
       }
-      a.out[(size_t)u * a.o_su + (size_t)hd * a.o_sh + e] = num / den;
+      if (rd) a.out[(size_t)u * a.o_su + (size_t)hd * a.o_sh + e] = num / den;
     }
     // ---- the new pair enters the ring slot n % eta (every read of the ring is done)
-    if (eta > 0) {
+    if (eta > 0 && up) {
       T* dk = ringk + (size_t)ringn * HD;
       T* dv = ringv + (size_t)ringn * HD;
       for (int i = tid - 64; i < 2 * PPR; i += kThreads - 64) {

@@ -136,6 +136,10 @@ struct DecodeArgs {
   int lam, eta, d, g, Hkv;
   int kc;                   // key rows per staged chunk (decode_plan)
   int branches;             // read mask, LOLA_READ_* bits (window always set)
+  // 0: read, then update (the chunk schedule); 1: update only; 2: read only,
+  // of a state that has just been updated (n counts the new token, which is
+  // already in the window: no new pair, nothing scored or written)
+  int phase;
   // element strides (one token): q / out [u][hd], k / v [u]
   long long q_su, q_sh, kv_su, o_su, o_sh;
 };

@@ -27,6 +27,7 @@ LOLA_DTYPE_F32 = 0
 LOLA_DTYPE_BF16 = 1
 KERNELS = ("phi", "chain", "attn", "finalize", "decode")
 READ_STATE, READ_CACHE, READ_WINDOW, READ_ALL = 1, 2, 4, 7   # lola_set_read_branches bits
+READ_BEFORE_UPDATE, READ_AFTER_UPDATE = 0, 1                 # lola_set_read_order
 
 EXPORTED = [
     "lola_state_init", "lola_state_free", "lola_state_tokens", "lola_prefill_workspace_bytes",
@@ -87,13 +88,14 @@ def library() -> ctypes.CDLL:
         lib.lola_state_export.argtypes = [vp, ctypes.POINTER(LolaStateView), vp]
         lib.lola_state_import.argtypes = [vp, ctypes.POINTER(LolaStateView), vp]
         lib.lola_set_read_branches.argtypes = [vp, i32]
+        lib.lola_set_read_order.argtypes = [vp, i32]
         lib.lola_strerror.argtypes = [i32]
         lib.lola_strerror.restype = ctypes.c_char_p
         lib.lola_last_error.restype = ctypes.c_char_p
         for f in ("lola_state_init", "lola_state_free", "lola_prefill_workspace_bytes",
                   "lola_prefill_chunk", "lola_prefill_debug", "lola_decode_step",
                   "lola_state_reset", "lola_state_check", "lola_profile", "lola_state_export",
-                  "lola_state_import", "lola_set_read_branches"):
+                  "lola_state_import", "lola_set_read_branches", "lola_set_read_order"):
             getattr(lib, f).restype = i32
         _lib = lib
     return _lib
@@ -162,6 +164,11 @@ class LolaLayer:
         """Read-branch mask of the following calls: bits READ_STATE (1),
         READ_CACHE (2), READ_WINDOW (4, required); updates are unaffected."""
         _check(self.lib.lola_set_read_branches(self._st, int(branches)), "lola_set_read_branches")
+
+    def set_read_order(self, order: int):
+        """READ_BEFORE_UPDATE (0, the chunk schedule) or READ_AFTER_UPDATE (1,
+        the literal token recurrence; decode and C = 1 prefill only)."""
+        _check(self.lib.lola_set_read_order(self._st, int(order)), "lola_set_read_order")
 
     def profile(self, enable: bool):
         """Return {kernel: (ms, launches)} accumulated since the last call and
