@@ -77,7 +77,8 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
 /* Synchronise the state's last stream and release everything.  NULL: no-op. */
 int lola_state_free(lola_state* st);
 
-/* Tokens already processed (n). */
+/* Tokens already processed (n); -1 while the sequences sit at different
+ * positions (lola_state_positions). */
 int64_t lola_state_tokens(const lola_state* st);
 
 /* Bytes of workspace lola_prefill_chunk needs for (T, C).  0 for T == 0. */
@@ -200,13 +201,38 @@ typedef struct {
   void* cache_v;
 } lola_state_view;
 
-/* Write the state into `dst` (dst->n is set on return; stream-ordered). */
+/* Write the state into `dst` (dst->n is set on return; stream-ordered).
+ * UNSUPPORTED while the sequences sit at different positions (export them
+ * one by one with lola_state_export_sequence). */
 int lola_state_export(const lola_state* st, lola_state_view* dst, void* stream);
 
 /* Replace the state with `src` (n = src->n).  Checks, on the host, that cache
  * positions are ascending, non-negative and older than the window; returns
  * LOLA_ERR_STATE otherwise.  Clears a poisoned state.  Synchronises stream. */
 int lola_state_import(lola_state* st, const lola_state_view* src, void* stream);
+
+/* Ragged batches.  Every memory of LoLA is per sequence and KV head (LoLA
+ * notes §2.1, §2.4), so the sequences of one state may sit at different
+ * positions: a serving loop prefills a new sequence in a state of its own
+ * (batch 1, same configuration) and moves it into a free slot of the
+ * batched decode state.
+ *
+ * lola_state_import_sequence copies `src`, a one-sequence state in the
+ * lola_state_view layout with B = 1 (position src->n), into sequence slot
+ * b; the checks of lola_state_import apply.  lola_state_export_sequence
+ * writes slot b into a one-sequence view (dst->n = its position).  While the
+ * positions differ, lola_decode_step advances every sequence by one token at
+ * its own position (in either read order), lola_prefill_chunk and
+ * lola_prefill_debug return UNSUPPORTED, lola_state_export returns
+ * UNSUPPORTED and lola_state_tokens returns -1; lola_state_import and
+ * lola_state_reset put every sequence at one position again.
+ * lola_state_positions writes the B positions to host memory `out`.
+ * Import and export synchronise `stream`.
+ * Errors: INVALID_ARG (NULL pointers, b out of range), STATE (bad cache
+ * positions in src), HIP. */
+int lola_state_import_sequence(lola_state* st, int b, const lola_state_view* src, void* stream);
+int lola_state_export_sequence(const lola_state* st, int b, lola_state_view* dst, void* stream);
+int lola_state_positions(const lola_state* st, int64_t* out);
 
 /* Text of a status code, and the last error detail of the calling thread. */
 const char* lola_strerror(int status);

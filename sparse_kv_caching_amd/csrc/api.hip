@@ -26,6 +26,10 @@ struct lola_state {
   bool poisoned;
   int branches;             // read mask (LOLA_READ_*)
   int order;                // LOLA_READ_BEFORE_UPDATE / LOLA_READ_AFTER_UPDATE
+  int64_t* nseq;            // position of every sequence (host, B entries)
+  bool ragged;              // some sequences sit at other positions than others
+  long long* npos_dev;      // [2][B] sequence positions for ragged decode steps
+  int npos_cur;             // the half decode reads next
   float* H;
   float* s;
   void* ring_k;
@@ -146,6 +150,13 @@ int supported_C(const lola_state* st, int C) {
   return LOLA_OK;
 }
 
+// Every sequence at position n.
+void set_uniform(lola_state* st, int64_t n) {
+  st->n = n;
+  for (int b = 0; b < st->cfg.batch; ++b) st->nseq[b] = n;
+  st->ragged = false;
+}
+
 // A read after the update with eta = 0 sees no window: it needs a memory
 // that is never empty then (the cache if lambda > 0, else the state).
 int check_read_config(const lola_state* st) {
@@ -163,6 +174,13 @@ int check_read_config(const lola_state* st) {
 // updated state at a.n + 1.
 hipError_t decode_token(lola_state* st, DecodeArgs a, hipStream_t s) {
   hipError_t e;
+  if (st->ragged) {   // the kernel reads each sequence's position, writes it + 1
+    a.npos = st->npos_dev + (size_t)st->npos_cur * st->cfg.batch;
+    a.npos_next = st->npos_dev + (size_t)(st->npos_cur ^ 1) * st->cfg.batch;
+  } else {
+    a.npos = nullptr;
+    a.npos_next = nullptr;
+  }
   if (st->order != LOLA_READ_AFTER_UPDATE) {
     a.phase = 0;
     ProfScope ps(st, LOLA_KERNEL_DECODE, s);
@@ -173,8 +191,22 @@ hipError_t decode_token(lola_state* st, DecodeArgs a, hipStream_t s) {
   if (e != hipSuccess) return e;
   a.phase = 2;
   a.n += 1;
+  if (a.npos) {
+    a.npos = a.npos_next;
+    a.npos_next = nullptr;
+  }
   ProfScope ps(st, LOLA_KERNEL_DECODE, s);
   return launch_decode(a, st->U, st->f32, s);
+}
+
+// After a decode step: every sequence one token further.
+void advance_positions(lola_state* st) {
+  if (!st->ragged) {
+    set_uniform(st, st->n + 1);
+    return;
+  }
+  for (int b = 0; b < st->cfg.batch; ++b) st->nseq[b] += 1;
+  st->npos_cur ^= 1;
 }
 
 }  // namespace
@@ -242,7 +274,9 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
             alloc(&st->ring_k, U * eta * d * st->esz) && alloc(&st->ring_v, U * eta * d * st->esz) &&
             alloc(&st->W, (size_t)c.kv_heads * d * kM * st->esz) &&
             alloc(&st->WT, (size_t)c.kv_heads * d * kM * st->esz) &&
-            alloc((void**)&st->dev_err, sizeof(int));
+            alloc((void**)&st->dev_err, sizeof(int)) &&
+            alloc((void**)&st->npos_dev, 2 * (size_t)c.batch * sizeof(long long));
+  st->nseq = new int64_t[c.batch]();
   for (int b = 0; b < 2 && ok; ++b)
     ok = alloc(&st->cache_k[b], U * lam * d * st->esz) &&
          alloc(&st->cache_v[b], U * lam * d * st->esz) &&
@@ -271,7 +305,9 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
 int lola_state_free(lola_state* st) {
   if (!st) return LOLA_OK;
   hipStreamSynchronize(st->last);
+  delete[] st->nseq;
   void* ps[] = {st->H, st->s, st->ring_k, st->ring_v, st->W, st->WT, st->dev_err, st->own_ws,
+                st->npos_dev,
                 st->cache_k[0], st->cache_k[1], st->cache_v[0], st->cache_v[1],
                 st->cache_pos[0], st->cache_pos[1]};
   for (void* p : ps)
@@ -284,7 +320,7 @@ int lola_state_free(lola_state* st) {
   return LOLA_OK;
 }
 
-int64_t lola_state_tokens(const lola_state* st) { return st ? st->n : -1; }
+int64_t lola_state_tokens(const lola_state* st) { return st && !st->ragged ? st->n : -1; }
 
 int lola_prefill_workspace_bytes(const lola_state* st, int T, int C, size_t* bytes) {
   if (!st || !bytes) return fail(LOLA_ERR_INVALID_ARG, "state and bytes must be non-NULL");
@@ -299,7 +335,8 @@ int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v
   if (rc) return rc;
   if (!q || !k || !v || !out) return fail(LOLA_ERR_INVALID_ARG, "q, k, v, out must be non-NULL");
   if (out_dtype != LOLA_DTYPE_F32) return fail(LOLA_ERR_UNSUPPORTED, "out_dtype must be F32");
-  if (st->n > (int64_t)0x7FFFFFF0) return fail(LOLA_ERR_UNSUPPORTED, "position overflow");
+  for (int b = 0; b < st->cfg.batch; ++b)
+    if (st->nseq[b] > (int64_t)0x7FFFFFF0) return fail(LOLA_ERR_UNSUPPORTED, "position overflow");
   if ((rc = check_read_config(st))) return rc;
   hipStream_t s = (hipStream_t)stream;
   DecodeArgs a;
@@ -319,7 +356,7 @@ int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v
   const hipError_t e = decode_token(st, a, s);
   if (e != hipSuccess) return hip_fail(st, e, "decode launch");
   st->last = s;
-  st->n += 1;
+  advance_positions(st);
   return LOLA_OK;
 }
 
@@ -333,6 +370,9 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   if (!q || !k || !v || !out) return fail(LOLA_ERR_INVALID_ARG, "q, k, v, out must be non-NULL");
   if (out_dtype != LOLA_DTYPE_F32) return fail(LOLA_ERR_UNSUPPORTED, "out_dtype must be F32");
   if ((rc = supported_C(st, C))) return rc;
+  if (st->ragged)
+    return fail(LOLA_ERR_UNSUPPORTED, "the sequences sit at different positions: prefill a new "
+                "sequence in a state of its own and import it (lola_state_import_sequence)");
   if (st->order == LOLA_READ_AFTER_UPDATE && C != 1)
     return fail(LOLA_ERR_UNSUPPORTED, "read after update is token by token: C must be 1");
   if ((rc = check_read_config(st))) return rc;
@@ -364,7 +404,7 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
       a.n = st->n;
       const hipError_t e = decode_token(st, a, s);
       if (e != hipSuccess) return hip_fail(st, e, "decode launch");
-      st->n += 1;
+      set_uniform(st, st->n + 1);
     }
     st->last = s;
     return LOLA_OK;
@@ -468,7 +508,7 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   { ProfScope ps(st, LOLA_KERNEL_FINALIZE, s); e = launch_finalize(fa, U, st->f32, s); }
   if (e != hipSuccess) return hip_fail(st, e, "finalize launch");
   st->cur = 1 - st->cur;
-  st->n = nend;
+  set_uniform(st, nend);
   st->last = s;
   return LOLA_OK;
 }
@@ -516,7 +556,7 @@ int lola_state_reset(lola_state* st, void* stream) {
     e = hipMemsetAsync(st->cache_pos[b], 0xFF, U * (lam ? lam : 1) * 4, s);
   if (e == hipSuccess) e = launch_zero_u32((unsigned*)st->dev_err, 1, s);
   if (e != hipSuccess) return hip_fail(st, e, "reset");
-  st->n = 0;
+  set_uniform(st, 0);
   st->poisoned = false;
   st->last = s;
   return LOLA_OK;
@@ -563,6 +603,9 @@ int lola_state_export(const lola_state* st, lola_state_view* dst, void* stream) 
   if (!st || !dst || !dst->H || !dst->s || !dst->win_k || !dst->win_v || !dst->cache_pos ||
       !dst->cache_k || !dst->cache_v)
     return fail(LOLA_ERR_INVALID_ARG, "state and every view pointer must be non-NULL");
+  if (st->ragged)
+    return fail(LOLA_ERR_UNSUPPORTED, "the sequences sit at different positions: export them "
+                "one by one (lola_state_export_sequence)");
   hipStream_t s = (hipStream_t)stream;
   const size_t U = st->U, d = st->d;
   const int lam = st->cfg.cache, eta = st->cfg.window;
@@ -610,9 +653,103 @@ int lola_state_import(lola_state* st, const lola_state_view* src, void* stream) 
                       src->cache_k, src->cache_v, src->cache_pos, src->n, eta, lam, gs, st->d, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return fail(LOLA_ERR_HIP, "import: %s", hipGetErrorString(e));
-  st->n = src->n;
+  set_uniform(st, src->n);
   st->poisoned = false;
   st->last = s;
+  return LOLA_OK;
+}
+
+int lola_state_import_sequence(lola_state* st, int b, const lola_state_view* src, void* stream) {
+  int rc = check_state(st);
+  if (rc) return rc;
+  if (!src || !src->H || !src->s || !src->win_k || !src->win_v || !src->cache_pos ||
+      !src->cache_k || !src->cache_v)
+    return fail(LOLA_ERR_INVALID_ARG, "every view pointer must be non-NULL");
+  if (b < 0 || b >= st->cfg.batch)
+    return fail(LOLA_ERR_INVALID_ARG, "sequence slot %d out of range [0, %d)", b, st->cfg.batch);
+  if (src->n < 0 || src->n > (int64_t)0x7FFFFFF0) return fail(LOLA_ERR_STATE, "bad n");
+  hipStream_t s = (hipStream_t)stream;
+  const int Hkv = st->cfg.kv_heads;
+  const size_t d = st->d, u0 = (size_t)b * Hkv;
+  const int lam = st->cfg.cache, eta = st->cfg.window;
+  const int gs = (int)std::min<int64_t>(lam, std::max<int64_t>(0, src->n - eta));
+  const int64_t w = std::min<int64_t>(eta, src->n);
+  if (lam > 0) {
+    std::vector<int32_t> pos((size_t)Hkv * lam);
+    hipError_t e = hipMemcpyAsync(pos.data(), src->cache_pos, pos.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(LOLA_ERR_HIP, "import: %s", hipGetErrorString(e));
+    for (int u = 0; u < Hkv; ++u)
+      for (int i = 0; i < gs; ++i) {
+        const int32_t p = pos[(size_t)u * lam + i];
+        if (p < 0 || p >= src->n - w || (i > 0 && p <= pos[(size_t)u * lam + i - 1]))
+          return fail(LOLA_ERR_STATE, "import: cache positions of head %d are not ascending "
+                      "and older than the window", u);
+      }
+  }
+  const size_t es = st->esz;
+  char* rk = (char*)st->ring_k + u0 * eta * d * es;
+  char* rv = (char*)st->ring_v + u0 * eta * d * es;
+  char* ck = (char*)st->cache_k[st->cur] + u0 * lam * d * es;
+  char* cv = (char*)st->cache_v[st->cur] + u0 * lam * d * es;
+  hipError_t e = launch_transpose_f32(src->H, st->H + u0 * d * kD, Hkv, kD, (int)d, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(st->s + u0 * kD, src->s, (size_t)Hkv * kD * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = launch_import(st->f32, Hkv, rk, rv, ck, cv, st->cache_pos[st->cur] + u0 * lam, src->win_k,
+                      src->win_v, src->cache_k, src->cache_v, src->cache_pos, src->n, eta, lam, gs,
+                      st->d, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(st, e, "import sequence");
+  st->nseq[b] = src->n;
+  bool same = true;
+  for (int i = 1; i < st->cfg.batch; ++i) same = same && st->nseq[i] == st->nseq[0];
+  if (same) {
+    set_uniform(st, st->nseq[0]);
+  } else {
+    // the positions decode reads next (a synchronous copy of the host array)
+    st->ragged = true;
+    st->n = -1;
+    std::vector<long long> np(st->nseq, st->nseq + st->cfg.batch);
+    e = hipMemcpy(st->npos_dev + (size_t)st->npos_cur * st->cfg.batch, np.data(),
+                  np.size() * sizeof(long long), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(st, e, "import sequence positions");
+  }
+  st->last = s;
+  return LOLA_OK;
+}
+
+int lola_state_export_sequence(const lola_state* st, int b, lola_state_view* dst, void* stream) {
+  if (!st || !dst || !dst->H || !dst->s || !dst->win_k || !dst->win_v || !dst->cache_pos ||
+      !dst->cache_k || !dst->cache_v)
+    return fail(LOLA_ERR_INVALID_ARG, "state and every view pointer must be non-NULL");
+  if (b < 0 || b >= st->cfg.batch)
+    return fail(LOLA_ERR_INVALID_ARG, "sequence slot %d out of range [0, %d)", b, st->cfg.batch);
+  hipStream_t s = (hipStream_t)stream;
+  const int Hkv = st->cfg.kv_heads;
+  const size_t d = st->d, u0 = (size_t)b * Hkv, es = st->esz;
+  const int lam = st->cfg.cache, eta = st->cfg.window;
+  const int64_t n = st->nseq[b];
+  const int gs = (int)std::min<int64_t>(lam, std::max<int64_t>(0, n - eta));
+  hipError_t e = launch_transpose_f32(st->H + u0 * d * kD, dst->H, Hkv, (int)d, kD, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(dst->s, st->s + u0 * kD, (size_t)Hkv * kD * 4, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess)
+    e = launch_export(st->f32, Hkv, (const char*)st->ring_k + u0 * eta * d * es,
+                      (const char*)st->ring_v + u0 * eta * d * es,
+                      (const char*)st->cache_k[st->cur] + u0 * lam * d * es,
+                      (const char*)st->cache_v[st->cur] + u0 * lam * d * es,
+                      st->cache_pos[st->cur] + u0 * lam, dst->win_k, dst->win_v, dst->cache_k,
+                      dst->cache_v, dst->cache_pos, n, eta, lam, gs, st->d, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(LOLA_ERR_HIP, "export sequence: %s", hipGetErrorString(e));
+  dst->n = n;
+  return LOLA_OK;
+}
+
+int lola_state_positions(const lola_state* st, int64_t* out) {
+  if (!st || !out) return fail(LOLA_ERR_INVALID_ARG, "state and out must be non-NULL");
+  for (int b = 0; b < st->cfg.batch; ++b) out[b] = st->nseq[b];
   return LOLA_OK;
 }
 

@@ -467,8 +467,9 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   const int n16 = lane & 15, q4 = lane >> 4;       // 16 x 16 MFMA layout: row / column, K group
   const int kg = lane / PPR, cp = lane % PPR;      // a lane's piece of a row: row group, piece
   const int kvh = u % a.Hkv;
-  const long long n = a.n;
+  const long long n = a.npos ? a.npos[u / a.Hkv] : a.n;   // this sequence's position
   const bool up = a.phase != 2, rd = a.phase != 1; // update the state / write the outputs
+  if (a.npos_next && threadIdx.x == 0 && u % a.Hkv == 0) a.npos_next[u / a.Hkv] = n + 1;
   const int gs = (int)min((long long)lam, max(0LL, n - eta));
   const bool has_leave = up && n >= eta;           // eta == 0: the new pair leaves at once
   const bool full = has_leave && gs + 1 > lam;     // score and fold

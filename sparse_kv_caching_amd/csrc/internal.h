@@ -140,6 +140,10 @@ struct DecodeArgs {
   // of a state that has just been updated (n counts the new token, which is
   // already in the window: no new pair, nothing scored or written)
   int phase;
+  // ragged batches: position of each sequence [B] (NULL: every sequence at
+  // n), and where to write the positions after this step (NULL: nowhere)
+  const long long* npos;
+  long long* npos_next;
   // element strides (one token): q / out [u][hd], k / v [u]
   long long q_su, q_sh, kv_su, o_su, o_sh;
 };

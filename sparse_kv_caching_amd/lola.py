@@ -89,13 +89,18 @@ def library() -> ctypes.CDLL:
         lib.lola_state_import.argtypes = [vp, ctypes.POINTER(LolaStateView), vp]
         lib.lola_set_read_branches.argtypes = [vp, i32]
         lib.lola_set_read_order.argtypes = [vp, i32]
+        lib.lola_state_import_sequence.argtypes = [vp, i32, ctypes.POINTER(LolaStateView), vp]
+        lib.lola_state_export_sequence.argtypes = [vp, i32, ctypes.POINTER(LolaStateView), vp]
+        lib.lola_state_positions.argtypes = [vp, ctypes.POINTER(i64)]
         lib.lola_strerror.argtypes = [i32]
         lib.lola_strerror.restype = ctypes.c_char_p
         lib.lola_last_error.restype = ctypes.c_char_p
         for f in ("lola_state_init", "lola_state_free", "lola_prefill_workspace_bytes",
                   "lola_prefill_chunk", "lola_prefill_debug", "lola_decode_step",
                   "lola_state_reset", "lola_state_check", "lola_profile", "lola_state_export",
-                  "lola_state_import", "lola_set_read_branches", "lola_set_read_order"):
+                  "lola_state_import", "lola_set_read_branches", "lola_set_read_order",
+                  "lola_state_import_sequence", "lola_state_export_sequence",
+                  "lola_state_positions"):
             getattr(lib, f).restype = i32
         _lib = lib
     return _lib
@@ -225,8 +230,8 @@ class LolaLayer:
         return out
 
     # ------------------------------------------------------ export / import
-    def _view_tensors(self, device) -> Dict[str, torch.Tensor]:
-        U, d, D, lam, eta = self.U, self.d, 2 * self.m, self.lam, self.eta
+    def _view_tensors(self, device, units: Optional[int] = None) -> Dict[str, torch.Tensor]:
+        U, d, D, lam, eta = units or self.U, self.d, 2 * self.m, self.lam, self.eta
         f = dict(device=device)
         return dict(H=torch.zeros((U, D, d), dtype=torch.float32, **f),
                     s=torch.zeros((U, D), dtype=torch.float32, **f),
@@ -248,6 +253,33 @@ class LolaLayer:
                "lola_state_export")
         t["n"] = int(view.n)
         return t
+
+    def export_sequence(self, b: int, stream=None) -> Dict[str, torch.Tensor]:
+        """Sequence slot b as a one-sequence state (the export layout with
+        B = 1, n = its position)."""
+        self.check(stream)
+        t = self._view_tensors(torch.device("cuda", torch.cuda.current_device()), self.Hkv)
+        view = LolaStateView(0, *[t[k].data_ptr() for k in
+                                  ("H", "s", "win_k", "win_v", "cache_pos", "cache_k", "cache_v")])
+        _check(self.lib.lola_state_export_sequence(self._st, int(b), ctypes.byref(view),
+                                                   _stream(stream)), "lola_state_export_sequence")
+        t["n"] = int(view.n)
+        return t
+
+    def import_sequence(self, b: int, st: Dict[str, torch.Tensor], stream=None):
+        """Put a one-sequence state (e.g. export() of a batch-1 layer with the
+        same configuration) into sequence slot b, at its own position."""
+        keep = [st[k].contiguous() for k in
+                ("H", "s", "win_k", "win_v", "cache_pos", "cache_k", "cache_v")]
+        view = LolaStateView(int(st["n"]), *[_ptr(t).value for t in keep])
+        _check(self.lib.lola_state_import_sequence(self._st, int(b), ctypes.byref(view),
+                                                   _stream(stream)), "lola_state_import_sequence")
+
+    def positions(self):
+        """Position (tokens processed) of every sequence."""
+        out = (ctypes.c_int64 * self.B)()
+        _check(self.lib.lola_state_positions(self._st, out), "lola_state_positions")
+        return [int(x) for x in out]
 
     def import_(self, st: Dict[str, torch.Tensor], stream=None):
         keep = [st[k].contiguous() for k in
