@@ -196,6 +196,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         ql[kb] = u32x4{0, 0, 0, 0};
       }
     }
+    // the operands are used here on every path: otherwise their loads would
+    // count as pending in the key loop, which would then wait for all of its
+    // own prefetches before the first product of every tile
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) __asm__ volatile("" :: "v"(qh[kb]), "v"(ql[kb]));
   }
   __syncthreads();
 
@@ -291,9 +296,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   const int kbase = (a.branches & LOLA_READ_CACHE) ? 0 : gsj;
   const int ntiles = (nkeys - kbase + KT - 1) / KT;
   // one tile's pieces in registers: keys (KPT pieces of 16 bytes) and one
-  // (key pair, 8 columns) item of V
+  // (key pair, 8 columns) item of V, kept as loaded: converting inside the
+  // load's branch would make the wave wait for the load right there, before
+  // the current tile's products
+  constexpr int VPC = (int)sizeof(T) / 2;        // 16-byte pieces per 8 V columns
   u32x4 kreg[KPT];
-  float vreg[2][8];
+  u32x4 vreg[2][VPC];
   auto load_tile = [&](int t0) {
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
@@ -307,8 +315,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq) {
         const int kk = t0 + 2 * pr + kq;
-        if (kk < nkeys) load8_f32(vrow(key_vi(kk), true) + c, vreg[kq]);
-        else for (int q = 0; q < 8; ++q) vreg[kq][q] = 0.f;
+#pragma unroll
+        for (int w = 0; w < VPC; ++w) vreg[kq][w] = u32x4{0, 0, 0, 0};
+        if (kk < nkeys) {
+          const u32x4* src = reinterpret_cast<const u32x4*>(vrow(key_vi(kk), true) + c);
+#pragma unroll
+          for (int w = 0; w < VPC; ++w) vreg[kq][w] = src[w];
+        }
       }
     }
   };
@@ -336,17 +349,29 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
       const int pr = tid % (KT / 2), c = (tid / (KT / 2)) * 8;
       uint16_t* VTb = (uint16_t*)(smem + buf_off(L.VT, b));
       uint16_t* VTLb = (uint16_t*)(smem + buf_off(L.VTL, b));
+      float vf[2][8];
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if constexpr (VPC == 1) {   // 8 bf16 in one piece
+            const uint32_t w = vreg[kq][0][q >> 1];
+            vf[kq][q] = __uint_as_float((q & 1) ? (w & 0xFFFF0000u) : (w << 16));
+          } else {                    // 8 fp32 in two pieces
+            vf[kq][q] = __uint_as_float(vreg[kq][q >> 2][q & 3]);
+          }
+        }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         uint32_t* row = reinterpret_cast<uint32_t*>(VTb + (c + q) * VTS) + pr;
         if constexpr (DT::kSplit) {
           uint32_t h0, l0, h1, l1;
-          DT::split(vreg[0][q], h0, l0);
-          DT::split(vreg[1][q], h1, l1);
+          DT::split(vf[0][q], h0, l0);
+          DT::split(vf[1][q], h1, l1);
           *row = h0 | (h1 << 16);
           *(reinterpret_cast<uint32_t*>(VTLb + (c + q) * VTS) + pr) = l0 | (l1 << 16);
         } else {
-          *row = f16_bits(vreg[0][q]) | (f16_bits(vreg[1][q]) << 16);
+          *row = f16_bits(vf[0][q]) | (f16_bits(vf[1][q]) << 16);
         }
       }
     }
