@@ -130,3 +130,31 @@ def brute_prefill(units: List[BruteUnit], q, k, v, C: int, n0: int = 0, branches
                 u.update(n, c)
                 t0 += c
     return y
+
+
+def brute_sre_map(unit: BruteUnit, k, v, C: int):
+    """The SRE of every memory in the linear state at each chunk start
+    (LoLA notes §4.4, Fig. 3): for one unit, k, v (T, d) the call's tokens.
+    Returns (map [nch][T], fold [T]) as nested lists, with the conventions of
+    ``oracle.lola.sre_map``: 0 for tokens not in the state, fold = the chunk
+    whose update wrote the token, -1 if none."""
+    T = len(k)
+    n0 = len(unit.hist_k)
+    nch = (T + C - 1) // C
+    m = [[0.0] * T for _ in range(nch)]
+    fold = [-1] * T
+    for j in range(nch):
+        t0 = j * C
+        for p in range(T):
+            if 0 <= fold[p] < j:
+                m[j][p] = unit.sre_of(n0 + p)
+        c = min(C, T - t0)
+        for t in range(t0, t0 + c):
+            unit.hist_k.append([float(x) for x in k[t]])
+            unit.hist_v.append([float(x) for x in v[t]])
+        before = set(unit.folded)
+        unit.update(n0 + t0, c)
+        for p in set(unit.folded) - before:
+            if p >= n0:
+                fold[p - n0] = j
+    return m, fold

@@ -388,6 +388,53 @@ def decode_step(st: LolaState, q, k, v, W, *, logs=None,
     return y[:, :, 0]
 
 
+# ------------------------------------------------------------- SRE diagnostics
+def sre_map(st: LolaState, k, v, W, C: int):
+    """Self-Recall Error of the memories inside the linear state, chunk by
+    chunk (the diagnostic of LoLA notes §4.4, Fig. 3, and Eq. (26)).
+
+    Runs the chunk schedule on k, v (B, Hkv, T, d) from ``st`` (updated in
+    place).  Returns
+
+    * ``m`` (U, nch, T): m[u, j, p] = SRE(k_p, v_p | H_j, s_j) with H_j, s_j
+      the state at the start of chunk j, for the call's tokens p folded into
+      the state by an earlier chunk of the call; 0 for tokens not (yet) in the
+      state (in the window or the cache: the notes show them as zero columns);
+    * ``fold`` (U, T) int: the chunk whose update folded token p, -1 if it
+      was not folded during the call.
+
+    The SRE at first write of p is m[u, fold + 1, p] (the first state that
+    holds it) and the relative SRE of Eq. (26) is m[u, j, p] minus it, for
+    j > fold."""
+    Hkv = np.asarray(W).shape[0]
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    B, _, T, d = k.shape
+    U = B * Hkv
+    ku = k.reshape(U, T, d)
+    vu = v.reshape(U, T, d)
+    Wu = np.tile(np.asarray(W, F64), (B, 1, 1))
+    n0 = st.n
+    nch = (T + C - 1) // C
+    m = np.zeros((U, nch, T))
+    fold = np.full((U, T), -1, dtype=np.int64)
+    phk = _phi_units(ku, Wu)                                  # (U, T, D)
+    for j in range(nch):
+        t0 = j * C
+        for u in range(U):
+            folded = np.nonzero((fold[u] >= 0) & (fold[u] < j))[0]
+            if folded.size:
+                m[u, j, folded] = sre(phk[u:u + 1, folded], vu[u:u + 1, folded],
+                                      st.H[u:u + 1], st.s[u:u + 1])[0]
+        lg = _update_chunk(st, ku[:, t0:t0 + C], vu[:, t0:t0 + C], Wu)
+        if lg.keep is not None:
+            for u in range(U):
+                out = lg.cand_pos[u][~lg.keep[u]] - n0          # call-relative positions
+                out = out[out >= 0]
+                fold[u, out] = j
+    return m, fold
+
+
 # ------------------------------------------------------------ export / import
 def export_state(st: LolaState) -> dict:
     """Canonical layout (per unit): n; H (U, D, d); s (U, D); window k/v oldest
