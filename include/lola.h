@@ -110,6 +110,23 @@ int lola_prefill_debug(lola_state* st, const void* q, const void* k, const void*
                        int C, void* out, int out_dtype, void* ws, size_t ws_bytes,
                        int32_t* snap_pos, uint64_t* cand_keys, void* stream);
 
+/* lola_prefill_chunk plus SRE diagnostics (LoLA notes §4.4, Fig. 3, and
+ * Eq. (26)), both outputs device memory and required:
+ *   sre_map    [B*Hkv, nch, T] float32: for chunk j and the call's token p,
+ *              the SRE (Eq. (10), squared) of (k_p, v_p) against the linear
+ *              state H_j, s_j at the start of chunk j when an earlier chunk
+ *              of this call folded p into it, else 0 (p in the window or the
+ *              cache, or folded later);
+ *   fold_chunk [B*Hkv, T] int32: the chunk whose update folded token p, -1
+ *              if p was not folded during the call.
+ * The SRE at first write of p is sre_map[u, fold_chunk[u, p] + 1, p], and the
+ * relative SRE of Eq. (26) is sre_map[u, j, p] minus it, j > fold_chunk[u, p].
+ * The map is fp32 from the chunk snapshots (hi/lo 16-bit planes of H_j).
+ * C must be > 1.  Errors as lola_prefill_chunk, INVALID_ARG for NULL outputs. */
+int lola_prefill_sre_map(lola_state* st, const void* q, const void* k, const void* v, int T,
+                         int C, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                         float* sre_map, int32_t* fold_chunk, void* stream);
+
 /* One token for every sequence: q [B, Hq, d], k, v [B, Hkv, d], out
  * [B, Hq, d] float32.  Exactly lola_prefill_chunk with T = 1, C = 1: the
  * query reads the state, then the pair leaving the window (if any) is scored

@@ -362,7 +362,8 @@ int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v
 
 static int prefill_impl(lola_state* st, const void* q, const void* k, const void* v, int T,
                         int C, void* out, int out_dtype, void* ws, size_t ws_bytes,
-                        int32_t* snap_pos, uint64_t* cand_keys, void* stream) {
+                        int32_t* snap_pos, uint64_t* cand_keys, void* stream,
+                        float* sre_map = nullptr, int32_t* fold_chunk = nullptr) {
   int rc = check_state(st);
   if (rc) return rc;
   if (T < 0 || C < 1) return fail(LOLA_ERR_INVALID_ARG, "T >= 0 and C >= 1 required");
@@ -465,6 +466,11 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   ca.snapG = (int32_t*)(base + L.snapG);
   ca.finalG = (int32_t*)(base + L.finalG);
   ca.NV = (int)NVs; ca.nch = nch; ca.C = C; ca.dbg_keys = cand_keys;
+  ca.dbg_fold = fold_chunk;
+  if (fold_chunk) {
+    e = hipMemsetAsync(fold_chunk, 0xFF, (size_t)U * T * sizeof(int32_t), s);
+    if (e != hipSuccess) return hip_fail(st, e, "debug reset");
+  }
   ca.k = chain_workgroups(U, st->ncu, d, lam, C);
   ca.xcd_group = (U % 8 == 0) ? 1 : 0;
   ca.xbuf = (uint64_t*)(base + L.xbuf);
@@ -481,6 +487,14 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   if (snap_pos) {
     e = launch_snappos(vr, ca.snapG, snap_pos, nch, C, U, s);
     if (e != hipSuccess) return hip_fail(st, e, "debug launch");
+  }
+  if (sre_map) {
+    SreMapArgs ma;
+    ma.vr = vr; ma.phi_hi = phi_hi; ma.phi_lo = phi_lo; ma.NV = (int)NVs;
+    ma.snapHT = ca.snapHT; ma.snaps = ca.snaps; ma.fold = fold_chunk; ma.out = sre_map;
+    ma.nch = nch;
+    e = launch_sre_map(ma, U, st->f32, s);
+    if (e != hipSuccess) return hip_fail(st, e, "diagnostics launch");
   }
 
   AttnArgs aa;
@@ -526,6 +540,16 @@ int lola_prefill_debug(lola_state* st, const void* q, const void* k, const void*
     return fail(LOLA_ERR_UNSUPPORTED, "debug export needs C > 1");
   return prefill_impl(st, q, k, v, T, C, out, out_dtype, ws, ws_bytes, snap_pos, cand_keys,
                       stream);
+}
+
+int lola_prefill_sre_map(lola_state* st, const void* q, const void* k, const void* v, int T,
+                         int C, void* out, int out_dtype, void* ws, size_t ws_bytes,
+                         float* sre_map, int32_t* fold_chunk, void* stream) {
+  if (!sre_map || !fold_chunk)
+    return fail(LOLA_ERR_INVALID_ARG, "sre_map and fold_chunk must be non-NULL");
+  if (C == 1) return fail(LOLA_ERR_UNSUPPORTED, "the SRE diagnostics need C > 1");
+  return prefill_impl(st, q, k, v, T, C, out, out_dtype, ws, ws_bytes, nullptr, nullptr, stream,
+                      sre_map, fold_chunk);
 }
 
 int lola_set_read_branches(lola_state* st, int branches) {

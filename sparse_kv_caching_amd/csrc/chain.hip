@@ -486,6 +486,9 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
         else if (in) {
           const int sidx = e - (kb + before);
           if (sidx < nE - lam) sm.S[sidx] = sm.E[e];
+          // (diagnostics) the step that folds each of the call's tokens
+          if (a.dbg_fold && rank == 0 && sm.E[e] >= lam + eta)
+            a.dbg_fold[(size_t)u * vr.T + (sm.E[e] - lam - eta)] = j;
         }
         kb += __popcll(bk);
       }

@@ -82,6 +82,7 @@ struct ChainArgs {
   int32_t* finalG;          // [U, lam]
   int NV, nch, C;
   uint64_t* dbg_keys;       // optional [U, nch, lam + C]: candidate keys per step
+  int32_t* dbg_fold;        // optional [U, T]: the step that folded each call token (else untouched)
   // k workgroups per unit: 1, 2, or (d / 32) x CS with CS candidate groups;
   // every workgroup of the grid resident at once
   int k;
@@ -148,11 +149,25 @@ struct DecodeArgs {
   long long q_su, q_sh, kv_su, o_su, o_sh;
 };
 
+// Diagnostics: SRE of the memories in the linear state at every chunk start.
+struct SreMapArgs {
+  VirtRows vr;
+  const uint16_t* phi_hi;   // [U, NV, kD]
+  const uint16_t* phi_lo;
+  int NV;
+  const uint16_t* snapHT;   // [U, nch, 2, d, kD]
+  const float* snaps;       // [U, nch, kD]
+  const int32_t* fold;      // [U, T] chunk that folded each call token, -1 none
+  float* out;               // [U, nch, T]
+  int nch;
+};
+
 // launchers (return hipError_t of the launch)
 hipError_t launch_phi(const PhiArgs& a, int U, bool f32, hipStream_t st);
 hipError_t launch_chain(const ChainArgs& a, int U, bool f32, hipStream_t st);
 size_t chain_lds_bytes(int lam, int C, int d, bool f32);
 hipError_t launch_attn(const AttnArgs& a, int U, bool f32, hipStream_t st);
+hipError_t launch_sre_map(const SreMapArgs& a, int U, bool f32, hipStream_t st);
 size_t attn_lds_bytes(int d, int lam, bool f32);
 int attn_positions_per_block(int C, int g);
 hipError_t launch_finalize(const FinalizeArgs& a, int U, bool f32, hipStream_t st);

@@ -88,6 +88,7 @@ def library() -> ctypes.CDLL:
         lib.lola_state_export.argtypes = [vp, ctypes.POINTER(LolaStateView), vp]
         lib.lola_state_import.argtypes = [vp, ctypes.POINTER(LolaStateView), vp]
         lib.lola_set_read_branches.argtypes = [vp, i32]
+        lib.lola_prefill_sre_map.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, sz, vp, vp, vp]
         lib.lola_set_read_order.argtypes = [vp, i32]
         lib.lola_state_import_sequence.argtypes = [vp, i32, ctypes.POINTER(LolaStateView), vp]
         lib.lola_state_export_sequence.argtypes = [vp, i32, ctypes.POINTER(LolaStateView), vp]
@@ -100,7 +101,7 @@ def library() -> ctypes.CDLL:
                   "lola_state_reset", "lola_state_check", "lola_profile", "lola_state_export",
                   "lola_state_import", "lola_set_read_branches", "lola_set_read_order",
                   "lola_state_import_sequence", "lola_state_export_sequence",
-                  "lola_state_positions"):
+                  "lola_state_positions", "lola_prefill_sre_map"):
             getattr(lib, f).restype = i32
         _lib = lib
     return _lib
@@ -220,6 +221,19 @@ class LolaLayer:
                                            LOLA_DTYPE_F32, ctypes.c_void_p(), 0, _ptr(sp),
                                            _ptr(ck), _stream(stream)), "lola_prefill_debug")
         return out, sp, ck
+
+    def prefill_sre_map(self, q, k, v, C: int, stream=None):
+        """prefill plus the SRE diagnostics: returns (y, sre_map (U, nch, T)
+        float32, fold_chunk (U, T) int32); see lola_prefill_sre_map."""
+        B, Hq, T, d = q.shape
+        nch = (T + C - 1) // C
+        out = torch.empty((B, Hq, T, d), dtype=torch.float32, device=q.device)
+        m = torch.empty((self.U, nch, T), dtype=torch.float32, device=q.device)
+        fold = torch.empty((self.U, T), dtype=torch.int32, device=q.device)
+        _check(self.lib.lola_prefill_sre_map(self._st, _ptr(q), _ptr(k), _ptr(v), T, C, _ptr(out),
+                                             LOLA_DTYPE_F32, None, 0, _ptr(m), _ptr(fold),
+                                             _stream(stream)), "lola_prefill_sre_map")
+        return out, m, fold
 
     def decode(self, q, k, v, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
         """q (B, Hq, d), k, v (B, Hkv, d) -> out (B, Hq, d) float32."""
