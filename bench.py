@@ -305,15 +305,18 @@ def bench_decode(steps):
     b = decode_bytes_per_step(wl)
     gbs = b / (avg_us * 1e-6) / 1e9
     # cold variant: the 67 MB state fits the 256 MB Infinity Cache, so the
-    # steady state above may be served partly from it; here 1 GiB is written
+    # steady state above may be served partly from it; here 1 GiB is read
     # between steps (outside the decode launches' event brackets), so every
-    # step reads the state from HBM
+    # step reads the state from HBM.  (A read, not a write: written lines
+    # would still be dirty in the caches and their write-back would be
+    # charged to the decode step.)
     layer.import_(snap)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.zeros((), dtype=torch.float32, device="cuda")
     n_cold = min(64, steps)
     layer.profile(True)
     for i in range(nw, nw + n_cold):
-        flush.fill_(float(i))
+        torch.sum(flush, dim=0, out=sink)
         layer.decode(qs[i], ks[i], vs[i], out=out)
     torch.cuda.synchronize()
     ms_c, cnt_c = layer.profile(False)["decode"]
@@ -330,7 +333,7 @@ def bench_decode(steps):
                               traffic=read_traffic("decode.hip", "decode", wl.name)),
                 cold=dict(steps=n_cold, kernel_avg_us=round(cold_us, 3),
                           achieved=round(cold_gbs, 1), frac=round(cold_gbs / PEAK_HBM_GBS, 4),
-                          flush_bytes_between_steps=1 << 30))
+                          flush_bytes_read_between_steps=1 << 30))
 
 
 if __name__ == "__main__":

@@ -543,9 +543,19 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   };
   auto load_vals = [&](int k0, int kn, int ln) {
     if (32 * wave < kn) {
+      // lane j (< 32) finds the V row of key j once; load j takes that
+      // address from lane j (a scalar base plus the lane's column offset)
+      // (as a byte offset from the cache's V rows, so that the loads stay
+      // global-memory loads)
+      const char* vb = reinterpret_cast<const char*>(cv);
+      const uint64_t ra = reinterpret_cast<uintptr_t>(key_row(k0 + min(32 * wave + (ln & 31), kn - 1), true)) -
+                          reinterpret_cast<uintptr_t>(vb);
+      const uint32_t rlo = (uint32_t)ra, rhi = (uint32_t)(ra >> 32);
 #pragma unroll
-      for (int j = 0; j < 32; ++j)
-        Vpv[j] = VCols<DT, CPL>::load(key_row(k0 + min(32 * wave + j, kn - 1), true) + CPL * ln);
+      for (int j = 0; j < 32; ++j) {
+        const uint64_t rj = ((uint64_t)__builtin_amdgcn_readlane(rhi, j) << 32) | __builtin_amdgcn_readlane(rlo, j);
+        Vpv[j] = VCols<DT, CPL>::load(reinterpret_cast<const T*>(vb + rj) + CPL * ln);
+      }
     }
   };
   // V values of candidate row row0 + rr at the lane's SRE columns
@@ -570,7 +580,10 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
     return reinterpret_cast<u32x4*>(sm_s + 4 * (i - 8 * PPR));
   };
 
-  // ---- first wave of reads: W^T and the small pieces (to LDS), the wave's keys
+  // ---- first wave of reads: the wave's keys, W^T and the small pieces (to
+  // LDS), the first kThreads cache positions (no load here waits for another)
+  const int kn0 = min(kKC, nko);
+  load_keys(0, kn0, lane);
   u32x4 wbuf[WPT], mbuf[MPT];
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
@@ -582,9 +595,8 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
     const u32x4* p = misc_src(j * kThreads + tid);
     if (p) mbuf[j] = *p;
   }
-  for (int i = tid; i < gs; i += kThreads) sm_cpos[i] = a.cache_pos[(size_t)u * lam + i];
-  const int kn0 = min(kKC, nko);
-  load_keys(0, kn0, lane);
+  int32_t cpos0 = 0;
+  if (tid < gs) cpos0 = a.cache_pos[(size_t)u * lam + tid];
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
     const int i = j * kThreads + tid;
@@ -595,11 +607,14 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
     const int i = j * kThreads + tid;
     if (misc_src(i)) *misc_dst(i) = mbuf[j];
   }
-  // ---- second wave, issued once the first wave's LDS data has arrived: the
-  // values of the wave's keys, the SRE values of the first phi tiles, the H
-  // slab (lane (n16, q4) holds H[sigma(kb, q4, j)][32 wave + 16 mb + n16]:
-  // two 16-byte pieces of an H^T row per block).  Logits and phi run while
-  // these stream in.
+  if (tid < gs) sm_cpos[tid] = cpos0;
+  for (int i = tid + kThreads; i < gs; i += kThreads) sm_cpos[i] = a.cache_pos[(size_t)u * lam + i];
+  __syncthreads();
+  // ---- second wave, issued once every wave's first-wave LDS data has
+  // arrived: the values of the wave's keys, the SRE values of the first phi
+  // tiles, the H slab (lane (n16, q4) holds H[sigma(kb, q4, j)][32 wave +
+  // 16 mb + n16]: two 16-byte pieces of an H^T row per block).  Logits and
+  // phi run while these stream in.
   __builtin_amdgcn_sched_barrier(0);
   load_vals(0, kn0, lane);
   VQuad<DT> vs[NVS][2];
@@ -618,7 +633,6 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
       }
     }
   }
-  __syncthreads();
 
   const float scale2 = kL2E / sqrtf((float)HD);   // logits in the log2 domain
   // the wave's running max and sum per head (the same in every lane); its
