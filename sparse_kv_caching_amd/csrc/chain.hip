@@ -94,13 +94,13 @@ __host__ __device__ inline ChainLayout chain_layout(int lam, int C, int spw, boo
   L.G = take(lam1 * 4);                    // cache (virtual indices)
   L.Gp = take(lam1 * 4);                   // cache positions
   L.S = take((uint32_t)C * 4);             // folded list (<= C per step)
-  L.misc = take(20 * 4);                   // [0..2] selection, [8..15] per wave, [16] abort
+  L.misc = take(20 * 4);                   // [8..15] per wave, [16] abort
   L.kred = take(2 * kWaves * 8);           // per-wave key min / max
   const uint32_t region = off;
   L.E = take(le * 4);                      // candidates (virtual indices)
   L.part = take((uint32_t)spw * le * 4);   // [slab][candidate] SRE parts
   L.keys = take(le * 8);
-  L.hist = take(512 * 4);                  // two radix histograms
+  L.hist = take(768 * 4);                  // three radix histograms
   const uint32_t sel_end = off;
   off = region;
   L.phT_hi = take(kD * STP * 2);           // [kD][STP]
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
       continue;
     }
     for (int i = tid; i < nE; i += kThreads) sm.E[i] = i < gs ? sm.G[i] : vi_L0 + (i - gs);
-    for (int i = tid; i < 512; i += kThreads) sm.hist[i] = 0;
+    for (int i = tid; i < 256; i += kThreads) sm.hist[i] = 0;
     lds_barrier();
 
     // ---- 4a. SRE parts over this workgroup's columns.  Wave w takes slab
@@ -397,9 +397,12 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     }
 
     // ---- 4b. exact top-lam: radix select of the lam-th largest key with
-    // 8-bit digits, from the highest bit where the keys differ down; one wave
-    // scans the 256 bins, and two histograms alternate so that a pass needs
-    // two barriers.  lam == 0: nothing is kept.
+    // 8-bit digits, from the highest bit where the keys differ down.  Pass p
+    // counts into histogram p % 3 and clears histogram (p + 1) % 3 for the
+    // next pass; after one barrier every wave scans the 256 bins itself (the
+    // same result in every wave), so a pass needs one barrier: a histogram is
+    // cleared two passes after it was scanned, behind the barrier of the pass
+    // between.  lam == 0: nothing is kept.
     uint64_t prefix = 0, mask = 0;
     if (lam > 0) {
       kmin = sm.kred[0];
@@ -419,38 +422,41 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
       for (;;) {
         const int lo = hi_bit > 8 ? hi_bit - 8 : 0;
         const uint32_t dmask = (1u << (hi_bit - lo)) - 1u;
+        const int nbuf = buf == 2 ? 0 : buf + 1;
         int32_t* H = sm.hist + 256 * buf;
         for (int e = tid; e < nE; e += kThreads) {
           const uint64_t k = sm.keys[e];
           if ((k & mask) == prefix) atomicAdd(&H[(uint32_t)(k >> lo) & dmask], 1);
         }
-        for (int i = tid; i < 256; i += kThreads) sm.hist[256 * (buf ^ 1) + i] = 0;
+        for (int i = tid; i < 256; i += kThreads) sm.hist[256 * nbuf + i] = 0;
         lds_barrier();
-        if (wave == 0) {
-          // lane l owns bins 255 - 4 l - q: the lanes in order walk the bins
-          // from the top down
-          int cnt[4], tot = 0;
+        // lane l owns bins 255 - 4 l - q: the lanes in order walk the bins
+        // from the top down; the one lane whose bin holds the need-th key
+        // hands the bin, the rank left in it and its count to the wave
+        int cnt[4], tot = 0;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) { cnt[q] = H[255 - 4 * lane - q]; tot += cnt[q]; }
-          int above = wave_incl_scan(tot) - tot;
+        for (int q = 0; q < 4; ++q) { cnt[q] = H[255 - 4 * lane - q]; tot += cnt[q]; }
+        int above = wave_incl_scan(tot) - tot;
+        int fb = 0, fneed = 0, fcnt = 0;
+        bool found = false;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (above < need && need <= above + cnt[q]) {
-              sm.misc[0] = 255 - 4 * lane - q;
-              sm.misc[1] = need - above;
-              sm.misc[2] = cnt[q];
-            }
-            above += cnt[q];
+        for (int q = 0; q < 4; ++q) {
+          if (above < need && need <= above + cnt[q]) {
+            found = true;
+            fb = 255 - 4 * lane - q;
+            fneed = need - above;
+            fcnt = cnt[q];
           }
+          above += cnt[q];
         }
-        lds_barrier();
-        const int bsel = sm.misc[0], cb = sm.misc[2];
-        need = sm.misc[1];
+        const int src = (int)__builtin_ctzll(__ballot(found));
+        const int bsel = __builtin_amdgcn_readlane(fb, src), cb = __builtin_amdgcn_readlane(fcnt, src);
+        need = __builtin_amdgcn_readlane(fneed, src);
         prefix |= (uint64_t)bsel << lo;
         mask |= (uint64_t)dmask << lo;
         if (cb == need || lo == 0) break;
         hi_bit = lo;
-        buf ^= 1;
+        buf = nbuf;
       }
     }
 
@@ -568,6 +574,8 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
           }
         }
         sacc += part;
+        // the last block's partial sums go out before its closing barrier
+        if (sb + 64 >= nS) sm.spart[(tid / kD) * kD + tid % kD] = sacc;
       }
       const int nkb = min(4, (nS - sb + 15) / 16);
       for (int kb = 0; kb < nkb; ++kb) {
@@ -588,8 +596,6 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
       }
       lds_barrier();
     }
-    sm.spart[(tid / kD) * kD + tid % kD] = sacc;
-    lds_barrier();
     for (int F = tid; F < kD; F += kThreads) {
       float add = 0.f;
 #pragma unroll
