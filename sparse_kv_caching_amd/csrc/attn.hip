@@ -37,6 +37,7 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int KT = 64;        // keys per staged tile
+constexpr float kSlack = 8.f; // log2 headroom of the softmax weights over the running maximum
 constexpr int HTS = kD + 8;   // LDS row of H^T (16-bit elements)
 constexpr int VTS = KT + 4;   // LDS row of the V^T tile (keys): 34 dwords, so that the 32 rows of a
                               // 64-bit operand read fall on distinct bank pairs
@@ -51,6 +52,19 @@ struct AttnLayout {
 };
 
 inline __host__ __device__ uint32_t al16(uint32_t x) { return (x + 15u) & ~15u; }
+
+// max / sum of a lane's value and the value 32 lanes away, in every lane, on
+// the VALU: v_permlane32_swap of x with itself gives r0 = x[l % 32] and
+// r1 = x[l % 32 + 32] in lane l (the same two operands, in the same order,
+// in both halves)
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __host__ __device__ inline AttnLayout attn_layout(int d, int lam, bool f32) {
   AttnLayout L;
@@ -406,20 +420,41 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
           }
         }
       }
+      // masks only where the tile has keys past the end or past the wave's
+      // first query position (every query of the wave sees a full tile);
+      // the scale goes into the exponent's fma
+      // (fp32 inputs: always the masked form; the two forms do not fit its
+      // registers together)
+      const int klast = t0 + KT - 1;
+      const bool full = !DT::kSplit && klast < nkeys && (klast < gsj || lo_j + (klast - gsj) <= p0);
       float tmax = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kk = t0 + 32 * kh + 8 * (i >> 2) + 4 * h + (i & 3);
-          bool ok = kk < nkeys;
-          if (ok && kk >= gsj) ok = lo_j + (kk - gsj) <= qpos;   // causal (diagonal included)
-          S[kh][i] = ok ? S[kh][i] * scale2 : -INFINITY;
-          tmax = fmaxf(tmax, S[kh][i]);
-        }
-      tmax = fmaxf(tmax, xor32(tmax));
-      const float mnew = fmaxf(m2, tmax);
-      if (mnew > m2) {
+          for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, S[kh][i]);
+      } else {
+        // (the lane's key offset made opaque here, so that the 32 key
+        // indices are not hoisted out of the tile loop into registers)
+        int kl0 = t0 + 4 * h;
+        __asm__ volatile("" : "+v"(kl0));
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kk = kl0 + 32 * kh + 8 * (i >> 2) + (i & 3);
+            bool ok = kk < nkeys;
+            if (ok && kk >= gsj) ok = lo_j + (kk - gsj) <= qpos;   // causal (diagonal included)
+            S[kh][i] = ok ? S[kh][i] : -INFINITY;
+            tmax = fmaxf(tmax, S[kh][i]);
+          }
+      }
+      tmax = half_max(tmax) * scale2;   // (the scale is positive)
+      // the running maximum moves only when a score would exceed it by more
+      // than kSlack (weights up to 2^kSlack, well inside fp16 and fp32), so
+      // that the accumulators are rarely rescaled
+      if (tmax > m2 + kSlack) {
+        const float mnew = tmax;
         const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
@@ -432,8 +467,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { S[kh][i] = __builtin_amdgcn_exp2f(S[kh][i] - m2); rs += S[kh][i]; }
-      rs += xor32(rs);
+        for (int i = 0; i < 16; ++i) {
+          S[kh][i] = __builtin_amdgcn_exp2f(fmaf(S[kh][i], scale2, -m2));
+          rs += S[kh][i];
+        }
+      rs = half_sum(rs);
       l += rs;
 #pragma unroll
       for (int kb = 0; kb < KT / 16; ++kb) {
