@@ -139,6 +139,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   const int nkeys = gsj + (int)(pend - lo_j);
   // last key any query of this wave sees (wave-uniform)
   const int wlast = gsj + (int)(min(p0 + 31, pend - 1) - lo_j);
+  // keys 0 .. vis_end - 1 are visible to the lane's query (cache, window and
+  // the causal prefix of the chunk up to and including the query)
+  const int vis_end = (int)min((long long)nkeys, gsj + (qpos - lo_j) + 1);
   const int n0e = eta > 0 ? (int)(n0 % eta) : 0;            // ring slot of position n0 - eta
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -422,33 +425,24 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
       }
       // masks only where the tile has keys past the end or past the wave's
       // first query position (every query of the wave sees a full tile);
-      // the scale goes into the exponent's fma
-      // (fp32 inputs: always the masked form; the two forms do not fit its
-      // registers together)
+      // the scale goes into the exponent's fma.  Key kk is visible to the
+      // lane's query iff kk < vis_end (cache keys precede the local ones, a
+      // local key is visible up to the query's own position).
       const int klast = t0 + KT - 1;
-      const bool full = !DT::kSplit && klast < nkeys && (klast < gsj || lo_j + (klast - gsj) <= p0);
-      float tmax = -INFINITY;
-      if (full) {
+      const bool full = klast < nkeys && (klast < gsj || lo_j + (klast - gsj) <= p0);
+      if (!full) {
+        const int dl = vis_end - t0 - 4 * h;      // the lane's offsets below dl are visible
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, S[kh][i]);
-      } else {
-        // (the lane's key offset made opaque here, so that the 32 key
-        // indices are not hoisted out of the tile loop into registers)
-        int kl0 = t0 + 4 * h;
-        __asm__ volatile("" : "+v"(kl0));
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kk = kl0 + 32 * kh + 8 * (i >> 2) + (i & 3);
-            bool ok = kk < nkeys;
-            if (ok && kk >= gsj) ok = lo_j + (kk - gsj) <= qpos;   // causal (diagonal included)
-            S[kh][i] = ok ? S[kh][i] : -INFINITY;
-            tmax = fmaxf(tmax, S[kh][i]);
-          }
+          for (int i = 0; i < 16; ++i)
+            if (32 * kh + 8 * (i >> 2) + (i & 3) >= dl) S[kh][i] = -INFINITY;
       }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, S[kh][i]);
       tmax = half_max(tmax) * scale2;   // (the scale is positive)
       // the running maximum moves only when a score would exceed it by more
       // than kSlack (weights up to 2^kSlack, well inside fp16 and fp32), so
