@@ -38,7 +38,8 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int KT = 64;        // keys per staged tile
 constexpr float kSlack = 8.f; // log2 headroom of the softmax weights over the running maximum
-constexpr int HTS = kD + 8;   // LDS row of H^T (16-bit elements)
+constexpr int HTS = kD + 4;   // LDS row of H^T (16-bit elements): 66 dwords, so that the 32
+                              // rows of a 64-bit operand read fall on distinct bank pairs
 constexpr int VTS = KT + 4;   // LDS row of the V^T tile (keys): 34 dwords, so that the 32 rows of a
                               // 64-bit operand read fall on distinct bank pairs
 
@@ -186,8 +187,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     for (int i = tid; i < 2 * HPIECES; i += kThreads) {
       const int pl = i / HPIECES, rem = i % HPIECES;
       const int row = rem / (kD / 8), col = (rem % (kD / 8)) * 8;
-      *reinterpret_cast<u32x4*>((pl ? sm_HT_lo : sm_HT_hi) + row * HTS + col) =
-          *reinterpret_cast<const u32x4*>(snap + (size_t)pl * HD * kD + (size_t)row * kD + col);
+      // (rows are 8-byte aligned: two 8-byte stores)
+      const u32x4 x = *reinterpret_cast<const u32x4*>(snap + (size_t)pl * HD * kD + (size_t)row * kD + col);
+      uint16_t* dst = (pl ? sm_HT_lo : sm_HT_hi) + row * HTS + col;
+      *reinterpret_cast<u32x2*>(dst) = u32x2{x[0], x[1]};
+      *reinterpret_cast<u32x2*>(dst + 4) = u32x2{x[2], x[3]};
     }
     const float* sj = a.snaps + ((size_t)u * a.nch + j) * kD;
     for (int F = tid; F < kD; F += kThreads) sm_s[F] = sj[F];
