@@ -98,6 +98,15 @@ __device__ __forceinline__ u32x4 sigma_load(const uint16_t* row16, int h) {
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
+// First V column (of 8) of thread tid's item in the V^T staging: the two
+// half-waves take column groups 2 apart (V^T rows 16 apart, 544 dwords:
+// 32 banks apart), so that their 4-byte writes to one key-pair column fall on
+// all 64 banks
+__device__ __forceinline__ int vt_cols(int tid) {
+  const int w = tid >> 6, hh = (tid >> 5) & 1;
+  return 8 * (4 * (w >> 1) + (w & 1) + 2 * hh);
+}
+
 __device__ __forceinline__ uint32_t f16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
@@ -332,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
                            : u32x4{0, 0, 0, 0};
     }
     if (tid < VITEMS) {
-      const int pr = tid % (KT / 2), c = (tid / (KT / 2)) * 8;
+      const int pr = tid % (KT / 2), c = vt_cols(tid);
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq) {
         const int kk = t0 + 2 * pr + kq;
@@ -367,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
       }
     }
     if (tid < VITEMS) {
-      const int pr = tid % (KT / 2), c = (tid / (KT / 2)) * 8;
+      const int pr = tid % (KT / 2), c = vt_cols(tid);
       uint16_t* VTb = (uint16_t*)(smem + buf_off(L.VT, b));
       uint16_t* VTLb = (uint16_t*)(smem + buf_off(L.VTL, b));
       float vf[2][8];
