@@ -32,6 +32,8 @@ struct lola_state {
   int npos_cur;             // the half decode reads next
   float* H;
   float* s;
+  float* pend;              // [U][kPend][kD + d] decode folds not yet written to H
+  int32_t* npend;           // [U] how many (H proper = H + their terms, in order)
   void* ring_k;
   void* ring_v;
   void* cache_k[2];
@@ -169,6 +171,11 @@ int check_read_config(const lola_state* st) {
   return LOLA_OK;
 }
 
+// H proper everywhere: the decode steps' held-back folds written into H
+hipError_t flush_pending(const lola_state* st, hipStream_t s) {
+  return launch_flush_pending(st->H, st->pend, st->npend, st->U, st->d, s);
+}
+
 // One token through the decode kernel at position a.n: read, then update;
 // or (read after update) an update launch, then a read launch of the
 // updated state at a.n + 1.
@@ -275,7 +282,9 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
             alloc(&st->W, (size_t)c.kv_heads * d * kM * st->esz) &&
             alloc(&st->WT, (size_t)c.kv_heads * d * kM * st->esz) &&
             alloc((void**)&st->dev_err, sizeof(int)) &&
-            alloc((void**)&st->npos_dev, 2 * (size_t)c.batch * sizeof(long long));
+            alloc((void**)&st->npos_dev, 2 * (size_t)c.batch * sizeof(long long)) &&
+            alloc((void**)&st->pend, U * kPend * (kD + d) * 4) &&
+            alloc((void**)&st->npend, U * 4);
   st->nseq = new int64_t[c.batch]();
   for (int b = 0; b < 2 && ok; ++b)
     ok = alloc(&st->cache_k[b], U * lam * d * st->esz) &&
@@ -294,6 +303,7 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
     e = hipMemcpyAsync(st->W, W, (size_t)c.kv_heads * d * kM * st->esz, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess) e = launch_transpose_w(st->W, st->WT, c.kv_heads, (int)d, st->f32, s);
   if (e == hipSuccess) e = launch_zero_u32((unsigned*)st->dev_err, 1, s);
+  if (e == hipSuccess) e = launch_zero_u32((unsigned*)st->npend, U, s);
   if (e != hipSuccess) {
     lola_state_free(st);
     return fail(LOLA_ERR_HIP, "state initialisation: %s", hipGetErrorString(e));
@@ -307,7 +317,7 @@ int lola_state_free(lola_state* st) {
   hipStreamSynchronize(st->last);
   delete[] st->nseq;
   void* ps[] = {st->H, st->s, st->ring_k, st->ring_v, st->W, st->WT, st->dev_err, st->own_ws,
-                st->npos_dev,
+                st->npos_dev, st->pend, st->npend,
                 st->cache_k[0], st->cache_k[1], st->cache_v[0], st->cache_v[1],
                 st->cache_pos[0], st->cache_pos[1]};
   for (void* p : ps)
@@ -342,6 +352,7 @@ int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v
   DecodeArgs a;
   a.q = q; a.k = k; a.v = v; a.WT = st->WT;
   a.H = st->H; a.s = st->s;
+  a.pend = st->pend; a.npend = st->npend;
   a.ring_k = st->ring_k; a.ring_v = st->ring_v;
   a.cache_k = st->cache_k[st->cur]; a.cache_v = st->cache_v[st->cur];
   a.cache_pos = st->cache_pos[st->cur];
@@ -388,6 +399,7 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
     // q [U, g, T, d], k / v [U, T, d] and writing out [U, g, T, d]
     DecodeArgs a;
     a.WT = st->WT; a.H = st->H; a.s = st->s;
+    a.pend = st->pend; a.npend = st->npend;
     a.ring_k = st->ring_k; a.ring_v = st->ring_v;
     a.cache_k = st->cache_k[st->cur]; a.cache_v = st->cache_v[st->cur];
     a.cache_pos = st->cache_pos[st->cur];
@@ -411,6 +423,8 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
     return LOLA_OK;
   }
 
+  // the chain reads H: the decode steps' held-back folds go in first
+  if (hipError_t e = flush_pending(st, s); e != hipSuccess) return hip_fail(st, e, "flush");
   const WsLayout L = ws_layout(st, T, C);
   char* base = (char*)ws;
   if (!base) {
@@ -579,6 +593,7 @@ int lola_state_reset(lola_state* st, void* stream) {
   for (int b = 0; b < 2 && e == hipSuccess; ++b)
     e = hipMemsetAsync(st->cache_pos[b], 0xFF, U * (lam ? lam : 1) * 4, s);
   if (e == hipSuccess) e = launch_zero_u32((unsigned*)st->dev_err, 1, s);
+  if (e == hipSuccess) e = launch_zero_u32((unsigned*)st->npend, U, s);
   if (e != hipSuccess) return hip_fail(st, e, "reset");
   set_uniform(st, 0);
   st->poisoned = false;
@@ -634,8 +649,9 @@ int lola_state_export(const lola_state* st, lola_state_view* dst, void* stream) 
   const size_t U = st->U, d = st->d;
   const int lam = st->cfg.cache, eta = st->cfg.window;
   const int gs = (int)std::min<int64_t>(lam, std::max<int64_t>(0, st->n - eta));
-  // the device keeps H^T [U, d, D]; the view holds H [U, D, d]
-  hipError_t e = launch_transpose_f32(st->H, dst->H, (int)U, (int)d, kD, s);
+  // the device keeps H^T [U, d, D] (plus held-back folds); the view holds H [U, D, d]
+  hipError_t e = flush_pending(st, s);
+  if (e == hipSuccess) e = launch_transpose_f32(st->H, dst->H, (int)U, (int)d, kD, s);
   if (e == hipSuccess) e = hipMemcpyAsync(dst->s, st->s, U * kD * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
     e = launch_export(st->f32, st->U, st->ring_k, st->ring_v, st->cache_k[st->cur],
@@ -670,6 +686,7 @@ int lola_state_import(lola_state* st, const lola_state_view* src, void* stream) 
       }
   }
   hipError_t e = launch_transpose_f32(src->H, st->H, (int)U, kD, (int)d, s);
+  if (e == hipSuccess) e = launch_zero_u32((unsigned*)st->npend, U, s);
   if (e == hipSuccess) e = hipMemcpyAsync(st->s, src->s, U * kD * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
     e = launch_import(st->f32, st->U, st->ring_k, st->ring_v, st->cache_k[st->cur],
@@ -716,7 +733,9 @@ int lola_state_import_sequence(lola_state* st, int b, const lola_state_view* src
   char* rv = (char*)st->ring_v + u0 * eta * d * es;
   char* ck = (char*)st->cache_k[st->cur] + u0 * lam * d * es;
   char* cv = (char*)st->cache_v[st->cur] + u0 * lam * d * es;
-  hipError_t e = launch_transpose_f32(src->H, st->H + u0 * d * kD, Hkv, kD, (int)d, s);
+  // every unit's held-back folds into H first (the slot's units are replaced)
+  hipError_t e = flush_pending(st, s);
+  if (e == hipSuccess) e = launch_transpose_f32(src->H, st->H + u0 * d * kD, Hkv, kD, (int)d, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(st->s + u0 * kD, src->s, (size_t)Hkv * kD * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
@@ -755,7 +774,8 @@ int lola_state_export_sequence(const lola_state* st, int b, lola_state_view* dst
   const int lam = st->cfg.cache, eta = st->cfg.window;
   const int64_t n = st->nseq[b];
   const int gs = (int)std::min<int64_t>(lam, std::max<int64_t>(0, n - eta));
-  hipError_t e = launch_transpose_f32(st->H + u0 * d * kD, dst->H, Hkv, (int)d, kD, s);
+  hipError_t e = flush_pending(st, s);
+  if (e == hipSuccess) e = launch_transpose_f32(st->H + u0 * d * kD, dst->H, Hkv, (int)d, kD, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(dst->s, st->s + u0 * kD, (size_t)Hkv * kD * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)

@@ -60,7 +60,7 @@ __host__ __device__ inline int dec_phi_tiles(int lam, int eta) {
 // Byte offsets of the LDS arrays.
 struct DecLayout {
   uint32_t wt, q, lk, lv, nk, nv, ve, s, cpos, spart, logit, nlin, pv, phe, wst, zq, red, slot,
-      meta, total;
+      meta, pend, total;
   int ntile;
 };
 
@@ -91,6 +91,8 @@ __host__ __device__ inline DecLayout dec_layout(int lam, int eta, int d, int esz
   L.red = take(16);                                    // the folded row
   L.slot = take((uint32_t)L.ntile * 8 * 64 * 16);      // [tile][kb][hi, lo][lane] phi operands
   L.meta = take((uint32_t)L.ntile * 16 * 16);          // [tile][row] 1/S+, 1/S-, phi^T s
+  // held-back fold terms [k][phi, v] (the one-chunk instance only)
+  L.pend = take(lam + eta <= kKC ? (uint32_t)kPend * (kD + d) * 4 : 0u);
   L.total = off;
   return L;
 }
@@ -502,6 +504,7 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   int32_t* sm_red = (int32_t*)(smem + L.red);
   u32x4* sm_slot = (u32x4*)(smem + L.slot);
   float* sm_meta = (float*)(smem + L.meta);
+  float* sm_pend = (float*)(smem + L.pend);
 
   const T* qg = reinterpret_cast<const T*>(a.q) + (size_t)u * a.q_su;
   const T* kin = reinterpret_cast<const T*>(a.k) + (size_t)u * a.kv_su;
@@ -597,6 +600,14 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   }
   int32_t cpos0 = 0;
   if (tid < gs) cpos0 = a.cache_pos[(size_t)u * lam + tid];
+  // the unit's held-back fold terms (phi, v: PQ 16-byte pieces each)
+  constexpr int PQ = (kD + HD) / 4;
+  static_assert(kPend * PQ <= kThreads, "one piece of the held-back terms per thread");
+  // (the chunked instance writes every fold at once and never holds one back)
+  const int np = !MULTI && a.npend ? max(0, min((int)a.npend[u], kPend)) : 0;
+  u32x4 pbuf = u32x4{0, 0, 0, 0};
+  if (tid < np * PQ)
+    pbuf = *reinterpret_cast<const u32x4*>(a.pend + (size_t)u * kPend * (kD + HD) + 4 * tid);
 #pragma unroll
   for (int j = 0; j < WPT; ++j) {
     const int i = j * kThreads + tid;
@@ -608,6 +619,7 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
     if (misc_src(i)) *misc_dst(i) = mbuf[j];
   }
   if (tid < gs) sm_cpos[tid] = cpos0;
+  if (tid < np * PQ) *reinterpret_cast<u32x4*>(sm_pend + 4 * tid) = pbuf;
   for (int i = tid + kThreads; i < gs; i += kThreads) sm_cpos[i] = a.cache_pos[(size_t)u * lam + i];
   __syncthreads();
   // ---- second wave, issued once every wave's first-wave LDS data has
@@ -832,6 +844,19 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
             float x[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) { x[j] = Hraw[mb][kb][0][j]; x[4 + j] = Hraw[mb][kb][1][j]; }
+            // the held-back folds, oldest first: the fma of the step that
+            // made each term (so H is bitwise the one written at once)
+            for (int k = 0; k < np; ++k) {
+              const float* pk = sm_pend + k * (kD + HD);
+              const f32x4 f0 = *reinterpret_cast<const f32x4*>(pk + 32 * kb + 4 * q4);
+              const f32x4 f1 = *reinterpret_cast<const f32x4*>(pk + 32 * kb + 16 + 4 * q4);
+              const float vk = pk[kD + 32 * wave + 16 * mb + n16];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                x[j] = fmaf(f0[j], vk, x[j]);
+                x[4 + j] = fmaf(f1[j], vk, x[4 + j]);
+              }
+            }
             Hs.set(mb, kb, x);
           }
       }
@@ -970,7 +995,17 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   // ---- update: fold into the slab and s, cache slot
   const int fold_row = full ? sm_red[0] : -1;      // < gs: cache slot; == gs: the leaving pair
   if (fold_row >= 0) {
-    if (has_slab) {
+    // H is written every kPend + 1 positions (the same steps for every unit
+    // of a uniform batch, so that the other steps write no H at all) or when the
+    // held-back list is full; otherwise the step's term joins the list
+    static_assert(((kPend + 1) & kPend) == 0, "the write period is a power of two");
+    const bool wr = MULTI || !a.pend || np >= kPend || ((uint32_t)n & (uint32_t)kPend) == 0;
+    if (!wr) {
+      float* dst = a.pend + ((size_t)u * kPend + np) * (kD + HD);
+      for (int i = tid; i < kD + HD; i += kThreads) dst[i] = i < kD ? sm_phe[i] : sm_ve[i - kD];
+    }
+    if (a.npend && tid == 0) a.npend[u] = wr ? 0 : np + 1;
+    if (has_slab && wr) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const float ve = sm_ve[32 * wave + 16 * mb + n16];
@@ -1005,6 +1040,32 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
       if (tid == 0) a.cache_pos[(size_t)u * lam + slot_in] = (int32_t)(n - eta);
     }
   }
+}
+
+// H += the held-back fold terms of each unit, npend = 0 (before anything
+// other than the decode step reads or replaces H).  One workgroup per unit.
+__global__ __launch_bounds__(256) void flush_pending_kernel(float* H, const float* pend,
+                                                            int32_t* npend, int d) {
+  const int u = blockIdx.x;
+  const int np = max(0, min((int)npend[u], kPend));
+  if (np == 0) return;
+  const float* pu = pend + (size_t)u * kPend * (kD + d);
+  float* Hu = H + (size_t)u * d * kD;                // H^T [d][kD]
+  for (int e = threadIdx.x; e < d * kD; e += blockDim.x) {
+    const int c = e / kD, F = e % kD;
+    float x = Hu[e];
+    for (int k = 0; k < np; ++k) x = fmaf(pu[k * (kD + d) + F], pu[k * (kD + d) + kD + c], x);
+    Hu[e] = x;
+  }
+  __syncthreads();                                   // every thread has read npend[u]
+  if (threadIdx.x == 0) npend[u] = 0;
+}
+
+hipError_t launch_flush_pending(float* H, const float* pend, int32_t* npend, int U, int d,
+                                hipStream_t st) {
+  if (U <= 0) return hipSuccess;
+  hipLaunchKernelGGL(flush_pending_kernel, dim3(U), dim3(256), 0, st, H, pend, npend, d);
+  return hipGetLastError();
 }
 
 // W [Hkv, d, kM] -> W^T [Hkv, kM, d] (once, at state creation)

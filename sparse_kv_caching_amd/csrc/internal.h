@@ -147,7 +147,17 @@ struct DecodeArgs {
   long long* npos_next;
   // element strides (one token): q / out [u][hd], k / v [u]
   long long q_su, q_sh, kv_su, o_su, o_sh;
+  // deferred folds: H is the stored H plus, in order, the rank-one terms
+  // phi v^T in pend [U][kPend][kD + d] (phi, then v; npend [U] of them);
+  // NULL: every fold is written to H at once
+  float* pend;
+  int32_t* npend;
 };
+
+// Rank-one fold terms a unit may hold back between writes of its H: a
+// decode step writes H only every kPend + 1 positions (staggered by unit) or
+// when the list is full, else it appends its term (1 KB instead of 64 KB).
+constexpr int kPend = 3;
 
 // Diagnostics: SRE of the memories in the linear state at every chunk start.
 struct SreMapArgs {
@@ -172,6 +182,10 @@ size_t attn_lds_bytes(int d, int lam, bool f32);
 int attn_positions_per_block(int C, int g);
 hipError_t launch_finalize(const FinalizeArgs& a, int U, bool f32, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int U, bool f32, hipStream_t st);
+// H += the held-back terms (in order, the same fma per element as the decode
+// step's fold) and npend = 0, for every unit
+hipError_t launch_flush_pending(float* H, const float* pend, int32_t* npend, int U, int d,
+                                hipStream_t st);
 hipError_t launch_export(bool f32, int U, const void* ring_k, const void* ring_v,
                          const void* cache_k, const void* cache_v, const int32_t* cache_pos,
                          void* win_k, void* win_v, void* out_ck, void* out_cv, int32_t* out_pos,
