@@ -131,6 +131,12 @@ int lola_prefill_sre_map(lola_state* st, const void* q, const void* k, const voi
  * [B, Hq, d] float32.  Exactly lola_prefill_chunk with T = 1, C = 1: the
  * query reads the state, then the pair leaving the window (if any) is scored
  * against the cache and the lowest-SRE candidate is folded (LoLA notes §2.4).
+ * Storage: when window + cache <= 128 keys, a step may hold its fold term
+ * (phi of the folded row and its value) in the state instead of rewriting H;
+ * H is rewritten every fourth position, and any other call that reads or
+ * replaces H (prefill, export, import, reset) first applies the held terms
+ * in order.  The state every entry point observes is the one of a fold
+ * applied at once, bit for bit.
  * Errors: INVALID_ARG, STATE, HIP. */
 int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v, void* out,
                      int out_dtype, void* stream);
