@@ -899,24 +899,33 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
 
   if (wave == 0) {
     if (full) {
-      // ---- the candidate to fold: lowest SRE, ties to the newer position
-      float best = INFINITY;
-      int bpos = -1, bi = 0;
+      // ---- the candidate to fold: lowest SRE, ties to the newer position,
+      // as the smallest 64-bit key (SRE bits, then the position complemented;
+      // SRE >= 0, so its bits order as the values); the wave minimum by DPP
+      // moves (lane 63), the winner's lane by a ballot
+      uint64_t key = ~0ull;
+      int bi = 0;
       for (int e = lane; e < ncand; e += 64) {
         float sre = 0.f;
 #pragma unroll
         for (int w = 0; w < NS; ++w) sre += sm_spart[w * (lam + 1) + e];
         const int pos = e < gs ? sm_cpos[e] : (int)(n - eta);
-        if (sre < best || (sre == best && pos > bpos)) { best = sre; bpos = pos; bi = e; }
+        const uint64_t k = ((uint64_t)__float_as_uint(sre) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)pos);
+        if (k < key) { key = k; bi = e; }
       }
-      float m = best;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) m = fminf(m, __shfl_xor(m, o, 64));
-      int p = best == m ? bpos : -1;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) p = max(p, __shfl_xor(p, o, 64));
-      const uint64_t win = __ballot(best == m && bpos == p);
-      bi = __shfl(bi, (int)__builtin_ctzll(win), 64);
+      uint64_t m = key;
+      {
+        auto mn = [&](uint64_t y) { m = y < m ? y : m; };
+        mn(dpp_u64<0x111, 0xf>(m, ~0ull));
+        mn(dpp_u64<0x112, 0xf>(m, ~0ull));
+        mn(dpp_u64<0x114, 0xf>(m, ~0ull));
+        mn(dpp_u64<0x118, 0xf>(m, ~0ull));
+        mn(dpp_u64<0x142, 0xa>(m, ~0ull));
+        mn(dpp_u64<0x143, 0xc>(m, ~0ull));
+      }
+      const uint64_t mk = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(m >> 32), 63) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)m, 63);
+      bi = __builtin_amdgcn_readlane(bi, (int)__builtin_ctzll(__ballot(key == mk)));
       if (lane == 0) sm_red[0] = bi;
       const T* vrow = bi == gs ? sm_lv : cv + (size_t)bi * HD;
       for (int e = lane; e < HD; e += 64) sm_ve[e] = ldf(vrow + e);
