@@ -137,11 +137,22 @@ __device__ __forceinline__ f32x4 mma16x(u32x4 ah, u32x4 al, u32x4 bh, u32x4 bl, 
 
 __device__ __forceinline__ float ldf(const uint16_t* p) { return bf16_bits_to_f32(*p); }
 __device__ __forceinline__ float ldf(const float* p) { return *p; }
-__device__ __forceinline__ float xor16(float x) { return __shfl_xor(x, 16, 64); }
-// sum / max / min over the four lane groups q of a 16-lane column
-__device__ __forceinline__ float qsum(float x) { x += xor16(x); return x + xor32(x); }
-__device__ __forceinline__ float qmax(float x) { x = fmaxf(x, xor16(x)); return fmaxf(x, xor32(x)); }
-__device__ __forceinline__ float qmin(float x) { x = fminf(x, xor16(x)); return fminf(x, xor32(x)); }
+// Sum / max / min over the four lane groups q of a 16-lane column, on the
+// VALU: v_permlane16_swap of x with itself gives the lanes of rows 2i and
+// 2i + 1 the pair (x in row 2i, x in row 2i + 1) of their column, and
+// v_permlane32_swap the pair of halves; every lane of the column combines the
+// same operands in the same order ((x0 o x1) o (x2 o x3)).  The four lanes
+// of a column are always active together.
+template <class Op>
+__device__ __forceinline__ float qreduce(float x, Op op) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float qsum(float x) { return qreduce(x, [](float a, float b) { return a + b; }); }
+__device__ __forceinline__ float qmax(float x) { return qreduce(x, [](float a, float b) { return fmaxf(a, b); }); }
+__device__ __forceinline__ float qmin(float x) { return qreduce(x, [](float a, float b) { return fminf(a, b); }); }
 
 constexpr float kL2E = 1.4426950408889634f;
 
