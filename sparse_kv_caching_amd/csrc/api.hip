@@ -34,6 +34,7 @@ struct lola_state {
   float* s;
   float* pend;              // [U][kPend][kD + d] decode folds not yet written to H
   int32_t* npend;           // [U] how many (H proper = H + their terms, in order)
+  mutable bool pend_maybe;  // a decode step ran since the last flush (terms may be held)
   void* ring_k;
   void* ring_v;
   void* cache_k[2];
@@ -173,7 +174,10 @@ int check_read_config(const lola_state* st) {
 
 // H proper everywhere: the decode steps' held-back folds written into H
 hipError_t flush_pending(const lola_state* st, hipStream_t s) {
-  return launch_flush_pending(st->H, st->pend, st->npend, st->U, st->d, s);
+  if (!st->pend_maybe) return hipSuccess;   // nothing can be held
+  const hipError_t e = launch_flush_pending(st->H, st->pend, st->npend, st->U, st->d, s);
+  if (e == hipSuccess) st->pend_maybe = false;
+  return e;
 }
 
 // One token through the decode kernel at position a.n: read, then update;
@@ -181,6 +185,7 @@ hipError_t flush_pending(const lola_state* st, hipStream_t s) {
 // updated state at a.n + 1.
 hipError_t decode_token(lola_state* st, DecodeArgs a, hipStream_t s) {
   hipError_t e;
+  st->pend_maybe = true;
   if (st->ragged) {   // the kernel reads each sequence's position, writes it + 1
     a.npos = st->npos_dev + (size_t)st->npos_cur * st->cfg.batch;
     a.npos_next = st->npos_dev + (size_t)(st->npos_cur ^ 1) * st->cfg.batch;
@@ -595,6 +600,7 @@ int lola_state_reset(lola_state* st, void* stream) {
   if (e == hipSuccess) e = launch_zero_u32((unsigned*)st->dev_err, 1, s);
   if (e == hipSuccess) e = launch_zero_u32((unsigned*)st->npend, U, s);
   if (e != hipSuccess) return hip_fail(st, e, "reset");
+  st->pend_maybe = false;
   set_uniform(st, 0);
   st->poisoned = false;
   st->last = s;
