@@ -28,7 +28,17 @@
  *  - Every call returns a lola_status.  Argument errors leave the state
  *    unchanged.  A failure reported by HIP after work was enqueued marks the
  *    state poisoned: later calls return LOLA_ERR_STATE until
- *    lola_state_import().  lola_last_error() gives a per-thread message.
+ *    lola_state_import() or lola_state_reset().  lola_last_error() gives a
+ *    per-thread message.
+ *  - Input ranges.  bf16 inputs: in the softmax branch of a prefill call V
+ *    is multiplied in fp16 (by weights in [0, 2^8], fp32 accumulation), so
+ *    |v| must stay below 65504 for y to stay finite, and values of magnitude
+ *    below 2^-14 (fp16 subnormals) keep fewer significant bits there.  fp32
+ *    inputs: every MFMA operand is split into fp16 hi + lo, so |q|, |k|, |v|
+ *    and the phi, H and s entries must stay below 65504, and values below
+ *    2^-14 lose relative precision (absolute error <= 2^-25 per split).
+ *    H, s and the outputs are fp32.  The library does not scan the inputs
+ *    for these ranges.
  */
 #ifndef LOLA_H_
 #define LOLA_H_
@@ -85,6 +95,14 @@ int64_t lola_state_tokens(const lola_state* st);
 int lola_prefill_workspace_bytes(const lola_state* st, int T, int C, size_t* bytes);
 
 /* Process T new tokens with chunk length C (LoLA notes §2.6, Eq. (15)).
+ * The serial chain of a call runs each unit on cooperating workgroups that
+ * exchange partial SRE values through memory and must all be resident on
+ * the GPU at once: the library sizes the grid to the device's compute units,
+ * and other work sharing the GPU can delay them.  A wait that exceeds its
+ * bound (see lola_debug_set) ends the chain with a device fault flag; every
+ * later kernel of the call then returns without touching the state, and
+ * lola_state_check() reports LOLA_ERR_STATE (the state must be reset or
+ * imported).
  *   q   [B, Hq, T, d]    k, v  [B, Hkv, T, d]    (cfg->dtype)
  *   out [B, Hq, T, d]    float32 (out_dtype must be LOLA_DTYPE_F32)
  *   ws  device workspace of at least lola_prefill_workspace_bytes(T, C)
@@ -137,7 +155,9 @@ int lola_prefill_sre_map(lola_state* st, const void* q, const void* k, const voi
  * replaces H (prefill, export, import, reset) first applies the held terms
  * in order.  The state every entry point observes is the one of a fold
  * applied at once, bit for bit.
- * Errors: INVALID_ARG, STATE, HIP. */
+ * Errors: INVALID_ARG, STATE, HIP; UNSUPPORTED while the sequences sit at
+ * different positions (lola_state_import_sequence) and window + cache > 128
+ * keys (that combination is not enabled). */
 int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v, void* out,
                      int out_dtype, void* stream);
 
@@ -229,9 +249,15 @@ typedef struct {
  * one by one with lola_state_export_sequence). */
 int lola_state_export(const lola_state* st, lola_state_view* dst, void* stream);
 
-/* Replace the state with `src` (n = src->n).  Checks, on the host, that cache
- * positions are ascending, non-negative and older than the window; returns
- * LOLA_ERR_STATE otherwise.  Clears a poisoned state.  Synchronises stream. */
+/* Replace the state with `src` (n = src->n).  Checks on the host what the
+ * state's composition fixes (LoLA notes §2.7), and returns LOLA_ERR_STATE,
+ * leaving the state unchanged, when one fails:
+ *   - every unit's cache holds min(lambda, max(0, n - eta)) positions,
+ *     ascending, non-negative and older than the window, then -1 padding;
+ *   - s >= 0 and 1^T s = 2 x (max(0, n - eta) - cache count) to 1e-3
+ *     relative (each half of phi sums to one, so a folded pair adds 2);
+ *   - H is finite.
+ * Clears a poisoned state and the device fault flags.  Synchronises stream. */
 int lola_state_import(lola_state* st, const lola_state_view* src, void* stream);
 
 /* Ragged batches.  Every memory of LoLA is per sequence and KV head (LoLA
@@ -250,12 +276,29 @@ int lola_state_import(lola_state* st, const lola_state_view* src, void* stream);
  * UNSUPPORTED and lola_state_tokens returns -1; lola_state_import and
  * lola_state_reset put every sequence at one position again.
  * lola_state_positions writes the B positions to host memory `out`.
+ * Decode with positions that differ needs window + cache <= 128 keys
+ * (UNSUPPORTED otherwise).
  * Import and export synchronise `stream`.
  * Errors: INVALID_ARG (NULL pointers, b out of range), STATE (bad cache
  * positions in src), HIP. */
 int lola_state_import_sequence(lola_state* st, int b, const lola_state_view* src, void* stream);
 int lola_state_export_sequence(const lola_state* st, int b, lola_state_view* dst, void* stream);
 int lola_state_positions(const lola_state* st, int64_t* out);
+
+/* Debug settings of a state (host-side, take effect at the next launch; not
+ * exported, kept across lola_state_reset):
+ *   LOLA_DEBUG_SPIN_LIMIT     polls of one exchange word of the chain before
+ *                             its partner workgroup counts as lost (>= 1;
+ *                             0 restores the default, 2^22);
+ *   LOLA_DEBUG_CHAIN_FAIL_AT  every workgroup of the chain gives up at this
+ *                             exchange step of a call, as if a partner were
+ *                             lost (-1: never, the default).
+ * Both exist to exercise the failure path: the chain sets its device fault
+ * flag and ends, the later kernels of the call return untouched, and
+ * lola_state_check() reports LOLA_ERR_STATE.
+ * Errors: INVALID_ARG (NULL state, unknown key, value out of range). */
+enum { LOLA_DEBUG_SPIN_LIMIT = 0, LOLA_DEBUG_CHAIN_FAIL_AT = 1 };
+int lola_debug_set(lola_state* st, int key, long long value);
 
 /* Text of a status code, and the last error detail of the calling thread. */
 const char* lola_strerror(int status);

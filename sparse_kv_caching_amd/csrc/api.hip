@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -44,6 +46,8 @@ struct lola_state {
   void* W;
   void* WT;                 // W transposed [Hkv, kM, d] (decode operands)
   int* dev_err;             // device error flags (exchange timeouts)
+  int spin_limit;           // exchange polls before a partner counts as lost (lola_debug_set)
+  int fail_at;              // debug: exchange step at which the chain gives up (-1: never)
   int ncu;                  // compute units of the device
   void* own_ws;
   size_t own_ws_bytes;
@@ -138,7 +142,8 @@ int chain_workgroups(int U, int ncu, int d, int lam, int C) {
 int check_state(const lola_state* st) {
   if (!st) return fail(LOLA_ERR_INVALID_ARG, "state is NULL");
   if (st->poisoned)
-    return fail(LOLA_ERR_STATE, "state is poisoned by an earlier HIP failure; import a state");
+    return fail(LOLA_ERR_STATE, "state is poisoned (an earlier HIP failure or a device fault "
+                "flag); import a state or reset it");
   return LOLA_OK;
 }
 
@@ -221,6 +226,53 @@ void advance_positions(lola_state* st) {
   st->npos_cur ^= 1;
 }
 
+// Checks of a state view about to be imported (units of it, position n), on
+// the host (LoLA notes §2.7: the state is the window, the cache, H and s):
+//  * the cache holds gs = min(lam, max(0, n - eta)) pairs: positions
+//    ascending, non-negative and older than the window, then -1 padding;
+//  * s >= 0 and 1^T s = 2 N_fold with N_fold = max(0, n - eta) - gs (each
+//    half of phi sums to one, so every folded pair adds 2), to 1e-3 relative
+//    (fp32 accumulation of the split features);
+//  * H is finite.
+int check_view(const lola_state* st, const lola_state_view* src, size_t units, hipStream_t s) {
+  const size_t d = st->d;
+  const int lam = st->cfg.cache, eta = st->cfg.window;
+  const int64_t n = src->n;
+  const int gs = (int)std::min<int64_t>(lam, std::max<int64_t>(0, n - eta));
+  const int64_t w = std::min<int64_t>(eta, n);
+  std::vector<int32_t> pos(units * (size_t)lam);
+  std::vector<float> sv(units * kD), hv(units * kD * d);
+  hipError_t e = hipSuccess;
+  if (lam > 0) e = hipMemcpyAsync(pos.data(), src->cache_pos, pos.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(sv.data(), src->s, sv.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(hv.data(), src->H, hv.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(LOLA_ERR_HIP, "import: %s", hipGetErrorString(e));
+  const double nfold = (double)(std::max<int64_t>(0, n - eta) - gs);
+  for (size_t u = 0; u < units; ++u) {
+    for (int i = 0; i < lam; ++i) {
+      const int32_t p = pos[u * lam + i];
+      if (i < gs ? (p < 0 || p >= n - w || (i > 0 && p <= pos[u * lam + i - 1])) : p != -1)
+        return fail(LOLA_ERR_STATE, "import: cache positions of unit %zu must be %d ascending "
+                    "positions older than the window, then -1 padding", u, gs);
+    }
+    double sum = 0.0;
+    for (int F = 0; F < kD; ++F) {
+      const float x = sv[u * kD + F];
+      if (!(x >= 0.f) || !std::isfinite(x))
+        return fail(LOLA_ERR_STATE, "import: s of unit %zu has a negative or non-finite entry", u);
+      sum += x;
+    }
+    if (std::fabs(sum - 2.0 * nfold) > 1e-3 * std::max(1.0, 2.0 * nfold))
+      return fail(LOLA_ERR_STATE, "import: 1^T s = %.6g for unit %zu, expected 2 x %.0f folded pairs",
+                  sum, u, nfold);
+    for (size_t i = 0; i < (size_t)kD * d; ++i)
+      if (!std::isfinite(hv[u * kD * d + i]))
+        return fail(LOLA_ERR_STATE, "import: H of unit %zu has a non-finite entry", u);
+  }
+  return LOLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -265,6 +317,8 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
   st->cfg = c;
   st->branches = LOLA_READ_ALL;
   st->order = LOLA_READ_BEFORE_UPDATE;
+  st->spin_limit = kSpinLimit;
+  st->fail_at = -1;
   st->U = c.batch * c.kv_heads;
   st->g = g;
   st->d = c.head_dim;
@@ -353,6 +407,10 @@ int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v
   for (int b = 0; b < st->cfg.batch; ++b)
     if (st->nseq[b] > (int64_t)0x7FFFFFF0) return fail(LOLA_ERR_UNSUPPORTED, "position overflow");
   if ((rc = check_read_config(st))) return rc;
+  if (st->ragged && st->cfg.cache + st->cfg.window > kDecodeOneChunkKeys)
+    return fail(LOLA_ERR_UNSUPPORTED, "sequences at different positions with window + cache = %d "
+                "> %d keys (the chunked decode kernel) are not supported",
+                st->cfg.cache + st->cfg.window, kDecodeOneChunkKeys);
   hipStream_t s = (hipStream_t)stream;
   DecodeArgs a;
   a.q = q; a.k = k; a.v = v; a.WT = st->WT;
@@ -497,6 +555,8 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   ca.j0 = 0;
   ca.j1 = nch;
   ca.xstep0 = 0;
+  ca.spin_limit = st->spin_limit;
+  ca.fail_at = st->fail_at;
   if (ca.k > 1) {
     e = launch_zero_u32((unsigned*)ca.xbuf, (size_t)U * 2 * (d / 32) * (lam + C) * 2, s);
     if (e != hipSuccess) return hip_fail(st, e, "exchange reset");
@@ -504,7 +564,7 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   { ProfScope ps(st, LOLA_KERNEL_CHAIN, s); e = launch_chain(ca, U, st->f32, s); }
   if (e != hipSuccess) return hip_fail(st, e, "chain launch");
   if (snap_pos) {
-    e = launch_snappos(vr, ca.snapG, snap_pos, nch, C, U, s);
+    e = launch_snappos(vr, ca.snapG, snap_pos, nch, C, U, st->dev_err, s);
     if (e != hipSuccess) return hip_fail(st, e, "debug launch");
   }
   if (sre_map) {
@@ -512,6 +572,7 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
     ma.vr = vr; ma.phi_hi = phi_hi; ma.phi_lo = phi_lo; ma.NV = (int)NVs;
     ma.snapHT = ca.snapHT; ma.snaps = ca.snaps; ma.fold = fold_chunk; ma.out = sre_map;
     ma.nch = nch;
+    ma.err = st->dev_err;
     e = launch_sre_map(ma, U, st->f32, s);
     if (e != hipSuccess) return hip_fail(st, e, "diagnostics launch");
   }
@@ -526,6 +587,7 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   aa.ch0 = 0;
   aa.nch_launch = nch;
   aa.branches = st->branches;
+  aa.err = st->dev_err;
   { ProfScope ps(st, LOLA_KERNEL_ATTN, s); e = launch_attn(aa, U, st->f32, s); }
   if (e != hipSuccess) return hip_fail(st, e, "attention launch");
 
@@ -538,6 +600,7 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   fa.ring_k = st->ring_k;
   fa.ring_v = st->ring_v;
   fa.gs_final = gs_final;
+  fa.err = st->dev_err;
   { ProfScope ps(st, LOLA_KERNEL_FINALIZE, s); e = launch_finalize(fa, U, st->f32, s); }
   if (e != hipSuccess) return hip_fail(st, e, "finalize launch");
   st->cur = 1 - st->cur;
@@ -587,6 +650,24 @@ int lola_set_read_order(lola_state* st, int order) {
                 LOLA_READ_BEFORE_UPDATE, LOLA_READ_AFTER_UPDATE);
   st->order = order;
   return LOLA_OK;
+}
+
+int lola_debug_set(lola_state* st, int key, long long value) {
+  if (!st) return fail(LOLA_ERR_INVALID_ARG, "state must be non-NULL");
+  switch (key) {
+    case LOLA_DEBUG_SPIN_LIMIT:
+      if (value < 0 || value > (1LL << 30))
+        return fail(LOLA_ERR_INVALID_ARG, "spin limit %lld out of [0, 2^30]", value);
+      st->spin_limit = value == 0 ? kSpinLimit : (int)value;   // 0: the default
+      return LOLA_OK;
+    case LOLA_DEBUG_CHAIN_FAIL_AT:
+      if (value < -1 || value > (1LL << 30))
+        return fail(LOLA_ERR_INVALID_ARG, "fail-at step %lld out of [-1, 2^30]", value);
+      st->fail_at = (int)value;
+      return LOLA_OK;
+    default:
+      return fail(LOLA_ERR_INVALID_ARG, "unknown debug key %d", key);
+  }
 }
 
 int lola_state_reset(lola_state* st, void* stream) {
@@ -677,22 +758,12 @@ int lola_state_import(lola_state* st, const lola_state_view* src, void* stream) 
   const size_t U = st->U, d = st->d;
   const int lam = st->cfg.cache, eta = st->cfg.window;
   const int gs = (int)std::min<int64_t>(lam, std::max<int64_t>(0, src->n - eta));
-  const int64_t w = std::min<int64_t>(eta, src->n);
-  if (lam > 0) {
-    std::vector<int32_t> pos(U * lam);
-    hipError_t e = hipMemcpyAsync(pos.data(), src->cache_pos, U * lam * 4, hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return fail(LOLA_ERR_HIP, "import: %s", hipGetErrorString(e));
-    for (size_t u = 0; u < U; ++u)
-      for (int i = 0; i < gs; ++i) {
-        const int32_t p = pos[u * lam + i];
-        if (p < 0 || p >= src->n - w || (i > 0 && p <= pos[u * lam + i - 1]))
-          return fail(LOLA_ERR_STATE, "import: cache positions of unit %zu are not ascending "
-                      "and older than the window", u);
-      }
-  }
+  if (int rc = check_view(st, src, U, s)) return rc;
+  // the state is replaced whole: the device fault flags and the held-back
+  // decode folds of the old one go with it
   hipError_t e = launch_transpose_f32(src->H, st->H, (int)U, kD, (int)d, s);
   if (e == hipSuccess) e = launch_zero_u32((unsigned*)st->npend, U, s);
+  if (e == hipSuccess) e = launch_zero_u32((unsigned*)st->dev_err, 1, s);
   if (e == hipSuccess) e = hipMemcpyAsync(st->s, src->s, U * kD * 4, hipMemcpyDeviceToDevice, s);
   if (e == hipSuccess)
     e = launch_import(st->f32, st->U, st->ring_k, st->ring_v, st->cache_k[st->cur],
@@ -720,20 +791,7 @@ int lola_state_import_sequence(lola_state* st, int b, const lola_state_view* src
   const size_t d = st->d, u0 = (size_t)b * Hkv;
   const int lam = st->cfg.cache, eta = st->cfg.window;
   const int gs = (int)std::min<int64_t>(lam, std::max<int64_t>(0, src->n - eta));
-  const int64_t w = std::min<int64_t>(eta, src->n);
-  if (lam > 0) {
-    std::vector<int32_t> pos((size_t)Hkv * lam);
-    hipError_t e = hipMemcpyAsync(pos.data(), src->cache_pos, pos.size() * 4, hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return fail(LOLA_ERR_HIP, "import: %s", hipGetErrorString(e));
-    for (int u = 0; u < Hkv; ++u)
-      for (int i = 0; i < gs; ++i) {
-        const int32_t p = pos[(size_t)u * lam + i];
-        if (p < 0 || p >= src->n - w || (i > 0 && p <= pos[(size_t)u * lam + i - 1]))
-          return fail(LOLA_ERR_STATE, "import: cache positions of head %d are not ascending "
-                      "and older than the window", u);
-      }
-  }
+  if (int rc = check_view(st, src, (size_t)Hkv, s)) return rc;
   const size_t es = st->esz;
   char* rk = (char*)st->ring_k + u0 * eta * d * es;
   char* rv = (char*)st->ring_v + u0 * eta * d * es;

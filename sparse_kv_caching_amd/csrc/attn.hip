@@ -139,6 +139,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   const long long pbase = nj + (long long)pt * a.ptile;
   const long long pend = min(pbase + a.ptile, nj + cj);     // exclusive
   if (pbase >= pend) return;                                // whole block idle (uniform)
+  // the chain gave up: the snapshots were not written (uniform)
+  if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile const int*>(a.err)) != 0) return;
   const int hd = wave / a.nblk, pblk = wave % a.nblk;
   const long long p0 = pbase + 32LL * pblk;
   const bool wactive = hd < a.g && p0 < pend;
@@ -205,7 +207,12 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const float* sj = a.snaps + ((size_t)u * a.nch + j) * kD;
     for (int F = tid; F < kD; F += kThreads) sm_s[F] = sj[F];
     const int32_t* Gj = a.snapG + ((size_t)u * a.nch + j) * lam;
-    for (int i = tid; i < gsj; i += kThreads) sm_G[i] = Gj[i];
+    // (virtual indices, kept inside the call's rows whatever the snapshot holds)
+    const uint32_t nv = (uint32_t)(lam + eta + vr.T);
+    for (int i = tid; i < gsj; i += kThreads) {
+      const uint32_t g = (uint32_t)Gj[i];
+      sm_G[i] = (int32_t)(g < nv ? g : 0u);
+    }
   }
 
   // ---- Q operands (B of S^T = K Q^T): lane = query r, K-slots 8h .. 8h+7
@@ -319,8 +326,11 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   }
   __syncthreads();   // the key tiles reuse the linear-read region
 
-  // ---- explicit branch: key tiles of KT, double-buffered
-  float m2 = 0.f, l = zlin;
+  // ---- explicit branch: key tiles of KT, double-buffered.  The linear
+  // terms enter with logit 0 (weight 2^-m2); without them (state hidden, or
+  // z_lin = 0: an empty state) the running maximum starts at -inf, so that
+  // the weights of very negative logits do not all underflow
+  float m2 = zlin > 0.f ? 0.f : -INFINITY, l = zlin;
   const float scale2 = 1.4426950408889634f / sqrtf((float)HD);
   // cache keys hidden from the read: the key loop starts past them
   const int kbase = (a.branches & LOLA_READ_CACHE) ? 0 : gsj;
@@ -462,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
       // that the accumulators are rarely rescaled
       if (tmax > m2 + kSlack) {
         const float mnew = tmax;
-        const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);
+        const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);   // 0 from m2 = -inf
 #pragma unroll
         for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
@@ -470,12 +480,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         l *= alpha;
         m2 = mnew;
       }
+      // (m2 is still -inf only while every key so far is masked for this
+      // query: its weights are then 0, exp2(-inf))
+      const float msub = m2 == -INFINITY ? 0.f : m2;
       float rs = 0.f;
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          S[kh][i] = __builtin_amdgcn_exp2f(fmaf(S[kh][i], scale2, -m2));
+          S[kh][i] = __builtin_amdgcn_exp2f(fmaf(S[kh][i], scale2, -msub));
           rs += S[kh][i];
         }
       rs = half_sum(rs);

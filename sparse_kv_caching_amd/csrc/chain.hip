@@ -65,7 +65,6 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int HTP = kD + 8;   // padded LDS row of H^T (16-bit elements)
 constexpr int STP = 64 + 8;   // padded LDS row of fold staging tiles (64 tokens)
-constexpr int kSpinLimit = 1 << 22;   // counter polls before an exchange is declared lost
 
 // Byte offsets of the LDS arrays (computed by value so that the kernel's
 // pointers stay plain LDS pointers).  The candidate list, parts, keys and
@@ -149,6 +148,9 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     u = blockIdx.x / k;
     rank = blockIdx.x % k;
   }
+  // a chain that gave up earlier left the state unfinished: nothing to do
+  // (every workgroup reads the same word, so the whole grid returns)
+  if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile const int*>(a.err)) != 0) return;
   const int grp = rank % NG, ch = rank / NG;      // slab group, candidate group
   const bool writer = ch == 0;                    // writes this slab group's columns
   const int col0 = 32 * SPW * grp;                // first H column of this workgroup
@@ -356,7 +358,9 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     // keys = (SRE bits << 32) | (0xFFFFFFFF - position); SRE = slab parts in
     // order (k > 1: read back from the exchange, waiting for each tag)
     uint64_t kmin = ~0ull, kmax = 0;
-    bool lost = false;
+    // (debug: the host can make every workgroup give up at one exchange step,
+    // the same outcome as a lost partner, deterministically)
+    bool lost = xstep - 1 == a.fail_at;
     for (int e = tid; lam > 0 && e < nE; e += kThreads) {
       float sre = 0.f;
       if (k > 1) {
@@ -368,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
         for (int q = 0; q < NSLAB; ++q) {
           int spins = 0;
           while ((uint32_t)(w[q] >> 32) != tag && !lost) {
-            if (++spins > kSpinLimit) lost = true;
+            if (++spins > a.spin_limit) lost = true;
             w[q] = __hip_atomic_load(xb + (size_t)q * LE + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
           sre += __uint_as_float((uint32_t)w[q]);

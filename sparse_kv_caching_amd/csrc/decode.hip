@@ -49,6 +49,7 @@ constexpr size_t kLdsPair = 80 * 1024;    // two workgroups per CU
 constexpr size_t kLdsOne = 160 * 1024;
 
 constexpr int kKC = 32 * kWaves;   // keys per chunk: a 32-key tile per wave
+static_assert(kKC == kDecodeOneChunkKeys, "the host's view of the one-chunk instance");
 
 // phi tiles of 16 rows per chunk: the candidate rows of the chunk, then (last
 // chunk) the new pair when it is a candidate and the g <= 4 query rows
@@ -716,13 +717,17 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
             mx = fmaxf(mx, S[kt][i]);
           }
         mx = qmax(mx);
+        // (a maximum still at -inf means no visible key so far in this wave,
+        // e.g. cache keys hidden from the read: nothing to rescale, and the
+        // weights exp2(-inf - 0) are 0)
 #pragma unroll
         for (int hd = 0; hd < 4; ++hd) {
           const float mn = fmaxf(mrun[hd], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), hd)));
-          alpha[hd] = __builtin_amdgcn_exp2f(mrun[hd] - mn);
+          alpha[hd] = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mrun[hd] - mn);
           mrun[hd] = mn;
         }
-        const float mr = n16 == 0 ? mrun[0] : (n16 == 1 ? mrun[1] : (n16 == 2 ? mrun[2] : mrun[3]));
+        const float mr0 = n16 == 0 ? mrun[0] : (n16 == 1 ? mrun[1] : (n16 == 2 ? mrun[2] : mrun[3]));
+        const float mr = mr0 == -INFINITY ? 0.f : mr0;
         float ls = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -812,7 +817,7 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
         for (int e = 0; e < CPL; ++e) v[e] = DT::to_f32(sm_nv[CPL * lane + e]);
 #pragma unroll
         for (int hd = 0; hd < 4; ++hd) {
-          const float mn = fmaxf(mrun[hd], snew[hd]);
+          const float mn = fmaxf(mrun[hd], snew[hd]);      // finite: the new pair is visible
           const float al = __builtin_amdgcn_exp2f(mrun[hd] - mn);
           const float p = __builtin_amdgcn_exp2f(snew[hd] - mn);
           lrun[hd] = fmaf(lrun[hd], al, p);
@@ -985,11 +990,14 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
     // ---- the outputs: the four waves' partials and the linear read (logit 0)
     for (int i = tid - 64; i < g * HD; i += kThreads - 64) {
       const int hd = i / HD, e = i % HD;
-      float m = 0.f;
+      // the linear read enters with logit 0 unless the state is hidden or
+      // empty (z = 0); without it the maximum is the waves' alone, so that
+      // the weights of very negative logits do not all underflow
+      const bool lin = (a.branches & LOLA_READ_STATE) && sm_zq[hd] > 0.f;
+      float m = lin ? 0.f : -INFINITY;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) m = fmaxf(m, sm_wst[w * 8 + hd]);
-      // the linear read (logit 0), unless the state is hidden from the read
-      const float em = (a.branches & LOLA_READ_STATE) ? __builtin_amdgcn_exp2f(-m) : 0.f;
+      const float em = lin ? __builtin_amdgcn_exp2f(-m) : 0.f;
       float num = em * sm_nlin[hd * HD + e], den = em * sm_zq[hd];
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {

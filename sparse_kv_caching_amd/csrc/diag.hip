@@ -23,6 +23,8 @@ template <class DT, int HD>
 __global__ __launch_bounds__(kThreads) void sre_map_kernel(SreMapArgs a) {
   using T = typename DT::T;
   const VirtRows vr = a.vr;
+  // the chain gave up: the snapshots and fold chunks were not written
+  if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile const int*>(a.err)) != 0) return;
   const int u = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
   const int lam = vr.lam, eta = vr.eta, Tn = vr.T;
   extern __shared__ __align__(16) unsigned char smem[];

@@ -91,6 +91,8 @@ struct ChainArgs {
   int* err;                 // device error flag: bit 0 = an exchange partner was lost
   int j0, j1;               // steps of this launch (a segment of the call's nch)
   int xstep0;               // exchange steps of the call before j0 (tags continue)
+  int spin_limit;           // polls of one exchange word before its partner counts as lost
+  int fail_at;              // debug: exchange step at which every workgroup gives up (-1: never)
 };
 
 // K3: window + cache softmax attention merged with the linear read.
@@ -105,6 +107,7 @@ struct AttnArgs {
   int g, Hkv, nch, C, ptile, nblk;  // positions per WG, 32-position blocks per WG
   int ch0, nch_launch;      // chunks ch0 .. ch0 + nch_launch - 1 in this launch
   int branches;             // read mask, LOLA_READ_* bits (window always set)
+  const int* err;           // device error flags: nonzero = the chain gave up, nothing to read
 };
 
 // Finalize: new cache rows / positions and window ring after a prefill call.
@@ -117,6 +120,7 @@ struct FinalizeArgs {
   void* ring_k;             // written in place
   void* ring_v;
   int gs_final;
+  const int* err;           // device error flags: nonzero = finalG was not written
 };
 
 // Decode step (C = 1) for every unit.
@@ -170,7 +174,14 @@ struct SreMapArgs {
   const int32_t* fold;      // [U, T] chunk that folded each call token, -1 none
   float* out;               // [U, nch, T]
   int nch;
+  const int* err;           // device error flags: nonzero = the snapshots were not written
 };
+
+// Polls of one exchange word before the chain declares its partner lost.
+constexpr int kSpinLimit = 1 << 22;
+// Window + cache keys the one-chunk decode instance holds; more run through
+// the chunked instance.
+constexpr int kDecodeOneChunkKeys = 128;
 
 // launchers (return hipError_t of the launch)
 hipError_t launch_phi(const PhiArgs& a, int U, bool f32, hipStream_t st);
@@ -203,6 +214,6 @@ hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st);
 hipError_t launch_transpose_f32(const float* src, float* dst, int batch, int rows, int cols,
                                 hipStream_t st);
 hipError_t launch_snappos(const VirtRows& vr, const int32_t* snapG, int32_t* out, int nch,
-                          int C, int U, hipStream_t st);
+                          int C, int U, const int* err, hipStream_t st);
 
 }  // namespace lola

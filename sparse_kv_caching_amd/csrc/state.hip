@@ -22,6 +22,8 @@ __device__ void copy_row(T* dst, const T* src, int d) {
 // launches so that every ring row the new cache takes is read before the
 // ring is overwritten.  Rows move as 16-byte pieces, many rows per block.
 __global__ __launch_bounds__(kThreads) void finalize_cache_kernel(FinalizeArgs a, int esz) {
+  // the chain gave up: finalG was not written (the state is poisoned)
+  if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile const int*>(a.err)) != 0) return;
   const VirtRows vr = a.vr;
   const int u = blockIdx.y, lam = vr.lam;
   const int pieces = vr.d * esz / 16;                  // 16-byte pieces per row
@@ -43,6 +45,7 @@ __global__ __launch_bounds__(kThreads) void finalize_cache_kernel(FinalizeArgs a
 }
 
 __global__ __launch_bounds__(kThreads) void finalize_ring_kernel(FinalizeArgs a, int esz) {
+  if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile const int*>(a.err)) != 0) return;
   const VirtRows vr = a.vr;
   const int u = blockIdx.y, eta = vr.eta;
   const long long nend = vr.n0 + vr.T;
@@ -183,7 +186,9 @@ hipError_t launch_import(bool f32, int U, void* ring_k, void* ring_v, void* cach
 }
 
 // positions of the cache at every chunk start (debug export)
-__global__ void snappos_kernel(VirtRows vr, const int32_t* snapG, int32_t* out, int nch, int C) {
+__global__ void snappos_kernel(VirtRows vr, const int32_t* snapG, int32_t* out, int nch, int C,
+                               const int* err) {
+  if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile const int*>(err)) != 0) return;
   const int u = blockIdx.y, j = blockIdx.x;
   const long long nj = vr.n0 + (long long)j * C;
   const int gs = (int)min((long long)vr.lam, max(0LL, nj - vr.eta));
@@ -194,9 +199,9 @@ __global__ void snappos_kernel(VirtRows vr, const int32_t* snapG, int32_t* out, 
 }
 
 hipError_t launch_snappos(const VirtRows& vr, const int32_t* snapG, int32_t* out, int nch,
-                          int C, int U, hipStream_t st) {
+                          int C, int U, const int* err, hipStream_t st) {
   if (U <= 0 || nch <= 0 || vr.lam <= 0) return hipSuccess;
-  hipLaunchKernelGGL(snappos_kernel, dim3(nch, U), dim3(256), 0, st, vr, snapG, out, nch, C);
+  hipLaunchKernelGGL(snappos_kernel, dim3(nch, U), dim3(256), 0, st, vr, snapG, out, nch, C, err);
   return hipGetLastError();
 }
 

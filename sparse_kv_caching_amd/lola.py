@@ -28,6 +28,7 @@ LOLA_DTYPE_BF16 = 1
 KERNELS = ("phi", "chain", "attn", "finalize", "decode")
 READ_STATE, READ_CACHE, READ_WINDOW, READ_ALL = 1, 2, 4, 7   # lola_set_read_branches bits
 READ_BEFORE_UPDATE, READ_AFTER_UPDATE = 0, 1                 # lola_set_read_order
+DEBUG_SPIN_LIMIT, DEBUG_CHAIN_FAIL_AT = 0, 1                 # lola_debug_set keys
 
 EXPORTED = [
     "lola_state_init", "lola_state_free", "lola_state_tokens", "lola_prefill_workspace_bytes",
@@ -93,6 +94,7 @@ def library() -> ctypes.CDLL:
         lib.lola_state_import_sequence.argtypes = [vp, i32, ctypes.POINTER(LolaStateView), vp]
         lib.lola_state_export_sequence.argtypes = [vp, i32, ctypes.POINTER(LolaStateView), vp]
         lib.lola_state_positions.argtypes = [vp, ctypes.POINTER(i64)]
+        lib.lola_debug_set.argtypes = [vp, i32, ctypes.c_longlong]
         lib.lola_strerror.argtypes = [i32]
         lib.lola_strerror.restype = ctypes.c_char_p
         lib.lola_last_error.restype = ctypes.c_char_p
@@ -101,7 +103,7 @@ def library() -> ctypes.CDLL:
                   "lola_state_reset", "lola_state_check", "lola_profile", "lola_state_export",
                   "lola_state_import", "lola_set_read_branches", "lola_set_read_order",
                   "lola_state_import_sequence", "lola_state_export_sequence",
-                  "lola_state_positions", "lola_prefill_sre_map"):
+                  "lola_state_positions", "lola_prefill_sre_map", "lola_debug_set"):
             getattr(lib, f).restype = i32
         _lib = lib
     return _lib
@@ -175,6 +177,12 @@ class LolaLayer:
         """READ_BEFORE_UPDATE (0, the chunk schedule) or READ_AFTER_UPDATE (1,
         the literal token recurrence; decode and C = 1 prefill only)."""
         _check(self.lib.lola_set_read_order(self._st, int(order)), "lola_set_read_order")
+
+    def debug_set(self, key: int, value: int):
+        """lola_debug_set: DEBUG_SPIN_LIMIT (exchange polls before a partner
+        counts as lost; 0 = default) or DEBUG_CHAIN_FAIL_AT (exchange step at
+        which the chain gives up; -1 = never)."""
+        _check(self.lib.lola_debug_set(self._st, int(key), int(value)), "lola_debug_set")
 
     def profile(self, enable: bool):
         """Return {kernel: (ms, launches)} accumulated since the last call and

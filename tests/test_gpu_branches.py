@@ -72,10 +72,13 @@ def test_masks_leave_the_state_bitwise_unchanged():
             assert torch.equal(got[key], ref[key]), (br, key)
 
 
-@pytest.mark.parametrize("branches,eta,lam", [(4, 16, 24), (5, 16, 24), (6, 16, 24), (6, 96, 64)])
+@pytest.mark.parametrize("branches,eta,lam", [(4, 16, 24), (5, 16, 24), (6, 16, 24), (6, 96, 64),
+                                               (4, 16, 64), (5, 16, 64), (5, 96, 64)])
 def test_masked_decode(branches, eta, lam):
     """Decode with masks, through the one-chunk kernel and (lam + eta > 128)
-    the chunked one; outputs per step against the oracle with the same mask."""
+    the chunked one; outputs per step against the oracle with the same mask.
+    With lam >= 32 and the cache hidden, a wave's 32 keys can all be hidden
+    (no visible key in its softmax)."""
     wl = WORKLOADS["decode_b64"].scaled(B=2, Hq=8, Hkv=2, T=192, eta=eta, lam=lam, C=32)
     print("masked decode", branches, wl, flush=True)
     inp = make_inputs(wl)
