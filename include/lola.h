@@ -117,6 +117,22 @@ int lola_prefill_chunk(lola_state* st, const void* q, const void* k, const void*
                        int C, void* out, int out_dtype, void* ws, size_t ws_bytes,
                        void* stream);
 
+/* lola_prefill_chunk for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the workspace is a static device array of the library, 64 MiB
+ * on every GPU it runs on, held until the process ends, so this call makes
+ * no hipMalloc, hipFree or other allocating call (nor timing events of
+ * lola_profile).  Arguments as lola_prefill_chunk, with no ws.
+ * Every call on one GPU shares that GPU's array (it keeps the previous call's
+ * contents; what must start at zero is cleared by a kernel of the call):
+ * calls that overlap in time on one GPU -- other streams, other states, other
+ * threads -- race and must be serialised by the caller.
+ * Errors: as lola_prefill_chunk; WORKSPACE when lola_prefill_workspace_bytes
+ * (T, C) exceeds 64 MiB (the state is then unchanged); HIP when the array's
+ * address could not be found on the state's device. */
+int lola_prefill_chunk_noalloc(lola_state* st, const void* q, const void* k, const void* v,
+                               int T, int C, void* out, int out_dtype, void* stream);
+
 /* lola_prefill_chunk plus a per-chunk record, for parity diagnostics:
  *   snap_pos  [B*Hkv, nch, lambda] int32: positions of the cache at the start
  *             of chunk j (in the chain's order, -1 padding), nch = ceil(T/C);

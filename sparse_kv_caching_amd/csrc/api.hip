@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -53,6 +54,7 @@ struct lola_state {
   size_t own_ws_bytes;
   // optional per-kernel timing with HIP events on the launch stream
   bool prof_on;
+  bool no_alloc_call;       // inside lola_prefill_chunk_noalloc: no timing events
   struct Pending { int kind; hipEvent_t a, b; };
   std::vector<Pending>* prof_pending;
   double prof_ms[LOLA_KERNEL_COUNT];
@@ -88,7 +90,7 @@ struct ProfScope {
   hipStream_t s;
   hipEvent_t a = nullptr, b = nullptr;
   ProfScope(lola_state* st_, int kind_, hipStream_t s_) : st(st_), kind(kind_), s(s_) {
-    if (!st->prof_on) return;
+    if (!st->prof_on || st->no_alloc_call) return;
     hipEventCreate(&a);
     hipEventCreate(&b);
     hipEventRecord(a, s);
@@ -99,6 +101,41 @@ struct ProfScope {
     st->prof_pending->push_back({kind, a, b});
   }
 };
+
+// ---------------------------------------------------------------------------
+// Workspace of lola_prefill_chunk_noalloc: a file-scope device array, one copy
+// per GPU the library runs on, held until the process ends.  Host code never
+// passes `scratch` itself (its name is a host-side stand-in): each device's
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current (at lola_state_init) and kept in scratch_ptr_of.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // per device, nullptr until looked up
+std::vector<int> g_scratch_err;     // per device, the lookup's hipError_t
+
+// Look up (once) the address of `scratch` on the current device, `dev`.
+void scratch_setup(int dev) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (dev < 0) return;
+  if ((size_t)dev >= g_scratch_ptr.size()) {
+    g_scratch_ptr.resize(dev + 1, nullptr);
+    g_scratch_err.resize(dev + 1, -1);
+  }
+  if (g_scratch_ptr[dev]) return;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  g_scratch_err[dev] = (int)e;
+  if (e == hipSuccess) g_scratch_ptr[dev] = p;
+}
+
+void* scratch_ptr_of(int dev, int* err) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (dev < 0 || (size_t)dev >= g_scratch_ptr.size()) { *err = -1; return nullptr; }
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
 
 struct WsLayout {
   size_t phi_hi, phi_lo, snapHT, snaps, snapG, finalG, xbuf, total;
@@ -327,6 +364,7 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
   st->last = (hipStream_t)stream;
   st->prof_pending = new std::vector<lola_state::Pending>();
   hipGetDevice(&st->device);
+  scratch_setup(st->device);     // the no-allocation entry point's workspace on this device
   st->ncu = 0;
   if (hipDeviceGetAttribute(&st->ncu, hipDeviceAttributeMultiprocessorCount, st->device) != hipSuccess ||
       st->ncu < 1)
@@ -613,6 +651,26 @@ int lola_prefill_chunk(lola_state* st, const void* q, const void* k, const void*
                        int C, void* out, int out_dtype, void* ws, size_t ws_bytes,
                        void* stream) {
   return prefill_impl(st, q, k, v, T, C, out, out_dtype, ws, ws_bytes, nullptr, nullptr, stream);
+}
+
+int lola_prefill_chunk_noalloc(lola_state* st, const void* q, const void* k, const void* v,
+                               int T, int C, void* out, int out_dtype, void* stream) {
+  if (!st) return fail(LOLA_ERR_INVALID_ARG, "state is NULL");
+  if (T < 0 || C < 1) return fail(LOLA_ERR_INVALID_ARG, "T >= 0 and C >= 1 required");
+  const size_t need = (T == 0 || C == 1) ? 0 : ws_layout(st, T, C).total;
+  if (need > kScratchBytes)
+    return fail(LOLA_ERR_WORKSPACE, "this call needs %zu bytes of workspace; the static "
+                "workspace of lola_prefill_chunk_noalloc holds %zu", need, kScratchBytes);
+  int err = 0;
+  void* ws = scratch_ptr_of(st->device, &err);
+  if (!ws)
+    return fail(LOLA_ERR_HIP, "no address of the static workspace on device %d (%s)", st->device,
+                err >= 0 ? hipGetErrorString((hipError_t)err) : "not looked up");
+  st->no_alloc_call = true;
+  const int rc = prefill_impl(st, q, k, v, T, C, out, out_dtype, ws, kScratchBytes, nullptr,
+                              nullptr, stream);
+  st->no_alloc_call = false;
+  return rc;
 }
 
 int lola_prefill_debug(lola_state* st, const void* q, const void* k, const void* v, int T,

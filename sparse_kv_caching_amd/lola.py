@@ -95,6 +95,7 @@ def library() -> ctypes.CDLL:
         lib.lola_state_export_sequence.argtypes = [vp, i32, ctypes.POINTER(LolaStateView), vp]
         lib.lola_state_positions.argtypes = [vp, ctypes.POINTER(i64)]
         lib.lola_debug_set.argtypes = [vp, i32, ctypes.c_longlong]
+        lib.lola_prefill_chunk_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp]
         lib.lola_strerror.argtypes = [i32]
         lib.lola_strerror.restype = ctypes.c_char_p
         lib.lola_last_error.restype = ctypes.c_char_p
@@ -103,7 +104,8 @@ def library() -> ctypes.CDLL:
                   "lola_state_reset", "lola_state_check", "lola_profile", "lola_state_export",
                   "lola_state_import", "lola_set_read_branches", "lola_set_read_order",
                   "lola_state_import_sequence", "lola_state_export_sequence",
-                  "lola_state_positions", "lola_prefill_sre_map", "lola_debug_set"):
+                  "lola_state_positions", "lola_prefill_sre_map", "lola_debug_set",
+                  "lola_prefill_chunk_noalloc"):
             getattr(lib, f).restype = i32
         _lib = lib
     return _lib
@@ -215,6 +217,15 @@ class LolaLayer:
         _check(self.lib.lola_prefill_chunk(self._st, _ptr(q), _ptr(k), _ptr(v), T, C, _ptr(out),
                                            LOLA_DTYPE_F32, wsp, wsb, _stream(stream)),
                "lola_prefill_chunk")
+        return out
+
+    def prefill_noalloc(self, q, k, v, C: int, out: torch.Tensor, stream=None) -> torch.Tensor:
+        """lola_prefill_chunk_noalloc: prefill with the library's static
+        workspace (no device allocation by the library); out preallocated."""
+        T = q.shape[2]
+        _check(self.lib.lola_prefill_chunk_noalloc(self._st, _ptr(q), _ptr(k), _ptr(v), T, C,
+                                                   _ptr(out), LOLA_DTYPE_F32, _stream(stream)),
+               "lola_prefill_chunk_noalloc")
         return out
 
     def prefill_debug(self, q, k, v, C: int, stream=None):
