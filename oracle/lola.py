@@ -147,6 +147,18 @@ def select_keep(scores: np.ndarray, pos: np.ndarray, lam: int) -> np.ndarray:
     return keep
 
 
+def _given_keep(E_pos: np.ndarray, keep_pos, lam: int) -> np.ndarray:
+    """Keep mask of an imposed kept set (see _update_chunk): exactly lam
+    candidates of every unit."""
+    keep = np.zeros(E_pos.shape, dtype=bool)
+    for u in range(E_pos.shape[0]):
+        want = np.asarray(sorted(keep_pos[u]), dtype=np.int64)
+        keep[u] = np.isin(E_pos[u], want)
+        if keep[u].sum() != lam or want.size != lam:
+            raise ValueError("unit %d: the kept set must be %d of the candidates" % (u, lam))
+    return keep
+
+
 def boundary_gap(scores: np.ndarray, lam: int) -> np.ndarray:
     """Relative gap (SRE_(lam) - SRE_(lam+1)) / SRE_(lam) at the capacity
     boundary, per unit (scores sorted descending; inf if SRE_(lam) == 0)."""
@@ -272,10 +284,15 @@ def _read_after(st: LolaState, qc: np.ndarray, Wu: np.ndarray,
 
 
 # ---------------------------------------------------------------------- update
-def _update_chunk(st: LolaState, kc: np.ndarray, vc: np.ndarray, Wu: np.ndarray
-                  ) -> ChunkLog:
+def _update_chunk(st: LolaState, kc: np.ndarray, vc: np.ndarray, Wu: np.ndarray,
+                  keep_pos=None) -> ChunkLog:
     """Steps 2-5 of the chunk schedule (candidates, keep-all, SRE, fold,
-    advance).  Mutates ``st``."""
+    advance).  Mutates ``st``.
+
+    ``keep_pos`` (per unit, lam positions of the candidates) replaces the
+    top-lam selection of a scored update by a given kept set: another correct
+    choice at a near-tie of the boundary (the compare rule's band), so that a
+    run can continue along the cache another implementation chose."""
     U, c, d = kc.shape
     n, eta, lam = st.n, st.eta, st.lam
     w = st.win_k.shape[1]
@@ -298,7 +315,8 @@ def _update_chunk(st: LolaState, kc: np.ndarray, vc: np.ndarray, Wu: np.ndarray
     else:
         phE = _phi_units(E_k, Wu)
         scores = sre(phE, E_v, st.H, st.s)                    # before-state
-        keep = select_keep(scores, E_pos, lam)
+        keep = select_keep(scores, E_pos, lam) if keep_pos is None else \
+            _given_keep(E_pos, keep_pos, lam)
         fold = (~keep).astype(F64)
         st.H = st.H + np.matmul((phE * fold[..., None]).transpose(0, 2, 1), E_v)
         st.s = st.s + (phE * fold[..., None]).sum(axis=1)
@@ -331,7 +349,8 @@ def _as_units(q, k, v, W, Hkv):
 
 def prefill(st: LolaState, q, k, v, W, C: int, *, outputs: bool = True,
             logs: Optional[List[ChunkLog]] = None,
-            branches: int = BRANCH_ALL, order: str = "before") -> Optional[np.ndarray]:
+            branches: int = BRANCH_ALL, order: str = "before",
+            keep=None) -> Optional[np.ndarray]:
     """Process T new tokens with chunk length C (the last chunk may be short).
 
     q (B, Hq, T, d); k, v (B, Hkv, T, d); W (Hkv, d, m); ``st`` holds U = B*Hkv
@@ -341,7 +360,9 @@ def prefill(st: LolaState, q, k, v, W, C: int, *, outputs: bool = True,
     the same for every mask.  ``order``: "before" (the chunk schedule, LoLA
     notes §2.6: the chunk's queries read the state at chunk start) or "after"
     (the literal token recurrence, §2.4-§2.5: with C = 1, token t's query
-    reads the state after token t's update).
+    reads the state after token t's update).  ``keep``: for a call of one
+    chunk (T <= C), the kept set to impose if its update is scored (per
+    unit, lam positions; see _update_chunk).
     """
     if C < 1:
         raise ValueError("C must be >= 1")
@@ -359,6 +380,8 @@ def prefill(st: LolaState, q, k, v, W, C: int, *, outputs: bool = True,
     U, g, T, d = qu.shape
     if st.H.shape[0] != U:
         raise ValueError("state unit count does not match the inputs")
+    if keep is not None and T > C:
+        raise ValueError("an imposed kept set applies to a call of one chunk")
     y = np.zeros(qu.shape) if outputs else None
     t0 = 0
     while t0 < T:
@@ -366,7 +389,7 @@ def prefill(st: LolaState, q, k, v, W, C: int, *, outputs: bool = True,
         sl = slice(t0, t0 + c)
         if outputs and order == "before":
             y[:, :, sl] = _read_chunk(st, qu[:, :, sl], ku[:, sl], vu[:, sl], Wu, branches)
-        lg = _update_chunk(st, ku[:, sl], vu[:, sl], Wu)
+        lg = _update_chunk(st, ku[:, sl], vu[:, sl], Wu, keep)
         if outputs and order == "after":
             y[:, :, sl] = _read_after(st, qu[:, :, sl], Wu, branches)
         if logs is not None:

@@ -21,6 +21,18 @@ Recipe:
   ``plant="uniform"`` takes p_i = floor((i + 1/2) P / N).
 * Decode steps draw fresh q (B, Hq, d), k, v (B, Hkv, d) from
   ``default_rng([seed, 1_000_000 + step])``.
+* Parity stress inputs (``keys`` other than "iid"; the workloads above are
+  all "iid") replace k and v: the centres or pairs come from
+  ``default_rng([seed, 7])``, each token's choice and noise from
+  ``default_rng([seed, 8])``:
+  "clustered": per (sequence, KV head) 16 centres c_j ~ N(0, 1) and 16 value
+  rows m_j ~ N(0, 1); token t takes a uniform cluster z_t and
+  k_t = c_{z_t} + 0.1 n_t, v_t = m_{z_t} + 0.1 n'_t (n, n' ~ N(0, 1)), so the
+  values are predictable from the keys;
+  "pool": per (sequence, KV head) 6 pairs (k, v) ~ N(0, 1), and token t takes
+  pair p_t uniform in 0..5: exact duplicate pairs, so candidates tie exactly.
+  Decode steps of these workloads draw their k, v the same way, the choice
+  and noise from ``default_rng([seed, 2_000_000 + step])``.
 """
 
 from __future__ import annotations
@@ -48,6 +60,7 @@ class Workload:
     planted: int = 0
     plant: str = "none"
     decode_steps: int = 0
+    keys: str = "iid"     # "iid", or the stress structures "clustered", "pool"
 
     @property
     def D(self) -> int:
@@ -137,6 +150,30 @@ def planted_positions(wl: Workload, rng: Optional[np.random.Generator]) -> np.nd
                     ).astype(np.int64)
 
 
+def _structure(wl: Workload):
+    """Centres (or pairs) of a stress structure: (Hk, Hv), each (B, Hkv, n, d)."""
+    rng = np.random.default_rng([wl.seed, 7])
+    n = 16 if wl.keys == "clustered" else 6
+    return (rng.standard_normal((wl.B, wl.Hkv, n, wl.d), dtype=np.float32),
+            rng.standard_normal((wl.B, wl.Hkv, n, wl.d), dtype=np.float32))
+
+
+def _structured_kv(wl: Workload, rng: np.random.Generator, T: int):
+    """k, v (B, Hkv, T, d) float32 of a stress structure."""
+    ck, cv = _structure(wl)
+    n = ck.shape[2]
+    z = rng.integers(0, n, size=(wl.B, wl.Hkv, T))
+    bi = np.arange(wl.B)[:, None, None]
+    hi = np.arange(wl.Hkv)[None, :, None]
+    k, v = ck[bi, hi, z], cv[bi, hi, z]
+    if wl.keys == "clustered":
+        k = k + np.float32(0.1) * rng.standard_normal(k.shape, dtype=np.float32)
+        v = v + np.float32(0.1) * rng.standard_normal(v.shape, dtype=np.float32)
+    elif wl.keys != "pool":
+        raise ValueError("unknown key structure %r" % wl.keys)
+    return np.ascontiguousarray(k), np.ascontiguousarray(v)
+
+
 def make_inputs(wl: Workload, with_q: bool = True) -> Inputs:
     """Draw the prefill inputs of a workload (see the module docstring).
 
@@ -149,6 +186,8 @@ def make_inputs(wl: Workload, with_q: bool = True) -> Inputs:
     pp = planted_positions(wl, rng)
     W = np.random.default_rng(wl.seed + 100).standard_normal(
         (wl.Hkv, wl.d, wl.m), dtype=np.float32) * np.float32(1.0 / np.sqrt(wl.d))
+    if wl.keys != "iid":
+        k, v = _structured_kv(wl, np.random.default_rng([wl.seed, 8]), wl.T)
     ks = _store(wl, k)
     del k
     vs = _store(wl, v)
@@ -172,6 +211,9 @@ def decode_inputs(wl: Workload, step: int):
     q = rng.standard_normal((wl.B, wl.Hq, wl.d), dtype=np.float32)
     k = rng.standard_normal((wl.B, wl.Hkv, wl.d), dtype=np.float32)
     v = rng.standard_normal((wl.B, wl.Hkv, wl.d), dtype=np.float32)
+    if wl.keys != "iid":
+        k, v = _structured_kv(wl, np.random.default_rng([wl.seed, 2_000_000 + step]), 1)
+        k, v = k[:, :, 0], v[:, :, 0]
     return _store(wl, q), _store(wl, k), _store(wl, v)
 
 

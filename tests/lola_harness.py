@@ -112,6 +112,63 @@ def membership(log: O.ChunkLog, gpu_sets, lam: int, rel: float = BAND):
     return exact, allowed, bad, msgs
 
 
+def decode_keys(keys: np.ndarray):
+    """Candidate keys of the debug record, (SRE bits << 32) | (0xFFFFFFFF -
+    position) as int64 patterns -> (SRE float32, position int64)."""
+    k = np.asarray(keys).view(np.uint64)
+    sre = (k >> np.uint64(32)).astype(np.uint32).view(np.float32)
+    pos = (np.uint64(0xFFFFFFFF) - (k & np.uint64(0xFFFFFFFF))).astype(np.int64)
+    return sre, pos
+
+
+def sre_check(log: O.ChunkLog, keys_units: np.ndarray, gpu_kept, lam: int):
+    """Compare the GPU's SRE of every candidate of one scored update with the
+    oracle's.  keys_units (units, >= nE) are the GPU's keys in its candidate
+    order; gpu_kept the positions it kept.  Checks: the GPU scored exactly
+    the oracle's candidates (positions, bit-exact); returns the largest
+    relative SRE difference.  Also checks the tie rule on the GPU's own
+    values: among candidates whose SRE is bitwise equal and split by the
+    capacity boundary, every kept one is older than every folded one."""
+    worst = 0.0
+    nties = 0
+    for u in range(log.cand_pos.shape[0]):
+        pos_o = log.cand_pos[u]
+        nE = pos_o.size
+        sre_g, pos_g = decode_keys(keys_units[u, :nE])
+        assert np.array_equal(np.sort(pos_g), np.sort(pos_o)), "unit %d: candidate sets differ" % u
+        og = np.argsort(pos_g)
+        oo = np.argsort(pos_o)
+        a = sre_g[og].astype(np.float64)
+        b = log.sre[u][oo]
+        rel = np.abs(a - b) / np.maximum(b, 1e-30)
+        worst = max(worst, float(rel.max()))
+        kept = np.isin(pos_g, np.asarray(sorted(gpu_kept[u]), dtype=np.int64))
+        bits = sre_g.view(np.uint32)
+        for val in np.unique(bits):
+            grp = bits == val
+            if grp.sum() > 1 and kept[grp].any() and (~kept[grp]).any():
+                nties += 1
+                assert pos_g[grp & kept].max() < pos_g[grp & ~kept].min(), \
+                    "unit %d: a tie at the boundary kept a newer position" % u
+    return worst, nties
+
+
+def rel_cols(a: np.ndarray, b: np.ndarray) -> float:
+    """max over units u and columns c of ||a[u,:,c] - b[u,:,c]|| / ||b[u,:,c]||
+    (H (U, D, d)): a wrong column slab shows here even when the whole
+    matrix's norm hides it."""
+    num = np.linalg.norm(a - b, axis=1)
+    den = np.linalg.norm(b, axis=1)
+    return float(np.max(np.where(den > 0, num / np.maximum(den, 1e-300), num))) if a.size else 0.0
+
+
+def rel_elem(a: np.ndarray, b: np.ndarray) -> float:
+    """max |a - b| / |b| elementwise, absolute where b == 0 (s (U, D))."""
+    d = np.abs(a - b)
+    m = np.abs(b)
+    return float(np.max(np.where(m > 0, d / np.maximum(m, 1e-300), d))) if a.size else 0.0
+
+
 def row_rel_err(y_gpu: np.ndarray, y_ref: np.ndarray) -> np.ndarray:
     """||dy||_2 / ||y||_2 per output row (last axis)."""
     num = np.linalg.norm(y_gpu - y_ref, axis=-1)

@@ -17,7 +17,7 @@ from sparse_kv_caching_amd.workloads import (WORKLOADS, bf16_bits, decode_inputs
 
 from lola_harness import dev, gpu_state, make_layer, membership, rel_fro, row_rel_err
 
-from test_gpu_parity import _full_size_single_call, _tol
+from test_gpu_parity import _full_size_single_call, _tol, check_state, new_stats
 
 pytestmark = pytest.mark.gpu
 
@@ -46,10 +46,11 @@ def _subset(st: O.LolaState, units, wl):
 @pytest.mark.timeout(900)
 def test_full_size_decode_b64():
     """64 sequences x 8 KV heads after a 4096-token prefill (eta = lambda = 64,
-    C = 64), then decode steps of fresh tokens for every sequence.  The prefill
-    state is checked through its invariants; each decode step is compared with
-    the oracle run from the GPU's previous state on sequences 0, 31 and 63
-    (outputs, eviction by the argmin rule, H and s)."""
+    C = 64), then decode steps of fresh tokens for every sequence; each step
+    compared with the oracle run from the GPU's previous state on sequences
+    0, 31 and 63 (outputs, eviction by the argmin rule, window and cache
+    exact, H per column, s per element).  The prefill itself is followed chunk
+    by chunk in test_gpu_stress.test_one_workgroup_per_unit_decode_prefill."""
     wl = WORKLOADS["decode_b64"]
     inp = make_inputs(wl, with_q=False)
     layer = make_layer(wl, inp.W)
@@ -58,42 +59,32 @@ def test_full_size_decode_b64():
     layer.prefill(q0, k, v, wl.C)
     del q0, k, v
     st = gpu_state(layer, wl)
-    # prefill invariants on every unit: window and cache rows are exact input
-    # rows, 1^T s = 2 N_fold, and H, s are the sums over the folded set (sampled)
-    kk = to_f64(wl, inp.k).reshape(wl.units, wl.T, wl.d)
-    vv = to_f64(wl, inp.v).reshape(wl.units, wl.T, wl.d)
-    n = wl.T
-    np.testing.assert_array_equal(st.win_k, kk[:, n - wl.eta:])
-    for u in range(wl.units):
-        np.testing.assert_array_equal(st.g_k[u], kk[u, st.g_pos[u]])
-        np.testing.assert_array_equal(st.g_v[u], vv[u, st.g_pos[u]])
-    np.testing.assert_allclose(st.s.sum(axis=1), 2 * (n - wl.eta - wl.lam), rtol=1e-5)
     Wf = inp.f64("W")
     tol = _tol(wl)
-    for u in range(0, wl.units, 37):
-        folded = np.setdiff1d(np.arange(n - wl.eta), st.g_pos[u])
-        f = O.phi(kk[u, folded], Wf[u % wl.Hkv])
-        assert np.linalg.norm(st.H[u] - f.T @ vv[u, folded]) / np.linalg.norm(f.T @ vv[u, folded]) <= tol
-    del kk, vv
     bsel = [0, 31, 63]
     units = [b * wl.Hkv + h for b in bsel for h in range(wl.Hkv)]
-    sub = wl.scaled(B=len(bsel))
-    stats = dict(exact=0, allowed=0)
+    stats = new_stats()
     for step in range(12):
         q, kn, vn = decode_inputs(wl, step)
         yg = layer.decode(dev(wl, q), dev(wl, kn), dev(wl, vn)).cpu().numpy().astype(np.float64)
         ost = _subset(st, units, wl)
+        pre = ost.copy()
         logs = []
         yo = O.decode_step(ost, to_f64(wl, q[bsel]), to_f64(wl, kn[bsel]), to_f64(wl, vn[bsel]), Wf,
                            logs=logs)
         assert row_rel_err(yg[bsel], yo).max() <= tol, step
         st = gpu_state(layer, wl)
         gsub = _subset(st, units, wl)
-        ex, al, bad, msgs = membership(logs[0], [set(g.tolist()) for g in gsub.g_pos], wl.lam)
+        gsets = [set(g.tolist()) for g in gsub.g_pos]
+        ex, al, bad, msgs = membership(logs[0], gsets, wl.lam)
         assert bad == 0, (step, msgs[:3])
+        stats["chunks"] += 1
         stats["exact"] += ex
-        stats["allowed"] += al
-        assert rel_fro(gsub.H, ost.H) <= tol and rel_fro(gsub.s, ost.s) <= tol, step
-        np.testing.assert_array_equal(gsub.win_k, ost.win_k)
-    print(stats)
+        if al:
+            stats["flips"] += al
+            ost = pre
+            O.prefill(ost, to_f64(wl, q[bsel])[:, :, None], to_f64(wl, kn[bsel])[:, :, None],
+                      to_f64(wl, vn[bsel])[:, :, None], Wf, 1, keep=gsets, outputs=False)
+        check_state(gsub, ost, tol, stats)
+    print("PARITY decode_b64", stats, flush=True)
     layer.free()

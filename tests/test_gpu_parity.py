@@ -14,14 +14,18 @@ import torch
 from oracle import lola as O
 from sparse_kv_caching_amd.workloads import WORKLOADS, Workload, make_inputs, to_f64
 
-from lola_harness import (dev, gpu_state, make_layer, membership, put_state, rel_fro,
-                          row_rel_err, slice_tokens)
+from lola_harness import (BAND, dev, gpu_state, make_layer, membership, put_state, rel_cols,
+                          rel_elem, rel_fro, row_rel_err, slice_tokens, sre_check)
 
 pytestmark = pytest.mark.gpu
 
 
 def _tol(wl):
     return 1e-5 if wl.dtype == "f32" else 2e-3
+
+
+def tdt(wl):
+    return torch.bfloat16 if wl.dtype == "bf16" else torch.float32
 
 
 def _oracle_inputs(inp):
@@ -33,10 +37,85 @@ def _units_y(wl, y):
     return y.reshape(wl.B, wl.Hkv, wl.g, y.shape[2], wl.d).reshape(wl.units, wl.g, y.shape[2], wl.d)
 
 
-def run_lockstep(wl: Workload, C=None, T_calls=None, check_continuous=True):
-    """Call the library one chunk at a time (T = C per call, or the given call
-    lengths), export its state after each call, and compare with the oracle
-    run from the GPU's previous state (resync every call).  Returns stats."""
+SRE_TOL = 2e-5      # relative difference of the GPU's SRE to the oracle's
+
+
+def new_stats():
+    return dict(chunks=0, scored=0, exact=0, flips=0, sre_max=0.0, ties=0, near=0, y_max=0.0,
+                H_max=0.0, Hcol_max=0.0, s_max=0.0)
+
+
+def follow_call(st, wl, qf, kf, vf, Wf, C, snap, keys, final_sets, stats, outputs=True,
+                strict=False):
+    """Step the oracle through one GPU call, chunk by chunk, against the GPU's
+    debug record of it (units = the compared ones, in order).
+
+    st: oracle state at the call start; qf, kf, vf: the call's inputs (float64,
+    compared sequences only); snap (units, nch, lam): the GPU's cache positions
+    at every chunk start; keys (units, nch, lam + C): its candidate keys;
+    final_sets: the positions it keeps after the call.  At every chunk start
+    the GPU's cache must equal the oracle's; after every scored update the
+    membership follows the compare rule (strict: bit-exact), the SRE of every
+    candidate agrees to SRE_TOL and the GPU's tie rule holds; at an allowed
+    near-tie flip the oracle continues along the GPU's kept set.  Returns the
+    oracle outputs (or None)."""
+    T = kf.shape[2]
+    nch = (T + C - 1) // C
+    units = kf.shape[0] * kf.shape[1]
+    ys = []
+    for j in range(nch):
+        t0, t1 = j * C, min(T, (j + 1) * C)
+        gs = st.g_pos.shape[1]
+        for i in range(units):
+            assert set(snap[i, j, :gs].tolist()) == set(st.g_pos[i].tolist()), (j, i)
+        pre = st.copy()
+        logs = []
+        sl = slice(t0, t1)
+        y = O.prefill(st, qf[:, :, sl], kf[:, :, sl], vf[:, :, sl], Wf, C, logs=logs,
+                      outputs=outputs)
+        ys.append(y)
+        lg = logs[0]
+        gs1 = st.g_pos.shape[1]
+        nxt = ([set(snap[i, j + 1, :gs1].tolist()) for i in range(units)] if j + 1 < nch
+               else final_sets)
+        ex, al, bad, msgs = membership(lg, nxt, wl.lam)
+        assert bad == 0, (j, msgs[:4])
+        assert not (strict and al), (j, "a flip where the tie rule fixes the set")
+        stats["chunks"] += 1
+        stats["exact"] += ex
+        if lg.sre is not None and wl.lam > 0:
+            stats["scored"] += 1
+            worst, nties = sre_check(lg, keys[:, j], nxt, wl.lam)
+            stats["sre_max"] = max(stats["sre_max"], worst)
+            stats["ties"] += nties
+            stats["near"] += int(np.sum(lg.gap < BAND))
+            assert worst <= SRE_TOL, (j, worst)
+        if al:
+            stats["flips"] += al
+            st.__dict__.update(pre.__dict__)
+            O.prefill(st, qf[:, :, sl], kf[:, :, sl], vf[:, :, sl], Wf, C, keep=nxt,
+                      outputs=False)
+    return np.concatenate(ys, axis=2) if outputs else None
+
+
+def check_state(gst, st, tol, stats):
+    """GPU state (exported) against the oracle's: window and cache rows
+    bit-exact, H per unit (Frobenius) and per column, s per element."""
+    np.testing.assert_array_equal(gst.win_k, st.win_k)
+    np.testing.assert_array_equal(gst.win_v, st.win_v)
+    np.testing.assert_array_equal(gst.g_pos, st.g_pos)
+    np.testing.assert_array_equal(gst.g_k, st.g_k)
+    eH, eC, es = rel_fro(gst.H, st.H), rel_cols(gst.H, st.H), rel_elem(gst.s, st.s)
+    stats["H_max"] = max(stats["H_max"], eH)
+    stats["Hcol_max"] = max(stats["Hcol_max"], eC)
+    stats["s_max"] = max(stats["s_max"], es)
+    assert eH <= tol and eC <= tol and es <= tol, (eH, eC, es)
+
+
+def run_lockstep(wl: Workload, C=None, T_calls=None, check_continuous=True, strict=False):
+    """Call the library once per call length (one chunk each unless given),
+    with its debug record, and follow every chunk with the oracle; after each
+    call compare the exported state and resync the oracle from it."""
     print("lockstep", wl, flush=True)
     inp = make_inputs(wl)
     qf, kf, vf, Wf = _oracle_inputs(inp)
@@ -45,7 +124,8 @@ def run_lockstep(wl: Workload, C=None, T_calls=None, check_continuous=True):
     tol = _tol(wl)
     st = O.new_state(wl.units, wl.d, wl.D, wl.eta, wl.lam)
     cont = O.new_state(wl.units, wl.d, wl.D, wl.eta, wl.lam)
-    stats = dict(exact=0, allowed=0, bad=0, max_y=0.0, max_H=0.0, max_s=0.0, cont_y=0.0)
+    stats = new_stats()
+    stats["cont_y"] = 0.0
     calls = T_calls or [C] * ((wl.T + C - 1) // C)
     t0 = 0
     for tc in calls:
@@ -53,38 +133,26 @@ def run_lockstep(wl: Workload, C=None, T_calls=None, check_continuous=True):
         q = dev(wl, slice_tokens(inp.q, t0, t1))
         k = dev(wl, slice_tokens(inp.k, t0, t1))
         v = dev(wl, slice_tokens(inp.v, t0, t1))
-        yg = layer.prefill(q, k, v, C).cpu().numpy().astype(np.float64)
-        logs = []
-        yo = O.prefill(st, qf[:, :, t0:t1], kf[:, :, t0:t1], vf[:, :, t0:t1], Wf, C, logs=logs)
-        yc = O.prefill(cont, qf[:, :, t0:t1], kf[:, :, t0:t1], vf[:, :, t0:t1], Wf, C)
-        e = row_rel_err(yg, yo)
-        stats["max_y"] = max(stats["max_y"], float(e.max()))
-        assert e.max() <= tol, "output rows off at tokens [%d, %d): max %.3g" % (t0, t1, e.max())
+        yg, snap, keys = layer.prefill_debug(q, k, v, C)
+        yg = yg.cpu().numpy().astype(np.float64)
+        snap, keys = snap.cpu().numpy(), keys.cpu().numpy()
         gst = gpu_state(layer, wl)
+        sl = slice(t0, t1)
+        yc = O.prefill(cont, qf[:, :, sl], kf[:, :, sl], vf[:, :, sl], Wf, C)
+        yo = follow_call(st, wl, qf[:, :, sl], kf[:, :, sl], vf[:, :, sl], Wf, C, snap, keys,
+                         [set(g.tolist()) for g in gst.g_pos], stats, strict=strict)
+        e = row_rel_err(yg, yo)
+        stats["y_max"] = max(stats["y_max"], float(e.max()))
+        assert e.max() <= tol, "output rows off at tokens [%d, %d): max %.3g" % (t0, t1, e.max())
         assert gst.n == st.n == t1
-        # membership: the oracle's last update against the GPU's cache now
-        for lg in logs[-1:]:
-            ex, al, bad, msgs = membership(lg, [set(g.tolist()) for g in gst.g_pos], wl.lam)
-            stats["exact"] += ex
-            stats["allowed"] += al
-            stats["bad"] += bad
-            assert bad == 0, msgs[:4]
-        # window pairs and cache pairs are bit-exact copies of the inputs
-        np.testing.assert_array_equal(gst.win_k, st.win_k)
-        np.testing.assert_array_equal(gst.win_v, st.win_v)
-        if stats["allowed"] == 0:
-            np.testing.assert_array_equal(gst.g_k, st.g_k)
-        eH, es = rel_fro(gst.H, st.H), rel_fro(gst.s, st.s)
-        stats["max_H"] = max(stats["max_H"], eH)
-        stats["max_s"] = max(stats["max_s"], es)
-        assert eH <= tol and es <= tol, (eH, es)
-        if check_continuous and stats["allowed"] == 0:
+        check_state(gst, st, tol, stats)
+        if check_continuous and stats["flips"] == 0:
             stats["cont_y"] = max(stats["cont_y"], float(row_rel_err(yg, yc).max()))
         st = gst                      # resync: the oracle continues from the GPU state
         t0 = t1
     layer.free()
-    print(stats, flush=True)
-    if check_continuous and stats["allowed"] == 0:
+    print("PARITY", wl.name, wl.keys, stats, flush=True)
+    if check_continuous and stats["flips"] == 0:
         assert stats["cont_y"] <= tol
     return stats
 
@@ -93,7 +161,7 @@ def test_tiny_fp32_lockstep():
     """The tiny fp32 workload at its full size: 1 head, d = 64, T = 512,
     eta = lam = C = 64, 8 planted pairs; tolerance 1e-5."""
     s = run_lockstep(WORKLOADS["tiny_fp32"])
-    assert s["exact"] + s["allowed"] > 0
+    assert s["scored"] > 0 and s["chunks"] == 8
 
 
 def test_bf16_lockstep_gqa_ragged():
@@ -137,64 +205,57 @@ def test_short_call_and_empty():
 
 def test_full_size_llama8b_single_call():
     """The Llama-3-8B-shaped layer prefill at its full size, one call with the
-    launch configuration the benchmark times.  Per chunk: the GPU's cache at
-    chunk start (debug record) equals the oracle's, and every output row
-    matches, up to the first allowed near-tie flip.  At the end, properties
-    that hold whatever flips occurred: window and cache rows are exact input
-    rows; 1^T s = 2 N_fold; H and s equal the sums over the GPU's own folded
-    set."""
-    wl = WORKLOADS["llama8b_4k"]
-    _full_size_single_call(wl, units=None)
+    launch configuration the benchmark times, every chunk compared (see
+    _full_size_single_call)."""
+    _full_size_single_call(WORKLOADS["llama8b_4k"], units=None)
 
 
-def _full_size_single_call(wl, units=None):
+def _full_size_single_call(wl, units=None, q_zero=False):
+    """One lola_prefill_debug call over the whole workload; the oracle follows
+    every chunk on the sequences ``units`` (all by default): the cache at every
+    chunk start, membership and SRE of every scored update, outputs (unless
+    q is zero: then the outputs of the compared rows are still checked), and
+    the final state (window, cache, H per column, s per element).  At an
+    allowed near-tie flip the oracle continues along the GPU's kept set, so
+    every chunk is compared.  Then properties of the final state that hold for
+    every unit whatever flips occurred."""
     print("full size", wl, flush=True)
-    inp = make_inputs(wl)
+    inp = make_inputs(wl, with_q=not q_zero)
     layer = make_layer(wl, inp.W)
-    q, k, v = dev(wl, inp.q), dev(wl, inp.k), dev(wl, inp.v)
+    k, v = dev(wl, inp.k), dev(wl, inp.v)
+    if q_zero:
+        q = torch.zeros((wl.B, wl.Hq, wl.T, wl.d), dtype=tdt(wl), device="cuda")
+    else:
+        q = dev(wl, inp.q)
     yg, snap, keys = layer.prefill_debug(q, k, v, wl.C)
-    torch.cuda.synchronize()
-    yg = _units_y(wl, yg.cpu().numpy().astype(np.float64))
-    snap = snap.cpu().numpy()
-    gst = gpu_state(layer, wl)
-    layer.free()
-    # oracle on a subset of sequences (units are independent)
+    del q
     bsel = list(range(wl.B)) if units is None else units
+    ust = [b * wl.Hkv + h for b in bsel for h in range(wl.Hkv)]
+    yg = yg[bsel].cpu().numpy().astype(np.float64)
+    snap = snap[ust].cpu().numpy()
+    keys = keys[ust].cpu().numpy()
+    gall = gpu_state(layer, wl)
+    layer.free()
     sub = wl.scaled(B=len(bsel))
-    qf = to_f64(wl, inp.q[bsel])
+    qf = (np.zeros((len(bsel), wl.Hq, wl.T, wl.d)) if q_zero else to_f64(wl, inp.q[bsel]))
     kf = to_f64(wl, inp.k[bsel])
     vf = to_f64(wl, inp.v[bsel])
     Wf = inp.f64("W")
-    ust = [b * wl.Hkv + h for b in bsel for h in range(wl.Hkv)]
     st = O.new_state(sub.units, wl.d, wl.D, wl.eta, wl.lam)
     tol = _tol(wl)
-    diverged = False
-    chunks_checked = 0
-    for j, t0 in enumerate(range(0, wl.T, wl.C)):
-        t1 = min(wl.T, t0 + wl.C)
-        gs = st.g_pos.shape[1]
-        gpu_sets = [set(snap[u, j, :gs].tolist()) for u in ust]
-        if any(gset != set(st.g_pos[i].tolist()) for i, gset in enumerate(gpu_sets)):
-            diverged = True
-            break
-        logs = []
-        yo = O.prefill(st, qf[:, :, t0:t1], kf[:, :, t0:t1], vf[:, :, t0:t1], Wf, wl.C, logs=logs)
-        yo = _units_y(sub, yo)
-        e = row_rel_err(yg[ust][:, :, t0:t1], yo)
-        assert e.max() <= tol, "chunk %d rows off: %.3g" % (j, e.max())
-        chunks_checked += 1
-        if j + 1 < snap.shape[1]:
-            gs1 = st.g_pos.shape[1]
-            ex, al, bad, msgs = membership(logs[0], [set(snap[u, j + 1, :gs1].tolist()) for u in ust],
-                                           wl.lam)
-            assert bad == 0, msgs[:4]
-            if al:
-                diverged = True
-                break
-    print("chunks compared exactly: %d, diverged by an allowed flip: %s" % (chunks_checked, diverged),
-          flush=True)
-    assert chunks_checked >= 1
-    # -- final-state properties (whatever flips occurred)
+    stats = new_stats()
+    final_sets = [set(gall.g_pos[u].tolist()) for u in ust]
+    yo = follow_call(st, sub, qf, kf, vf, Wf, wl.C, snap, keys, final_sets, stats)
+    e = row_rel_err(yg, yo)
+    stats["y_max"] = float(e.max())
+    assert e.max() <= tol, e.max()
+    gsub = O.import_state({kk: (vv[ust] if isinstance(vv, np.ndarray) and vv.ndim >= 1 else vv)
+                           for kk, vv in O.export_state(gall).items()}, wl.eta, wl.lam)
+    check_state(gsub, st, tol, stats)
+    print("PARITY", wl.name, "units", len(ust), stats, flush=True)
+    assert stats["chunks"] == (wl.T + wl.C - 1) // wl.C
+    # -- final-state properties on every unit (whatever flips occurred)
+    gst = gall
     n = wl.T
     kk = to_f64(wl, inp.k).reshape(wl.units, wl.T, wl.d)
     vv = to_f64(wl, inp.v).reshape(wl.units, wl.T, wl.d)
@@ -205,19 +266,22 @@ def _full_size_single_call(wl, units=None):
         np.testing.assert_array_equal(gst.g_v[u], vv[u, gst.g_pos[u]])
     n_fold = n - wl.eta - wl.lam
     np.testing.assert_allclose(gst.s.sum(axis=1), 2 * n_fold, rtol=1e-5)
-    Wf = inp.f64("W")
     for u in (list(range(wl.units)) if wl.units <= 8 else list(range(0, wl.units, wl.units // 8))):
         folded = np.setdiff1d(np.arange(n - wl.eta), gst.g_pos[u])
         f = O.phi(kk[u, folded], Wf[u % wl.Hkv])
         H = f.T @ vv[u, folded]
-        s = f.sum(0)
-        assert np.linalg.norm(gst.H[u] - H) / np.linalg.norm(H) <= tol
-        assert np.linalg.norm(gst.s[u] - s) / np.linalg.norm(s) <= tol
+        s_ = f.sum(0)
+        assert rel_cols(gst.H[u:u + 1], H[None]) <= tol
+        assert rel_elem(gst.s[u:u + 1], s_[None]) <= tol
+    return stats
 
 
-def _decode_lockstep(wl, steps):
+def _decode_lockstep(wl, steps, strict=False):
     """Prefill, then token-by-token decode: every step's outputs, cache
-    membership (argmin rule) and state against the oracle (resync per step)."""
+    membership (the argmin rule; strict: bit-exact) and state (window and
+    cache exact, H per column, s per element) against the oracle, which
+    continues along the GPU's choice at an allowed near-tie flip; resync from
+    the exported state every step."""
     print("decode lockstep", wl, flush=True)
     inp = make_inputs(wl)
     layer = make_layer(wl, inp.W)
@@ -225,23 +289,36 @@ def _decode_lockstep(wl, steps):
     st = gpu_state(layer, wl)
     Wf = inp.f64("W")
     tol = _tol(wl)
-    stats = dict(exact=0, allowed=0)
+    stats = new_stats()
     from sparse_kv_caching_amd.workloads import decode_inputs
     for step in range(steps):
         q, k, v = decode_inputs(wl, step)
         yg = layer.decode(dev(wl, q), dev(wl, k), dev(wl, v)).cpu().numpy().astype(np.float64)
+        pre = st.copy()
         logs = []
-        yo = O.decode_step(st, to_f64(wl, q), to_f64(wl, k), to_f64(wl, v), Wf, logs=logs)
-        assert row_rel_err(yg, yo).max() <= tol, step
+        qf, kf, vf = to_f64(wl, q), to_f64(wl, k), to_f64(wl, v)
+        yo = O.decode_step(st, qf, kf, vf, Wf, logs=logs)
+        e = float(row_rel_err(yg, yo).max())
+        stats["y_max"] = max(stats["y_max"], e)
+        assert e <= tol, step
         gst = gpu_state(layer, wl)
-        ex, al, bad, msgs = membership(logs[0], [set(g.tolist()) for g in gst.g_pos], wl.lam)
+        gsets = [set(g.tolist()) for g in gst.g_pos]
+        ex, al, bad, msgs = membership(logs[0], gsets, wl.lam)
         assert bad == 0, (step, msgs[:3])
+        assert not (strict and al), (step, "a flip where the tie rule fixes the set")
+        stats["chunks"] += 1
         stats["exact"] += ex
-        stats["allowed"] += al
-        assert rel_fro(gst.H, st.H) <= tol and rel_fro(gst.s, st.s) <= tol, step
-        np.testing.assert_array_equal(gst.win_k, st.win_k)
+        if logs[0].sre is not None and wl.lam > 0:
+            stats["scored"] += 1
+            stats["near"] += int(np.sum(logs[0].gap < BAND))
+        if al:
+            stats["flips"] += al
+            st = pre
+            O.prefill(st, qf[:, :, None], kf[:, :, None], vf[:, :, None], Wf, 1, keep=gsets,
+                      outputs=False)
+        check_state(gst, st, tol, stats)
         st = gst
-    print(stats)
+    print("PARITY decode", wl.name, wl.keys, stats, flush=True)
     layer.free()
     return stats
 

@@ -371,3 +371,86 @@ def test_gqa_equals_replicated_kv_heads():
     kr, vr, Wr = np.repeat(k, 3, 1), np.repeat(v, 3, 1), np.repeat(W, 3, 0)
     yr, _ = _run(q, kr, vr, Wr, 5, 4, 3)
     np.testing.assert_allclose(y, yr, rtol=1e-13)
+
+
+# ------------------------------------------------------ boundary gap (chunk log)
+def test_boundary_gap_hand_values():
+    """gamma = (SRE_(lam) - SRE_(lam+1)) / SRE_(lam) with SRE_(i) the i-th
+    largest: values worked by hand, a tie at the boundary (0), and a zero
+    lam-th value (inf)."""
+    sc = np.array([[4.0, 9.0, 1.0, 7.0, 4.0]])
+    assert O.boundary_gap(sc, 1)[0] == pytest.approx(2 / 9)      # 9 vs 7
+    assert O.boundary_gap(sc, 2)[0] == pytest.approx(3 / 7)      # 7 vs 4
+    assert O.boundary_gap(sc, 3)[0] == 0.0                      # 4 vs 4: a tie
+    assert O.boundary_gap(sc, 4)[0] == pytest.approx(3 / 4)      # 4 vs 1
+    assert O.boundary_gap(np.array([[0.0, 0.0, 0.0]]), 1)[0] == np.inf
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_boundary_gap_is_the_kept_minimum_against_the_folded_maximum(seed):
+    """The lam-th largest SRE is the smallest kept one and the (lam+1)-th the
+    largest folded one, for the membership select_keep gives (itself pinned
+    by rank counting above).  Catches an off-by-one in either order statistic."""
+    rng = np.random.default_rng(seed)
+    U, E = 4, 30
+    scores = rng.random((U, E)) + 0.1
+    scores[:, :6] = scores[:, 6:12]                              # some exact ties
+    pos = np.stack([rng.permutation(E) for _ in range(U)])
+    for lam in (1, 5, 17, 29):
+        keep = O.select_keep(scores, pos, lam)
+        g = O.boundary_gap(scores, lam)
+        for u in range(U):
+            a, b = scores[u][keep[u]].min(), scores[u][~keep[u]].max()
+            assert g[u] == pytest.approx((a - b) / a, rel=1e-14, abs=1e-300)
+
+
+def test_identical_pairs_score_bitwise_equal():
+    """Duplicate (k, v) pairs among the candidates get bitwise-equal SRE, so
+    the tie rule (older position first) decides between them; the exact-tie
+    stress inputs rely on this."""
+    rng = np.random.default_rng(5)
+    U, d, m = 2, 16, 8
+    W = rng.standard_normal((d, m)) / np.sqrt(d)
+    pool_k, pool_v = rng.standard_normal((5, d)), rng.standard_normal((5, d))
+    idx = rng.integers(0, 5, size=97)
+    k = np.broadcast_to(pool_k[idx], (U, 97, d))
+    v = np.broadcast_to(pool_v[idx], (U, 97, d))
+    ph = np.stack([O.phi(k[u], W) for u in range(U)])
+    H, s = rng.random((U, 2 * m, d)), rng.random((U, 2 * m))
+    sc = O.sre(ph, v, H, s)
+    for u in range(U):
+        for j in range(5):
+            grp = sc[u][idx == j]
+            assert np.all(grp == grp[0])
+
+
+def test_imposed_kept_set():
+    """Continuing along another kept set (an allowed choice at a near-tie):
+    imposing the set the oracle itself selects reproduces its state bit for
+    bit; imposing another set keeps the bookkeeping invariants and moves the
+    swapped pairs between the cache and H, s."""
+    q, k, v, W = _problem(B=1, Hq=2, Hkv=1, T=40, d=8, m=6, seed=3)
+    eta, lam, C = 4, 5, 8
+    st = O.new_state(1, 8, 12, eta, lam)
+    O.prefill(st, q[:, :, :24], k[:, :, :24], v[:, :, :24], W, C)
+    a, b = st.copy(), st.copy()
+    logs = []
+    ya = O.prefill(a, q[:, :, 24:32], k[:, :, 24:32], v[:, :, 24:32], W, C, logs=logs)
+    lg = logs[0]
+    assert lg.sre is not None
+    own = [set(lg.cand_pos[0][lg.keep[0]].tolist())]
+    yb = O.prefill(b, q[:, :, 24:32], k[:, :, 24:32], v[:, :, 24:32], W, C, keep=own)
+    assert np.array_equal(ya, yb) and np.array_equal(a.H, b.H) and np.array_equal(a.g_pos, b.g_pos)
+    # swap the weakest kept candidate with the strongest folded one
+    order = np.lexsort((lg.cand_pos[0], -lg.sre[0]))
+    alt = set(lg.cand_pos[0][order[:lam - 1]].tolist()) | {int(lg.cand_pos[0][order[lam]])}
+    c = st.copy()
+    O.prefill(c, q[:, :, 24:32], k[:, :, 24:32], v[:, :, 24:32], W, C, keep=[alt])
+    assert set(c.g_pos[0].tolist()) == alt and c.n_fold == a.n_fold
+    np.testing.assert_allclose(c.s.sum(), 2 * c.n_fold, rtol=1e-12)
+    x, y = int(lg.cand_pos[0][order[lam - 1]]), int(lg.cand_pos[0][order[lam]])
+    dH = O.phi(k[0, 0, x], W[0])[:, None] * v[0, 0, x] - O.phi(k[0, 0, y], W[0])[:, None] * v[0, 0, y]
+    np.testing.assert_allclose(c.H[0] - a.H[0], dH, rtol=1e-10, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.prefill(st.copy(), q[:, :, 24:32], k[:, :, 24:32], v[:, :, 24:32], W, C,
+                  keep=[set(list(alt)[:2])])
