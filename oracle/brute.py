@@ -32,10 +32,28 @@ def _phi_row(x: Sequence[float], W: Sequence[Sequence[float]]) -> List[float]:
     return [e / sp for e in ep] + [e / sn for e in en]
 
 
-class BruteUnit:
-    """One (sequence, KV head) unit with its own history and memories."""
+def _rule_term(rule: str, e: float, c: float) -> float:
+    """One (query, key) term of an accumulated scoring rule (LoLA notes §4.5,
+    Table 4): e the exponential kernel, c the feature kernel."""
+    if rule == "kernel_sq":
+        return (e - c) * (e - c)
+    if rule == "kernel_abs":
+        return abs(e - c)
+    if rule == "kernel_ratio":
+        return c / e
+    if rule == "local_attn":
+        return e
+    raise ValueError(rule)
 
-    def __init__(self, d: int, W, eta: int, lam: int):
+
+class BruteUnit:
+    """One (sequence, KV head) unit with its own history and memories.
+
+    ``rule``: "sre", or an accumulated rule whose per-position scores live in
+    ``acc``: every query that sees a position through the window adds its
+    term while the position is in the window."""
+
+    def __init__(self, d: int, W, eta: int, lam: int, rule: str = "sre"):
         self.d = d
         self.W = [list(map(float, row)) for row in W]
         self.D = 2 * len(self.W[0])
@@ -46,6 +64,19 @@ class BruteUnit:
         self.H = [[0.0] * d for _ in range(self.D)]
         self.s = [0.0] * self.D
         self.folded: List[int] = []
+        self.rule = rule
+        self.acc = {}                              # position -> accumulated score
+
+    # -- the accumulated rules: query q (of token t, chunk start n) adds its
+    # term to every position it sees through the window
+    def accumulate(self, q: Sequence[float], t: int, n: int) -> None:
+        fq = _phi_row(q, self.W)
+        for p in range(max(0, n - self.eta), t + 1):
+            k = self.hist_k[p]
+            e = math.exp(sum(q[i] * k[i] for i in range(self.d)) / math.sqrt(self.d))
+            fk = _phi_row(k, self.W)
+            c = sum(fq[i] * fk[i] for i in range(self.D))
+            self.acc[p] = self.acc.get(p, 0.0) + _rule_term(self.rule, e, c)
 
     # -- Eq. (14), state at chunk start; `branches` (bit 1 state, 2 cache,
     # 4 window) leaves out the hidden memories (LoLA notes §4.8, Table 12)
@@ -85,7 +116,10 @@ class BruteUnit:
         if len(cand) <= self.lam:
             self.cache = cand
             return
-        score = {p: self.sre_of(p) for p in cand}  # all against the before-state
+        if self.rule == "sre":
+            score = {p: self.sre_of(p) for p in cand}   # all against the before-state
+        else:
+            score = {p: self.acc[p] for p in cand}      # frozen since p left the window
         kept, out = [], []
         for p in cand:
             better = sum(1 for o in cand
@@ -127,6 +161,10 @@ def brute_prefill(units: List[BruteUnit], q, k, v, C: int, n0: int = 0, branches
                     for j in range(g):
                         y[b][h * g + j][t] = u.read([float(x) for x in q[b][h * g + j][t]],
                                                     n0 + t, n, branches)
+                if u.rule != "sre":
+                    for t in range(t0, t0 + c):
+                        for j in range(g):
+                            u.accumulate([float(x) for x in q[b][h * g + j][t]], n0 + t, n)
                 u.update(n, c)
                 t0 += c
     return y

@@ -72,6 +72,35 @@ BRANCH_WINDOW = 4     # local positions max(0, n - eta) .. t
 BRANCH_ALL = 7
 
 
+# Cache scoring rules (LoLA notes §4.5, Table 4; the formulas of the notes'
+# Appendix F are not on the pages, so these are readings of the table's
+# words).  SRE is the method's rule; the other four score a key by what the
+# local queries saw of it while it was in the sliding window, accumulated
+# over those queries (and the query heads of its KV head) and frozen when it
+# leaves the window.  With e = exp(q.k / sqrt(d)) the exponential kernel and
+# c = phi(q)^T phi(k) the feature kernel of one (query, key) pair:
+SCORE_SRE = "sre"                    # ||H^T phi(k) / phi(k)^T s - v||^2 (Eq. (10))
+SCORE_KERNEL_SQ = "kernel_sq"        # sum (e - c)^2: squared kernel error
+SCORE_KERNEL_ABS = "kernel_abs"      # sum |e - c|: absolute kernel error
+SCORE_KERNEL_RATIO = "kernel_ratio"  # sum c / e: keys the feature kernel overestimates
+SCORE_LOCAL_ATTN = "local_attn"      # sum e: accumulated local attention
+SCORES = (SCORE_SRE, SCORE_KERNEL_SQ, SCORE_KERNEL_ABS, SCORE_KERNEL_RATIO, SCORE_LOCAL_ATTN)
+
+
+def score_terms(rule: str, e: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """The per-(query, key) term that an accumulated rule adds to a key's
+    score, from the exponential kernel e and the feature kernel c."""
+    if rule == SCORE_KERNEL_SQ:
+        return (e - c) ** 2
+    if rule == SCORE_KERNEL_ABS:
+        return np.abs(e - c)
+    if rule == SCORE_KERNEL_RATIO:
+        return c / e
+    if rule == SCORE_LOCAL_ATTN:
+        return e
+    raise ValueError("not an accumulated scoring rule: %r" % rule)
+
+
 def check_branches(branches: int) -> int:
     """A read-branch mask: bits BRANCH_*, with the window bit set."""
     b = int(branches)
@@ -191,18 +220,28 @@ class LolaState:
     g_k: np.ndarray
     g_v: np.ndarray
     n_fold: int = 0
+    rule: str = SCORE_SRE
+    win_score: Optional[np.ndarray] = None   # (U, w) accumulated scores (other rules)
+    g_score: Optional[np.ndarray] = None     # (U, |G|) frozen scores of the cache
 
     def copy(self) -> "LolaState":
+        cp = lambda a: None if a is None else a.copy()
         return LolaState(self.eta, self.lam, self.n, self.H.copy(), self.s.copy(),
                          self.win_k.copy(), self.win_v.copy(), self.g_pos.copy(),
-                         self.g_k.copy(), self.g_v.copy(), self.n_fold)
+                         self.g_k.copy(), self.g_v.copy(), self.n_fold, self.rule,
+                         cp(self.win_score), cp(self.g_score))
 
 
-def new_state(U: int, d: int, D: int, eta: int, lam: int) -> LolaState:
-    """Empty state: n = 0, H = 0, s = 0, no window, no cache."""
+def new_state(U: int, d: int, D: int, eta: int, lam: int, rule: str = SCORE_SRE) -> LolaState:
+    """Empty state: n = 0, H = 0, s = 0, no window, no cache; ``rule`` the
+    cache scoring rule (SCORES)."""
+    if rule not in SCORES:
+        raise ValueError("unknown scoring rule %r" % rule)
     z = np.zeros
+    acc = rule != SCORE_SRE
     return LolaState(eta, lam, 0, z((U, D, d)), z((U, D)), z((U, 0, d)), z((U, 0, d)),
-                     z((U, 0), dtype=np.int64), z((U, 0, d)), z((U, 0, d)), 0)
+                     z((U, 0), dtype=np.int64), z((U, 0, d)), z((U, 0, d)), 0, rule,
+                     z((U, 0)) if acc else None, z((U, 0)) if acc else None)
 
 
 def state_elements(d_k: int, d_v: int, D: int, eta: int, lam: int, t: int) -> int:
@@ -284,8 +323,27 @@ def _read_after(st: LolaState, qc: np.ndarray, Wu: np.ndarray,
 
 
 # ---------------------------------------------------------------------- update
+def _local_scores(st: LolaState, qc: np.ndarray, kc: np.ndarray, Wu: np.ndarray) -> np.ndarray:
+    """The chunk's contribution to the accumulated scores of the local keys
+    (window, then the chunk's own keys): for every query t of the chunk and
+    every key i it sees through the window (positions max(0, n - eta) .. t),
+    the rule's term of (q_t, k_i), summed over t and the g query heads.
+    qc (U, g, c, d), kc (U, c, d).  Returns (U, w + c)."""
+    U, g, c, d = qc.shape
+    keys = np.concatenate([st.win_k, kc], axis=1)             # (U, nloc, d)
+    w = st.win_k.shape[1]
+    e = np.exp(np.matmul(qc, keys[:, None].transpose(0, 1, 3, 2)) / np.sqrt(d))
+    if not np.all(np.isfinite(e)):
+        raise FloatingPointError("exp(q.k/sqrt(d)) overflowed in float64")
+    cfeat = np.matmul(_phi_units(qc, Wu), _phi_units(keys, Wu)[:, None].transpose(0, 1, 3, 2))
+    terms = score_terms(st.rule, e, cfeat)                    # (U, g, c, nloc)
+    vis = np.ones((c, w + c), dtype=bool)
+    vis[:, w:] = np.tril(np.ones((c, c), dtype=bool))         # query t sees chunk keys <= t
+    return (terms * vis).sum(axis=(1, 2))
+
+
 def _update_chunk(st: LolaState, kc: np.ndarray, vc: np.ndarray, Wu: np.ndarray,
-                  keep_pos=None) -> ChunkLog:
+                  keep_pos=None, qc: Optional[np.ndarray] = None) -> ChunkLog:
     """Steps 2-5 of the chunk schedule (candidates, keep-all, SRE, fold,
     advance).  Mutates ``st``.
 
@@ -306,15 +364,26 @@ def _update_chunk(st: LolaState, kc: np.ndarray, vc: np.ndarray, Wu: np.ndarray,
     E_pos = np.concatenate([st.g_pos, leave_pos], axis=1)
     E_k = np.concatenate([st.g_k, local_k[:, :n_leave]], axis=1)
     E_v = np.concatenate([st.g_v, local_v[:, :n_leave]], axis=1)
+    acc = st.rule != SCORE_SRE
+    if acc:
+        if qc is None:
+            raise ValueError("the %r rule accumulates the queries' view of the keys" % st.rule)
+        local_s = np.concatenate([st.win_score, np.zeros((U, c))], axis=1) + \
+            _local_scores(st, qc, kc, Wu)
+        E_score = np.concatenate([st.g_score, local_s[:, :n_leave]], axis=1)
+        st.win_score = local_s[:, n_leave:].copy()
     st.win_k = local_k[:, n_leave:].copy()
     st.win_v = local_v[:, n_leave:].copy()
     log = ChunkLog(n=n, c=c, cand_pos=E_pos.copy())
     nE = E_pos.shape[1]
     if nE <= lam:
         st.g_pos, st.g_k, st.g_v = E_pos.copy(), E_k, E_v
+        if acc:
+            st.g_score = E_score.copy()
     else:
         phE = _phi_units(E_k, Wu)
-        scores = sre(phE, E_v, st.H, st.s)                    # before-state
+        # SRE against the before-state, or the frozen accumulated scores
+        scores = sre(phE, E_v, st.H, st.s) if not acc else E_score
         keep = select_keep(scores, E_pos, lam) if keep_pos is None else \
             _given_keep(E_pos, keep_pos, lam)
         fold = (~keep).astype(F64)
@@ -323,6 +392,8 @@ def _update_chunk(st: LolaState, kc: np.ndarray, vc: np.ndarray, Wu: np.ndarray,
         st.g_pos = E_pos[keep].reshape(U, lam)
         st.g_k = E_k[keep].reshape(U, lam, d)
         st.g_v = E_v[keep].reshape(U, lam, d)
+        if acc:
+            st.g_score = E_score[keep].reshape(U, lam)
         st.n_fold += nE - lam
         log.sre, log.keep = scores, keep
         log.gap = boundary_gap(scores, lam) if lam > 0 else None
@@ -371,6 +442,8 @@ def prefill(st: LolaState, q, k, v, W, C: int, *, outputs: bool = True,
         raise ValueError("order must be 'before' or 'after'")
     if order == "after" and C != 1:
         raise ValueError("the read-after-update order is defined token by token (C = 1)")
+    if order == "after" and st.rule != SCORE_SRE:
+        raise ValueError("the accumulated scoring rules are defined for the chunk schedule")
     if order == "after" and outputs and st.eta == 0 and not (
             (st.lam > 0 and branches & BRANCH_SPARSE) or (st.lam == 0 and branches & BRANCH_STATE)):
         raise ValueError("eta = 0 reads no window after the update: keep a memory that is "
@@ -389,7 +462,7 @@ def prefill(st: LolaState, q, k, v, W, C: int, *, outputs: bool = True,
         sl = slice(t0, t0 + c)
         if outputs and order == "before":
             y[:, :, sl] = _read_chunk(st, qu[:, :, sl], ku[:, sl], vu[:, sl], Wu, branches)
-        lg = _update_chunk(st, ku[:, sl], vu[:, sl], Wu, keep)
+        lg = _update_chunk(st, ku[:, sl], vu[:, sl], Wu, keep, qu[:, :, sl])
         if outputs and order == "after":
             y[:, :, sl] = _read_after(st, qu[:, :, sl], Wu, branches)
         if logs is not None:
@@ -429,6 +502,8 @@ def sre_map(st: LolaState, k, v, W, C: int):
     The SRE at first write of p is m[u, fold + 1, p] (the first state that
     holds it) and the relative SRE of Eq. (26) is m[u, j, p] minus it, for
     j > fold."""
+    if st.rule != SCORE_SRE:
+        raise ValueError("the SRE map describes the SRE rule")
     Hkv = np.asarray(W).shape[0]
     k = np.asarray(k, F64)
     v = np.asarray(v, F64)
@@ -462,9 +537,12 @@ def sre_map(st: LolaState, k, v, W, C: int):
 def export_state(st: LolaState) -> dict:
     """Canonical layout (per unit): n; H (U, D, d); s (U, D); window k/v oldest
     to newest (U, w, d); cache positions ascending (U, |G|) with its k/v."""
-    return dict(n=st.n, n_fold=st.n_fold, H=st.H.copy(), s=st.s.copy(),
-                win_k=st.win_k.copy(), win_v=st.win_v.copy(),
-                g_pos=st.g_pos.copy(), g_k=st.g_k.copy(), g_v=st.g_v.copy())
+    d = dict(n=st.n, n_fold=st.n_fold, H=st.H.copy(), s=st.s.copy(),
+             win_k=st.win_k.copy(), win_v=st.win_v.copy(),
+             g_pos=st.g_pos.copy(), g_k=st.g_k.copy(), g_v=st.g_v.copy(), rule=st.rule)
+    if st.rule != SCORE_SRE:
+        d["win_score"], d["g_score"] = st.win_score.copy(), st.g_score.copy()
+    return d
 
 
 def import_state(d: dict, eta: int, lam: int) -> LolaState:
@@ -483,6 +561,12 @@ def import_state(d: dict, eta: int, lam: int) -> LolaState:
     if gs and (np.any(np.diff(gp, axis=1) <= 0) or np.any(gp >= n - w) or np.any(gp < 0)):
         raise ValueError("cache positions must be ascending and older than the window")
     n_fold = int(d.get("n_fold", max(0, n - eta) - gs))
+    rule = d.get("rule", SCORE_SRE)
+    ws = gsc = None
+    if rule != SCORE_SRE:
+        ws, gsc = np.array(d["win_score"], F64), np.array(d["g_score"], F64)
+        if ws.shape != (U, w) or gsc.shape != (U, gs):
+            raise ValueError("accumulated scores must match the window and the cache")
     return LolaState(eta, lam, n, np.array(d["H"], F64), np.array(d["s"], F64),
                      np.array(d["win_k"], F64), np.array(d["win_v"], F64), gp.copy(),
-                     np.array(d["g_k"], F64), np.array(d["g_v"], F64), n_fold)
+                     np.array(d["g_k"], F64), np.array(d["g_v"], F64), n_fold, rule, ws, gsc)

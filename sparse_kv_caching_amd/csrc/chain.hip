@@ -120,6 +120,26 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 
+// Four consecutive input elements as loaded (converted where staged).
+template <class T> struct VRaw;
+template <> struct VRaw<uint16_t> {
+  u32x2 w;
+  __device__ __forceinline__ void load(bool valid, const uint16_t* p) {
+    w = valid ? *reinterpret_cast<const u32x2*>(p) : u32x2{0, 0};
+  }
+  __device__ __forceinline__ float get(int i) const {
+    const uint32_t x = w[i >> 1];
+    return __uint_as_float((i & 1) ? (x & 0xFFFF0000u) : (x << 16));
+  }
+};
+template <> struct VRaw<float> {
+  f32x4 w;
+  __device__ __forceinline__ void load(bool valid, const float* p) {
+    w = valid ? *reinterpret_cast<const f32x4*>(p) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ float get(int i) const { return w[i]; }
+};
+
 }  // namespace
 
 size_t chain_lds_bytes(int lam, int C, int d, bool f32) {
@@ -133,6 +153,9 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
   constexpr int NTILE = 4 * SPW;                  // own H tiles (feature block, slab)
   constexpr int NPW = (NTILE + kWaves - 1) / kWaves;   // H tiles per wave (1 or 2)
   constexpr int NG = NSLAB / SPW;                 // slab groups
+  // the workgroups of a unit exchange SRE parts when they split the columns:
+  // the host launches SPW < NSLAB exactly when k > 1
+  constexpr bool kExch = SPW < NSLAB;
   const VirtRows vr = a.vr;
   const int lam = vr.lam, eta = vr.eta, k = a.k, CS = a.k / NG;
   const int LE = lam + a.C;                       // candidates per step, at most
@@ -343,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
             }
           acc += xor32(acc);
           if (ev && h == 0) {
-            if (k == 1) sm.part[sw * LE + e] = acc;
+            if constexpr (!kExch) sm.part[sw * LE + e] = acc;
             else __hip_atomic_store(xb + (size_t)(grp * SPW + sw) * LE + e,
                                     ((uint64_t)tag << 32) | __float_as_uint(acc),
                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -361,31 +384,49 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     // (debug: the host can make every workgroup give up at one exchange step,
     // the same outcome as a lost partner, deterministically)
     bool lost = xstep - 1 == a.fail_at;
-    for (int e = tid; lam > 0 && e < nE; e += kThreads) {
-      float sre = 0.f;
-      if (k > 1) {
-        uint64_t w[NSLAB];
+    // the candidates of a thread are read back in batches of XB: every word
+    // of a batch is requested before any tag is checked, so the batch costs
+    // one round trip to L2 rather than one per candidate
+    constexpr int XB = kExch ? 4 : 1;
+    for (int e0 = tid; lam > 0 && e0 < nE; e0 += XB * kThreads) {
+      uint64_t w[kExch ? XB : 1][NSLAB];
+      if constexpr (kExch) {
 #pragma unroll
-        for (int q = 0; q < NSLAB; ++q)
-          w[q] = __hip_atomic_load(xb + (size_t)q * LE + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i = 0; i < XB; ++i) {
+          const int e = e0 + i * kThreads;
 #pragma unroll
-        for (int q = 0; q < NSLAB; ++q) {
-          int spins = 0;
-          while ((uint32_t)(w[q] >> 32) != tag && !lost) {
-            if (++spins > a.spin_limit) lost = true;
-            w[q] = __hip_atomic_load(xb + (size_t)q * LE + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-          sre += __uint_as_float((uint32_t)w[q]);
+          for (int q = 0; q < NSLAB; ++q)
+            w[i][q] = e < nE ? __hip_atomic_load(xb + (size_t)q * LE + e, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                             : ((uint64_t)tag << 32);
         }
-      } else {
-#pragma unroll
-        for (int q = 0; q < NSLAB; ++q) sre += sm.part[q * LE + e];
       }
-      const uint32_t pos = e < gs ? (uint32_t)sm.Gp[e] : (uint32_t)(lo_p + (e - gs));
-      const uint64_t key = ((uint64_t)__float_as_uint(sre) << 32) | (uint64_t)(0xFFFFFFFFu - pos);
-      sm.keys[e] = key;
-      kmin = key < kmin ? key : kmin;
-      kmax = key > kmax ? key : kmax;
+#pragma unroll
+      for (int i = 0; i < XB; ++i) {
+        const int e = e0 + i * kThreads;
+        if (e >= nE) break;
+        float sre = 0.f;
+        if constexpr (kExch) {
+#pragma unroll
+          for (int q = 0; q < NSLAB; ++q) {
+            int spins = 0;
+            while ((uint32_t)(w[i][q] >> 32) != tag && !lost) {
+              if (++spins > a.spin_limit) lost = true;
+              w[i][q] = __hip_atomic_load(xb + (size_t)q * LE + e, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+            }
+            sre += __uint_as_float((uint32_t)w[i][q]);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < NSLAB; ++q) sre += sm.part[q * LE + e];
+        }
+        const uint32_t pos = e < gs ? (uint32_t)sm.Gp[e] : (uint32_t)(lo_p + (e - gs));
+        const uint64_t key = ((uint64_t)__float_as_uint(sre) << 32) | (uint64_t)(0xFFFFFFFFu - pos);
+        sm.keys[e] = key;
+        kmin = key < kmin ? key : kmin;
+        kmax = key > kmax ? key : kmax;
+      }
     }
     wave_minmax_u64(kmin, kmax);
     if (lane == 63) { sm.kred[2 * wave] = kmin; sm.kred[2 * wave + 1] = kmax; }
@@ -509,96 +550,99 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     // ---- 4d. fold the rest into own columns of H (MFMA) and into s, 64
     // tokens per block.  The gather is by rows: lane = token, wave = feature
     // / column chunks, with 16-byte loads where possible; the tiles are
-    // written transposed (token-contiguous) for the MFMA operands.
+    // written transposed (token-contiguous) for the MFMA operands.  The
+    // gathers of up to GB blocks are issued together (they are latency-bound,
+    // and a later block's loads then stay in flight while an earlier block is
+    // staged and multiplied); values stay as loaded until they are staged.
     const int nS = nE - lam;
     float sacc = 0.f;
-    for (int sb = 0; sb < nS; sb += 64) {
-      const int tok = sb + lane;
-      const bool tv = tok < nS;
-      const int vi = tv ? sm.S[tok] : 0;
-      {
-        // phi: 16 chunks of 8 features, two per wave
-        constexpr int FCW = 16 / kWaves;                 // 8-feature chunks per wave
-        u32x4 xh[FCW], xl[FCW];
+    constexpr int FCW = 16 / kWaves;                     // 8-feature chunks of phi per wave
+    constexpr int VC = 32 * SPW / kWaves;                // own V columns per wave: 4, 8 or 16
+    constexpr int GB = SPW == 1 ? 4 : (SPW == 2 ? 2 : 1);   // blocks gathered together
+    struct Gather {
+      u32x4 xh[FCW], xl[FCW];
+      VRaw<T> v[VC / 4];
+    };
+    for (int sb0 = 0; sb0 < nS; sb0 += 64 * GB) {
+      Gather gb[GB];
+#pragma unroll
+      for (int b = 0; b < GB; ++b) {
+        const int tok = sb0 + 64 * b + lane;
+        const bool tv = tok < nS;
+        const int vi = tv ? sm.S[tok] : 0;
 #pragma unroll
         for (int q = 0; q < FCW; ++q) {
           const int f0 = 8 * (FCW * wave + q);
-          xh[q] = tv ? ld16(a.phi_hi + phi_unit + (size_t)vi * kD + f0) : u32x4{0, 0, 0, 0};
-          xl[q] = tv ? ld16(a.phi_lo + phi_unit + (size_t)vi * kD + f0) : u32x4{0, 0, 0, 0};
+          gb[b].xh[q] = tv ? ld16(a.phi_hi + phi_unit + (size_t)vi * kD + f0) : u32x4{0, 0, 0, 0};
+          gb[b].xl[q] = tv ? ld16(a.phi_lo + phi_unit + (size_t)vi * kD + f0) : u32x4{0, 0, 0, 0};
         }
-        // V: own columns, VC per wave
-        constexpr int VC = 32 * SPW / kWaves;            // 4, 8 or 16 columns
-        float vx[VC];
-        {
-          const T* vrow = reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))) + col0 + VC * wave;
+        const T* vrow = reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))) + col0 + VC * wave;
 #pragma unroll
-          for (int q4 = 0; q4 < VC; q4 += 4) {
-            float x[4];
-            if (tv) load4_f32(vrow + q4, x);
-            else for (int q = 0; q < 4; ++q) x[q] = 0.f;
+        for (int q4 = 0; q4 < VC / 4; ++q4) gb[b].v[q4].load(tv, vrow + 4 * q4);
+      }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) vx[q4 + q] = x[q];
-          }
-        }
+      for (int b = 0; b < GB; ++b) {
+        const int sb = sb0 + 64 * b;
+        if (sb >= nS) break;
 #pragma unroll
         for (int q = 0; q < FCW; ++q) {
           const int f0 = 8 * (FCW * wave + q);
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            sm.phT_hi[(f0 + 2 * w) * STP + lane] = (uint16_t)(xh[q][w] & 0xFFFFu);
-            sm.phT_hi[(f0 + 2 * w + 1) * STP + lane] = (uint16_t)(xh[q][w] >> 16);
-            sm.phT_lo[(f0 + 2 * w) * STP + lane] = (uint16_t)(xl[q][w] & 0xFFFFu);
-            sm.phT_lo[(f0 + 2 * w + 1) * STP + lane] = (uint16_t)(xl[q][w] >> 16);
+            sm.phT_hi[(f0 + 2 * w) * STP + lane] = (uint16_t)(gb[b].xh[q][w] & 0xFFFFu);
+            sm.phT_hi[(f0 + 2 * w + 1) * STP + lane] = (uint16_t)(gb[b].xh[q][w] >> 16);
+            sm.phT_lo[(f0 + 2 * w) * STP + lane] = (uint16_t)(gb[b].xl[q][w] & 0xFFFFu);
+            sm.phT_lo[(f0 + 2 * w + 1) * STP + lane] = (uint16_t)(gb[b].xl[q][w] >> 16);
           }
         }
 #pragma unroll
         for (int q = 0; q < VC; ++q) {
           uint32_t hi, lo;
-          DT::split(vx[q], hi, lo);
+          DT::split(gb[b].v[q >> 2].get(q & 3), hi, lo);
           sm.VT_hi[(VC * wave + q) * STP + lane] = (uint16_t)hi;
           if constexpr (DT::kSplit) sm.VT_lo[(VC * wave + q) * STP + lane] = (uint16_t)lo;
         }
-      }
-      lds_barrier();
-      {
-        // s partial sums: feature F, 64 / NPART tokens per part, fixed order
-        const int F = tid % kD, qt = tid / kD;
-        constexpr int TPP = 64 / (kThreads / kD);
-        static_assert(TPP % 8 == 0, "parts are read as 8-token pieces");
-        float part = 0.f;
+        lds_barrier();
+        {
+          // s partial sums: feature F, 64 / NPART tokens per part, fixed order
+          const int F = tid % kD, qt = tid / kD;
+          constexpr int TPP = 64 / (kThreads / kD);
+          static_assert(TPP % 8 == 0, "parts are read as 8-token pieces");
+          float part = 0.f;
 #pragma unroll
-        for (int q8 = 0; q8 < TPP / 8; ++q8) {
-          const u32x4 wh = ld16(sm.phT_hi + F * STP + TPP * qt + 8 * q8);
-          const u32x4 wl = ld16(sm.phT_lo + F * STP + TPP * qt + 8 * q8);
+          for (int q8 = 0; q8 < TPP / 8; ++q8) {
+            const u32x4 wh = ld16(sm.phT_hi + F * STP + TPP * qt + 8 * q8);
+            const u32x4 wl = ld16(sm.phT_lo + F * STP + TPP * qt + 8 * q8);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const uint32_t bh = (q & 1) ? wh[q >> 1] >> 16 : wh[q >> 1] & 0xFFFFu;
-            const uint32_t bl = (q & 1) ? wl[q >> 1] >> 16 : wl[q >> 1] & 0xFFFFu;
-            part += DT::from_bits(bh) + DT::from_bits(bl);
+            for (int q = 0; q < 8; ++q) {
+              const uint32_t bh = (q & 1) ? wh[q >> 1] >> 16 : wh[q >> 1] & 0xFFFFu;
+              const uint32_t bl = (q & 1) ? wl[q >> 1] >> 16 : wl[q >> 1] & 0xFFFFu;
+              part += DT::from_bits(bh) + DT::from_bits(bl);
+            }
+          }
+          sacc += part;
+          // the last block's partial sums go out before its closing barrier
+          if (sb + 64 >= nS) sm.spart[(tid / kD) * kD + tid % kD] = sacc;
+        }
+        const int nkb = min(4, (nS - sb + 15) / 16);
+        for (int kb = 0; kb < nkb; ++kb) {
+          const int k0 = 16 * kb + 8 * h;
+#pragma unroll
+          for (int i = 0; i < NPW; ++i) {
+            const int p = wave + kWaves * i, sw = p >> 2, mt = p & 3;
+            if (p < NTILE) {
+              const u32x4 bv = ld16(sm.VT_hi + (32 * sw + r) * STP + k0);
+              const u32x4 ah = ld16(sm.phT_hi + (32 * mt + r) * STP + k0);
+              const u32x4 al = ld16(sm.phT_lo + (32 * mt + r) * STP + k0);
+              Hreg[i] = DT::mma(ah, bv, Hreg[i]);
+              Hreg[i] = DT::mma(al, bv, Hreg[i]);
+              if constexpr (DT::kSplit)
+                Hreg[i] = DT::mma(ah, ld16(sm.VT_lo + (32 * sw + r) * STP + k0), Hreg[i]);
+            }
           }
         }
-        sacc += part;
-        // the last block's partial sums go out before its closing barrier
-        if (sb + 64 >= nS) sm.spart[(tid / kD) * kD + tid % kD] = sacc;
+        lds_barrier();
       }
-      const int nkb = min(4, (nS - sb + 15) / 16);
-      for (int kb = 0; kb < nkb; ++kb) {
-        const int k0 = 16 * kb + 8 * h;
-#pragma unroll
-        for (int i = 0; i < NPW; ++i) {
-          const int p = wave + kWaves * i, sw = p >> 2, mt = p & 3;
-          if (p < NTILE) {
-            const u32x4 bv = ld16(sm.VT_hi + (32 * sw + r) * STP + k0);
-            const u32x4 ah = ld16(sm.phT_hi + (32 * mt + r) * STP + k0);
-            const u32x4 al = ld16(sm.phT_lo + (32 * mt + r) * STP + k0);
-            Hreg[i] = DT::mma(ah, bv, Hreg[i]);
-            Hreg[i] = DT::mma(al, bv, Hreg[i]);
-            if constexpr (DT::kSplit)
-              Hreg[i] = DT::mma(ah, ld16(sm.VT_lo + (32 * sw + r) * STP + k0), Hreg[i]);
-          }
-        }
-      }
-      lds_barrier();
     }
     for (int F = tid; F < kD; F += kThreads) {
       float add = 0.f;
@@ -639,6 +683,8 @@ static hipError_t launch_chain_t(const ChainArgs& a, int U, hipStream_t st) {
   return hipGetLastError();
 }
 
+// k >= NSLAB: one column slab per workgroup; k == 2 (NSLAB = 4): two; k == 1:
+// all of them (the only instance that exchanges nothing)
 template <class DT, int HD>
 static hipError_t launch_chain_k(const ChainArgs& a, int U, hipStream_t st) {
   constexpr int NSLAB = HD / 32;
