@@ -205,6 +205,37 @@ enum {
                                    the leaving pair was kept or folded (§2.5) */
 };
 
+/* Cache scoring rule (LoLA notes §4.5, Table 4: an ablation that replaces
+ * the Self-Recall Error by other scores while everything else runs as
+ * before).  The notes give the alternatives in words; with e = exp(q.k /
+ * sqrt(d)) the exponential kernel and c = phi(q)^T phi(k) the feature
+ * kernel of a (query, key) pair, a key's score is the sum of the rule's term
+ * over every query head and every query that sees the key through the
+ * sliding window (query t with chunk start n_t sees key i iff
+ * max(0, n_t - eta) <= i <= t), frozen when the key leaves the window; the
+ * cache keeps the lambda highest scores (ties: the older position). */
+enum {
+  LOLA_SCORE_SRE = 0,           /* ||H^T phi(k) / phi(k)^T s - v||^2 (the method) */
+  LOLA_SCORE_KERNEL_SQ = 1,     /* sum (e - c)^2 */
+  LOLA_SCORE_KERNEL_ABS = 2,    /* sum |e - c| */
+  LOLA_SCORE_KERNEL_RATIO = 3,  /* sum c / e: keys the feature kernel overestimates */
+  LOLA_SCORE_LOCAL_ATTN = 4     /* sum e: accumulated local attention */
+};
+
+/* Set the scoring rule of a state that holds no token yet (n = 0: fresh or
+ * reset; kept across lola_state_reset).  The running scores of the window
+ * and the frozen scores of the cache live in the state (allocated here).
+ * With a rule other than LOLA_SCORE_SRE: prefill needs C > 1 and the read
+ * order before update; decode, lola_state_import and
+ * lola_state_import_sequence return UNSUPPORTED (the scores are not part of
+ * the state view; lola_state_export writes the rest of the state);
+ * lola_prefill_debug's cand_keys hold (score bits << 32) | (0xFFFFFFFF -
+ * position).  The scores are fp32 sums; e must stay finite (q.k / sqrt(d)
+ * below 88).
+ * Errors: INVALID_ARG (NULL state, unknown rule), STATE (n > 0),
+ * OUT_OF_MEMORY, HIP. */
+int lola_set_scoring(lola_state* st, int rule);
+
 /* Set the read order of the following decode calls and prefill calls with
  * C = 1 (default LOLA_READ_BEFORE_UPDATE).  With LOLA_READ_AFTER_UPDATE a
  * prefill with C > 1 returns UNSUPPORTED, and every token costs two decode

@@ -47,6 +47,9 @@ struct lola_state {
   void* W;
   void* WT;                 // W transposed [Hkv, kM, d] (decode operands)
   int* dev_err;             // device error flags (exchange timeouts)
+  int rule;                 // cache scoring rule (LOLA_SCORE_*)
+  float* ring_score;        // [U, eta] running scores of the window (rule != SRE)
+  float* cache_score[2];    // [U, lam] frozen scores of the cache, with its two buffers
   int spin_limit;           // exchange polls before a partner counts as lost (lola_debug_set)
   int fail_at;              // debug: exchange step at which the chain gives up (-1: never)
   int ncu;                  // compute units of the device
@@ -138,7 +141,7 @@ void* scratch_ptr_of(int dev, int* err) {
 }
 
 struct WsLayout {
-  size_t phi_hi, phi_lo, snapHT, snaps, snapG, finalG, xbuf, total;
+  size_t phi_hi, phi_lo, snapHT, snaps, snapG, finalG, xbuf, vscore, total;
 };
 
 WsLayout ws_layout(const lola_state* st, int T, int C) {
@@ -155,6 +158,8 @@ WsLayout ws_layout(const lola_state* st, int T, int C) {
   w.snapG = off; off = align256(off + U * nch * lam1 * 4);
   w.finalG = off; off = align256(off + U * lam1 * 4);
   w.xbuf = off; off = align256(off + U * 2 * (d / 32) * (lam + (size_t)C) * 8);
+  w.vscore = off;                 // scores of the local rows (accumulated rules only)
+  if (st->rule != LOLA_SCORE_SRE) off = align256(off + U * (eta + (size_t)T) * 4);
   w.total = off;
   return w;
 }
@@ -414,7 +419,8 @@ int lola_state_free(lola_state* st) {
   hipStreamSynchronize(st->last);
   delete[] st->nseq;
   void* ps[] = {st->H, st->s, st->ring_k, st->ring_v, st->W, st->WT, st->dev_err, st->own_ws,
-                st->npos_dev, st->pend, st->npend,
+                st->npos_dev, st->pend, st->npend, st->ring_score, st->cache_score[0],
+                st->cache_score[1],
                 st->cache_k[0], st->cache_k[1], st->cache_v[0], st->cache_v[1],
                 st->cache_pos[0], st->cache_pos[1]};
   for (void* p : ps)
@@ -445,6 +451,8 @@ int lola_decode_step(lola_state* st, const void* q, const void* k, const void* v
   for (int b = 0; b < st->cfg.batch; ++b)
     if (st->nseq[b] > (int64_t)0x7FFFFFF0) return fail(LOLA_ERR_UNSUPPORTED, "position overflow");
   if ((rc = check_read_config(st))) return rc;
+  if (st->rule != LOLA_SCORE_SRE)
+    return fail(LOLA_ERR_UNSUPPORTED, "decode with an accumulated scoring rule is not supported");
   if (st->ragged && st->cfg.cache + st->cfg.window > kDecodeOneChunkKeys)
     return fail(LOLA_ERR_UNSUPPORTED, "sequences at different positions with window + cache = %d "
                 "> %d keys (the chunked decode kernel) are not supported",
@@ -488,6 +496,8 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
                 "sequence in a state of its own and import it (lola_state_import_sequence)");
   if (st->order == LOLA_READ_AFTER_UPDATE && C != 1)
     return fail(LOLA_ERR_UNSUPPORTED, "read after update is token by token: C must be 1");
+  if (st->rule != LOLA_SCORE_SRE && C == 1)
+    return fail(LOLA_ERR_UNSUPPORTED, "an accumulated scoring rule needs C > 1");
   if ((rc = check_read_config(st))) return rc;
   if (st->n + T > (int64_t)0x7FFFFFF0) return fail(LOLA_ERR_UNSUPPORTED, "position overflow");
   const size_t NVs = (size_t)st->cfg.cache + st->cfg.window + T;
@@ -572,6 +582,15 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   hipError_t e;
   { ProfScope ps(st, LOLA_KERNEL_PHI, s); e = launch_phi(pa, U, st->f32, s); }
   if (e != hipSuccess) return hip_fail(st, e, "phi launch");
+  float* vscore = st->rule != LOLA_SCORE_SRE ? (float*)(base + L.vscore) : nullptr;
+  if (vscore) {
+    ScoreArgs sa;
+    sa.vr = vr; sa.q = q; sa.W = st->W; sa.phi_hi = phi_hi; sa.phi_lo = phi_lo;
+    sa.NV = (int)NVs; sa.g = g; sa.Hkv = st->cfg.kv_heads; sa.C = C; sa.rule = st->rule;
+    sa.ring_score = st->ring_score; sa.vscore = vscore;
+    e = launch_score(sa, U, st->f32, s);
+    if (e != hipSuccess) return hip_fail(st, e, "score launch");
+  }
 
   ChainArgs ca;
   ca.vr = vr; ca.phi_hi = phi_hi; ca.phi_lo = phi_lo;
@@ -595,6 +614,8 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   ca.xstep0 = 0;
   ca.spin_limit = st->spin_limit;
   ca.fail_at = st->fail_at;
+  ca.vscore = vscore;
+  ca.cscore = vscore ? st->cache_score[st->cur] : nullptr;
   if (ca.k > 1) {
     e = launch_zero_u32((unsigned*)ca.xbuf, (size_t)U * 2 * (d / 32) * (lam + C) * 2, s);
     if (e != hipSuccess) return hip_fail(st, e, "exchange reset");
@@ -641,6 +662,14 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   fa.err = st->dev_err;
   { ProfScope ps(st, LOLA_KERNEL_FINALIZE, s); e = launch_finalize(fa, U, st->f32, s); }
   if (e != hipSuccess) return hip_fail(st, e, "finalize launch");
+  if (vscore) {
+    ScoreWriteArgs wa;
+    wa.vr = vr; wa.finalG = ca.finalG; wa.cscore_in = st->cache_score[st->cur];
+    wa.vscore = vscore; wa.cscore_out = st->cache_score[1 - st->cur];
+    wa.ring_score = st->ring_score; wa.gs_final = gs_final; wa.err = st->dev_err;
+    e = launch_score_writeback(wa, U, s);
+    if (e != hipSuccess) return hip_fail(st, e, "score write-back launch");
+  }
   st->cur = 1 - st->cur;
   set_uniform(st, nend);
   st->last = s;
@@ -707,6 +736,30 @@ int lola_set_read_order(lola_state* st, int order) {
     return fail(LOLA_ERR_INVALID_ARG, "read order %d: need %d or %d", order,
                 LOLA_READ_BEFORE_UPDATE, LOLA_READ_AFTER_UPDATE);
   st->order = order;
+  return LOLA_OK;
+}
+
+int lola_set_scoring(lola_state* st, int rule) {
+  if (!st) return fail(LOLA_ERR_INVALID_ARG, "state must be non-NULL");
+  if (rule < LOLA_SCORE_SRE || rule > LOLA_SCORE_LOCAL_ATTN)
+    return fail(LOLA_ERR_INVALID_ARG, "unknown scoring rule %d", rule);
+  if (st->ragged || st->n != 0)
+    return fail(LOLA_ERR_STATE, "the scoring rule is set on a state that holds no token "
+                "(n = 0, after init or reset)");
+  if (rule != LOLA_SCORE_SRE && !st->ring_score) {
+    const size_t U = st->U, eta = st->cfg.window, lam = st->cfg.cache;
+    auto alloc = [&](void** p, size_t bytes) -> bool {
+      return hipMalloc(p, bytes ? bytes : 256) == hipSuccess;
+    };
+    if (!alloc((void**)&st->ring_score, U * eta * 4) ||
+        !alloc((void**)&st->cache_score[0], U * lam * 4) ||
+        !alloc((void**)&st->cache_score[1], U * lam * 4)) {
+      for (float** p : {&st->ring_score, &st->cache_score[0], &st->cache_score[1]})
+        if (*p) { hipFree(*p); *p = nullptr; }
+      return fail(LOLA_ERR_OUT_OF_MEMORY, "hipMalloc failed for the scores");
+    }
+  }
+  st->rule = rule;
   return LOLA_OK;
 }
 
@@ -812,6 +865,8 @@ int lola_state_import(lola_state* st, const lola_state_view* src, void* stream) 
       !src->cache_k || !src->cache_v)
     return fail(LOLA_ERR_INVALID_ARG, "state and every view pointer must be non-NULL");
   if (src->n < 0 || src->n > (int64_t)0x7FFFFFF0) return fail(LOLA_ERR_STATE, "bad n");
+  if (st->rule != LOLA_SCORE_SRE)
+    return fail(LOLA_ERR_UNSUPPORTED, "the accumulated scores are not part of a state view");
   hipStream_t s = (hipStream_t)stream;
   const size_t U = st->U, d = st->d;
   const int lam = st->cfg.cache, eta = st->cfg.window;
@@ -844,6 +899,8 @@ int lola_state_import_sequence(lola_state* st, int b, const lola_state_view* src
   if (b < 0 || b >= st->cfg.batch)
     return fail(LOLA_ERR_INVALID_ARG, "sequence slot %d out of range [0, %d)", b, st->cfg.batch);
   if (src->n < 0 || src->n > (int64_t)0x7FFFFFF0) return fail(LOLA_ERR_STATE, "bad n");
+  if (st->rule != LOLA_SCORE_SRE)
+    return fail(LOLA_ERR_UNSUPPORTED, "the accumulated scores are not part of a state view");
   hipStream_t s = (hipStream_t)stream;
   const int Hkv = st->cfg.kv_heads;
   const size_t d = st->d, u0 = (size_t)b * Hkv;

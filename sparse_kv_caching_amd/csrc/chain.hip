@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     const int ntile_own = ntile > ch ? (ntile - ch + CS - 1) / CS : 0;
     const uint32_t tag = (uint32_t)(xstep + 1);
     uint64_t* xb = a.xbuf + ((size_t)u * 2 + (xstep & 1)) * NSLAB * LE;
-    {
+    if (!a.vscore) {
       const int sw = wave % SPW;
       const int t_first = wave / SPW;
       constexpr int TSTEP = kWaves / SPW;
@@ -386,9 +386,24 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(ChainArgs a) {
     bool lost = xstep - 1 == a.fail_at;
     // the candidates of a thread are read back in batches of XB: every word
     // of a batch is requested before any tag is checked, so the batch costs
-    // one round trip to L2 rather than one per candidate
+    // one round trip to L2 rather than one per candidate.  (With an
+    // accumulated scoring rule the keys come from the frozen scores: no
+    // products, no exchange.)
+    if (a.vscore) {
+      const int nloc = eta + vr.T;
+      for (int e = tid; lam > 0 && e < nE; e += kThreads) {
+        const int vi = sm.E[e];
+        const float sc = vi < lam ? a.cscore[(size_t)u * lam + vi]
+                                  : a.vscore[(size_t)u * nloc + (vi - lam)];
+        const uint32_t pos = e < gs ? (uint32_t)sm.Gp[e] : (uint32_t)(lo_p + (e - gs));
+        const uint64_t key = ((uint64_t)__float_as_uint(sc) << 32) | (uint64_t)(0xFFFFFFFFu - pos);
+        sm.keys[e] = key;
+        kmin = key < kmin ? key : kmin;
+        kmax = key > kmax ? key : kmax;
+      }
+    }
     constexpr int XB = kExch ? 4 : 1;
-    for (int e0 = tid; lam > 0 && e0 < nE; e0 += XB * kThreads) {
+    for (int e0 = tid; !a.vscore && lam > 0 && e0 < nE; e0 += XB * kThreads) {
       uint64_t w[kExch ? XB : 1][NSLAB];
       if constexpr (kExch) {
 #pragma unroll

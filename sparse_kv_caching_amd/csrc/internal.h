@@ -93,6 +93,10 @@ struct ChainArgs {
   int xstep0;               // exchange steps of the call before j0 (tags continue)
   int spin_limit;           // polls of one exchange word before its partner counts as lost
   int fail_at;              // debug: exchange step at which every workgroup gives up (-1: never)
+  // accumulated scoring rules: the candidates are ranked by frozen scores
+  // instead of SRE (no SRE products, no exchange); NULL for SRE
+  const float* vscore;      // [U, eta + T] scores of the local rows (virtual index - lam)
+  const float* cscore;      // [U, lam] scores of the cache slots at the call's start
 };
 
 // K3: window + cache softmax attention merged with the linear read.
@@ -163,6 +167,31 @@ struct DecodeArgs {
 // when the list is full, else it appends its term (1 KB instead of 64 KB).
 constexpr int kPend = 3;
 
+// Accumulated cache scores of the local keys of a prefill call (the window
+// at the call's start, then the call's keys): the alternative scoring rules.
+struct ScoreArgs {
+  VirtRows vr;
+  const void* q;            // [U, g, T, d]
+  const void* W;            // [Hkv, d, kM]
+  const uint16_t* phi_hi;   // [U, NV, kD]
+  const uint16_t* phi_lo;
+  int NV, g, Hkv, C, rule;  // rule: LOLA_SCORE_*
+  const float* ring_score;  // [U, eta] running scores of the window (slot p % eta)
+  float* vscore;            // [U, eta + T] out: score of every local row
+};
+
+// The new cache's frozen scores and the window's running scores after a call.
+struct ScoreWriteArgs {
+  VirtRows vr;
+  const int32_t* finalG;    // [U, lam]
+  const float* cscore_in;   // [U, lam] cache scores at the call's start
+  const float* vscore;      // [U, eta + T]
+  float* cscore_out;        // [U, lam] scores of the new cache (its slot order)
+  float* ring_score;        // [U, eta]
+  int gs_final;
+  const int* err;
+};
+
 // Diagnostics: SRE of the memories in the linear state at every chunk start.
 struct SreMapArgs {
   VirtRows vr;
@@ -189,6 +218,9 @@ hipError_t launch_chain(const ChainArgs& a, int U, bool f32, hipStream_t st);
 size_t chain_lds_bytes(int lam, int C, int d, bool f32);
 hipError_t launch_attn(const AttnArgs& a, int U, bool f32, hipStream_t st);
 hipError_t launch_sre_map(const SreMapArgs& a, int U, bool f32, hipStream_t st);
+hipError_t launch_score(const ScoreArgs& a, int U, bool f32, hipStream_t st);
+size_t score_lds_bytes(int d);
+hipError_t launch_score_writeback(const ScoreWriteArgs& a, int U, hipStream_t st);
 size_t attn_lds_bytes(int d, int lam, bool f32);
 int attn_positions_per_block(int C, int g);
 hipError_t launch_finalize(const FinalizeArgs& a, int U, bool f32, hipStream_t st);

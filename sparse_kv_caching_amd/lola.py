@@ -29,6 +29,7 @@ KERNELS = ("phi", "chain", "attn", "finalize", "decode")
 READ_STATE, READ_CACHE, READ_WINDOW, READ_ALL = 1, 2, 4, 7   # lola_set_read_branches bits
 READ_BEFORE_UPDATE, READ_AFTER_UPDATE = 0, 1                 # lola_set_read_order
 DEBUG_SPIN_LIMIT, DEBUG_CHAIN_FAIL_AT = 0, 1                 # lola_debug_set keys
+SCORE_SRE, SCORE_KERNEL_SQ, SCORE_KERNEL_ABS, SCORE_KERNEL_RATIO, SCORE_LOCAL_ATTN = range(5)
 
 EXPORTED = [
     "lola_state_init", "lola_state_free", "lola_state_tokens", "lola_prefill_workspace_bytes",
@@ -95,6 +96,7 @@ def library() -> ctypes.CDLL:
         lib.lola_state_export_sequence.argtypes = [vp, i32, ctypes.POINTER(LolaStateView), vp]
         lib.lola_state_positions.argtypes = [vp, ctypes.POINTER(i64)]
         lib.lola_debug_set.argtypes = [vp, i32, ctypes.c_longlong]
+        lib.lola_set_scoring.argtypes = [vp, i32]
         lib.lola_prefill_chunk_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp]
         lib.lola_strerror.argtypes = [i32]
         lib.lola_strerror.restype = ctypes.c_char_p
@@ -105,7 +107,7 @@ def library() -> ctypes.CDLL:
                   "lola_state_import", "lola_set_read_branches", "lola_set_read_order",
                   "lola_state_import_sequence", "lola_state_export_sequence",
                   "lola_state_positions", "lola_prefill_sre_map", "lola_debug_set",
-                  "lola_prefill_chunk_noalloc"):
+                  "lola_prefill_chunk_noalloc", "lola_set_scoring"):
             getattr(lib, f).restype = i32
         _lib = lib
     return _lib
@@ -179,6 +181,10 @@ class LolaLayer:
         """READ_BEFORE_UPDATE (0, the chunk schedule) or READ_AFTER_UPDATE (1,
         the literal token recurrence; decode and C = 1 prefill only)."""
         _check(self.lib.lola_set_read_order(self._st, int(order)), "lola_set_read_order")
+
+    def set_scoring(self, rule: int):
+        """Cache scoring rule (SCORE_*) of a state holding no token yet."""
+        _check(self.lib.lola_set_scoring(self._st, int(rule)), "lola_set_scoring")
 
     def debug_set(self, key: int, value: int):
         """lola_debug_set: DEBUG_SPIN_LIMIT (exchange polls before a partner
