@@ -195,8 +195,8 @@ int supported_C(const lola_state* st, int C) {
     return fail(LOLA_ERR_UNSUPPORTED, "chunk length C=%d: need C == 1 or a multiple of 32 <= 256", C);
   if (chain_lds_bytes(st->cfg.cache, C, st->d, st->f32) > kMaxLds)
     return fail(LOLA_ERR_UNSUPPORTED, "lambda + C too large for the chain kernel's LDS");
-  if (attn_lds_bytes(st->d, st->cfg.cache, st->f32) > kMaxLds)
-    return fail(LOLA_ERR_UNSUPPORTED, "lambda too large for the attention kernel's LDS");
+  if (attn_lds_bytes(st->d, st->cfg.cache, st->cfg.window, C, st->f32) > kMaxLds)
+    return fail(LOLA_ERR_UNSUPPORTED, "lambda + eta + C too large for the attention kernel's LDS");
   return LOLA_OK;
 }
 

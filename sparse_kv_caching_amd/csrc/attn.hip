@@ -46,7 +46,7 @@ constexpr int VTS = KT + 4;   // LDS row of the V^T tile (keys): 34 dwords, so t
 // Byte offsets of the LDS arrays; the key phase reuses the region of the
 // linear-read phase.
 struct AttnLayout {
-  uint32_t G;                                  // both phases
+  uint32_t tab;                                // both phases: row of every key of the chunk
   uint32_t WT, HT_hi, HT_lo, s;                // linear-read phase
   uint32_t K[2], KL[2], VT[2], VTL[2];         // key phase, two buffers
   uint32_t total;
@@ -67,12 +67,15 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__host__ __device__ inline AttnLayout attn_layout(int d, int lam, bool f32) {
+__host__ __device__ inline AttnLayout attn_layout(int d, int lam, int eta, int C, bool f32) {
   AttnLayout L;
   uint32_t off = 0;
   auto take = [&](uint32_t b) { const uint32_t o = off; off = al16(off + b); return o; };
   const uint32_t esz = f32 ? 4 : 2;
-  L.G = take((uint32_t)(lam > 0 ? lam : 1) * 4);      // cache at chunk start (virtual indices)
+  // the keys a chunk's queries see: the cache at chunk start, the window,
+  // the chunk's own positions; per key its source (cache, ring, input) and
+  // row, packed as (source << 30) | row
+  L.tab = take((uint32_t)(lam + eta + C) * 4);
   const uint32_t base = off;
   L.WT = take((uint32_t)kM * (d + 8) * esz);          // [kM][d + 8] W^T, input dtype
   L.HT_hi = take((uint32_t)d * HTS * 2);               // [d][HTS]
@@ -91,6 +94,11 @@ __host__ __device__ inline AttnLayout attn_layout(int d, int lam, bool f32) {
 }
 
 __device__ __forceinline__ u32x2 ld8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// 16 bytes at a global-memory byte address (a global load, not a flat one)
+__device__ __forceinline__ u32x4 ldg16(uint64_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(addr);
+}
 
 // operand with K-slots sigma_h: elements [4h, 4h+4) and [8+4h, 8+4h+4) of a 16-block
 __device__ __forceinline__ u32x4 sigma_load(const uint16_t* row16, int h) {
@@ -113,7 +121,9 @@ __device__ __forceinline__ uint32_t f16_bits(float x) {
 
 }  // namespace
 
-size_t attn_lds_bytes(int d, int lam, bool f32) { return attn_layout(d, lam, f32).total; }
+size_t attn_lds_bytes(int d, int lam, int eta, int C, bool f32) {
+  return attn_layout(d, lam, eta, C, f32).total;
+}
 
 template <class DT, int HD>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
@@ -157,33 +167,44 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   const int n0e = eta > 0 ? (int)(n0 % eta) : 0;            // ring slot of position n0 - eta
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const AttnLayout L = attn_layout(HD, lam, DT::kSplit);
-  int32_t* sm_G = (int32_t*)(smem + L.G);
+  const AttnLayout L = attn_layout(HD, lam, eta, a.C, DT::kSplit);
+  uint32_t* sm_tab = (uint32_t*)(smem + L.tab);
   T* sm_WT = (T*)(smem + L.WT);
   uint16_t* sm_HT_hi = (uint16_t*)(smem + L.HT_hi);
   uint16_t* sm_HT_lo = (uint16_t*)(smem + L.HT_lo);
   float* sm_s = (float*)(smem + L.s);
 
-  // row of virtual index vi (cache slot, ring slot or input row), 32-bit math
+  // the three sources of key rows, this unit's part
   const T* ck = reinterpret_cast<const T*>(vr.cache_k) + (size_t)u * lam * HD;
   const T* cv = reinterpret_cast<const T*>(vr.cache_v) + (size_t)u * lam * HD;
   const T* rk = reinterpret_cast<const T*>(vr.ring_k) + (size_t)u * eta * HD;
   const T* rv = reinterpret_cast<const T*>(vr.ring_v) + (size_t)u * eta * HD;
   const T* ik = reinterpret_cast<const T*>(vr.in_k) + (size_t)u * vr.T * HD;
   const T* iv = reinterpret_cast<const T*>(vr.in_v) + (size_t)u * vr.T * HD;
-  auto vrow = [&](int vi, bool val) -> const T* {
-    if (vi < lam) return (val ? cv : ck) + (size_t)vi * HD;
+  // (source, row) of virtual index vi: cache slot, ring slot or input row
+  auto vsrc = [&](int vi) -> uint32_t {
+    if (vi < lam) return (uint32_t)vi;
     const int off = vi - lam;                       // position n0 - eta + off
     if (off < eta) {
       int slot = n0e + off;
       if (slot >= eta) slot -= eta;
-      return (val ? rv : rk) + (size_t)slot * HD;
+      return (1u << 30) | (uint32_t)slot;
     }
-    return (val ? iv : ik) + (size_t)(off - eta) * HD;
+    return (2u << 30) | (uint32_t)(off - eta);
+  };
+  // the byte address of key kk's row from the table entry e (built once per
+  // workgroup below): the cache base plus the distance to the ring (source
+  // bit 0) or to the input (source bit 1), plus the row -- adds and masks,
+  // no selection among pointers
+  const uint64_t bk = (uint64_t)(uintptr_t)ck, bv = (uint64_t)(uintptr_t)cv;
+  const uint64_t dk1 = (uint64_t)(uintptr_t)rk - bk, dk2 = (uint64_t)(uintptr_t)ik - bk;
+  const uint64_t dv1 = (uint64_t)(uintptr_t)rv - bv, dv2 = (uint64_t)(uintptr_t)iv - bv;
+  auto row_addr = [](uint32_t e, uint64_t b, uint64_t d1, uint64_t d2) -> uint64_t {
+    const uint64_t m1 = 0ull - (uint64_t)((e >> 30) & 1u), m2 = 0ull - (uint64_t)(e >> 31);
+    return b + (d1 & m1) + (d2 & m2) + (uint64_t)(e & 0x3FFFFFFFu) * (HD * sizeof(T));
   };
   // virtual index of key kk: cache G_j, then local positions lo_j ..
   const int vi_loc0 = lam + eta + (int)(lo_j - n0);
-  auto key_vi = [&](int kk) -> int { return kk < gsj ? sm_G[kk] : vi_loc0 + (kk - gsj); };
 
   // ---- stage W^T (this KV head), H_j^T hi / lo, s_j and G_j
   {
@@ -207,11 +228,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     const float* sj = a.snaps + ((size_t)u * a.nch + j) * kD;
     for (int F = tid; F < kD; F += kThreads) sm_s[F] = sj[F];
     const int32_t* Gj = a.snapG + ((size_t)u * a.nch + j) * lam;
-    // (virtual indices, kept inside the call's rows whatever the snapshot holds)
+    // the key table: cache keys from the snapshot's virtual indices (kept
+    // inside the call's rows whatever the snapshot holds), then the local
+    // positions
     const uint32_t nv = (uint32_t)(lam + eta + vr.T);
-    for (int i = tid; i < gsj; i += kThreads) {
-      const uint32_t g = (uint32_t)Gj[i];
-      sm_G[i] = (int32_t)(g < nv ? g : 0u);
+    for (int i = tid; i < nkeys; i += kThreads) {
+      int vi;
+      if (i < gsj) {
+        const uint32_t g = (uint32_t)Gj[i];
+        vi = (int)(g < nv ? g : 0u);
+      } else {
+        vi = vi_loc0 + (i - gsj);
+      }
+      sm_tab[i] = vsrc(vi);
     }
   }
 
@@ -347,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     for (int q = 0; q < KPT; ++q) {
       const int pc = q * kThreads + tid, kl = pc / (HD / PER), c = (pc % (HD / PER)) * PER;
       const int kk = t0 + kl;
-      kreg[q] = kk < nkeys ? *reinterpret_cast<const u32x4*>(vrow(key_vi(kk), false) + c)
+      kreg[q] = kk < nkeys ? ldg16(row_addr(sm_tab[kk], bk, dk1, dk2) + c * sizeof(T))
                            : u32x4{0, 0, 0, 0};
     }
     if (tid < VITEMS) {
@@ -358,9 +387,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int w = 0; w < VPC; ++w) vreg[kq][w] = u32x4{0, 0, 0, 0};
         if (kk < nkeys) {
-          const u32x4* src = reinterpret_cast<const u32x4*>(vrow(key_vi(kk), true) + c);
+          const uint64_t src = row_addr(sm_tab[kk], bv, dv1, dv2) + c * sizeof(T);
 #pragma unroll
-          for (int w = 0; w < VPC; ++w) vreg[kq][w] = src[w];
+          for (int w = 0; w < VPC; ++w) vreg[kq][w] = ldg16(src + 16 * w);
         }
       }
     }
@@ -547,7 +576,7 @@ template <class DT, int HD>
 static hipError_t launch_attn_t(const AttnArgs& a, int U, hipStream_t st) {
   const int nptile = (a.C + a.ptile - 1) / a.ptile;
   dim3 grid(U, a.nch_launch, nptile);
-  const size_t lds = attn_lds_bytes(HD, a.vr.lam, DT::kSplit);
+  const size_t lds = attn_lds_bytes(HD, a.vr.lam, a.vr.eta, a.C, DT::kSplit);
   const void* fn = (const void*)attn_kernel<DT, HD>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
