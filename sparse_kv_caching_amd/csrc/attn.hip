@@ -115,8 +115,12 @@ __device__ __forceinline__ int vt_cols(int tid) {
   return 8 * (4 * (w >> 1) + (w & 1) + 2 * hh);
 }
 
-__device__ __forceinline__ uint32_t f16_bits(float x) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+// two floats as a pair of fp16 (round to nearest even), the first in the low half
+__device__ __forceinline__ uint32_t f16_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
 }
 
 }  // namespace
@@ -206,67 +210,95 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   // virtual index of key kk: cache G_j, then local positions lo_j ..
   const int vi_loc0 = lam + eta + (int)(lo_j - n0);
 
-  // ---- stage W^T (this KV head), H_j^T hi / lo, s_j and G_j
-  {
-    const T* WT = reinterpret_cast<const T*>(a.WT) + (size_t)kvh * kM * HD;
-    constexpr int WPIECES = kM * HD / PER;
-    for (int i = tid; i < WPIECES; i += kThreads) {
-      const int f = i / (HD / PER), c = (i % (HD / PER)) * PER;
-      *reinterpret_cast<u32x4*>(sm_WT + f * KRS + c) = *reinterpret_cast<const u32x4*>(WT + (size_t)f * HD + c);
-    }
-    const uint16_t* snap = a.snapHT + ((size_t)u * a.nch + j) * 2 * HD * kD;
-    constexpr int HPIECES = HD * (kD / 8);
-    for (int i = tid; i < 2 * HPIECES; i += kThreads) {
-      const int pl = i / HPIECES, rem = i % HPIECES;
-      const int row = rem / (kD / 8), col = (rem % (kD / 8)) * 8;
-      // (rows are 8-byte aligned: two 8-byte stores)
-      const u32x4 x = *reinterpret_cast<const u32x4*>(snap + (size_t)pl * HD * kD + (size_t)row * kD + col);
-      uint16_t* dst = (pl ? sm_HT_lo : sm_HT_hi) + row * HTS + col;
-      *reinterpret_cast<u32x2*>(dst) = u32x2{x[0], x[1]};
-      *reinterpret_cast<u32x2*>(dst + 4) = u32x2{x[2], x[3]};
-    }
-    const float* sj = a.snaps + ((size_t)u * a.nch + j) * kD;
-    for (int F = tid; F < kD; F += kThreads) sm_s[F] = sj[F];
-    const int32_t* Gj = a.snapG + ((size_t)u * a.nch + j) * lam;
-    // the key table: cache keys from the snapshot's virtual indices (kept
-    // inside the call's rows whatever the snapshot holds), then the local
-    // positions
-    const uint32_t nv = (uint32_t)(lam + eta + vr.T);
-    for (int i = tid; i < nkeys; i += kThreads) {
-      int vi;
-      if (i < gsj) {
-        const uint32_t g = (uint32_t)Gj[i];
-        vi = (int)(g < nv ? g : 0u);
-      } else {
-        vi = vi_loc0 + (i - gsj);
-      }
-      sm_tab[i] = vsrc(vi);
+  // ---- Q operands (B of S^T = K Q^T): lane = query r, K-slots 8h .. 8h+7.
+  // 16-bit inputs: loaded here, in flight with the staging loads below
+  u32x4 qh[KB], ql[KB];
+  const T* qrow = reinterpret_cast<const T*>(a.q) +
+                  (((size_t)u * a.g + (wactive ? hd : 0)) * vr.T + (size_t)(qvalid ? qpos - n0 : 0)) * HD;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int k0 = 16 * kb + 8 * h;
+    if constexpr (!DT::kSplit) {
+      qh[kb] = qvalid ? ld16(reinterpret_cast<const uint16_t*>(qrow) + k0) : u32x4{0, 0, 0, 0};
+      ql[kb] = u32x4{0, 0, 0, 0};
     }
   }
 
-  // ---- Q operands (B of S^T = K Q^T): lane = query r, K-slots 8h .. 8h+7
-  u32x4 qh[KB], ql[KB];
+  // ---- stage W^T (this KV head), H_j^T hi / lo, s_j and the key table.
+  // Every global load of this phase is issued before any of them is
+  // stored (fixed trip counts, so the loads stay in flight together): the
+  // phase then costs one round trip to memory, not one per loop iteration.
   {
-    const T* qrow = reinterpret_cast<const T*>(a.q) +
-                    (((size_t)u * a.g + (wactive ? hd : 0)) * vr.T + (size_t)(qvalid ? qpos - n0 : 0)) * HD;
+    const T* WT = reinterpret_cast<const T*>(a.WT) + (size_t)kvh * kM * HD;
+    constexpr int WPIECES = kM * HD / PER;
+    constexpr int HPIECES = HD * (kD / 8);
+    static_assert(WPIECES % kThreads == 0 && (2 * HPIECES) % kThreads == 0, "fixed trip counts");
+    constexpr int WPT = WPIECES / kThreads, HPT = 2 * HPIECES / kThreads;
+    const uint16_t* snap = a.snapHT + ((size_t)u * a.nch + j) * 2 * HD * kD;
+    u32x4 wv[WPT], hv[HPT];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int k0 = 16 * kb + 8 * h;
-      if constexpr (DT::kSplit) {
-        float x[8];
-        if (qvalid) load8_f32(qrow + k0, x);
-        else for (int q = 0; q < 8; ++q) x[q] = 0.f;
-        splitop<DT>(x, qh[kb], ql[kb]);
-      } else {
-        qh[kb] = qvalid ? ld16(reinterpret_cast<const uint16_t*>(qrow) + k0) : u32x4{0, 0, 0, 0};
-        ql[kb] = u32x4{0, 0, 0, 0};
+    for (int k = 0; k < WPT; ++k) {
+      const int i = tid + k * kThreads, f = i / (HD / PER), c = (i % (HD / PER)) * PER;
+      wv[k] = *reinterpret_cast<const u32x4*>(WT + (size_t)f * HD + c);
+    }
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) {
+      const int i = tid + k * kThreads, pl = i / HPIECES, rem = i % HPIECES;
+      const int row = rem / (kD / 8), col = (rem % (kD / 8)) * 8;
+      hv[k] = *reinterpret_cast<const u32x4*>(snap + (size_t)pl * HD * kD + (size_t)row * kD + col);
+    }
+    const float* sj = a.snaps + ((size_t)u * a.nch + j) * kD;
+    const float sv = tid < kD ? sj[tid] : 0.f;
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      const int i = tid + k * kThreads, f = i / (HD / PER), c = (i % (HD / PER)) * PER;
+      *reinterpret_cast<u32x4*>(sm_WT + f * KRS + c) = wv[k];
+    }
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) {
+      const int i = tid + k * kThreads, pl = i / HPIECES, rem = i % HPIECES;
+      const int row = rem / (kD / 8), col = (rem % (kD / 8)) * 8;
+      // (rows are 8-byte aligned: two 8-byte stores)
+      uint16_t* dst = (pl ? sm_HT_lo : sm_HT_hi) + row * HTS + col;
+      *reinterpret_cast<u32x2*>(dst) = u32x2{hv[k][0], hv[k][1]};
+      *reinterpret_cast<u32x2*>(dst + 4) = u32x2{hv[k][2], hv[k][3]};
+    }
+    if (tid < kD) sm_s[tid] = sv;
+    // the key table: cache keys from the snapshot's virtual indices (kept
+    // inside the call's rows whatever the snapshot holds), then the local
+    // positions; the snapshot's entries are read GT per thread at a time
+    const int32_t* Gj = a.snapG + ((size_t)u * a.nch + j) * lam;
+    const uint32_t nv = (uint32_t)(lam + eta + vr.T);
+    constexpr int GT = 4;
+    for (int i0 = 0; i0 < nkeys; i0 += GT * kThreads) {
+      uint32_t gv[GT];
+#pragma unroll
+      for (int k = 0; k < GT; ++k) {
+        const int i = i0 + k * kThreads + tid;
+        gv[k] = i < gsj ? (uint32_t)Gj[i] : 0u;
+      }
+#pragma unroll
+      for (int k = 0; k < GT; ++k) {
+        const int i = i0 + k * kThreads + tid;
+        if (i < nkeys) sm_tab[i] = vsrc(i < gsj ? (int)(gv[k] < nv ? gv[k] : 0u) : vi_loc0 + (i - gsj));
       }
     }
-    // the operands are used here on every path: otherwise their loads would
-    // count as pending in the key loop, which would then wait for all of its
-    // own prefetches before the first product of every tile
+  }
+
+  // (fp32 inputs: split into fp16 hi / lo here.)  The operands are used
+  // here on every path: otherwise their loads would count as pending in the
+  // key loop, which would then wait for all of its own prefetches before the
+  // first product of every tile
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) __asm__ volatile("" :: "v"(qh[kb]), "v"(ql[kb]));
+  for (int kb = 0; kb < KB; ++kb) {
+    if constexpr (DT::kSplit) {
+      const int k0 = 16 * kb + 8 * h;
+      float x[8];
+      if (qvalid) load8_f32(qrow + k0, x);
+      else for (int q = 0; q < 8; ++q) x[q] = 0.f;
+      splitop<DT>(x, qh[kb], ql[kb]);
+    }
+    __asm__ volatile("" :: "v"(qh[kb]), "v"(ql[kb]));
   }
   __syncthreads();
 
@@ -364,39 +396,47 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   // cache keys hidden from the read: the key loop starts past them
   const int kbase = (a.branches & LOLA_READ_CACHE) ? 0 : gsj;
   const int ntiles = (nkeys - kbase + KT - 1) / KT;
-  // one tile's pieces in registers: keys (KPT pieces of 16 bytes) and one
-  // (key pair, 8 columns) item of V, kept as loaded: converting inside the
-  // load's branch would make the wave wait for the load right there, before
-  // the current tile's products
+  // The key loop is a three-stage pipeline over tiles of KT keys.  At the
+  // top of iteration t the LDS holds K of tile t + 1 and V of tile t, the
+  // registers hold the scores of tile t (computed in iteration t - 1) and
+  // the raw global loads of K of tile t + 2 and V of tile t + 1 (issued in
+  // iteration t - 1).  Iteration t stages those loads into the buffers
+  // nobody reads in this iteration, issues the loads of K of tile t + 3
+  // and V of tile t + 2, and multiplies: S_{t+1} = K Q^T next to tile t's
+  // exponentials, then O += V_t P_t.  For 16-bit inputs the staging goes
+  // between the score products and the loads between the value products
+  // (scheduling fences fix the order), so the matrix cores are fed while
+  // the vector, LDS and memory work of the pipeline is done; one barrier
+  // per tile publishes the staged buffers.  Rows past the last key are
+  // loaded from the last key's row (finite values whose weights are
+  // exactly 0 after the mask), so the loads need no branch.
   constexpr int VPC = (int)sizeof(T) / 2;        // 16-byte pieces per 8 V columns
   u32x4 kreg[KPT];
   u32x4 vreg[2][VPC];
-  auto load_tile = [&](int t0) {
+  const bool vthread = VITEMS >= kThreads || tid < VITEMS;   // (wave-uniform)
+  const int vpr = tid % (KT / 2), vcol = vt_cols(tid);        // this thread's V item
+  auto load_k = [&](int t0) {
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
       const int pc = q * kThreads + tid, kl = pc / (HD / PER), c = (pc % (HD / PER)) * PER;
-      const int kk = t0 + kl;
-      kreg[q] = kk < nkeys ? ldg16(row_addr(sm_tab[kk], bk, dk1, dk2) + c * sizeof(T))
-                           : u32x4{0, 0, 0, 0};
+      const int kk = min(t0 + kl, nkeys - 1);
+      kreg[q] = ldg16(row_addr(sm_tab[kk], bk, dk1, dk2) + c * sizeof(T));
     }
-    if (tid < VITEMS) {
-      const int pr = tid % (KT / 2), c = vt_cols(tid);
+  };
+  auto load_v = [&](int t0) {
+    if (vthread) {
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq) {
-        const int kk = t0 + 2 * pr + kq;
+        const int kk = min(t0 + 2 * vpr + kq, nkeys - 1);
+        const uint64_t src = row_addr(sm_tab[kk], bv, dv1, dv2) + vcol * sizeof(T);
 #pragma unroll
-        for (int w = 0; w < VPC; ++w) vreg[kq][w] = u32x4{0, 0, 0, 0};
-        if (kk < nkeys) {
-          const uint64_t src = row_addr(sm_tab[kk], bv, dv1, dv2) + c * sizeof(T);
-#pragma unroll
-          for (int w = 0; w < VPC; ++w) vreg[kq][w] = ldg16(src + 16 * w);
-        }
+        for (int w = 0; w < VPC; ++w) vreg[kq][w] = ldg16(src + 16 * w);
       }
     }
   };
   // buffer b's arrays (selects, so that the offsets stay in registers)
   auto buf_off = [&](const uint32_t (&o)[2], int b) -> uint32_t { return b ? o[1] : o[0]; };
-  auto store_tile = [&](int b) {
+  auto store_k = [&](int b) {
     uint16_t* Kb = (uint16_t*)(smem + buf_off(L.K, b));
     uint16_t* KLb = (uint16_t*)(smem + buf_off(L.KL, b));
 #pragma unroll
@@ -414,67 +454,85 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
         *reinterpret_cast<u32x4*>(Kb + kl * KRS + c) = kreg[q];
       }
     }
-    if (tid < VITEMS) {
-      const int pr = tid % (KT / 2), c = vt_cols(tid);
-      uint16_t* VTb = (uint16_t*)(smem + buf_off(L.VT, b));
-      uint16_t* VTLb = (uint16_t*)(smem + buf_off(L.VTL, b));
-      float vf[2][8];
+  };
+  // V column q (of the thread's 8) of its two keys into V^T buffer b
+  auto store_v_col = [&](int b, int q) {
+    uint16_t* VTb = (uint16_t*)(smem + buf_off(L.VT, b));
+    uint16_t* VTLb = (uint16_t*)(smem + buf_off(L.VTL, b));
+    float vf[2];
 #pragma unroll
-      for (int kq = 0; kq < 2; ++kq)
+    for (int kq = 0; kq < 2; ++kq) {
+      if constexpr (VPC == 1) {   // 8 bf16 in one piece
+        const uint32_t w = vreg[kq][0][q >> 1];
+        vf[kq] = __uint_as_float((q & 1) ? (w & 0xFFFF0000u) : (w << 16));
+      } else {                    // 8 fp32 in two pieces
+        vf[kq] = __uint_as_float(vreg[kq][q >> 2][q & 3]);
+      }
+    }
+    uint32_t* row = reinterpret_cast<uint32_t*>(VTb + (vcol + q) * VTS) + vpr;
+    if constexpr (DT::kSplit) {
+      uint32_t h0, l0, h1, l1;
+      DT::split(vf[0], h0, l0);
+      DT::split(vf[1], h1, l1);
+      *row = h0 | (h1 << 16);
+      *(reinterpret_cast<uint32_t*>(VTLb + (vcol + q) * VTS) + vpr) = l0 | (l1 << 16);
+    } else {
+      *row = f16_pair(vf[0], vf[1]);
+    }
+  };
+  auto store_v = [&](int b) {
+    if (vthread) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          if constexpr (VPC == 1) {   // 8 bf16 in one piece
-            const uint32_t w = vreg[kq][0][q >> 1];
-            vf[kq][q] = __uint_as_float((q & 1) ? (w & 0xFFFF0000u) : (w << 16));
-          } else {                    // 8 fp32 in two pieces
-            vf[kq][q] = __uint_as_float(vreg[kq][q >> 2][q & 3]);
-          }
-        }
+      for (int q = 0; q < 8; ++q) store_v_col(b, q);
+    }
+  };
+  // S^T = K Q^T of the tile in K buffer b (32 keys x 32 queries per half kh)
+  auto scores = [&](int b, f32x16 (&Sx)[2]) {
+    const uint16_t* Kb = (const uint16_t*)(smem + buf_off(L.K, b));
+    const uint16_t* KLb = (const uint16_t*)(smem + buf_off(L.KL, b));
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        uint32_t* row = reinterpret_cast<uint32_t*>(VTb + (c + q) * VTS) + pr;
+    for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Sx[kh][i] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int k0 = 16 * kb + 8 * h;
+        const u32x4 ah = ld16(Kb + (32 * kh + r) * KRS + k0);
+        Sx[kh] = DT::mma(ah, qh[kb], Sx[kh]);
         if constexpr (DT::kSplit) {
-          uint32_t h0, l0, h1, l1;
-          DT::split(vf[0][q], h0, l0);
-          DT::split(vf[1][q], h1, l1);
-          *row = h0 | (h1 << 16);
-          *(reinterpret_cast<uint32_t*>(VTLb + (c + q) * VTS) + pr) = l0 | (l1 << 16);
-        } else {
-          *row = f16_bits(vf[0][q]) | (f16_bits(vf[1][q]) << 16);
+          const u32x4 al = ld16(KLb + (32 * kh + r) * KRS + k0);
+          Sx[kh] = DT::mma(ah, ql[kb], Sx[kh]);
+          Sx[kh] = DT::mma(al, qh[kb], Sx[kh]);
         }
       }
     }
   };
+  f32x16 S[2];
   if (ntiles > 0) {
-    load_tile(kbase);
-    store_tile(0);
+    load_k(kbase);
+    load_v(kbase);
+    store_k(0);
+    store_v(0);
   }
+  if (ntiles > 1) {
+    load_k(kbase + KT);
+    store_k(1);
+    load_v(kbase + KT);               // staged in iteration 0
+  }
+  if (ntiles > 2) load_k(kbase + 2 * KT);   // staged in iteration 0
+  __syncthreads();
+  if (ntiles > 0 && wactive && kbase <= wlast) scores(0, S);
+  // (iteration 0 overwrites K buffer 0 with tile 2: every wave has read it)
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int t0 = kbase + t * KT, b = t & 1;
-    if (t + 1 < ntiles) load_tile(t0 + KT);       // in flight during this tile's products
+    // staged here: K of tile t + 2 into K buffer b, V of tile t + 1 into V
+    // buffer b ^ 1; loaded here: K of tile t + 3, V of tile t + 2
+    const bool stk = t + 2 < ntiles, stv = t + 1 < ntiles;
+    const bool ldk = t + 3 < ntiles, ldv = t + 2 < ntiles;
     if (wactive && t0 <= wlast) {
-      const uint16_t* Kb = (const uint16_t*)(smem + buf_off(L.K, b));
-      const uint16_t* KLb = (const uint16_t*)(smem + buf_off(L.KL, b));
       const uint16_t* VTb = (const uint16_t*)(smem + buf_off(L.VT, b));
       const uint16_t* VTLb = (const uint16_t*)(smem + buf_off(L.VTL, b));
-      f32x16 S[2];
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) S[kh][i] = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int k0 = 16 * kb + 8 * h;
-          const u32x4 ah = ld16(Kb + (32 * kh + r) * KRS + k0);
-          S[kh] = DT::mma(ah, qh[kb], S[kh]);
-          if constexpr (DT::kSplit) {
-            const u32x4 al = ld16(KLb + (32 * kh + r) * KRS + k0);
-            S[kh] = DT::mma(ah, ql[kb], S[kh]);
-            S[kh] = DT::mma(al, qh[kb], S[kh]);
-          }
-        }
-      }
       // masks only where the tile has keys past the end or past the wave's
       // first query position (every query of the wave sees a full tile);
       // the scale goes into the exponent's fma.  Key kk is visible to the
@@ -513,19 +571,21 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
       // query: its weights are then 0, exp2(-inf))
       const float msub = m2 == -INFINITY ? 0.f : m2;
       float rs = 0.f;
+      if constexpr (DT::kSplit) {
+        if (stk) store_k(b);
+        if (stv) store_v(b ^ 1);
+        if (ldk) load_k(t0 + 3 * KT);
+        if (ldv) load_v(t0 + 2 * KT);
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
+        for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          S[kh][i] = __builtin_amdgcn_exp2f(fmaf(S[kh][i], scale2, -msub));
-          rs += S[kh][i];
-        }
-      rs = half_sum(rs);
-      l += rs;
+          for (int i = 0; i < 16; ++i) {
+            S[kh][i] = __builtin_amdgcn_exp2f(fmaf(S[kh][i], scale2, -msub));
+            rs += S[kh][i];
+          }
 #pragma unroll
-      for (int kb = 0; kb < KT / 16; ++kb) {
-        const int kh = kb >> 1, i0 = 8 * (kb & 1);
-        if constexpr (DT::kSplit) {
+        for (int kb = 0; kb < KT / 16; ++kb) {
+          const int kh = kb >> 1, i0 = 8 * (kb & 1);
           u32x4 ph8, pl8;
           float pv[8];
 #pragma unroll
@@ -540,20 +600,84 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
             O[mo] = DT::mma(vh, pl8, O[mo]);
             O[mo] = DT::mma(vl, ph8, O[mo]);
           }
-        } else {
-          f16x8 p8;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) p8[q] = (_Float16)S[kh][i0 + q];
-#pragma unroll
-          for (int mo = 0; mo < NMT; ++mo) {
-            const int row = 32 * mo + r;
-            const f16x8 vh = __builtin_bit_cast(f16x8, sigma_load(VTb + row * VTS + 16 * kb, h));
-            O[mo] = mfma_f16(vh, p8, O[mo]);
-          }
         }
+        // (fp32 inputs take three products per operand pair: the next
+        // tile's scores come after this tile's products, in the same
+        // registers, as two sets of them would not fit)
+        scores(b ^ 1, S);
+      } else {
+        // The next tile's score products, one at a time, each followed by
+        // EPC of this tile's weights (the exponentials, rounded to fp16 as
+        // the value products take them) and, early on, the staging of the
+        // loaded rows; a scheduling fence after each step keeps that order.
+        // Operands are read from LDS LA products ahead.  (After a wave's
+        // last tile the products are taken of whatever the buffer holds and
+        // never used.)
+        constexpr int LA = 3;
+        constexpr int NS = 2 * KB;                 // score products
+        constexpr int EPC = 32 / NS;               // weights per product
+        constexpr int NP = (KT / 16) * NMT;        // value products
+        static_assert(NS >= 8 && NP >= 4, "staging and loads are spread over these steps");
+        const uint16_t* Kn = (const uint16_t*)(smem + buf_off(L.K, b ^ 1));
+        auto kaddr = [&](int c) { return Kn + (32 * (c & 1) + r) * KRS + 16 * (c >> 1) + 8 * h; };
+        auto vaddr = [&](int c) { return VTb + (32 * (c % NMT) + r) * VTS + 16 * (c / NMT); };
+        u32x4 ka[LA], va[LA];
+#pragma unroll
+        for (int i = 0; i < LA; ++i) ka[i] = ld16(kaddr(i));
+        f32x16 Sn[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) Sn[kh][i] = 0.f;
+        f16x8 p8[KT / 16];
+#pragma unroll
+        for (int c = 0; c < NS; ++c) {
+          const int kh = c & 1, kb = c >> 1;
+          const u32x4 ac = ka[c % LA];
+          if (c + LA < NS) ka[c % LA] = ld16(kaddr(c + LA));
+          else va[(c + LA - NS) % LA] = sigma_load(vaddr(c + LA - NS), h);
+          Sn[kh] = DT::mma(ac, qh[kb], Sn[kh]);
+#pragma unroll
+          for (int x = 0; x < EPC; ++x) {
+            const int e = EPC * c + x, kp = e >> 3, q = e & 7;   // weight e: block kp, slot q
+            p8[kp][q] = (_Float16)__builtin_amdgcn_exp2f(
+                fmaf(S[kp >> 1][8 * (kp & 1) + q], scale2, -msub));
+          }
+          if (c == 0 && stk) store_k(b);
+          if (c < 8 && stv && vthread) store_v_col(b ^ 1, c);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // the value products, each with one step of the row sum (pairwise
+        // dot products of the same rounded weights with 1), and the next
+        // loads
+        constexpr int DPC = 16 / NP;               // row-sum steps per product
+        constexpr f16x2 one2 = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+        for (int c = 0; c < NP; ++c) {
+          const int kb = c / NMT, mo = c % NMT;
+          const u32x4 vc = va[c % LA];
+          if (c + LA < NP) va[c % LA] = sigma_load(vaddr(c + LA), h);
+          O[mo] = mfma_f16(__builtin_bit_cast(f16x8, vc), p8[kb], O[mo]);
+#pragma unroll
+          for (int x = 0; x < DPC; ++x) {
+            const int pq = DPC * c + x, kp = pq >> 2, w = pq & 3;   // pair w of block kp
+            rs = __builtin_amdgcn_fdot2(f16x2{p8[kp][2 * w], p8[kp][2 * w + 1]}, one2, rs, false);
+          }
+          if (c == 1 && ldk) load_k(t0 + 3 * KT);
+          if (c == 3 && ldv) load_v(t0 + 2 * KT);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) S[kh] = Sn[kh];
       }
+      rs = half_sum(rs);
+      l += rs;
+    } else {
+      if (stk) store_k(b);
+      if (stv) store_v(b ^ 1);
+      if (ldk) load_k(t0 + 3 * KT);
+      if (ldv) load_v(t0 + 2 * KT);
     }
-    if (t + 1 < ntiles) store_tile(b ^ 1);
     __syncthreads();
   }
 
