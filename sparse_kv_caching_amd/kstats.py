@@ -1,0 +1,79 @@
+"""Per-workload kernel durations from a rocprofv3 kernel trace.
+
+``rocprofv3 --kernel-trace --stats`` aggregates each kernel over the whole
+run; ``bench.py`` runs several prefill workloads one after the other, so its
+per-kernel statistics mix them.  This splits the trace
+(``<dir>/run_kernel_trace.csv``) by workload: the dispatches of each prefill
+kernel (φ, chain, attention, finalize), in time order, are cut into
+consecutive segments of the given call counts, one per workload in the order
+``bench.py`` runs them.  Every other kernel is reported over the whole run.
+
+    python3 -m sparse_kv_caching_amd.kstats <dir>/run_kernel_trace.csv \
+        --segments long_32k:12,batched_8k:12,llama8b_4k:12,decode_b64:1
+
+prints a Markdown table (calls, average / min / max in microseconds).
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+from collections import defaultdict
+
+PREFILL = ("lola::phi_kernel", "lola::chain_kernel", "lola::attn_kernel",
+           "lola::finalize_cache_kernel", "lola::finalize_ring_kernel")
+
+
+def _family(name: str) -> str:
+    for p in PREFILL:
+        if p in name:
+            return p
+    return ""
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("trace")
+    ap.add_argument("--segments", required=True,
+                    help="workload:calls,... in the order the prefill workloads ran")
+    args = ap.parse_args()
+    segs = []
+    for item in args.segments.split(","):
+        w, n = item.split(":")
+        segs.append((w, int(n)))
+    rows = []
+    with open(args.trace) as fh:
+        for r in csv.DictReader(fh):
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            rows.append((t0, r["Kernel_Name"], (t1 - t0) / 1e3))
+    rows.sort()
+    fam_seen = defaultdict(int)
+    groups = defaultdict(list)        # (label, kernel name) -> durations
+    for t0, name, us in rows:
+        fam = _family(name)
+        label = "whole run"
+        if fam:
+            i = fam_seen[fam]
+            fam_seen[fam] += 1
+            acc = 0
+            label = "after the listed segments"
+            for w, n in segs:
+                if i < acc + n:
+                    label = w
+                    break
+                acc += n
+        short = name.split("(")[0].replace("void ", "")
+        groups[(label, short)].append(us)
+    order = [w for w, _ in segs] + ["after the listed segments", "whole run"]
+    print("| Workload | Kernel | Calls | Avg (us) | Min (us) | Max (us) |")
+    print("|---|---|---|---|---|---|")
+    for label in order:
+        items = sorted(((k, v) for k, v in groups.items() if k[0] == label),
+                       key=lambda kv: -sum(kv[1]))
+        for (lab, name), v in items:
+            print("| %s | `%s` | %d | %.1f | %.1f | %.1f |"
+                  % (lab, name, len(v), sum(v) / len(v), min(v), max(v)))
+
+
+if __name__ == "__main__":
+    main()

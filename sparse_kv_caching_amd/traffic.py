@@ -16,6 +16,10 @@ Two modes:
               counters calibrate the scale: bytes = counter * 1024 * factor
               with factor = copy bytes / (copy counter * 1024).
 
+``counters``  prints one kernel's SQ / TCC counters (any number of
+              ``--pmc`` folders of the same run command) with per-wave and
+              per-cycle ratios.
+
 ``summarize`` reads the two rocprofv3 output folders and writes
               ``profiles/traffic_<kernel>_<workload>.txt`` with the measured
               bytes per launch (the average over the measured launches), the
@@ -174,6 +178,43 @@ def _summarize(args):
     print(open(out).read())
 
 
+def _counters(args):
+    """SQ / TCC counters of one kernel (its last `--last` launches, averaged)
+    from several rocprofv3 --pmc folders, with per-wave and per-cycle ratios."""
+    fname, prefix = KERNELS[args.kernel]
+    vals = {}
+    for folder in args.dirs:
+        files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+        for path in files:
+            per = defaultdict(lambda: defaultdict(float))
+            with open(path) as fh:
+                for row in csv.DictReader(fh):
+                    if prefix not in row.get("Kernel_Name", ""):
+                        continue
+                    did = int(row.get("Dispatch_Id") or row.get("Correlation_Id") or 0)
+                    per[row["Counter_Name"]][did] += float(row["Counter_Value"])
+            for name, byd in per.items():
+                last = [byd[d] for d in sorted(byd)][-args.last:]
+                vals[name] = sum(last) / len(last)
+    print("[%s, %s, source %s]" % (prefix, args.workload, kernel_source_hash(fname)))
+    for k in sorted(vals):
+        print("%s = %.6g" % (k, vals[k]))
+    w = vals.get("SQ_WAVES")
+    if w:
+        for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD"):
+            if k in vals:
+                print("per_wave_%s = %.1f" % (k[9:].lower(), vals[k] / w))
+    wc = vals.get("SQ_WAVE_CYCLES")
+    if wc:
+        for k in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                  "SQ_ACTIVE_INST_LDS"):
+            if k in vals:
+                print("%s_fraction_of_wave_cycles = %.3f" % (k[3:].lower(), vals[k] / wc))
+    if "TCC_HIT_sum" in vals and "TCC_MISS_sum" in vals:
+        h, m = vals["TCC_HIT_sum"], vals["TCC_MISS_sum"]
+        print("l2_hit_rate = %.3f" % (h / max(h + m, 1.0)))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -187,9 +228,16 @@ def main():
     s.add_argument("--write", required=True)
     s.add_argument("--last", type=int, default=1)
     s.add_argument("--algorithmic", type=int, default=0)
+    c = sub.add_parser("counters")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--kernel", required=True, choices=sorted(KERNELS))
+    c.add_argument("--dirs", nargs="+", required=True)
+    c.add_argument("--last", type=int, default=1)
     args = ap.parse_args()
     if args.mode == "run":
         _run(args)
+    elif args.mode == "counters":
+        _counters(args)
     else:
         _summarize(args)
 
