@@ -263,7 +263,8 @@ enum {
   LOLA_KERNEL_ATTN = 2,      /* chunk attention + linear read */
   LOLA_KERNEL_FINALIZE = 3,  /* cache / window write-back */
   LOLA_KERNEL_DECODE = 4,    /* decode step */
-  LOLA_KERNEL_COUNT = 5
+  LOLA_KERNEL_OVERLAP = 5,   /* chain and the read of finished chunks in one launch */
+  LOLA_KERNEL_COUNT = 6
 };
 
 /* Per-kernel timing with HIP events recorded on the launch stream around
@@ -332,19 +333,32 @@ int lola_state_import_sequence(lola_state* st, int b, const lola_state_view* src
 int lola_state_export_sequence(const lola_state* st, int b, lola_state_view* dst, void* stream);
 int lola_state_positions(const lola_state* st, int64_t* out);
 
-/* Debug settings of a state (host-side, take effect at the next launch; not
- * exported, kept across lola_state_reset):
+/* Debug and schedule settings of a state (host-side, take effect at the next
+ * launch; not exported, kept across lola_state_reset):
  *   LOLA_DEBUG_SPIN_LIMIT     polls of one exchange word of the chain before
- *                             its partner workgroup counts as lost (>= 1;
- *                             0 restores the default, 2^22);
+ *                             its partner workgroup counts as lost, and of
+ *                             the published-chunk counter by a concurrent
+ *                             read (>= 1; 0 restores the default, 2^22);
  *   LOLA_DEBUG_CHAIN_FAIL_AT  every workgroup of the chain gives up at this
  *                             exchange step of a call, as if a partner were
- *                             lost (-1: never, the default).
- * Both exist to exercise the failure path: the chain sets its device fault
- * flag and ends, the later kernels of the call return untouched, and
+ *                             lost (-1: never, the default);
+ *   LOLA_DEBUG_OVERLAP        schedule of a chunked prefill call: 0 = the chain
+ *                             over every chunk, then the read of every chunk;
+ *                             1 = one launch in which the chain runs on half
+ *                             of the compute units and the read of each chunk
+ *                             starts as soon as the chain has published that
+ *                             chunk's state (when the chain fits half of the
+ *                             compute units and the call has >= 2 chunks;
+ *                             otherwise as 0); -1 (default) = 1 for calls of
+ *                             >= 4 chunks, else 0.
+ *                             Both schedules give bitwise the same results
+ *                             (the chain's results do not depend on its
+ *                             workgroup count).
+ * The first two exist to exercise the failure path: the chain sets its device
+ * fault flag and ends, the later kernels of the call return untouched, and
  * lola_state_check() reports LOLA_ERR_STATE.
  * Errors: INVALID_ARG (NULL state, unknown key, value out of range). */
-enum { LOLA_DEBUG_SPIN_LIMIT = 0, LOLA_DEBUG_CHAIN_FAIL_AT = 1 };
+enum { LOLA_DEBUG_SPIN_LIMIT = 0, LOLA_DEBUG_CHAIN_FAIL_AT = 1, LOLA_DEBUG_OVERLAP = 2 };
 int lola_debug_set(lola_state* st, int key, long long value);
 
 /* Text of a status code, and the last error detail of the calling thread. */

@@ -17,8 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "liblola.so")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "phi.hip", "chain.hip", "attn.hip", "decode.hip", "state.hip", "diag.hip",
-           "score.hip"]
+SOURCES = ["api.hip", "phi.hip", "chain.hip", "attn.hip", "fused.hip", "decode.hip", "state.hip",
+           "diag.hip", "score.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

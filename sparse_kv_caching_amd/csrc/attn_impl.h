@@ -1,0 +1,739 @@
+// K3: the read of every chunk, LoLA notes §2.5, Eq. (14):
+//
+//   y_t = (H_j^T phi(q_t) + sum_{i in V(t)} a_ti v_i)
+//         / (phi(q_t)^T s_j + sum_{i in V(t)} a_ti),   a_ti = exp(q_t.k_i / sqrt(d)),
+//
+// V(t) = G_j (cache at chunk start) plus the local positions
+// max(0, n_j - eta) .. t (window and the causal prefix of the chunk).  All
+// chunks run in parallel: they only need the per-chunk snapshots (H_j, s_j,
+// G_j) written by the chain kernel.
+//
+// One workgroup = one unit, one chunk, one tile of up to 256 / g positions,
+// and 8 waves; wave = one q-head x 32 positions, so the GQA heads of a unit
+// share every staged K/V tile.  Keys are staged 64 at a time, double-buffered:
+// the global loads of tile t + 1 are in flight while tile t is multiplied,
+// and one barrier per tile separates the buffers.  Scores are computed
+// transposed, S^T = K Q^T (32 keys x 32 queries per MFMA), so each lane owns
+// one query and softmax statistics need a single cross-half exchange; P then
+// feeds O^T += V^T P^T straight from registers (the K index of that MFMA is
+// permuted to match the result layout, see common.h), with V staged
+// transposed (key pairs packed per dword).
+//
+// Exponentials are unshifted in Eq. (14); here they are shifted by a running
+// maximum m >= 0 (log2 domain) and the linear terms are scaled by the same
+// 2^{-m}:  y = (2^-m N_lin + sum 2^{x-m} v) / (2^-m z_lin + sum 2^{x-m}),
+// which is the same quantity.  The linear read is done first with m = 0.
+//
+// Precision: q.k is exact-product bf16 MFMA with fp32 accumulation; P and V
+// go through fp16 MFMA (11-bit significand, P in [0, 1]); the linear read
+// uses the hi/lo bf16 split on both phi(q) and H.  fp32 inputs split every
+// operand into hi/lo fp16 (three passes, ~2^-22 per product).
+#pragma once
+#include "internal.h"
+
+namespace lola {
+
+namespace attn_ns {
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int KT = 64;        // keys per staged tile
+constexpr float kSlack = 8.f; // log2 headroom of the softmax weights over the running maximum
+constexpr int HTS = kD + 4;   // LDS row of H^T (16-bit elements): 66 dwords, so that the 32
+                              // rows of a 64-bit operand read fall on distinct bank pairs
+constexpr int VTS = KT + 4;   // LDS row of the V^T tile (keys): 34 dwords, so that the 32 rows of a
+                              // 64-bit operand read fall on distinct bank pairs
+
+// Byte offsets of the LDS arrays; the key phase reuses the region of the
+// linear-read phase.
+struct AttnLayout {
+  uint32_t tab;                                // both phases: row of every key of the chunk
+  uint32_t WT, HT_hi, HT_lo, s;                // linear-read phase
+  uint32_t K[2], KL[2], VT[2], VTL[2];         // key phase, two buffers
+  uint32_t total;
+};
+
+inline __host__ __device__ uint32_t al16(uint32_t x) { return (x + 15u) & ~15u; }
+
+// max / sum of a lane's value and the value 32 lanes away, in every lane, on
+// the VALU: v_permlane32_swap of x with itself gives r0 = x[l % 32] and
+// r1 = x[l % 32 + 32] in lane l (the same two operands, in the same order,
+// in both halves)
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__host__ __device__ inline AttnLayout attn_layout(int d, int lam, int eta, int C, bool f32) {
+  AttnLayout L;
+  uint32_t off = 0;
+  auto take = [&](uint32_t b) { const uint32_t o = off; off = al16(off + b); return o; };
+  const uint32_t esz = f32 ? 4 : 2;
+  // the keys a chunk's queries see: the cache at chunk start, the window,
+  // the chunk's own positions; per key its source (cache, ring, input) and
+  // row, packed as (source << 30) | row
+  L.tab = take((uint32_t)(lam + eta + C) * 4);
+  const uint32_t base = off;
+  L.WT = take((uint32_t)kM * (d + 8) * esz);          // [kM][d + 8] W^T, input dtype
+  L.HT_hi = take((uint32_t)d * HTS * 2);               // [d][HTS]
+  L.HT_lo = take((uint32_t)d * HTS * 2);
+  L.s = take(kD * 4);
+  const uint32_t phaseA = off;
+  off = base;
+  for (int b = 0; b < 2; ++b) {
+    L.K[b] = take((uint32_t)KT * (d + 8) * 2);         // [KT][d + 8] bf16 (fp32 inputs: fp16 hi)
+    L.KL[b] = take(f32 ? (uint32_t)KT * (d + 8) * 2 : 16);   //                  fp16 lo
+    L.VT[b] = take((uint32_t)d * VTS * 2);             // [d][VTS] fp16 (fp32 inputs: hi)
+    L.VTL[b] = take(f32 ? (uint32_t)d * VTS * 2 : 16); //                       lo
+  }
+  L.total = phaseA > off ? phaseA : off;
+  return L;
+}
+
+__device__ __forceinline__ u32x2 ld8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// 16 bytes written during this launch by another workgroup: two coherent
+// (device-scope atomic) 8-byte loads
+__device__ __forceinline__ u32x4 ld16_coherent(const uint16_t* p) {
+  uint64_t* q = reinterpret_cast<uint64_t*>(const_cast<uint16_t*>(p));
+  const uint64_t x = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t y = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return u32x4{(uint32_t)x, (uint32_t)(x >> 32), (uint32_t)y, (uint32_t)(y >> 32)};
+}
+
+// 16 bytes at a global-memory byte address (a global load, not a flat one)
+__device__ __forceinline__ u32x4 ldg16(uint64_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(addr);
+}
+
+// operand with K-slots sigma_h: elements [4h, 4h+4) and [8+4h, 8+4h+4) of a 16-block
+__device__ __forceinline__ u32x4 sigma_load(const uint16_t* row16, int h) {
+  u32x2 a = ld8(row16 + 4 * h), b = ld8(row16 + 8 + 4 * h);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+
+// First V column (of 8) of thread tid's item in the V^T staging: the two
+// half-waves take column groups 2 apart (V^T rows 16 apart, 544 dwords:
+// 32 banks apart), so that their 4-byte writes to one key-pair column fall on
+// all 64 banks
+__device__ __forceinline__ int vt_cols(int tid) {
+  const int w = tid >> 6, hh = (tid >> 5) & 1;
+  return 8 * (4 * (w >> 1) + (w & 1) + 2 * hh);
+}
+
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+// two floats as a pair of fp16 (round to nearest even), the first in the low half
+__device__ __forceinline__ uint32_t f16_pair(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
+
+}  // namespace attn_ns
+
+// One workgroup of the read: unit u, chunk ch0 + jrel, position tile pt.
+template <class DT, int HD>
+__device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, int pt_) {
+  using namespace attn_ns;
+  using T = typename DT::T;
+  constexpr int KB = HD / 16;     // 16-wide K blocks over the head dim
+  constexpr int NMT = HD / 32;    // 32-row tiles of the output
+  constexpr int KRS = HD + 8;     // LDS row of a staged key (elements)
+  constexpr int PER = 16 / (int)sizeof(T);       // input elements per 16-byte piece
+  constexpr int KPT = KT * HD / PER / kThreads;  // key pieces per thread and tile
+  constexpr int VITEMS = (KT / 2) * (HD / 8);    // (key pair, 8 columns) items per tile
+  const VirtRows vr = a.vr;
+  const int lam = vr.lam, eta = vr.eta;
+  // unit fastest: with the unit count a multiple of 8, a unit's chunks share
+  // an XCD (blocks are dealt to the 8 XCDs round-robin) and its K/V rows,
+  // re-read by every chunk, stay in that XCD's L2
+  const int u = u_, j = a.ch0 + jrel, pt = pt_;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, r = lane & 31;
+  const int kvh = u % a.Hkv;
+  const long long n0 = vr.n0;
+  const long long nj = n0 + (long long)j * a.C;
+  const int cj = min(a.C, vr.T - j * a.C);
+  const long long pbase = nj + (long long)pt * a.ptile;
+  const long long pend = min(pbase + a.ptile, nj + cj);     // exclusive
+  if (pbase >= pend) return;                                // whole block idle (uniform)
+  // the chain gave up: the snapshots were not written (uniform)
+  if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile const int*>(a.err)) != 0) return;
+  // (concurrent read) wait until the chain has published this chunk's
+  // snapshot: one thread polls, bounded; a chain that gave up, or a poll that
+  // runs out, ends the workgroup (the latter sets the error flag)
+  if (a.ready) {
+    __shared__ int go;
+    if (threadIdx.x == 0) {
+      const int need = a.ready_need * (j + 1);
+      int ok = 1, spins = 0;
+      while (__hip_atomic_load(a.ready + u_, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+        if (*reinterpret_cast<volatile const int*>(a.err) != 0) { ok = 0; break; }
+        if (++spins > a.spin_limit) {
+          atomicOr(a.err, 2);
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
+      go = ok;
+    }
+    __syncthreads();
+    if (!go) return;
+  }
+  const int hd = wave / a.nblk, pblk = wave % a.nblk;
+  const long long p0 = pbase + 32LL * pblk;
+  const bool wactive = hd < a.g && p0 < pend;
+  const long long qpos = p0 + r;
+  const bool qvalid = wactive && qpos < pend;
+  const int gsj = (int)min((long long)lam, max(0LL, nj - eta));
+  const long long lo_j = max(0LL, nj - eta);
+  const int nkeys = gsj + (int)(pend - lo_j);
+  // last key any query of this wave sees (wave-uniform)
+  const int wlast = gsj + (int)(min(p0 + 31, pend - 1) - lo_j);
+  // keys 0 .. vis_end - 1 are visible to the lane's query (cache, window and
+  // the causal prefix of the chunk up to and including the query)
+  const int vis_end = (int)min((long long)nkeys, gsj + (qpos - lo_j) + 1);
+  const int n0e = eta > 0 ? (int)(n0 % eta) : 0;            // ring slot of position n0 - eta
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const AttnLayout L = attn_layout(HD, lam, eta, a.C, DT::kSplit);
+  uint32_t* sm_tab = (uint32_t*)(smem + L.tab);
+  T* sm_WT = (T*)(smem + L.WT);
+  uint16_t* sm_HT_hi = (uint16_t*)(smem + L.HT_hi);
+  uint16_t* sm_HT_lo = (uint16_t*)(smem + L.HT_lo);
+  float* sm_s = (float*)(smem + L.s);
+
+  // the three sources of key rows, this unit's part
+  const T* ck = reinterpret_cast<const T*>(vr.cache_k) + (size_t)u * lam * HD;
+  const T* cv = reinterpret_cast<const T*>(vr.cache_v) + (size_t)u * lam * HD;
+  const T* rk = reinterpret_cast<const T*>(vr.ring_k) + (size_t)u * eta * HD;
+  const T* rv = reinterpret_cast<const T*>(vr.ring_v) + (size_t)u * eta * HD;
+  const T* ik = reinterpret_cast<const T*>(vr.in_k) + (size_t)u * vr.T * HD;
+  const T* iv = reinterpret_cast<const T*>(vr.in_v) + (size_t)u * vr.T * HD;
+  // (source, row) of virtual index vi: cache slot, ring slot or input row
+  auto vsrc = [&](int vi) -> uint32_t {
+    if (vi < lam) return (uint32_t)vi;
+    const int off = vi - lam;                       // position n0 - eta + off
+    if (off < eta) {
+      int slot = n0e + off;
+      if (slot >= eta) slot -= eta;
+      return (1u << 30) | (uint32_t)slot;
+    }
+    return (2u << 30) | (uint32_t)(off - eta);
+  };
+  // the byte address of key kk's row from the table entry e (built once per
+  // workgroup below): the cache base plus the distance to the ring (source
+  // bit 0) or to the input (source bit 1), plus the row -- adds and masks,
+  // no selection among pointers
+  const uint64_t bk = (uint64_t)(uintptr_t)ck, bv = (uint64_t)(uintptr_t)cv;
+  const uint64_t dk1 = (uint64_t)(uintptr_t)rk - bk, dk2 = (uint64_t)(uintptr_t)ik - bk;
+  const uint64_t dv1 = (uint64_t)(uintptr_t)rv - bv, dv2 = (uint64_t)(uintptr_t)iv - bv;
+  auto row_addr = [](uint32_t e, uint64_t b, uint64_t d1, uint64_t d2) -> uint64_t {
+    const uint64_t m1 = 0ull - (uint64_t)((e >> 30) & 1u), m2 = 0ull - (uint64_t)(e >> 31);
+    return b + (d1 & m1) + (d2 & m2) + (uint64_t)(e & 0x3FFFFFFFu) * (HD * sizeof(T));
+  };
+  // virtual index of key kk: cache G_j, then local positions lo_j ..
+  const int vi_loc0 = lam + eta + (int)(lo_j - n0);
+
+  // ---- Q operands (B of S^T = K Q^T): lane = query r, K-slots 8h .. 8h+7.
+  // 16-bit inputs: loaded here, in flight with the staging loads below
+  u32x4 qh[KB], ql[KB];
+  const T* qrow = reinterpret_cast<const T*>(a.q) +
+                  (((size_t)u * a.g + (wactive ? hd : 0)) * vr.T + (size_t)(qvalid ? qpos - n0 : 0)) * HD;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int k0 = 16 * kb + 8 * h;
+    if constexpr (!DT::kSplit) {
+      qh[kb] = qvalid ? ld16(reinterpret_cast<const uint16_t*>(qrow) + k0) : u32x4{0, 0, 0, 0};
+      ql[kb] = u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // ---- stage W^T (this KV head), H_j^T hi / lo, s_j and the key table.
+  // Every global load of this phase is issued before any of them is
+  // stored (fixed trip counts, so the loads stay in flight together): the
+  // phase then costs one round trip to memory, not one per loop iteration.
+  {
+    const T* WT = reinterpret_cast<const T*>(a.WT) + (size_t)kvh * kM * HD;
+    constexpr int WPIECES = kM * HD / PER;
+    constexpr int HPIECES = HD * (kD / 8);
+    static_assert(WPIECES % kThreads == 0 && (2 * HPIECES) % kThreads == 0, "fixed trip counts");
+    constexpr int WPT = WPIECES / kThreads, HPT = 2 * HPIECES / kThreads;
+    const uint16_t* snap = a.snapHT + ((size_t)u * a.nch + j) * 2 * HD * kD;
+    u32x4 wv[WPT], hv[HPT];
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      const int i = tid + k * kThreads, f = i / (HD / PER), c = (i % (HD / PER)) * PER;
+      wv[k] = *reinterpret_cast<const u32x4*>(WT + (size_t)f * HD + c);
+    }
+    const bool coh = a.ready != nullptr;   // snapshots written during this launch
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) {
+      const int i = tid + k * kThreads, pl = i / HPIECES, rem = i % HPIECES;
+      const int row = rem / (kD / 8), col = (rem % (kD / 8)) * 8;
+      const uint16_t* src = snap + (size_t)pl * HD * kD + (size_t)row * kD + col;
+      hv[k] = coh ? ld16_coherent(src) : *reinterpret_cast<const u32x4*>(src);
+    }
+    const float* sj = a.snaps + ((size_t)u * a.nch + j) * kD;
+    float sv = 0.f;
+    if (tid < kD)
+      sv = coh ? __uint_as_float(__hip_atomic_load(const_cast<uint32_t*>(
+                                                       reinterpret_cast<const uint32_t*>(sj) + tid),
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+               : sj[tid];
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+      const int i = tid + k * kThreads, f = i / (HD / PER), c = (i % (HD / PER)) * PER;
+      *reinterpret_cast<u32x4*>(sm_WT + f * KRS + c) = wv[k];
+    }
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) {
+      const int i = tid + k * kThreads, pl = i / HPIECES, rem = i % HPIECES;
+      const int row = rem / (kD / 8), col = (rem % (kD / 8)) * 8;
+      // (rows are 8-byte aligned: two 8-byte stores)
+      uint16_t* dst = (pl ? sm_HT_lo : sm_HT_hi) + row * HTS + col;
+      *reinterpret_cast<u32x2*>(dst) = u32x2{hv[k][0], hv[k][1]};
+      *reinterpret_cast<u32x2*>(dst + 4) = u32x2{hv[k][2], hv[k][3]};
+    }
+    if (tid < kD) sm_s[tid] = sv;
+    // the key table: cache keys from the snapshot's virtual indices (kept
+    // inside the call's rows whatever the snapshot holds), then the local
+    // positions; the snapshot's entries are read GT per thread at a time
+    const int32_t* Gj = a.snapG + ((size_t)u * a.nch + j) * lam;
+    const uint32_t nv = (uint32_t)(lam + eta + vr.T);
+    constexpr int GT = 4;
+    for (int i0 = 0; i0 < nkeys; i0 += GT * kThreads) {
+      uint32_t gv[GT];
+#pragma unroll
+      for (int k = 0; k < GT; ++k) {
+        const int i = i0 + k * kThreads + tid;
+        gv[k] = i >= gsj ? 0u
+                : coh ? (uint32_t)__hip_atomic_load(const_cast<int32_t*>(Gj) + i, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                      : (uint32_t)Gj[i];
+      }
+#pragma unroll
+      for (int k = 0; k < GT; ++k) {
+        const int i = i0 + k * kThreads + tid;
+        if (i < nkeys) sm_tab[i] = vsrc(i < gsj ? (int)(gv[k] < nv ? gv[k] : 0u) : vi_loc0 + (i - gsj));
+      }
+    }
+  }
+
+  // (fp32 inputs: split into fp16 hi / lo here.)  The operands are used
+  // here on every path: otherwise their loads would count as pending in the
+  // key loop, which would then wait for all of its own prefetches before the
+  // first product of every tile
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    if constexpr (DT::kSplit) {
+      const int k0 = 16 * kb + 8 * h;
+      float x[8];
+      if (qvalid) load8_f32(qrow + k0, x);
+      else for (int q = 0; q < 8; ++q) x[q] = 0.f;
+      splitop<DT>(x, qh[kb], ql[kb]);
+    }
+    __asm__ volatile("" :: "v"(qh[kb]), "v"(ql[kb]));
+  }
+  __syncthreads();
+
+  // ---- phi(q): u^T = W^T q^T (64 features x 32 queries), softmax halves
+  float ph[2][2][16];   // [half pos/neg][mt][i]: feature 64*half + 32*mt + 8(i/4) + 4h + (i%4)
+  float zlin = 0.f;
+  {
+    f32x16 acc[2];
+    for (int mt = 0; mt < 2; ++mt) for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+    if (wactive) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int k0 = 16 * kb + 8 * h;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const T* wrow = sm_WT + (32 * mt + r) * KRS + k0;
+          if constexpr (DT::kSplit) {
+            float x[8];
+            load8_f32(wrow, x);
+            u32x4 ah, al;
+            splitop<DT>(x, ah, al);
+            acc[mt] = DT::mma(ah, qh[kb], acc[mt]);
+            acc[mt] = DT::mma(ah, ql[kb], acc[mt]);
+            acc[mt] = DT::mma(al, qh[kb], acc[mt]);
+          } else {
+            acc[mt] = DT::mma(ld16(reinterpret_cast<const uint16_t*>(wrow)), qh[kb], acc[mt]);
+          }
+        }
+      }
+    }
+    float mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      for (int i = 0; i < 16; ++i) { mx = fmaxf(mx, acc[mt][i]); mn = fminf(mn, acc[mt][i]); }
+    mx = fmaxf(mx, xor32(mx));
+    mn = fminf(mn, xor32(mn));
+    constexpr float kL2E = 1.4426950408889634f;
+    const float mxl = mx * kL2E, mnl = mn * kL2E;
+    float sp = 0.f, sn = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      for (int i = 0; i < 16; ++i) {
+        ph[0][mt][i] = __builtin_amdgcn_exp2f(fmaf(acc[mt][i], kL2E, -mxl));
+        ph[1][mt][i] = __builtin_amdgcn_exp2f(fmaf(-acc[mt][i], kL2E, mnl));
+        sp += ph[0][mt][i];
+        sn += ph[1][mt][i];
+      }
+    sp += xor32(sp);
+    sn += xor32(sn);
+    const float ip = 1.f / sp, in_ = 1.f / sn;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      for (int i = 0; i < 16; ++i) {
+        ph[0][mt][i] *= ip;
+        ph[1][mt][i] *= in_;
+        const int f = 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
+        zlin = fmaf(ph[0][mt][i], sm_s[f], zlin);
+        zlin = fmaf(ph[1][mt][i], sm_s[kM + f], zlin);
+      }
+    zlin += xor32(zlin);
+    if (!(a.branches & LOLA_READ_STATE)) zlin = 0.f;   // state hidden from the read
+  }
+
+  // ---- linear read N_lin^T = H_j^T phi^T into the output accumulator
+  f32x16 O[NMT];
+#pragma unroll
+  for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[mt][i] = 0.f;
+  if (wactive && (a.branches & LOLA_READ_STATE)) {
+#pragma unroll
+    for (int kb = 0; kb < kD / 16; ++kb) {
+      const int half = kb >> 2, mt = (kb >> 1) & 1, i0 = 8 * (kb & 1);
+      u32x4 bh, bl;
+      splitop<DT>(&ph[half][mt][i0], bh, bl);
+#pragma unroll
+      for (int mo = 0; mo < NMT; ++mo) {
+        const int row = 32 * mo + r;
+        const u32x4 ah = sigma_load(sm_HT_hi + row * HTS + 16 * kb, h);
+        const u32x4 al = sigma_load(sm_HT_lo + row * HTS + 16 * kb, h);
+        O[mo] = DT::mma(ah, bh, O[mo]);
+        O[mo] = DT::mma(ah, bl, O[mo]);
+        O[mo] = DT::mma(al, bh, O[mo]);
+      }
+    }
+  }
+  __syncthreads();   // the key tiles reuse the linear-read region
+
+  // ---- explicit branch: key tiles of KT, double-buffered.  The linear
+  // terms enter with logit 0 (weight 2^-m2); without them (state hidden, or
+  // z_lin = 0: an empty state) the running maximum starts at -inf, so that
+  // the weights of very negative logits do not all underflow
+  float m2 = zlin > 0.f ? 0.f : -INFINITY, l = zlin;
+  const float scale2 = 1.4426950408889634f / sqrtf((float)HD);
+  // cache keys hidden from the read: the key loop starts past them
+  const int kbase = (a.branches & LOLA_READ_CACHE) ? 0 : gsj;
+  const int ntiles = (nkeys - kbase + KT - 1) / KT;
+  // The key loop is a three-stage pipeline over tiles of KT keys.  At the
+  // top of iteration t the LDS holds K of tile t + 1 and V of tile t, the
+  // registers hold the scores of tile t (computed in iteration t - 1) and
+  // the raw global loads of K of tile t + 2 and V of tile t + 1 (issued in
+  // iteration t - 1).  Iteration t stages those loads into the buffers
+  // nobody reads in this iteration, issues the loads of K of tile t + 3
+  // and V of tile t + 2, and multiplies: S_{t+1} = K Q^T next to tile t's
+  // exponentials, then O += V_t P_t.  For 16-bit inputs the staging goes
+  // between the score products and the loads between the value products
+  // (scheduling fences fix the order), so the matrix cores are fed while
+  // the vector, LDS and memory work of the pipeline is done; one barrier
+  // per tile publishes the staged buffers.  Rows past the last key are
+  // loaded from the last key's row (finite values whose weights are
+  // exactly 0 after the mask), so the loads need no branch.
+  constexpr int VPC = (int)sizeof(T) / 2;        // 16-byte pieces per 8 V columns
+  u32x4 kreg[KPT];
+  u32x4 vreg[2][VPC];
+  const bool vthread = VITEMS >= kThreads || tid < VITEMS;   // (wave-uniform)
+  const int vpr = tid % (KT / 2), vcol = vt_cols(tid);        // this thread's V item
+  auto load_k = [&](int t0) {
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      const int pc = q * kThreads + tid, kl = pc / (HD / PER), c = (pc % (HD / PER)) * PER;
+      const int kk = min(t0 + kl, nkeys - 1);
+      kreg[q] = ldg16(row_addr(sm_tab[kk], bk, dk1, dk2) + c * sizeof(T));
+    }
+  };
+  auto load_v = [&](int t0) {
+    if (vthread) {
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        const int kk = min(t0 + 2 * vpr + kq, nkeys - 1);
+        const uint64_t src = row_addr(sm_tab[kk], bv, dv1, dv2) + vcol * sizeof(T);
+#pragma unroll
+        for (int w = 0; w < VPC; ++w) vreg[kq][w] = ldg16(src + 16 * w);
+      }
+    }
+  };
+  // buffer b's arrays (selects, so that the offsets stay in registers)
+  auto buf_off = [&](const uint32_t (&o)[2], int b) -> uint32_t { return b ? o[1] : o[0]; };
+  auto store_k = [&](int b) {
+    uint16_t* Kb = (uint16_t*)(smem + buf_off(L.K, b));
+    uint16_t* KLb = (uint16_t*)(smem + buf_off(L.KL, b));
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      const int pc = q * kThreads + tid, kl = pc / (HD / PER), c = (pc % (HD / PER)) * PER;
+      if constexpr (DT::kSplit) {
+        float x[4] = {__uint_as_float(kreg[q][0]), __uint_as_float(kreg[q][1]),
+                      __uint_as_float(kreg[q][2]), __uint_as_float(kreg[q][3])};
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) DT::split(x[e], hi[e], lo[e]);
+        *reinterpret_cast<u32x2*>(Kb + kl * KRS + c) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+        *reinterpret_cast<u32x2*>(KLb + kl * KRS + c) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+      } else {
+        *reinterpret_cast<u32x4*>(Kb + kl * KRS + c) = kreg[q];
+      }
+    }
+  };
+  // V column q (of the thread's 8) of its two keys into V^T buffer b
+  auto store_v_col = [&](int b, int q) {
+    uint16_t* VTb = (uint16_t*)(smem + buf_off(L.VT, b));
+    uint16_t* VTLb = (uint16_t*)(smem + buf_off(L.VTL, b));
+    float vf[2];
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq) {
+      if constexpr (VPC == 1) {   // 8 bf16 in one piece
+        const uint32_t w = vreg[kq][0][q >> 1];
+        vf[kq] = __uint_as_float((q & 1) ? (w & 0xFFFF0000u) : (w << 16));
+      } else {                    // 8 fp32 in two pieces
+        vf[kq] = __uint_as_float(vreg[kq][q >> 2][q & 3]);
+      }
+    }
+    uint32_t* row = reinterpret_cast<uint32_t*>(VTb + (vcol + q) * VTS) + vpr;
+    if constexpr (DT::kSplit) {
+      uint32_t h0, l0, h1, l1;
+      DT::split(vf[0], h0, l0);
+      DT::split(vf[1], h1, l1);
+      *row = h0 | (h1 << 16);
+      *(reinterpret_cast<uint32_t*>(VTLb + (vcol + q) * VTS) + vpr) = l0 | (l1 << 16);
+    } else {
+      *row = f16_pair(vf[0], vf[1]);
+    }
+  };
+  auto store_v = [&](int b) {
+    if (vthread) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) store_v_col(b, q);
+    }
+  };
+  // S^T = K Q^T of the tile in K buffer b (32 keys x 32 queries per half kh)
+  auto scores = [&](int b, f32x16 (&Sx)[2]) {
+    const uint16_t* Kb = (const uint16_t*)(smem + buf_off(L.K, b));
+    const uint16_t* KLb = (const uint16_t*)(smem + buf_off(L.KL, b));
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Sx[kh][i] = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int k0 = 16 * kb + 8 * h;
+        const u32x4 ah = ld16(Kb + (32 * kh + r) * KRS + k0);
+        Sx[kh] = DT::mma(ah, qh[kb], Sx[kh]);
+        if constexpr (DT::kSplit) {
+          const u32x4 al = ld16(KLb + (32 * kh + r) * KRS + k0);
+          Sx[kh] = DT::mma(ah, ql[kb], Sx[kh]);
+          Sx[kh] = DT::mma(al, qh[kb], Sx[kh]);
+        }
+      }
+    }
+  };
+  f32x16 S[2];
+  if (ntiles > 0) {
+    load_k(kbase);
+    load_v(kbase);
+    store_k(0);
+    store_v(0);
+  }
+  if (ntiles > 1) {
+    load_k(kbase + KT);
+    store_k(1);
+    load_v(kbase + KT);               // staged in iteration 0
+  }
+  if (ntiles > 2) load_k(kbase + 2 * KT);   // staged in iteration 0
+  __syncthreads();
+  if (ntiles > 0 && wactive && kbase <= wlast) scores(0, S);
+  // (iteration 0 overwrites K buffer 0 with tile 2: every wave has read it)
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int t0 = kbase + t * KT, b = t & 1;
+    // staged here: K of tile t + 2 into K buffer b, V of tile t + 1 into V
+    // buffer b ^ 1; loaded here: K of tile t + 3, V of tile t + 2
+    const bool stk = t + 2 < ntiles, stv = t + 1 < ntiles;
+    const bool ldk = t + 3 < ntiles, ldv = t + 2 < ntiles;
+    if (wactive && t0 <= wlast) {
+      const uint16_t* VTb = (const uint16_t*)(smem + buf_off(L.VT, b));
+      const uint16_t* VTLb = (const uint16_t*)(smem + buf_off(L.VTL, b));
+      // masks only where the tile has keys past the end or past the wave's
+      // first query position (every query of the wave sees a full tile);
+      // the scale goes into the exponent's fma.  Key kk is visible to the
+      // lane's query iff kk < vis_end (cache keys precede the local ones, a
+      // local key is visible up to the query's own position).
+      const int klast = t0 + KT - 1;
+      const bool full = klast < nkeys && (klast < gsj || lo_j + (klast - gsj) <= p0);
+      if (!full) {
+        const int dl = vis_end - t0 - 4 * h;      // the lane's offsets below dl are visible
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (32 * kh + 8 * (i >> 2) + (i & 3) >= dl) S[kh][i] = -INFINITY;
+      }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, S[kh][i]);
+      tmax = half_max(tmax) * scale2;   // (the scale is positive)
+      // the running maximum moves only when a score would exceed it by more
+      // than kSlack (weights up to 2^kSlack, well inside fp16 and fp32), so
+      // that the accumulators are rarely rescaled
+      if (tmax > m2 + kSlack) {
+        const float mnew = tmax;
+        const float alpha = __builtin_amdgcn_exp2f(m2 - mnew);   // 0 from m2 = -inf
+#pragma unroll
+        for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) O[mt][i] *= alpha;
+        l *= alpha;
+        m2 = mnew;
+      }
+      // (m2 is still -inf only while every key so far is masked for this
+      // query: its weights are then 0, exp2(-inf))
+      const float msub = m2 == -INFINITY ? 0.f : m2;
+      float rs = 0.f;
+      if constexpr (DT::kSplit) {
+        if (stk) store_k(b);
+        if (stv) store_v(b ^ 1);
+        if (ldk) load_k(t0 + 3 * KT);
+        if (ldv) load_v(t0 + 2 * KT);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            S[kh][i] = __builtin_amdgcn_exp2f(fmaf(S[kh][i], scale2, -msub));
+            rs += S[kh][i];
+          }
+#pragma unroll
+        for (int kb = 0; kb < KT / 16; ++kb) {
+          const int kh = kb >> 1, i0 = 8 * (kb & 1);
+          u32x4 ph8, pl8;
+          float pv[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) pv[q] = S[kh][i0 + q];
+          splitop<DT>(pv, ph8, pl8);
+#pragma unroll
+          for (int mo = 0; mo < NMT; ++mo) {
+            const int row = 32 * mo + r;
+            const u32x4 vh = sigma_load(VTb + row * VTS + 16 * kb, h);
+            const u32x4 vl = sigma_load(VTLb + row * VTS + 16 * kb, h);
+            O[mo] = DT::mma(vh, ph8, O[mo]);
+            O[mo] = DT::mma(vh, pl8, O[mo]);
+            O[mo] = DT::mma(vl, ph8, O[mo]);
+          }
+        }
+        // (fp32 inputs take three products per operand pair: the next
+        // tile's scores come after this tile's products, in the same
+        // registers, as two sets of them would not fit)
+        scores(b ^ 1, S);
+      } else {
+        // The next tile's score products, one at a time, each followed by
+        // EPC of this tile's weights (the exponentials, rounded to fp16 as
+        // the value products take them) and, early on, the staging of the
+        // loaded rows; a scheduling fence after each step keeps that order.
+        // Operands are read from LDS LA products ahead.  (After a wave's
+        // last tile the products are taken of whatever the buffer holds and
+        // never used.)
+        constexpr int LA = 3;
+        constexpr int NS = 2 * KB;                 // score products
+        constexpr int EPC = 32 / NS;               // weights per product
+        constexpr int NP = (KT / 16) * NMT;        // value products
+        static_assert(NS >= 8 && NP >= 4, "staging and loads are spread over these steps");
+        const uint16_t* Kn = (const uint16_t*)(smem + buf_off(L.K, b ^ 1));
+        auto kaddr = [&](int c) { return Kn + (32 * (c & 1) + r) * KRS + 16 * (c >> 1) + 8 * h; };
+        auto vaddr = [&](int c) { return VTb + (32 * (c % NMT) + r) * VTS + 16 * (c / NMT); };
+        u32x4 ka[LA], va[LA];
+#pragma unroll
+        for (int i = 0; i < LA; ++i) ka[i] = ld16(kaddr(i));
+        f32x16 Sn[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) Sn[kh][i] = 0.f;
+        f16x8 p8[KT / 16];
+#pragma unroll
+        for (int c = 0; c < NS; ++c) {
+          const int kh = c & 1, kb = c >> 1;
+          const u32x4 ac = ka[c % LA];
+          if (c + LA < NS) ka[c % LA] = ld16(kaddr(c + LA));
+          else va[(c + LA - NS) % LA] = sigma_load(vaddr(c + LA - NS), h);
+          Sn[kh] = DT::mma(ac, qh[kb], Sn[kh]);
+#pragma unroll
+          for (int x = 0; x < EPC; ++x) {
+            const int e = EPC * c + x, kp = e >> 3, q = e & 7;   // weight e: block kp, slot q
+            p8[kp][q] = (_Float16)__builtin_amdgcn_exp2f(
+                fmaf(S[kp >> 1][8 * (kp & 1) + q], scale2, -msub));
+          }
+          if (c == 0 && stk) store_k(b);
+          if (c < 8 && stv && vthread) store_v_col(b ^ 1, c);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // the value products, each with one step of the row sum (pairwise
+        // dot products of the same rounded weights with 1), and the next
+        // loads
+        constexpr int DPC = 16 / NP;               // row-sum steps per product
+        constexpr f16x2 one2 = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+        for (int c = 0; c < NP; ++c) {
+          const int kb = c / NMT, mo = c % NMT;
+          const u32x4 vc = va[c % LA];
+          if (c + LA < NP) va[c % LA] = sigma_load(vaddr(c + LA), h);
+          O[mo] = mfma_f16(__builtin_bit_cast(f16x8, vc), p8[kb], O[mo]);
+#pragma unroll
+          for (int x = 0; x < DPC; ++x) {
+            const int pq = DPC * c + x, kp = pq >> 2, w = pq & 3;   // pair w of block kp
+            rs = __builtin_amdgcn_fdot2(f16x2{p8[kp][2 * w], p8[kp][2 * w + 1]}, one2, rs, false);
+          }
+          if (c == 1 && ldk) load_k(t0 + 3 * KT);
+          if (c == 3 && ldv) load_v(t0 + 2 * KT);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) S[kh] = Sn[kh];
+      }
+      rs = half_sum(rs);
+      l += rs;
+    } else {
+      if (stk) store_k(b);
+      if (stv) store_v(b ^ 1);
+      if (ldk) load_k(t0 + 3 * KT);
+      if (ldv) load_v(t0 + 2 * KT);
+    }
+    __syncthreads();
+  }
+
+  // ---- y = O / l
+  if (!qvalid) return;
+  const float il = 1.f / l;
+  float* orow = a.out + (((size_t)u * a.g + hd) * vr.T + (size_t)(qpos - n0)) * HD;
+#pragma unroll
+  for (int mo = 0; mo < NMT; ++mo)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int cc = 32 * mo + 8 * g4 + 4 * h;
+      f32x4 y;
+      for (int q = 0; q < 4; ++q) y[q] = O[mo][4 * g4 + q] * il;
+      *reinterpret_cast<f32x4*>(orow + cc) = y;
+    }
+}
+
+}  // namespace lola

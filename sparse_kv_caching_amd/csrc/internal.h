@@ -97,6 +97,10 @@ struct ChainArgs {
   // instead of SRE (no SRE products, no exchange); NULL for SRE
   const float* vscore;      // [U, eta + T] scores of the local rows (virtual index - lam)
   const float* cscore;      // [U, lam] scores of the cache slots at the call's start
+  // concurrent read (NULL: none): the snapshots are written with coherent
+  // stores, and each writer workgroup adds 1 to ready[u] once the snapshot
+  // of a chunk is complete (writer workgroups per unit: d / 32 / SPW)
+  int* ready;               // [U]
 };
 
 // K3: window + cache softmax attention merged with the linear read.
@@ -111,7 +115,13 @@ struct AttnArgs {
   int g, Hkv, nch, C, ptile, nblk;  // positions per WG, 32-position blocks per WG
   int ch0, nch_launch;      // chunks ch0 .. ch0 + nch_launch - 1 in this launch
   int branches;             // read mask, LOLA_READ_* bits (window always set)
-  const int* err;           // device error flags: nonzero = the chain gave up, nothing to read
+  int* err;                 // device error flags: nonzero = the chain gave up, nothing to read
+  // concurrent read (NULL: the snapshots are complete at launch): chunk j
+  // of unit u may be read once ready[u] >= ready_need * (j + 1); the
+  // snapshots are then read with coherent loads
+  const int* ready;
+  int ready_need;
+  int spin_limit;           // polls of ready before the read gives up (sets err)
 };
 
 // Finalize: new cache rows / positions and window ring after a prefill call.
@@ -217,6 +227,12 @@ hipError_t launch_phi(const PhiArgs& a, int U, bool f32, hipStream_t st);
 hipError_t launch_chain(const ChainArgs& a, int U, bool f32, hipStream_t st);
 size_t chain_lds_bytes(int lam, int C, int d, bool f32);
 hipError_t launch_attn(const AttnArgs& a, int U, bool f32, hipStream_t st);
+// The chain and the read of finished chunks in one launch: the chain's U * k
+// workgroups come first in the grid (so they are all placed before any
+// workgroup of the read), the read's workgroups (unit fastest, then position
+// tile, then chunk) wait for their chunk's snapshot.  c.ready and a.ready
+// point to the same zeroed counters.
+hipError_t launch_overlap(const ChainArgs& c, const AttnArgs& a, int U, bool f32, hipStream_t st);
 hipError_t launch_sre_map(const SreMapArgs& a, int U, bool f32, hipStream_t st);
 hipError_t launch_score(const ScoreArgs& a, int U, bool f32, hipStream_t st);
 size_t score_lds_bytes(int d);

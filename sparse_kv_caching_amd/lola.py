@@ -25,10 +25,10 @@ LOLA_ERR_STATE = 5
 LOLA_ERR_WORKSPACE = 6
 LOLA_DTYPE_F32 = 0
 LOLA_DTYPE_BF16 = 1
-KERNELS = ("phi", "chain", "attn", "finalize", "decode")
+KERNELS = ("phi", "chain", "attn", "finalize", "decode", "overlap")
 READ_STATE, READ_CACHE, READ_WINDOW, READ_ALL = 1, 2, 4, 7   # lola_set_read_branches bits
 READ_BEFORE_UPDATE, READ_AFTER_UPDATE = 0, 1                 # lola_set_read_order
-DEBUG_SPIN_LIMIT, DEBUG_CHAIN_FAIL_AT = 0, 1                 # lola_debug_set keys
+DEBUG_SPIN_LIMIT, DEBUG_CHAIN_FAIL_AT, DEBUG_OVERLAP = 0, 1, 2  # lola_debug_set keys
 SCORE_SRE, SCORE_KERNEL_SQ, SCORE_KERNEL_ABS, SCORE_KERNEL_RATIO, SCORE_LOCAL_ATTN = range(5)
 
 EXPORTED = [
@@ -188,8 +188,9 @@ class LolaLayer:
 
     def debug_set(self, key: int, value: int):
         """lola_debug_set: DEBUG_SPIN_LIMIT (exchange polls before a partner
-        counts as lost; 0 = default) or DEBUG_CHAIN_FAIL_AT (exchange step at
-        which the chain gives up; -1 = never)."""
+        counts as lost; 0 = default), DEBUG_CHAIN_FAIL_AT (exchange step at
+        which the chain gives up; -1 = never) or DEBUG_OVERLAP (prefill
+        schedule: -1 auto, 0 chain then read, 1 read beside the chain)."""
         _check(self.lib.lola_debug_set(self._st, int(key), int(value)), "lola_debug_set")
 
     def profile(self, enable: bool):

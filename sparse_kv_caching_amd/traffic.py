@@ -48,12 +48,23 @@ KERNELS = {
     "chain": ("chain.hip", "lola::chain_kernel"),
     "attn": ("attn.hip", "lola::attn_kernel"),
     "decode": ("decode.hip", "lola::decode_kernel"),
+    "overlap": ("fused.hip", "lola::overlap_kernel"),
 }
 
 
 def kernel_source_hash(fname: str) -> str:
+    """Hash of a kernel's sources: its file, the bodies it includes
+    (``*_impl.h``: both for the fused chain + attention kernel) and the shared
+    headers."""
+    files = [fname]
+    if fname == "fused.hip":
+        files += ["chain_impl.h", "attn_impl.h"]
+    else:
+        impl = fname.replace(".hip", "_impl.h")
+        if os.path.exists(os.path.join(CSRC, impl)):
+            files.append(impl)
     h = hashlib.sha256()
-    for f in (fname, "common.h", "internal.h"):
+    for f in files + ["common.h", "internal.h"]:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
