@@ -102,6 +102,9 @@ def _run(args):
         inp = make_inputs(wl)
         layer = LolaLayer(batch=wl.B, q_heads=wl.Hq, kv_heads=wl.Hkv, head_dim=wl.d,
                           window=wl.eta, cache=wl.lam, W=to_dev(inp.W), dtype=torch.bfloat16)
+        if args.overlap is not None:
+            from sparse_kv_caching_amd.lola import DEBUG_OVERLAP
+            layer.debug_set(DEBUG_OVERLAP, args.overlap)
         q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
         for _ in range(2):
             layer.reset()
@@ -232,6 +235,8 @@ def main():
     r = sub.add_parser("run")
     r.add_argument("--workload", required=True)
     r.add_argument("--steps", type=int, default=16)
+    r.add_argument("--overlap", type=int, default=None, choices=(-1, 0, 1),
+                   help="prefill schedule (LOLA_DEBUG_OVERLAP); default: the library's choice")
     s = sub.add_parser("summarize")
     s.add_argument("--workload", required=True)
     s.add_argument("--kernel", required=True, choices=sorted(KERNELS))
