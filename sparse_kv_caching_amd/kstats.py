@@ -3,10 +3,13 @@
 ``rocprofv3 --kernel-trace --stats`` aggregates each kernel over the whole
 run; ``bench.py`` runs several prefill workloads one after the other, so its
 per-kernel statistics mix them.  This splits the trace
-(``<dir>/run_kernel_trace.csv``) by workload: the dispatches of each prefill
-kernel (φ, chain, attention, finalize), in time order, are cut into
-consecutive segments of the given call counts, one per workload in the order
-``bench.py`` runs them.  Every other kernel is reported over the whole run.
+(``<dir>/run_kernel_trace.csv``) by workload: every prefill call launches the
+φ kernel first, so the φ dispatches, in time order, are cut into consecutive
+segments of the given call counts (one per workload, in the order
+``bench.py`` runs them), and each dispatch of a prefill kernel (φ, chain,
+attention, the chain and read in one launch, finalize) takes the workload of
+the segment its start time falls in.  Every other kernel is reported over
+the whole run.
 
     python3 -m sparse_kv_caching_amd.kstats <dir>/run_kernel_trace.csv \
         --segments long_32k:12,batched_8k:12,llama8b_4k:12,decode_b64:1
@@ -21,7 +24,7 @@ import csv
 from collections import defaultdict
 
 PREFILL = ("lola::phi_kernel", "lola::chain_kernel", "lola::attn_kernel",
-           "lola::finalize_cache_kernel", "lola::finalize_ring_kernel")
+           "lola::overlap_kernel", "lola::finalize_cache_kernel", "lola::finalize_ring_kernel")
 
 
 def _family(name: str) -> str:
@@ -47,24 +50,25 @@ def main():
             t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
             rows.append((t0, r["Kernel_Name"], (t1 - t0) / 1e3))
     rows.sort()
-    fam_seen = defaultdict(int)
+    # segment start times from the phi dispatches
+    phi_t = [t0 for t0, name, _ in rows if "lola::phi_kernel" in name]
+    starts, i = [], 0
+    for w, n in segs:
+        if i >= len(phi_t):
+            break
+        starts.append((phi_t[i], w))
+        i += n
     groups = defaultdict(list)        # (label, kernel name) -> durations
     for t0, name, us in rows:
-        fam = _family(name)
         label = "whole run"
-        if fam:
-            i = fam_seen[fam]
-            fam_seen[fam] += 1
-            acc = 0
-            label = "after the listed segments"
-            for w, n in segs:
-                if i < acc + n:
+        if _family(name):
+            label = "before the first segment"
+            for ts, w in starts:
+                if t0 >= ts:
                     label = w
-                    break
-                acc += n
         short = name.split("(")[0].replace("void ", "")
         groups[(label, short)].append(us)
-    order = [w for w, _ in segs] + ["after the listed segments", "whole run"]
+    order = ["before the first segment"] + [w for w, _ in segs] + ["whole run"]
     print("| Workload | Kernel | Calls | Avg (us) | Min (us) | Max (us) |")
     print("|---|---|---|---|---|---|")
     for label in order:
