@@ -16,30 +16,15 @@
 
 namespace lola {
 
-template <class DT>
+template <class DT, int HD>
 __global__ __launch_bounds__(256) void phi_kernel(PhiArgs a) {
   using T = typename DT::T;
   constexpr int WPAD = 8;
-  const int d = a.vr.d;
+  constexpr int d = HD;
   const int u = blockIdx.y;
   const int kvh = u % a.Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5, r = lane & 31;
-
-  // W^T for this KV head: wT[f][k] (hi and, for fp32 inputs, lo planes)
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint16_t* wT_hi = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* wT_lo = wT_hi + kM * (d + WPAD);
-  const T* W = reinterpret_cast<const T*>(a.W) + (size_t)kvh * d * kM;
-  for (int i = threadIdx.x; i < d * kM; i += blockDim.x) {
-    int k = i / kM, f = i % kM;
-    float w = DT::to_f32(W[i]);
-    uint32_t hi, lo;
-    DT::split(w, hi, lo);
-    wT_hi[f * (d + WPAD) + k] = (uint16_t)hi;
-    if (DT::kSplit) wT_lo[f * (d + WPAD) + k] = (uint16_t)lo;
-  }
-  __syncthreads();
 
   const int vi = blockIdx.x * 128 + wave * 32 + r;
   bool valid = vi < a.NV;
@@ -48,10 +33,64 @@ __global__ __launch_bounds__(256) void phi_kernel(PhiArgs a) {
     else valid = (a.vr.n0 - a.vr.eta + (vi - a.vr.lam)) >= 0;
   }
   const T* xrow = valid ? reinterpret_cast<const T*>(a.vr.krow(u, vi, sizeof(T))) : nullptr;
+  // 16-bit inputs: the row's operands are loaded first, in flight with the
+  // staging of W below (fixed trip counts: every load of the wave is issued
+  // before any is used)
+  u32x4 bx[HD / 16];
+  if constexpr (!DT::kSplit) {
+#pragma unroll
+    for (int kb = 0; kb < HD / 16; ++kb)
+      bx[kb] = valid ? ld16(reinterpret_cast<const uint16_t*>(xrow) + kb * 16 + 8 * h)
+                     : u32x4{0, 0, 0, 0};
+  }
+
+  // W^T for this KV head: wT[f][k] (hi and, for fp32 inputs, lo planes);
+  // 8 consecutive features of one k per piece, all pieces loaded first
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint16_t* wT_hi = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* wT_lo = wT_hi + kM * (d + WPAD);
+  const T* W = reinterpret_cast<const T*>(a.W) + (size_t)kvh * d * kM;
+  {
+    constexpr int PIECES = d * kM / 8;
+    static_assert(PIECES % 256 == 0, "fixed trip count");
+    constexpr int PT = PIECES / 256;
+    float wv[PT][8];
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      const int i = threadIdx.x + 256 * q;
+      const int k = i / (kM / 8), f0 = (i % (kM / 8)) * 8;
+      if constexpr (sizeof(T) == 2) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(W + (size_t)k * kM + f0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) wv[q][j] = DT::from_bits((x[j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+      } else {
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(W + (size_t)k * kM + f0);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(W + (size_t)k * kM + f0 + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { wv[q][j] = x0[j]; wv[q][4 + j] = x1[j]; }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      const int i = threadIdx.x + 256 * q;
+      const int k = i / (kM / 8), f0 = (i % (kM / 8)) * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t hi, lo;
+        DT::split(wv[q][j], hi, lo);
+        wT_hi[(f0 + j) * (d + WPAD) + k] = (uint16_t)hi;
+        if (DT::kSplit) wT_lo[(f0 + j) * (d + WPAD) + k] = (uint16_t)lo;
+      }
+    }
+  }
+  __syncthreads();
 
   f32x16 acc[2];
+#pragma unroll
   for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
     for (int i = 0; i < 16; ++i) acc[mt][i] = 0.f;
+#pragma unroll
   for (int kb = 0; kb < d / 16; ++kb) {
     const int k0 = kb * 16 + 8 * h;
     u32x4 bx_hi, bx_lo;
@@ -61,7 +100,7 @@ __global__ __launch_bounds__(256) void phi_kernel(PhiArgs a) {
       else for (int j = 0; j < 8; ++j) xv[j] = 0.f;
       splitop<DT>(xv, bx_hi, bx_lo);
     } else {
-      bx_hi = valid ? ld16(reinterpret_cast<const uint16_t*>(xrow) + k0) : u32x4{0, 0, 0, 0};
+      bx_hi = bx[kb];
     }
     for (int mt = 0; mt < 2; ++mt) {
       const int f = mt * 32 + r;
@@ -117,8 +156,13 @@ hipError_t launch_phi(const PhiArgs& a, int U, bool f32, hipStream_t st) {
   if (a.NV <= 0 || U <= 0) return hipSuccess;
   dim3 grid((a.NV + 127) / 128, U);
   size_t lds = (size_t)2 * kM * (a.vr.d + 8) * sizeof(uint16_t);
-  if (f32) hipLaunchKernelGGL(phi_kernel<F32>, grid, dim3(256), lds, st, a);
-  else hipLaunchKernelGGL(phi_kernel<BF16>, grid, dim3(256), lds, st, a);
+  if (a.vr.d == 64) {
+    if (f32) hipLaunchKernelGGL((phi_kernel<F32, 64>), grid, dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((phi_kernel<BF16, 64>), grid, dim3(256), lds, st, a);
+  } else {
+    if (f32) hipLaunchKernelGGL((phi_kernel<F32, 128>), grid, dim3(256), lds, st, a);
+    else hipLaunchKernelGGL((phi_kernel<BF16, 128>), grid, dim3(256), lds, st, a);
+  }
   return hipGetLastError();
 }
 
