@@ -5,7 +5,15 @@
 namespace lola {
 
 size_t chain_lds_bytes(int lam, int C, int d, bool f32) {
-  return chain_ns::chain_layout(lam, C, d / 32, f32).total;   // the largest case, k = 1
+  // the largest of the instances the library can launch: one slab per
+  // workgroup and two slabs (two fold buffers), all slabs (one)
+  const int nslab = d / 32;
+  size_t m = chain_ns::chain_layout(lam, C, nslab, f32, 1).total;
+  for (int spw = 1; spw < nslab; spw *= 2) {
+    const size_t x = chain_ns::chain_layout(lam, C, spw, f32, 2).total;
+    if (x > m) m = x;
+  }
+  return m;
 }
 
 template <class DT, int HD, int SPW>
@@ -15,7 +23,7 @@ __global__ __launch_bounds__(chain_ns::kThreads) void chain_kernel(ChainArgs a) 
 
 template <class DT, int HD, int SPW>
 static hipError_t launch_chain_t(const ChainArgs& a, int U, hipStream_t st) {
-  const size_t lds = chain_ns::chain_layout(a.vr.lam, a.C, SPW, DT::kSplit).total;
+  const size_t lds = chain_ns::chain_layout(a.vr.lam, a.C, SPW, DT::kSplit, chain_ns::kFoldBufs<HD, SPW>).total;
   const void* fn = (const void*)chain_kernel<DT, HD, SPW>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

@@ -66,6 +66,9 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int HTP = kD + 8;   // padded LDS row of H^T (16-bit elements)
 constexpr int STP = 64 + 8;   // padded LDS row of fold staging tiles (64 tokens)
+// fold staging buffers: two where the workgroup holds fewer than all slabs
+// (the two then fit the LDS of the all-slab layout with one)
+template <int HD, int SPW> constexpr int kFoldBufs = SPW < HD / 32 ? 2 : 1;
 
 // Byte offsets of the LDS arrays (computed by value so that the kernel's
 // pointers stay plain LDS pointers).  The candidate list, parts, keys and
@@ -80,7 +83,9 @@ struct ChainLayout {
 
 __host__ __device__ inline uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
 
-__host__ __device__ inline ChainLayout chain_layout(int lam, int C, int spw, bool f32) {
+// nbuf: fold staging buffers (2 lets a block be staged while the previous
+// one is multiplied, one barrier per block)
+__host__ __device__ inline ChainLayout chain_layout(int lam, int C, int spw, bool f32, int nbuf = 1) {
   ChainLayout L;
   uint32_t off = 0;
   auto take = [&](uint32_t bytes) { const uint32_t o = off; off = align16(off + bytes); return o; };
@@ -103,10 +108,11 @@ __host__ __device__ inline ChainLayout chain_layout(int lam, int C, int spw, boo
   L.hist = take(768 * 4);                  // three radix histograms
   const uint32_t sel_end = off;
   off = region;
-  L.phT_hi = take(kD * STP * 2);           // [kD][STP]
-  L.phT_lo = take(kD * STP * 2);
-  L.VT_hi = take(ncol * STP * 2);          // [ncol][STP]
-  L.VT_lo = take(f32 ? ncol * STP * 2 : 16);
+  const uint32_t nb = (uint32_t)nbuf;
+  L.phT_hi = take(nb * kD * STP * 2);      // [nbuf][kD][STP]
+  L.phT_lo = take(nb * kD * STP * 2);
+  L.VT_hi = take(nb * ncol * STP * 2);     // [nbuf][ncol][STP]
+  L.VT_lo = take(f32 ? nb * ncol * STP * 2 : 16);
   L.total = off > sel_end ? off : sel_end;
   return L;
 }
@@ -180,7 +186,7 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
   const int h = lane >> 5, r = lane & 31;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const ChainLayout L = chain_layout(lam, a.C, SPW, DT::kSplit);
+  const ChainLayout L = chain_layout(lam, a.C, SPW, DT::kSplit, kFoldBufs<HD, SPW>);
   struct {
     uint16_t *HT_hi, *HT_lo;
     float *s32, *spart;
@@ -606,6 +612,8 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
       u32x4 xh[FCW], xl[FCW];
       VRaw<T> v[VC / 4];
     };
+    constexpr int NBUF = kFoldBufs<HD, SPW>;
+    int blk = 0;                                         // blocks staged so far
     for (int sb0 = 0; sb0 < nS; sb0 += 64 * GB) {
       Gather gb[GB];
 #pragma unroll
@@ -627,24 +635,34 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
       for (int b = 0; b < GB; ++b) {
         const int sb = sb0 + 64 * b;
         if (sb >= nS) break;
+        // this block's staging buffer
+        const int fb = NBUF == 2 ? (blk & 1) : 0;
+        ++blk;
+        uint16_t* pTh = sm.phT_hi + fb * (kD * STP);
+        uint16_t* pTl = sm.phT_lo + fb * (kD * STP);
+        uint16_t* vTh = sm.VT_hi + fb * (32 * SPW * STP);
+        uint16_t* vTl = sm.VT_lo + (DT::kSplit ? fb * (32 * SPW * STP) : 0);
 #pragma unroll
         for (int q = 0; q < FCW; ++q) {
           const int f0 = 8 * (FCW * wave + q);
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            sm.phT_hi[(f0 + 2 * w) * STP + lane] = (uint16_t)(gb[b].xh[q][w] & 0xFFFFu);
-            sm.phT_hi[(f0 + 2 * w + 1) * STP + lane] = (uint16_t)(gb[b].xh[q][w] >> 16);
-            sm.phT_lo[(f0 + 2 * w) * STP + lane] = (uint16_t)(gb[b].xl[q][w] & 0xFFFFu);
-            sm.phT_lo[(f0 + 2 * w + 1) * STP + lane] = (uint16_t)(gb[b].xl[q][w] >> 16);
+            pTh[(f0 + 2 * w) * STP + lane] = (uint16_t)(gb[b].xh[q][w] & 0xFFFFu);
+            pTh[(f0 + 2 * w + 1) * STP + lane] = (uint16_t)(gb[b].xh[q][w] >> 16);
+            pTl[(f0 + 2 * w) * STP + lane] = (uint16_t)(gb[b].xl[q][w] & 0xFFFFu);
+            pTl[(f0 + 2 * w + 1) * STP + lane] = (uint16_t)(gb[b].xl[q][w] >> 16);
           }
         }
 #pragma unroll
         for (int q = 0; q < VC; ++q) {
           uint32_t hi, lo;
           DT::split(gb[b].v[q >> 2].get(q & 3), hi, lo);
-          sm.VT_hi[(VC * wave + q) * STP + lane] = (uint16_t)hi;
-          if constexpr (DT::kSplit) sm.VT_lo[(VC * wave + q) * STP + lane] = (uint16_t)lo;
+          vTh[(VC * wave + q) * STP + lane] = (uint16_t)hi;
+          if constexpr (DT::kSplit) vTl[(VC * wave + q) * STP + lane] = (uint16_t)lo;
         }
+        // (two buffers: a wave stages block b + 2 into this buffer only
+        // after this barrier's successor, which every wave reaches after
+        // its products of block b)
         lds_barrier();
         {
           // s partial sums: feature F, 64 / NPART tokens per part, fixed order
@@ -654,8 +672,8 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
           float part = 0.f;
 #pragma unroll
           for (int q8 = 0; q8 < TPP / 8; ++q8) {
-            const u32x4 wh = ld16(sm.phT_hi + F * STP + TPP * qt + 8 * q8);
-            const u32x4 wl = ld16(sm.phT_lo + F * STP + TPP * qt + 8 * q8);
+            const u32x4 wh = ld16(pTh + F * STP + TPP * qt + 8 * q8);
+            const u32x4 wl = ld16(pTl + F * STP + TPP * qt + 8 * q8);
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
               const uint32_t bh = (q & 1) ? wh[q >> 1] >> 16 : wh[q >> 1] & 0xFFFFu;
@@ -674,19 +692,20 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
           for (int i = 0; i < NPW; ++i) {
             const int p = wave + kWaves * i, sw = p >> 2, mt = p & 3;
             if (p < NTILE) {
-              const u32x4 bv = ld16(sm.VT_hi + (32 * sw + r) * STP + k0);
-              const u32x4 ah = ld16(sm.phT_hi + (32 * mt + r) * STP + k0);
-              const u32x4 al = ld16(sm.phT_lo + (32 * mt + r) * STP + k0);
+              const u32x4 bv = ld16(vTh + (32 * sw + r) * STP + k0);
+              const u32x4 ah = ld16(pTh + (32 * mt + r) * STP + k0);
+              const u32x4 al = ld16(pTl + (32 * mt + r) * STP + k0);
               Hreg[i] = DT::mma(ah, bv, Hreg[i]);
               Hreg[i] = DT::mma(al, bv, Hreg[i]);
               if constexpr (DT::kSplit)
-                Hreg[i] = DT::mma(ah, ld16(sm.VT_lo + (32 * sw + r) * STP + k0), Hreg[i]);
+                Hreg[i] = DT::mma(ah, ld16(vTl + (32 * sw + r) * STP + k0), Hreg[i]);
             }
           }
         }
-        lds_barrier();
+        if constexpr (NBUF == 1) lds_barrier();
       }
     }
+    if constexpr (NBUF == 2) lds_barrier();   // the last block's s partial sums
     for (int F = tid; F < kD; F += kThreads) {
       float add = 0.f;
 #pragma unroll

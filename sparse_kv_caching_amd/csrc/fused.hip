@@ -43,7 +43,8 @@ __global__ __launch_bounds__(chain_ns::kThreads) void overlap_kernel(OverlapArgs
 
 template <class DT, int HD, int SPW>
 static hipError_t launch_overlap_t(const OverlapArgs& o, hipStream_t st) {
-  const size_t lc = chain_ns::chain_layout(o.c.vr.lam, o.c.C, SPW, DT::kSplit).total;
+  const size_t lc =
+      chain_ns::chain_layout(o.c.vr.lam, o.c.C, SPW, DT::kSplit, chain_ns::kFoldBufs<HD, SPW>).total;
   const size_t la = attn_ns::attn_layout(HD, o.a.vr.lam, o.a.vr.eta, o.a.C, DT::kSplit).total;
   const size_t lds = lc > la ? lc : la;
   const void* fn = (const void*)overlap_kernel<DT, HD, SPW>;
