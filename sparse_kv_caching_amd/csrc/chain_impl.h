@@ -559,6 +559,60 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
     {
       const int seg = ((nE + kWaves - 1) / kWaves + 63) / 64 * 64;
       const int e0 = wave * seg, e1 = min(nE, e0 + seg);
+      const int nit = e1 > e0 ? (e1 - e0 + 63) / 64 : 0;   // 64-candidate rows of the wave
+      constexpr int MAXIT = 8;
+      if (nit <= MAXIT) {
+        // the wave's keys and virtual indices are read once, all at once
+        // (rows of the wave only; indices clamped into the candidates: nE
+        // >= 1 here), and the first pass's ballots are kept for the second
+        uint64_t kk[MAXIT], bks[MAXIT];
+        int32_t ev[MAXIT];
+#pragma unroll
+        for (int it = 0; it < MAXIT; ++it) {
+          kk[it] = 0;
+          ev[it] = 0;
+          if (it < nit) {
+            const int ec = min(e0 + 64 * it + lane, nE - 1);
+            kk[it] = sm.keys[ec];
+            ev[it] = sm.E[ec];
+          }
+        }
+        int kept = 0;
+#pragma unroll
+        for (int it = 0; it < MAXIT; ++it) {
+          const int e = e0 + 64 * it + lane;
+          const bool kp = it < nit && e < e1 && lam > 0 && (kk[it] & mask) >= prefix;
+          bks[it] = __ballot(kp);
+          kept += __popcll(bks[it]);
+        }
+        if (lane == 0) sm.misc[8 + wave] = kept;
+        lds_barrier();
+        int kb = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+          if (w < wave) kb += sm.misc[8 + w];
+#pragma unroll
+        for (int it = 0; it < MAXIT; ++it) {
+          if (it >= nit) break;
+          const int e = e0 + 64 * it + lane;
+          const bool in = e < e1;
+          const bool kp = in && lam > 0 && (kk[it] & mask) >= prefix;
+          const unsigned long long bk = bks[it];
+          const int before = __popcll(bk & ((1ull << lane) - 1ull));
+          if (kp) {
+            if (kb + before < lam) {
+              sm.G[kb + before] = ev[it];
+              sm.Gp[kb + before] = (int32_t)(0xFFFFFFFFu - (uint32_t)kk[it]);
+            }
+          } else if (in) {
+            const int sidx = e - (kb + before);
+            if (sidx < nE - lam) sm.S[sidx] = ev[it];
+            if (a.dbg_fold && rank == 0 && ev[it] >= lam + eta)
+              a.dbg_fold[(size_t)u * vr.T + (ev[it] - lam - eta)] = j;
+          }
+          kb += __popcll(bk);
+        }
+      } else {
       int kept = 0;
       for (int base = e0; base < e1; base += 64) {
         const int e = base + lane;
@@ -591,6 +645,7 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
             a.dbg_fold[(size_t)u * vr.T + (sm.E[e] - lam - eta)] = j;
         }
         kb += __popcll(bk);
+      }
       }
     }
     gs = lam;
