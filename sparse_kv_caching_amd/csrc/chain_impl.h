@@ -127,25 +127,18 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 
-// Four consecutive input elements as loaded (converted where staged).
-template <class T> struct VRaw;
-template <> struct VRaw<uint16_t> {
-  u32x2 w;
-  __device__ __forceinline__ void load(bool valid, const uint16_t* p) {
-    w = valid ? *reinterpret_cast<const u32x2*>(p) : u32x2{0, 0};
-  }
-  __device__ __forceinline__ float get(int i) const {
-    const uint32_t x = w[i >> 1];
-    return __uint_as_float((i & 1) ? (x & 0xFFFF0000u) : (x << 16));
-  }
-};
-template <> struct VRaw<float> {
-  f32x4 w;
-  __device__ __forceinline__ void load(bool valid, const float* p) {
-    w = valid ? *reinterpret_cast<const f32x4*>(p) : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  __device__ __forceinline__ float get(int i) const { return w[i]; }
-};
+// y[d] = x[(d + r) % 4] for a lane-dependent r in 0 .. 3 (two selects per
+// dword, no indexed registers).
+__device__ __forceinline__ u32x4 rot_dw(u32x4 x, int r) {
+  const bool r1 = r & 1, r2 = r & 2;
+  const u32x4 y = {r1 ? x[1] : x[0], r1 ? x[2] : x[1], r1 ? x[3] : x[2], r1 ? x[0] : x[3]};
+  return u32x4{r2 ? y[2] : y[0], r2 ? y[3] : y[1], r2 ? y[0] : y[2], r2 ? y[1] : y[3]};
+}
+
+// Halfword e (0 .. 7) of a 16-byte piece.
+__device__ __forceinline__ uint16_t half_of(u32x4 x, int e) {
+  return (uint16_t)((e & 1) ? x[e >> 1] >> 16 : x[e >> 1] & 0xFFFFu);
+}
 
 }  // namespace chain_ns
 
@@ -652,39 +645,52 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
     lds_barrier();
 
     // ---- 4d. fold the rest into own columns of H (MFMA) and into s, 64
-    // tokens per block.  The gather is by rows: lane = token, wave = feature
-    // / column chunks, with 16-byte loads where possible; the tiles are
-    // written transposed (token-contiguous) for the MFMA operands.  The
-    // gathers of up to GB blocks are issued together (they are latency-bound,
-    // and a later block's loads then stay in flight while an earlier block is
-    // staged and multiplied); values stay as loaded until they are staged.
+    // tokens per block.  The gather reads rows four lanes to 64 contiguous
+    // bytes (a 16-byte piece each), so that one load instruction touches 16
+    // rows rather than 64 (a gather's cost in the vector memory unit grows
+    // with the rows one instruction touches): wave w loads plane w / 4 (hi,
+    // lo) of feature quarter w % 4 for the block's 64 tokens (tokens
+    // 16 i + lane / 4), and the own V columns of tokens 8 w .. 8 w + 7.  The
+    // tiles are written transposed (token-contiguous) for the MFMA operands;
+    // a lane writes its eight values starting at the one 2 (piece % 4) on, so
+    // that the lanes of one write hit distinct banks.  The gathers of up to
+    // GB blocks are issued together (they are latency-bound, and a later
+    // block's loads then stay in flight while an earlier block is staged and
+    // multiplied); values stay as loaded until they are staged.
     const int nS = nE - lam;
     float sacc = 0.f;
-    constexpr int FCW = 16 / kWaves;                     // 8-feature chunks of phi per wave
-    constexpr int VC = 32 * SPW / kWaves;                // own V columns per wave: 4, 8 or 16
+    static_assert(kWaves == 8 && kD == 128, "two planes x four feature quarters, one per wave");
+    constexpr int PER = 16 / (int)sizeof(T);             // V elements per 16-byte piece
+    constexpr int VPR = 32 * SPW / PER;                  // V pieces of an own row
+    constexpr int VL = (8 * VPR + 63) / 64;              // V pieces per lane
     constexpr int GB = SPW == 1 ? 4 : (SPW == 2 ? 2 : 1);   // blocks gathered together
     struct Gather {
-      u32x4 xh[FCW], xl[FCW];
-      VRaw<T> v[VC / 4];
+      u32x4 x[4];
+      u32x4 v[VL];
     };
+    const int pq = lane & 3, tq = lane >> 2;             // phi piece, token within 16
+    const int fq = 32 * (wave & 3) + 8 * pq;             // the lane's first feature
+    const uint16_t* pplane = (wave < 4 ? a.phi_hi : a.phi_lo) + phi_unit + fq;
     constexpr int NBUF = kFoldBufs<HD, SPW>;
     int blk = 0;                                         // blocks staged so far
     for (int sb0 = 0; sb0 < nS; sb0 += 64 * GB) {
       Gather gb[GB];
 #pragma unroll
       for (int b = 0; b < GB; ++b) {
-        const int tok = sb0 + 64 * b + lane;
-        const bool tv = tok < nS;
-        const int vi = tv ? sm.S[tok] : 0;
 #pragma unroll
-        for (int q = 0; q < FCW; ++q) {
-          const int f0 = 8 * (FCW * wave + q);
-          gb[b].xh[q] = tv ? ld16(a.phi_hi + phi_unit + (size_t)vi * kD + f0) : u32x4{0, 0, 0, 0};
-          gb[b].xl[q] = tv ? ld16(a.phi_lo + phi_unit + (size_t)vi * kD + f0) : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < 4; ++i) {
+          const int tok = sb0 + 64 * b + 16 * i + tq;
+          gb[b].x[i] = tok < nS ? ld16(pplane + (size_t)sm.S[tok] * kD) : u32x4{0, 0, 0, 0};
         }
-        const T* vrow = reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))) + col0 + VC * wave;
 #pragma unroll
-        for (int q4 = 0; q4 < VC / 4; ++q4) gb[b].v[q4].load(tv, vrow + 4 * q4);
+        for (int m = 0; m < VL; ++m) {
+          const int idx = lane + 64 * m, pc = idx % VPR;
+          const int tok = sb0 + 64 * b + 8 * wave + idx / VPR;
+          gb[b].v[m] = idx < 8 * VPR && tok < nS
+                           ? *reinterpret_cast<const u32x4*>(
+                                 reinterpret_cast<const T*>(vr.vrow(u, sm.S[tok], sizeof(T))) + col0 + PER * pc)
+                           : u32x4{0, 0, 0, 0};
+        }
       }
 #pragma unroll
       for (int b = 0; b < GB; ++b) {
@@ -697,23 +703,34 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
         uint16_t* pTl = sm.phT_lo + fb * (kD * STP);
         uint16_t* vTh = sm.VT_hi + fb * (32 * SPW * STP);
         uint16_t* vTl = sm.VT_lo + (DT::kSplit ? fb * (32 * SPW * STP) : 0);
+        {
+          uint16_t* dst = (wave < 4 ? pTh : pTl) + tq;
 #pragma unroll
-        for (int q = 0; q < FCW; ++q) {
-          const int f0 = 8 * (FCW * wave + q);
+          for (int i = 0; i < 4; ++i) {
+            const u32x4 y = rot_dw(gb[b].x[i], pq);
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            pTh[(f0 + 2 * w) * STP + lane] = (uint16_t)(gb[b].xh[q][w] & 0xFFFFu);
-            pTh[(f0 + 2 * w + 1) * STP + lane] = (uint16_t)(gb[b].xh[q][w] >> 16);
-            pTl[(f0 + 2 * w) * STP + lane] = (uint16_t)(gb[b].xl[q][w] & 0xFFFFu);
-            pTl[(f0 + 2 * w + 1) * STP + lane] = (uint16_t)(gb[b].xl[q][w] >> 16);
+            for (int e = 0; e < 8; ++e) dst[(fq + ((e + 2 * pq) & 7)) * STP + 16 * i] = half_of(y, e);
           }
         }
 #pragma unroll
-        for (int q = 0; q < VC; ++q) {
-          uint32_t hi, lo;
-          DT::split(gb[b].v[q >> 2].get(q & 3), hi, lo);
-          vTh[(VC * wave + q) * STP + lane] = (uint16_t)hi;
-          if constexpr (DT::kSplit) vTl[(VC * wave + q) * STP + lane] = (uint16_t)lo;
+        for (int m = 0; m < VL; ++m) {
+          const int idx = lane + 64 * m, pc = idx % VPR, t = 8 * wave + idx / VPR;
+          if (idx < 8 * VPR) {
+            const u32x4 y = rot_dw(gb[b].v[m], pc & 3);
+            if constexpr (DT::kSplit) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int c = PER * pc + ((e + (pc & 3)) & 3);
+                uint32_t hi, lo;
+                DT::split(__uint_as_float(y[e]), hi, lo);
+                vTh[c * STP + t] = (uint16_t)hi;
+                vTl[c * STP + t] = (uint16_t)lo;
+              }
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) vTh[(PER * pc + ((e + 2 * (pc & 3)) & 7)) * STP + t] = half_of(y, e);
+            }
+          }
         }
         // (two buffers: a wave stages block b + 2 into this buffer only
         // after this barrier's successor, which every wave reaches after
