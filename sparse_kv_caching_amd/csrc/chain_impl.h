@@ -339,8 +339,13 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
       const int t_first = wave / SPW;
       constexpr int TSTEP = kWaves / SPW;
       if (t_first < ntile_own) {
-        const uint16_t* Ahi = sm.HT_hi + (32 * sw + r) * HTP + 8 * h;
-        const uint16_t* Alo = sm.HT_lo + (32 * sw + r) * HTP + 8 * h;
+        // A row r supplies slab column 16 ((r >> 2) & 1) + 4 (r >> 3) + (r & 3),
+        // so that accumulator row 8 g + 4 h + q (lane half h) is column
+        // 16 h + 4 g + q: a lane's 16 columns are contiguous, and its V values
+        // whole 16-byte pieces of the row
+        const int pr = 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+        const uint16_t* Ahi = sm.HT_hi + (32 * sw + pr) * HTP + 8 * h;
+        const uint16_t* Alo = sm.HT_lo + (32 * sw + pr) * HTP + 8 * h;
         for (int lt = t_first; lt < ntile_own; lt += TSTEP) {
           const int e = 32 * (ch + CS * lt) + r;
           const bool ev = e < nE;
@@ -350,10 +355,21 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
           u32x4 bh[8], bl[8];
 #pragma unroll
           for (int kb = 0; kb < 8; ++kb) { bh[kb] = ld16(ph + 16 * kb); bl[kb] = ld16(pl + 16 * kb); }
-          const T* vrow = reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))) + col0 + 32 * sw + 4 * h;
-          float vv[4][4];
+          const T* vrow = reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))) + col0 + 32 * sw + 16 * h;
+          float vv[16];
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) load4_f32(vrow + 8 * g4, vv[g4]);
+          for (int c = 0; c < (int)sizeof(T); ++c) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(vrow + 16 / sizeof(T) * c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if constexpr (sizeof(T) == 2) {
+                vv[8 * c + 2 * j] = __uint_as_float(w[j] << 16);
+                vv[8 * c + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+              } else {
+                vv[4 * c + j] = __uint_as_float(w[j]);
+              }
+            }
+          }
           // z = phi^T s with phi = hi + lo, as the GEMM sees it
           float z = 0.f;
 #pragma unroll
@@ -388,7 +404,7 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
           for (int g4 = 0; g4 < 4; ++g4)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float df = (P0[4 * g4 + q] + P1[4 * g4 + q]) * iz - vv[g4][q];
+              const float df = (P0[4 * g4 + q] + P1[4 * g4 + q]) * iz - vv[4 * g4 + q];
               acc = fmaf(df, df, acc);
             }
           acc += xor32(acc);
