@@ -354,11 +354,20 @@ int lola_state_positions(const lola_state* st, int64_t* out);
  *                             Both schedules give bitwise the same results
  *                             (the chain's results do not depend on its
  *                             workgroup count).
+ *   LOLA_DEBUG_CHAIN_SPLIT    how the chain's k > 1 workgroups of a unit share
+ *                             the work: 0 = column slabs of H times groups of
+ *                             candidates; 1 = groups of candidates only, every
+ *                             workgroup holding all of H (when its LDS layout
+ *                             fits; otherwise as 0); -1 (default) = 1 when a
+ *                             workgroup scores >= 8 tiles of 32 candidates
+ *                             per step, else 0.  Both give bitwise the same
+ *                             results.
  * The first two exist to exercise the failure path: the chain sets its device
  * fault flag and ends, the later kernels of the call return untouched, and
  * lola_state_check() reports LOLA_ERR_STATE.
  * Errors: INVALID_ARG (NULL state, unknown key, value out of range). */
-enum { LOLA_DEBUG_SPIN_LIMIT = 0, LOLA_DEBUG_CHAIN_FAIL_AT = 1, LOLA_DEBUG_OVERLAP = 2 };
+enum { LOLA_DEBUG_SPIN_LIMIT = 0, LOLA_DEBUG_CHAIN_FAIL_AT = 1, LOLA_DEBUG_OVERLAP = 2,
+       LOLA_DEBUG_CHAIN_SPLIT = 3 };
 int lola_debug_set(lola_state* st, int key, long long value);
 
 /* Text of a status code, and the last error detail of the calling thread. */

@@ -53,6 +53,7 @@ struct lola_state {
   int spin_limit;           // exchange polls before a partner counts as lost (lola_debug_set)
   int fail_at;              // debug: exchange step at which the chain gives up (-1: never)
   int overlap;              // prefill schedule: -1 auto, 0 sequential, 1 concurrent read
+  int split;                // chain work split (k > 1): -1 auto, 0 slabs x candidates, 1 candidates
   int ncu;                  // compute units of the device
   void* own_ws;
   size_t own_ws_bytes;
@@ -384,6 +385,7 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
   st->spin_limit = kSpinLimit;
   st->fail_at = -1;
   st->overlap = -1;
+  st->split = -1;
   st->U = c.batch * c.kv_heads;
   st->g = g;
   st->d = c.head_dim;
@@ -630,6 +632,16 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   }
   const int k_ovl = overlap_workgroups(st, T, C, nch);
   ca.k = k_ovl ? k_ovl : chain_workgroups(U, st->ncu, d, lam, C);
+  // k > 1: the candidate split where its LDS layout fits and (automatic
+  // choice) a workgroup scores >= 8 tiles of 32 candidates per step, so that
+  // staging the tiles once for all slabs pays for holding all of H (folds
+  // over all columns, a larger H^T rebuild).  Measured on MI355X, chain
+  // step at 2 workgroups per unit with 20 tiles: 34.8 -> 31.2 us; at 16
+  // with 72 tiles: 27.0 -> 27.3 us
+  ca.xs = ca.k > 1 && st->split != 0 && chain_split_lds_bytes(lam, C, d, st->f32) + 64 <= kMaxLds &&
+                  (st->split == 1 || (lam + C + 31) / 32 >= 8 * ca.k)
+              ? 1
+              : 0;
   ca.xcd_group = (U % 8 == 0) ? 1 : 0;
   ca.xbuf = (uint64_t*)(base + L.xbuf);
   ca.err = st->dev_err;
@@ -658,7 +670,8 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   aa.branches = st->branches;
   aa.err = st->dev_err;
   aa.ready = ca.ready;
-  // writer workgroups per unit: one per slab group (d / 32 / SPW)
+  // writer workgroups per unit: one per slab group (d / 32 / SPW), or
+  // min(k, d / 32) with the candidate split (the same counts)
   const int nslab = d / 32;
   aa.ready_need = ca.k >= nslab ? nslab : (ca.k == 1 ? 1 : nslab / 2);
   aa.spin_limit = st->spin_limit;
@@ -821,6 +834,11 @@ int lola_debug_set(lola_state* st, int key, long long value) {
       if (value < -1 || value > 1)
         return fail(LOLA_ERR_INVALID_ARG, "overlap %lld not in {-1, 0, 1}", value);
       st->overlap = (int)value;
+      return LOLA_OK;
+    case LOLA_DEBUG_CHAIN_SPLIT:
+      if (value < -1 || value > 1)
+        return fail(LOLA_ERR_INVALID_ARG, "chain split %lld not in {-1, 0, 1}", value);
+      st->split = (int)value;
       return LOLA_OK;
     default:
       return fail(LOLA_ERR_INVALID_ARG, "unknown debug key %d", key);

@@ -21,9 +21,16 @@ __global__ __launch_bounds__(chain_ns::kThreads) void chain_kernel(ChainArgs a) 
   chain_body<DT, HD, SPW>(a, blockIdx.x);
 }
 
+// LDS layout of the candidate split (every workgroup holding all slabs)
+size_t chain_split_lds_bytes(int lam, int C, int d, bool f32) {
+  return chain_ns::chain_layout(lam, C, d / 32, f32, 1, true).total;
+}
+
 template <class DT, int HD, int SPW>
 static hipError_t launch_chain_t(const ChainArgs& a, int U, hipStream_t st) {
-  const size_t lds = chain_ns::chain_layout(a.vr.lam, a.C, SPW, DT::kSplit, chain_ns::kFoldBufs<HD, SPW>).total;
+  const bool xs = SPW == HD / 32 && a.xs && a.k > 1;
+  const size_t lds =
+      chain_ns::chain_layout(a.vr.lam, a.C, SPW, DT::kSplit, chain_ns::kFoldBufs<HD, SPW>, xs).total;
   const void* fn = (const void*)chain_kernel<DT, HD, SPW>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -32,10 +39,12 @@ static hipError_t launch_chain_t(const ChainArgs& a, int U, hipStream_t st) {
 }
 
 // k >= NSLAB: one column slab per workgroup; k == 2 (NSLAB = 4): two; k == 1:
-// all of them (the only instance that exchanges nothing)
+// all of them (the only instance that exchanges nothing); the candidate split:
+// all of them, k candidate groups
 template <class DT, int HD>
 static hipError_t launch_chain_k(const ChainArgs& a, int U, hipStream_t st) {
   constexpr int NSLAB = HD / 32;
+  if (a.xs && a.k > 1) return launch_chain_t<DT, HD, NSLAB>(a, U, st);
   if (a.k >= NSLAB) return launch_chain_t<DT, HD, 1>(a, U, st);   // k = NSLAB * CS
   if (a.k == 1) return launch_chain_t<DT, HD, NSLAB>(a, U, st);
   if constexpr (NSLAB == 4) {

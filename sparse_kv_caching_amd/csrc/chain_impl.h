@@ -1,7 +1,6 @@
 // K2: LoLA's serial memory-allocation chain, one step per chunk.  A unit
-// (b, KV head) is processed by k cooperating workgroups (k = 1, 2 or 4, so
-// that every workgroup of the grid is resident at once); workgroup r owns
-// SPW = (d / 32) / k column slabs of H.
+// (b, KV head) is processed by k cooperating workgroups, every workgroup of
+// the grid resident at once (the work split is below).
 //
 // Per chunk j (LoLA notes §2.6, Eq. (15); §2.4, Eqs. (11)-(13)):
 //   1. snapshot (H_j, s_j, G_j): the state the chunk's queries read (each
@@ -31,8 +30,8 @@
 // Layout.  A workgroup's H columns live in registers for the whole call in
 // MFMA result layout (32 x 32 tiles (feature block mt, slab)); folds
 // accumulate into them in place.  After each fold the columns are written to
-// LDS as H^T hi/lo rows, from which every wave loads its slab's A operands of
-// the next SRE GEMM once per step.
+// LDS as H^T hi/lo rows, from which the waves read their slab's A operands
+// of the next SRE GEMM.
 //
 // Work split.  A unit's k workgroups form NG = (d / 32) / SPW slab groups
 // times CS candidate groups: workgroup (g, ch) owns the columns of slab group
@@ -76,7 +75,7 @@ template <int HD, int SPW> constexpr int kFoldBufs = SPW < HD / 32 ? 2 : 1;
 // staging tiles, which are live only after the selection.
 struct ChainLayout {
   uint32_t HT_hi, HT_lo, s32, spart, G, Gp, S, misc, kred;
-  uint32_t E, part, keys, hist;                // selection phase
+  uint32_t E, part, keys, hist, stage;         // selection phase
   uint32_t phT_hi, phT_lo, VT_hi, VT_lo;       // fold phase (same region)
   uint32_t total;
 };
@@ -84,8 +83,11 @@ struct ChainLayout {
 __host__ __device__ inline uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
 
 // nbuf: fold staging buffers (2 lets a block be staged while the previous
-// one is multiplied, one barrier per block)
-__host__ __device__ inline ChainLayout chain_layout(int lam, int C, int spw, bool f32, int nbuf = 1) {
+// one is multiplied, one barrier per block).  xs: the candidate split (parts
+// go through the exchange only; the phi tiles of a round of the SRE are
+// staged after the histograms)
+__host__ __device__ inline ChainLayout chain_layout(int lam, int C, int spw, bool f32, int nbuf = 1,
+                                                   bool xs = false) {
   ChainLayout L;
   uint32_t off = 0;
   auto take = [&](uint32_t bytes) { const uint32_t o = off; off = align16(off + bytes); return o; };
@@ -103,9 +105,10 @@ __host__ __device__ inline ChainLayout chain_layout(int lam, int C, int spw, boo
   L.kred = take(2 * kWaves * 8);           // per-wave key min / max
   const uint32_t region = off;
   L.E = take(le * 4);                      // candidates (virtual indices)
-  L.part = take((uint32_t)spw * le * 4);   // [slab][candidate] SRE parts
+  L.part = take(xs ? 2u * kWaves * 32 * 4 : (uint32_t)spw * le * 4);   // SRE parts
   L.keys = take(le * 8);
   L.hist = take(768 * 4);                  // three radix histograms
+  L.stage = xs ? take((uint32_t)(kWaves / spw) * 2 * 32 * HTP * 2) : 0;   // [tile][plane][32][HTP]
   const uint32_t sel_end = off;
   off = region;
   const uint32_t nb = (uint32_t)nbuf;
@@ -151,9 +154,12 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
   constexpr int NTILE = 4 * SPW;                  // own H tiles (feature block, slab)
   constexpr int NPW = (NTILE + kWaves - 1) / kWaves;   // H tiles per wave (1 or 2)
   constexpr int NG = NSLAB / SPW;                 // slab groups
-  // the workgroups of a unit exchange SRE parts when they split the columns:
-  // the host launches SPW < NSLAB exactly when k > 1
+  // the workgroups of a unit exchange SRE parts when they split the columns
+  // (the host launches SPW < NSLAB exactly when k > 1) or the candidates
+  // (the candidate split: the all-slab instance with k > 1)
   constexpr bool kExch = SPW < NSLAB;
+  const bool xs = SPW == NSLAB && a.xs != 0 && a.k > 1;
+  const bool xch = kExch || xs;
   const VirtRows vr = a.vr;
   const int lam = vr.lam, eta = vr.eta, k = a.k, CS = a.k / NG;
   const int LE = lam + a.C;                       // candidates per step, at most
@@ -173,13 +179,19 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
   // (every workgroup reads the same word, so the whole grid returns)
   if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile const int*>(a.err)) != 0) return;
   const int grp = rank % NG, ch = rank / NG;      // slab group, candidate group
-  const bool writer = ch == 0;                    // writes this slab group's columns
   const int col0 = 32 * SPW * grp;                // first H column of this workgroup
+  // snapshot writers: candidate group 0 of each slab group (its columns), or
+  // with the candidate split the first min(k, NSLAB) workgroups, a share of
+  // the columns each
+  const int nw = xs ? min(CS, NSLAB) : 1;
+  const bool writer = ch < nw;
+  const int wr0 = xs ? 32 * (NSLAB / nw) * ch : col0;   // first column written
+  const int wrn = xs ? 32 * (NSLAB / nw) : 32 * SPW;    // columns written
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, r = lane & 31;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const ChainLayout L = chain_layout(lam, a.C, SPW, DT::kSplit, kFoldBufs<HD, SPW>);
+  const ChainLayout L = chain_layout(lam, a.C, SPW, DT::kSplit, kFoldBufs<HD, SPW>, xs);
   struct {
     uint16_t *HT_hi, *HT_lo;
     float *s32, *spart;
@@ -275,12 +287,12 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
     if (writer) {
       if (a.ready && j > a.j0) publish();
       uint16_t* dst = a.snapHT + ((size_t)u * a.nch + j) * 2 * HD * kD;
-      constexpr int chunks = 32 * SPW * (kD / 8);   // 16-byte pieces per plane
+      const int chunks = wrn * (kD / 8);             // 16-byte pieces per plane
       for (int i = tid; i < 2 * chunks; i += kThreads) {
         const int pl = i / chunks, rem = i % chunks;
         const int row = rem / (kD / 8), col = (rem % (kD / 8)) * 8;
-        const uint16_t* src = (pl ? sm.HT_lo : sm.HT_hi) + row * HTP + col;
-        uint16_t* d16 = dst + (size_t)pl * HD * kD + (size_t)(col0 + row) * kD + col;
+        const uint16_t* src = (pl ? sm.HT_lo : sm.HT_hi) + (wr0 - col0 + row) * HTP + col;
+        uint16_t* d16 = dst + (size_t)pl * HD * kD + (size_t)(wr0 + row) * kD + col;
         const u32x4 x = *reinterpret_cast<const u32x4*>(src);
         if (a.ready) {
           uint64_t* d64 = reinterpret_cast<uint64_t*>(d16);
@@ -326,95 +338,189 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
     for (int i = tid; i < 256; i += kThreads) sm.hist[i] = 0;
     lds_barrier();
 
-    // ---- 4a. SRE parts over this workgroup's columns.  Wave w takes slab
-    // w % SPW (A operands from its H^T rows in LDS) and the
-    // candidate tiles t = w / SPW, w / SPW + kWaves / SPW, ...; per tile the
-    // phi rows (B operands) and V columns come from global memory.
+    // ---- 4a. SRE parts over this workgroup's columns, by tiles of 32
+    // candidates (t with t % CS == ch).  A tile's part over a slab is one
+    // wave's work: A operands from the slab's H^T rows in LDS, B operands
+    // the candidates' phi rows, then the error over the slab's columns
+    // against the candidates' V values (from global memory).
     const int ntile = lam > 0 ? (nE + 31) / 32 : 0;
     const int ntile_own = ntile > ch ? (ntile - ch + CS - 1) / CS : 0;
     const uint32_t tag = (uint32_t)(xstep + 1);
     uint64_t* xb = a.xbuf + ((size_t)u * 2 + (xstep & 1)) * NSLAB * LE;
-    if (!a.vscore) {
+    // row r of the A operand is slab column 16 ((r >> 2) & 1) + 4 (r >> 3) +
+    // (r & 3), so that accumulator row 8 g + 4 h + q (lane half h) is column
+    // 16 h + 4 g + q: a lane's 16 columns are contiguous, and its V values
+    // whole 16-byte pieces of the row
+    const int pr = 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
+    // the V values of the lane's 16 columns of candidate row vi, slab sw
+    auto load_v = [&](u32x4 (&v)[sizeof(T)], int vi, int sw) {
+      const T* vrow = reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))) + col0 + 32 * sw + 16 * h;
+#pragma unroll
+      for (int c = 0; c < (int)sizeof(T); ++c) v[c] = *reinterpret_cast<const u32x4*>(vrow + 16 / sizeof(T) * c);
+    };
+    // the part over slab sw of the candidate of lane row r (returned in
+    // both lane halves), from its phi row's hi / lo pieces (get(kb, hi, lo):
+    // lane half h, features 16 kb + 8 h ..) and V values
+    // (merged: one pass over kb for z and the products, the operands read
+    // once each; else z first, as the register-held operands allow)
+    auto sre_tile = [&](auto merged, auto&& get, const u32x4 (&vw)[sizeof(T)], int sw, auto&& put) {
+      const uint16_t* Ahi = sm.HT_hi + (32 * sw + pr) * HTP + 8 * h;
+      const uint16_t* Alo = sm.HT_lo + (32 * sw + pr) * HTP + 8 * h;
+      float vv[16];
+#pragma unroll
+      for (int c = 0; c < (int)sizeof(T); ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (sizeof(T) == 2) {
+            vv[8 * c + 2 * j] = __uint_as_float(vw[c][j] << 16);
+            vv[8 * c + 2 * j + 1] = __uint_as_float(vw[c][j] & 0xFFFF0000u);
+          } else {
+            vv[4 * c + j] = __uint_as_float(vw[c][j]);
+          }
+        }
+      // z = phi^T s with phi = hi + lo, as the GEMM sees it, and P^T (this
+      // slab's 32 columns x 32 candidates) in two accumulators
+      float z = 0.f;
+      f32x16 P0, P1;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) { P0[q] = 0.f; P1[q] = 0.f; }
+      auto zpart = [&](int kb, const u32x4& bh, const u32x4& bl) {
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(sm.s32 + 16 * kb + 8 * h);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(sm.s32 + 16 * kb + 8 * h + 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t wh = bh[q], wl = bl[q];
+          const float f0 = DT::from_bits(wh & 0xFFFFu) + DT::from_bits(wl & 0xFFFFu);
+          const float f1 = DT::from_bits(wh >> 16) + DT::from_bits(wl >> 16);
+          z = fmaf(f0, q < 2 ? s0[2 * q] : s1[2 * q - 4], z);
+          z = fmaf(f1, q < 2 ? s0[2 * q + 1] : s1[2 * q - 3], z);
+        }
+      };
+      auto prod = [&](int kb, const u32x4& bh, const u32x4& bl) {
+        const u32x4 ah = ld16(Ahi + 16 * kb), al = ld16(Alo + 16 * kb);
+        f32x16& P = (kb & 1) ? P1 : P0;
+        P = DT::mma(ah, bh, P);
+        P = DT::mma(al, bh, P);
+        P = DT::mma(ah, bl, P);
+      };
+      if constexpr (decltype(merged)::value) {
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+          u32x4 bh, bl;
+          get(kb, bh, bl);
+          zpart(kb, bh, bl);
+          prod(kb, bh, bl);
+        }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+          u32x4 bh, bl;
+          get(kb, bh, bl);
+          zpart(kb, bh, bl);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+          u32x4 bh, bl;
+          get(kb, bh, bl);
+          prod(kb, bh, bl);
+        }
+      }
+      z += xor32(z);
+      const float iz = z > 0.f ? 1.f / z : 0.f;   // z == 0: prediction 0
+      float acc = 0.f;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float df = (P0[4 * g4 + q] + P1[4 * g4 + q]) * iz - vv[4 * g4 + q];
+          acc = fmaf(df, df, acc);
+        }
+      put(acc + xor32(acc));
+    };
+    if (!a.vscore && xs) {
+      // candidate split: rounds of TPR tiles, each staged in LDS once (rows
+      // read 16 lanes to 256 contiguous bytes) and shared by the NSLAB waves
+      // of its slabs; the next round's rows and V values are in flight while
+      // the current round computes.  The NSLAB parts of a candidate meet in
+      // LDS and one word per candidate (their sum in slab order, the same
+      // value a reader of per-slab parts forms) goes to the exchange.
+      constexpr int TPR = kWaves / NSLAB;            // tiles per round
+      static_assert(kThreads == 512, "a thread stages one 16-byte piece of one row per tile and plane");
+      uint16_t* stg = reinterpret_cast<uint16_t*>(smem + L.stage);
+      const int ts = wave / NSLAB, sw = wave % NSLAB;
+      const int nround = (ntile_own + TPR - 1) / TPR;
+      // a thread stages piece tid % 16 of row tid / 16 of every tile tt and
+      // plane pl (its piece m = 2 tt + pl)
+      const int srow = tid >> 4, spc = tid & 15;
+      uint16_t* sdst = stg + srow * HTP + 8 * spc;
+      u32x4 sg[2 * TPR], vn[sizeof(T)];
+      float* rp = sm.part;                           // [2][kWaves][32]: round parity, (tile, slab), row
+      auto publish_sums = [&](int ro) {
+        if (tid < TPR * 32) {
+          const int tt = tid >> 5, row = tid & 31, lt = ro * TPR + tt, e = 32 * (ch + CS * lt) + row;
+          if (lt < ntile_own && e < nE) {
+            float sre = 0.f;
+#pragma unroll
+            for (int q = 0; q < NSLAB; ++q) sre += rp[((ro & 1) * kWaves + tt * NSLAB + q) * 32 + row];
+            __hip_atomic_store(xb + e, ((uint64_t)tag << 32) | __float_as_uint(sre), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      };
+      auto stage_load = [&](int ro) {
+#pragma unroll
+        for (int tt = 0; tt < TPR; ++tt) {
+          const int lt = ro * TPR + tt, e = 32 * (ch + CS * lt) + srow;
+          const size_t off = phi_unit + (size_t)(lt < ntile_own && e < nE ? sm.E[e] : sm.E[0]) * kD + 8 * spc;
+          sg[2 * tt] = lt < ntile_own ? ld16(a.phi_hi + off) : u32x4{0, 0, 0, 0};
+          sg[2 * tt + 1] = lt < ntile_own ? ld16(a.phi_lo + off) : u32x4{0, 0, 0, 0};
+        }
+        const int lt = ro * TPR + ts, e = 32 * (ch + CS * lt) + r;
+        if (lt < ntile_own) load_v(vn, e < nE ? sm.E[e] : sm.E[0], sw);
+      };
+      if (nround > 0) stage_load(0);
+      for (int ro = 0; ro < nround; ++ro) {
+#pragma unroll
+        for (int m = 0; m < 2 * TPR; ++m) *reinterpret_cast<u32x4*>(sdst + m * 32 * HTP) = sg[m];
+        u32x4 vc[sizeof(T)];
+#pragma unroll
+        for (int c = 0; c < (int)sizeof(T); ++c) vc[c] = vn[c];
+        lds_barrier();
+        if (ro > 0) publish_sums(ro - 1);
+        if (ro + 1 < nround) stage_load(ro + 1);
+        const int lt = ro * TPR + ts;
+        if (lt < ntile_own) {
+          const uint16_t* sh = stg + ((ts * 2) * 32 + r) * HTP + 8 * h;
+          const uint16_t* sl = sh + 32 * HTP;
+          sre_tile(std::true_type{}, [&](int kb, u32x4& x, u32x4& y) { x = ld16(sh + 16 * kb); y = ld16(sl + 16 * kb); }, vc, sw,
+                   [&](float acc) { if (h == 0) rp[((ro & 1) * kWaves + wave) * 32 + r] = acc; });
+        }
+        lds_barrier();                               // the round's tiles are read
+      }
+      if (nround > 0) publish_sums(nround - 1);
+    } else if (!a.vscore) {
+      // wave w takes slab w % SPW and the tiles t_first = w / SPW,
+      // t_first + kWaves / SPW, ...; phi rows and V values from global memory
       const int sw = wave % SPW;
       const int t_first = wave / SPW;
       constexpr int TSTEP = kWaves / SPW;
-      if (t_first < ntile_own) {
-        // A row r supplies slab column 16 ((r >> 2) & 1) + 4 (r >> 3) + (r & 3),
-        // so that accumulator row 8 g + 4 h + q (lane half h) is column
-        // 16 h + 4 g + q: a lane's 16 columns are contiguous, and its V values
-        // whole 16-byte pieces of the row
-        const int pr = 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3);
-        const uint16_t* Ahi = sm.HT_hi + (32 * sw + pr) * HTP + 8 * h;
-        const uint16_t* Alo = sm.HT_lo + (32 * sw + pr) * HTP + 8 * h;
-        for (int lt = t_first; lt < ntile_own; lt += TSTEP) {
-          const int e = 32 * (ch + CS * lt) + r;
-          const bool ev = e < nE;
-          const int vi = ev ? sm.E[e] : sm.E[0];
-          const uint16_t* ph = a.phi_hi + phi_unit + (size_t)vi * kD + 8 * h;
-          const uint16_t* pl = a.phi_lo + phi_unit + (size_t)vi * kD + 8 * h;
-          u32x4 bh[8], bl[8];
+      for (int lt = t_first; lt < ntile_own; lt += TSTEP) {
+        const int e = 32 * (ch + CS * lt) + r;
+        const int vi = e < nE ? sm.E[e] : sm.E[0];
+        const uint16_t* ph = a.phi_hi + phi_unit + (size_t)vi * kD + 8 * h;
+        const uint16_t* pl = a.phi_lo + phi_unit + (size_t)vi * kD + 8 * h;
+        u32x4 bh[8], bl[8], vw[sizeof(T)];
 #pragma unroll
-          for (int kb = 0; kb < 8; ++kb) { bh[kb] = ld16(ph + 16 * kb); bl[kb] = ld16(pl + 16 * kb); }
-          const T* vrow = reinterpret_cast<const T*>(vr.vrow(u, vi, sizeof(T))) + col0 + 32 * sw + 16 * h;
-          float vv[16];
-#pragma unroll
-          for (int c = 0; c < (int)sizeof(T); ++c) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(vrow + 16 / sizeof(T) * c);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              if constexpr (sizeof(T) == 2) {
-                vv[8 * c + 2 * j] = __uint_as_float(w[j] << 16);
-                vv[8 * c + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-              } else {
-                vv[4 * c + j] = __uint_as_float(w[j]);
-              }
-            }
-          }
-          // z = phi^T s with phi = hi + lo, as the GEMM sees it
-          float z = 0.f;
-#pragma unroll
-          for (int kb = 0; kb < 8; ++kb) {
-            const f32x4 s0 = *reinterpret_cast<const f32x4*>(sm.s32 + 16 * kb + 8 * h);
-            const f32x4 s1 = *reinterpret_cast<const f32x4*>(sm.s32 + 16 * kb + 8 * h + 4);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint32_t wh = bh[kb][q], wl = bl[kb][q];
-              const float f0 = DT::from_bits(wh & 0xFFFFu) + DT::from_bits(wl & 0xFFFFu);
-              const float f1 = DT::from_bits(wh >> 16) + DT::from_bits(wl >> 16);
-              z = fmaf(f0, q < 2 ? s0[2 * q] : s1[2 * q - 4], z);
-              z = fmaf(f1, q < 2 ? s0[2 * q + 1] : s1[2 * q - 3], z);
-            }
-          }
-          z += xor32(z);
-          // P^T (this slab's 32 columns x 32 candidates), two accumulators
-          f32x16 P0, P1;
-#pragma unroll
-          for (int q = 0; q < 16; ++q) { P0[q] = 0.f; P1[q] = 0.f; }
-#pragma unroll
-          for (int kb = 0; kb < 8; ++kb) {
-            const u32x4 ah = ld16(Ahi + 16 * kb), al = ld16(Alo + 16 * kb);
-            f32x16& P = (kb & 1) ? P1 : P0;
-            P = DT::mma(ah, bh[kb], P);
-            P = DT::mma(al, bh[kb], P);
-            P = DT::mma(ah, bl[kb], P);
-          }
-          const float iz = z > 0.f ? 1.f / z : 0.f;   // z == 0: prediction 0
-          float acc = 0.f;
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float df = (P0[4 * g4 + q] + P1[4 * g4 + q]) * iz - vv[4 * g4 + q];
-              acc = fmaf(df, df, acc);
-            }
-          acc += xor32(acc);
-          if (ev && h == 0) {
-            if constexpr (!kExch) sm.part[sw * LE + e] = acc;
+        for (int kb = 0; kb < 8; ++kb) { bh[kb] = ld16(ph + 16 * kb); bl[kb] = ld16(pl + 16 * kb); }
+        load_v(vw, vi, sw);
+        sre_tile(std::false_type{}, [&](int kb, u32x4& x, u32x4& y) { x = bh[kb]; y = bl[kb]; }, vw, sw, [&](float acc) {
+          if (e < nE && h == 0) {
+            if (!xch) sm.part[sw * LE + e] = acc;
             else __hip_atomic_store(xb + (size_t)(grp * SPW + sw) * LE + e,
                                     ((uint64_t)tag << 32) | __float_as_uint(acc),
                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
-        }
+        });
       }
     }
     lds_barrier();
@@ -445,15 +551,18 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
         kmax = key > kmax ? key : kmax;
       }
     }
-    constexpr int XB = kExch ? 4 : 1;
+    // (per-slab words with the column split; one word, the sum, with the
+    // candidate split)
+    constexpr int XB = 4;
+    constexpr int NQ = kExch ? NSLAB : 1;
     for (int e0 = tid; !a.vscore && lam > 0 && e0 < nE; e0 += XB * kThreads) {
-      uint64_t w[kExch ? XB : 1][NSLAB];
-      if constexpr (kExch) {
+      uint64_t w[XB][NQ];
+      if (xch) {
 #pragma unroll
         for (int i = 0; i < XB; ++i) {
           const int e = e0 + i * kThreads;
 #pragma unroll
-          for (int q = 0; q < NSLAB; ++q)
+          for (int q = 0; q < NQ; ++q)
             w[i][q] = e < nE ? __hip_atomic_load(xb + (size_t)q * LE + e, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT)
                              : ((uint64_t)tag << 32);
@@ -464,9 +573,9 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
         const int e = e0 + i * kThreads;
         if (e >= nE) break;
         float sre = 0.f;
-        if constexpr (kExch) {
+        if (xch) {
 #pragma unroll
-          for (int q = 0; q < NSLAB; ++q) {
+          for (int q = 0; q < NQ; ++q) {
             int spins = 0;
             while ((uint32_t)(w[i][q] >> 32) != tag && !lost) {
               if (++spins > a.spin_limit) lost = true;
@@ -679,7 +788,7 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
     constexpr int PER = 16 / (int)sizeof(T);             // V elements per 16-byte piece
     constexpr int VPR = 32 * SPW / PER;                  // V pieces of an own row
     constexpr int VL = (8 * VPR + 63) / 64;              // V pieces per lane
-    constexpr int GB = SPW == 1 ? 4 : (SPW == 2 ? 2 : 1);   // blocks gathered together
+    constexpr int GB = SPW == 1 ? 4 : 2;                 // blocks gathered together
     struct Gather {
       u32x4 x[4];
       u32x4 v[VL];
@@ -811,7 +920,7 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
 #pragma unroll
   for (int i = 0; i < NPW; ++i) {
     const int p = wave + kWaves * i, sw = p >> 2, mt = p & 3;
-    if (p < NTILE && writer) {
+    if (p < NTILE && ch == 0) {
       float* hc = Ho + (size_t)(col0 + 32 * sw + r) * kD + 32 * mt + 4 * h;
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4)

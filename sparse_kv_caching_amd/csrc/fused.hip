@@ -43,8 +43,9 @@ __global__ __launch_bounds__(chain_ns::kThreads) void overlap_kernel(OverlapArgs
 
 template <class DT, int HD, int SPW>
 static hipError_t launch_overlap_t(const OverlapArgs& o, hipStream_t st) {
+  const bool xs = SPW == HD / 32 && o.c.xs && o.c.k > 1;
   const size_t lc =
-      chain_ns::chain_layout(o.c.vr.lam, o.c.C, SPW, DT::kSplit, chain_ns::kFoldBufs<HD, SPW>).total;
+      chain_ns::chain_layout(o.c.vr.lam, o.c.C, SPW, DT::kSplit, chain_ns::kFoldBufs<HD, SPW>, xs).total;
   const size_t la = attn_ns::attn_layout(HD, o.a.vr.lam, o.a.vr.eta, o.a.C, DT::kSplit).total;
   const size_t lds = lc > la ? lc : la;
   const void* fn = (const void*)overlap_kernel<DT, HD, SPW>;
@@ -59,6 +60,7 @@ static hipError_t launch_overlap_t(const OverlapArgs& o, hipStream_t st) {
 template <class DT, int HD>
 static hipError_t launch_overlap_k(const OverlapArgs& o, hipStream_t st) {
   constexpr int NSLAB = HD / 32;
+  if (o.c.xs && o.c.k > 1) return launch_overlap_t<DT, HD, NSLAB>(o, st);
   if (o.c.k >= NSLAB) return launch_overlap_t<DT, HD, 1>(o, st);
   if (o.c.k == 1) return launch_overlap_t<DT, HD, NSLAB>(o, st);
   if constexpr (NSLAB == 4) {

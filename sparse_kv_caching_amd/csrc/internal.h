@@ -86,6 +86,10 @@ struct ChainArgs {
   // k workgroups per unit: 1, 2, or (d / 32) x CS with CS candidate groups;
   // every workgroup of the grid resident at once
   int k;
+  // candidate split (k > 1): every workgroup holds all of H's columns and the
+  // k workgroups are candidate groups; phi tiles are staged in LDS and shared
+  // by the slabs' waves
+  int xs;
   int xcd_group;            // U % 8 == 0: a unit's workgroups share a block residue mod 8
   uint64_t* xbuf;           // [U, 2, d / 32, lam + C]  tagged SRE parts per slab (k > 1), zeroed
   int* err;                 // device error flag: bit 0 = an exchange partner was lost
@@ -99,7 +103,8 @@ struct ChainArgs {
   const float* cscore;      // [U, lam] scores of the cache slots at the call's start
   // concurrent read (NULL: none): the snapshots are written with coherent
   // stores, and each writer workgroup adds 1 to ready[u] once the snapshot
-  // of a chunk is complete (writer workgroups per unit: d / 32 / SPW)
+  // of a chunk is complete (writer workgroups per unit: d / 32 / SPW, or
+  // min(k, d / 32) with the candidate split)
   int* ready;               // [U]
 };
 
@@ -225,6 +230,7 @@ constexpr int kDecodeOneChunkKeys = 128;
 // launchers (return hipError_t of the launch)
 hipError_t launch_phi(const PhiArgs& a, int U, bool f32, hipStream_t st);
 hipError_t launch_chain(const ChainArgs& a, int U, bool f32, hipStream_t st);
+size_t chain_split_lds_bytes(int lam, int C, int d, bool f32);
 size_t chain_lds_bytes(int lam, int C, int d, bool f32);
 hipError_t launch_attn(const AttnArgs& a, int U, bool f32, hipStream_t st);
 // The chain and the read of finished chunks in one launch: the chain's U * k

@@ -6,7 +6,8 @@ count, and the read sees the same snapshots.  Shapes cover the three chain
 instances the concurrent schedule can pick (one column slab per workgroup
 with candidate groups, two slabs, all slabs), fp32 inputs, a second call on a
 non-empty state, and the failure path (a read that cannot wait for its
-chunk ends, and the state reports the fault).  Parity with the oracle of the
+chunk ends, and the state reports the fault); and the two work splits of
+the chain's workgroups.  Parity with the oracle of the
 concurrent schedule itself is covered where the automatic choice takes it:
 the full-size long-context and Llama-shaped calls in test_gpu_parity and
 test_gpu_fullsize follow every chunk against the oracle."""
@@ -15,7 +16,7 @@ import numpy as np
 import pytest
 import torch
 
-from sparse_kv_caching_amd.lola import DEBUG_OVERLAP, DEBUG_SPIN_LIMIT, LolaError
+from sparse_kv_caching_amd.lola import DEBUG_CHAIN_SPLIT, DEBUG_OVERLAP, DEBUG_SPIN_LIMIT, LolaError
 from sparse_kv_caching_amd.workloads import WORKLOADS, make_inputs
 
 from lola_harness import dev, make_layer
@@ -23,10 +24,11 @@ from lola_harness import dev, make_layer
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, overlap, calls=1):
+def _run(wl, overlap, calls=1, split=-1):
     inp = make_inputs(wl)
     layer = make_layer(wl, inp.W)
     layer.debug_set(DEBUG_OVERLAP, overlap)
+    layer.debug_set(DEBUG_CHAIN_SPLIT, split)
     q, k, v = dev(wl, inp.q), dev(wl, inp.k), dev(wl, inp.v)
     outs, recs = [], []
     T = wl.T
@@ -42,9 +44,9 @@ def _run(wl, overlap, calls=1):
     return outs, recs, st
 
 
-def _same(wl, calls=1):
-    a = _run(wl, 0, calls)
-    b = _run(wl, 1, calls)
+def _same(wl, calls=1, a_args=(0, -1), b_args=(1, -1)):
+    a = _run(wl, a_args[0], calls, a_args[1])
+    b = _run(wl, b_args[0], calls, b_args[1])
     for ya, yb in zip(a[0], b[0]):
         assert torch.equal(ya, yb), "outputs differ between the schedules"
     for (spa, cka), (spb, ckb) in zip(a[1], b[1]):
@@ -81,6 +83,24 @@ def test_overlap_fp32_and_gqa():
 def test_overlap_second_call():
     """Two calls: the second starts from a full cache and window."""
     _same(WORKLOADS["llama8b_4k"].scaled(B=1, Hq=4, Hkv=1, T=640, eta=64, lam=96, C=64), calls=2)
+
+
+# The two ways the chain's workgroups of a unit share the work (column slabs
+# times candidate groups, or candidate groups holding all of H, whose parts
+# meet in LDS and whose phi tiles are staged there) give bitwise the same
+# results, in either schedule.
+SPLIT_SHAPES = {
+    "k16": WORKLOADS["llama8b_4k"].scaled(B=1, Hq=8, Hkv=2, T=1024, eta=128, lam=192, C=64),
+    "k2": WORKLOADS["llama8b_4k"].scaled(B=6, Hq=16, Hkv=8, T=256, eta=64, lam=64, C=32),
+    "d64": WORKLOADS["llama8b_4k"].scaled(B=2, Hq=8, Hkv=4, d=64, T=640, eta=64, lam=96, C=64),
+    "fp32": WORKLOADS["tiny_fp32"].scaled(B=2, Hq=4, Hkv=2, d=128, T=300, eta=32, lam=48, C=32),
+}
+
+
+@pytest.mark.parametrize("shape", list(SPLIT_SHAPES))
+@pytest.mark.parametrize("overlap", [0, 1])
+def test_chain_split_same(shape, overlap):
+    _same(SPLIT_SHAPES[shape], a_args=(overlap, 0), b_args=(overlap, 1))
 
 
 def test_overlap_read_gives_up():
