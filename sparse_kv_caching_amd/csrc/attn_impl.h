@@ -260,6 +260,34 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
   // phase then costs one round trip to memory, not one per loop iteration.
   {
     const T* WT = reinterpret_cast<const T*>(a.WT) + (size_t)kvh * kM * HD;
+    const bool coh = a.ready != nullptr;   // snapshots written during this launch
+    // the key table: cache keys from the snapshot's virtual indices (kept
+    // inside the call's rows whatever the snapshot holds), then the local
+    // positions.  The snapshot's entries of the first GT * kThreads keys are
+    // loaded first: the table, and with it the first key tile's loads, need
+    // only them
+    const int32_t* Gj = a.snapG + ((size_t)u * a.nch + j) * lam;
+    const uint32_t nv = (uint32_t)(lam + eta + vr.T);
+    constexpr int GT = 4;
+    auto load_g = [&](int i0, uint32_t (&gv)[GT]) {
+#pragma unroll
+      for (int k = 0; k < GT; ++k) {
+        const int i = i0 + k * kThreads + tid;
+        gv[k] = i >= gsj ? 0u
+                : coh ? (uint32_t)__hip_atomic_load(const_cast<int32_t*>(Gj) + i, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                      : (uint32_t)Gj[i];
+      }
+    };
+    auto store_g = [&](int i0, const uint32_t (&gv)[GT]) {
+#pragma unroll
+      for (int k = 0; k < GT; ++k) {
+        const int i = i0 + k * kThreads + tid;
+        if (i < nkeys) sm_tab[i] = vsrc(i < gsj ? (int)(gv[k] < nv ? gv[k] : 0u) : vi_loc0 + (i - gsj));
+      }
+    };
+    uint32_t gv0[GT];
+    load_g(0, gv0);
     constexpr int WPIECES = kM * HD / PER;
     constexpr int HPIECES = HD * (kD / 8);
     static_assert(WPIECES % kThreads == 0 && (2 * HPIECES) % kThreads == 0, "fixed trip counts");
@@ -271,7 +299,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
       const int i = tid + k * kThreads, f = i / (HD / PER), c = (i % (HD / PER)) * PER;
       wv[k] = *reinterpret_cast<const u32x4*>(WT + (size_t)f * HD + c);
     }
-    const bool coh = a.ready != nullptr;   // snapshots written during this launch
 #pragma unroll
     for (int k = 0; k < HPT; ++k) {
       const int i = tid + k * kThreads, pl = i / HPIECES, rem = i % HPIECES;
@@ -286,6 +313,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
                                                        reinterpret_cast<const uint32_t*>(sj) + tid),
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
                : sj[tid];
+    // the key table (the rest of it, past GT * kThreads keys, read GT per
+    // thread at a time)
+    store_g(0, gv0);
+    for (int i0 = GT * kThreads; i0 < nkeys; i0 += GT * kThreads) {
+      uint32_t gv[GT];
+      load_g(i0, gv);
+      store_g(i0, gv);
+    }
 #pragma unroll
     for (int k = 0; k < WPT; ++k) {
       const int i = tid + k * kThreads, f = i / (HD / PER), c = (i % (HD / PER)) * PER;
@@ -301,28 +336,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
       *reinterpret_cast<u32x2*>(dst + 4) = u32x2{hv[k][2], hv[k][3]};
     }
     if (tid < kD) sm_s[tid] = sv;
-    // the key table: cache keys from the snapshot's virtual indices (kept
-    // inside the call's rows whatever the snapshot holds), then the local
-    // positions; the snapshot's entries are read GT per thread at a time
-    const int32_t* Gj = a.snapG + ((size_t)u * a.nch + j) * lam;
-    const uint32_t nv = (uint32_t)(lam + eta + vr.T);
-    constexpr int GT = 4;
-    for (int i0 = 0; i0 < nkeys; i0 += GT * kThreads) {
-      uint32_t gv[GT];
-#pragma unroll
-      for (int k = 0; k < GT; ++k) {
-        const int i = i0 + k * kThreads + tid;
-        gv[k] = i >= gsj ? 0u
-                : coh ? (uint32_t)__hip_atomic_load(const_cast<int32_t*>(Gj) + i, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT)
-                      : (uint32_t)Gj[i];
-      }
-#pragma unroll
-      for (int k = 0; k < GT; ++k) {
-        const int i = i0 + k * kThreads + tid;
-        if (i < nkeys) sm_tab[i] = vsrc(i < gsj ? (int)(gv[k] < nv ? gv[k] : 0u) : vi_loc0 + (i - gsj));
-      }
-    }
   }
 
   // (fp32 inputs: split into fp16 hi / lo here.)  The operands are used
@@ -341,6 +354,96 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
     __asm__ volatile("" :: "v"(qh[kb]), "v"(ql[kb]));
   }
   __syncthreads();
+
+  // ---- the key tiles' loads, staging and buffers (the loop below).  Rows
+  // past the last key are loaded from the last key's row (finite values
+  // whose weights are exactly 0 after the mask), so the loads need no
+  // branch.
+  constexpr int VPC = (int)sizeof(T) / 2;        // 16-byte pieces per 8 V columns
+  u32x4 kreg[KPT];
+  u32x4 vreg[2][VPC];
+  const bool vthread = VITEMS >= kThreads || tid < VITEMS;   // (wave-uniform)
+  const int vpr = tid % (KT / 2), vcol = vt_cols(tid);        // this thread's V item
+  auto load_k = [&](int t0) {
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      const int pc = q * kThreads + tid, kl = pc / (HD / PER), c = (pc % (HD / PER)) * PER;
+      const int kk = min(t0 + kl, nkeys - 1);
+      kreg[q] = ldg16(row_addr(sm_tab[kk], bk, dk1, dk2) + c * sizeof(T));
+    }
+  };
+  auto load_v = [&](int t0) {
+    if (vthread) {
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        const int kk = min(t0 + 2 * vpr + kq, nkeys - 1);
+        const uint64_t src = row_addr(sm_tab[kk], bv, dv1, dv2) + vcol * sizeof(T);
+#pragma unroll
+        for (int w = 0; w < VPC; ++w) vreg[kq][w] = ldg16(src + 16 * w);
+      }
+    }
+  };
+  // buffer b's arrays (selects, so that the offsets stay in registers)
+  auto buf_off = [&](const uint32_t (&o)[2], int b) -> uint32_t { return b ? o[1] : o[0]; };
+  auto store_k = [&](int b) {
+    uint16_t* Kb = (uint16_t*)(smem + buf_off(L.K, b));
+    uint16_t* KLb = (uint16_t*)(smem + buf_off(L.KL, b));
+#pragma unroll
+    for (int q = 0; q < KPT; ++q) {
+      const int pc = q * kThreads + tid, kl = pc / (HD / PER), c = (pc % (HD / PER)) * PER;
+      if constexpr (DT::kSplit) {
+        float x[4] = {__uint_as_float(kreg[q][0]), __uint_as_float(kreg[q][1]),
+                      __uint_as_float(kreg[q][2]), __uint_as_float(kreg[q][3])};
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) DT::split(x[e], hi[e], lo[e]);
+        *reinterpret_cast<u32x2*>(Kb + kl * KRS + c) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+        *reinterpret_cast<u32x2*>(KLb + kl * KRS + c) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+      } else {
+        *reinterpret_cast<u32x4*>(Kb + kl * KRS + c) = kreg[q];
+      }
+    }
+  };
+  // V column q (of the thread's 8) of its two keys into V^T buffer b
+  auto store_v_col = [&](int b, int q) {
+    uint16_t* VTb = (uint16_t*)(smem + buf_off(L.VT, b));
+    uint16_t* VTLb = (uint16_t*)(smem + buf_off(L.VTL, b));
+    float vf[2];
+#pragma unroll
+    for (int kq = 0; kq < 2; ++kq) {
+      if constexpr (VPC == 1) {   // 8 bf16 in one piece
+        const uint32_t w = vreg[kq][0][q >> 1];
+        vf[kq] = __uint_as_float((q & 1) ? (w & 0xFFFF0000u) : (w << 16));
+      } else {                    // 8 fp32 in two pieces
+        vf[kq] = __uint_as_float(vreg[kq][q >> 2][q & 3]);
+      }
+    }
+    uint32_t* row = reinterpret_cast<uint32_t*>(VTb + (vcol + q) * VTS) + vpr;
+    if constexpr (DT::kSplit) {
+      uint32_t h0, l0, h1, l1;
+      DT::split(vf[0], h0, l0);
+      DT::split(vf[1], h1, l1);
+      *row = h0 | (h1 << 16);
+      *(reinterpret_cast<uint32_t*>(VTLb + (vcol + q) * VTS) + vpr) = l0 | (l1 << 16);
+    } else {
+      *row = f16_pair(vf[0], vf[1]);
+    }
+  };
+  auto store_v = [&](int b) {
+    if (vthread) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) store_v_col(b, q);
+    }
+  };
+  // cache keys hidden from the read: the key loop starts past them
+  const int kbase = (a.branches & LOLA_READ_CACHE) ? 0 : gsj;
+  const int ntiles = (nkeys - kbase + KT - 1) / KT;
+  // the first tile's rows load while phi(q) and the linear read run
+  // (16-bit inputs; fp32 inputs hold too many registers there)
+  if (!DT::kSplit && ntiles > 0) {
+    load_k(kbase);
+    load_v(kbase);
+  }
 
   // ---- phi(q): u^T = W^T q^T (64 features x 32 queries), softmax halves
   float ph[2][2][16];   // [half pos/neg][mt][i]: feature 64*half + 32*mt + 8(i/4) + 4h + (i%4)
@@ -433,9 +536,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
   // the weights of very negative logits do not all underflow
   float m2 = zlin > 0.f ? 0.f : -INFINITY, l = zlin;
   const float scale2 = 1.4426950408889634f / sqrtf((float)HD);
-  // cache keys hidden from the read: the key loop starts past them
-  const int kbase = (a.branches & LOLA_READ_CACHE) ? 0 : gsj;
-  const int ntiles = (nkeys - kbase + KT - 1) / KT;
   // The key loop is a three-stage pipeline over tiles of KT keys.  At the
   // top of iteration t the LDS holds K of tile t + 1 and V of tile t, the
   // registers hold the scores of tile t (computed in iteration t - 1) and
@@ -447,85 +547,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
   // between the score products and the loads between the value products
   // (scheduling fences fix the order), so the matrix cores are fed while
   // the vector, LDS and memory work of the pipeline is done; one barrier
-  // per tile publishes the staged buffers.  Rows past the last key are
-  // loaded from the last key's row (finite values whose weights are
-  // exactly 0 after the mask), so the loads need no branch.
-  constexpr int VPC = (int)sizeof(T) / 2;        // 16-byte pieces per 8 V columns
-  u32x4 kreg[KPT];
-  u32x4 vreg[2][VPC];
-  const bool vthread = VITEMS >= kThreads || tid < VITEMS;   // (wave-uniform)
-  const int vpr = tid % (KT / 2), vcol = vt_cols(tid);        // this thread's V item
-  auto load_k = [&](int t0) {
-#pragma unroll
-    for (int q = 0; q < KPT; ++q) {
-      const int pc = q * kThreads + tid, kl = pc / (HD / PER), c = (pc % (HD / PER)) * PER;
-      const int kk = min(t0 + kl, nkeys - 1);
-      kreg[q] = ldg16(row_addr(sm_tab[kk], bk, dk1, dk2) + c * sizeof(T));
-    }
-  };
-  auto load_v = [&](int t0) {
-    if (vthread) {
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq) {
-        const int kk = min(t0 + 2 * vpr + kq, nkeys - 1);
-        const uint64_t src = row_addr(sm_tab[kk], bv, dv1, dv2) + vcol * sizeof(T);
-#pragma unroll
-        for (int w = 0; w < VPC; ++w) vreg[kq][w] = ldg16(src + 16 * w);
-      }
-    }
-  };
-  // buffer b's arrays (selects, so that the offsets stay in registers)
-  auto buf_off = [&](const uint32_t (&o)[2], int b) -> uint32_t { return b ? o[1] : o[0]; };
-  auto store_k = [&](int b) {
-    uint16_t* Kb = (uint16_t*)(smem + buf_off(L.K, b));
-    uint16_t* KLb = (uint16_t*)(smem + buf_off(L.KL, b));
-#pragma unroll
-    for (int q = 0; q < KPT; ++q) {
-      const int pc = q * kThreads + tid, kl = pc / (HD / PER), c = (pc % (HD / PER)) * PER;
-      if constexpr (DT::kSplit) {
-        float x[4] = {__uint_as_float(kreg[q][0]), __uint_as_float(kreg[q][1]),
-                      __uint_as_float(kreg[q][2]), __uint_as_float(kreg[q][3])};
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) DT::split(x[e], hi[e], lo[e]);
-        *reinterpret_cast<u32x2*>(Kb + kl * KRS + c) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
-        *reinterpret_cast<u32x2*>(KLb + kl * KRS + c) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
-      } else {
-        *reinterpret_cast<u32x4*>(Kb + kl * KRS + c) = kreg[q];
-      }
-    }
-  };
-  // V column q (of the thread's 8) of its two keys into V^T buffer b
-  auto store_v_col = [&](int b, int q) {
-    uint16_t* VTb = (uint16_t*)(smem + buf_off(L.VT, b));
-    uint16_t* VTLb = (uint16_t*)(smem + buf_off(L.VTL, b));
-    float vf[2];
-#pragma unroll
-    for (int kq = 0; kq < 2; ++kq) {
-      if constexpr (VPC == 1) {   // 8 bf16 in one piece
-        const uint32_t w = vreg[kq][0][q >> 1];
-        vf[kq] = __uint_as_float((q & 1) ? (w & 0xFFFF0000u) : (w << 16));
-      } else {                    // 8 fp32 in two pieces
-        vf[kq] = __uint_as_float(vreg[kq][q >> 2][q & 3]);
-      }
-    }
-    uint32_t* row = reinterpret_cast<uint32_t*>(VTb + (vcol + q) * VTS) + vpr;
-    if constexpr (DT::kSplit) {
-      uint32_t h0, l0, h1, l1;
-      DT::split(vf[0], h0, l0);
-      DT::split(vf[1], h1, l1);
-      *row = h0 | (h1 << 16);
-      *(reinterpret_cast<uint32_t*>(VTLb + (vcol + q) * VTS) + vpr) = l0 | (l1 << 16);
-    } else {
-      *row = f16_pair(vf[0], vf[1]);
-    }
-  };
-  auto store_v = [&](int b) {
-    if (vthread) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) store_v_col(b, q);
-    }
-  };
+  // per tile publishes the staged buffers.  The first tile's rows were
+  // loaded before phi(q) (16-bit inputs).
   // S^T = K Q^T of the tile in K buffer b (32 keys x 32 queries per half kh)
   auto scores = [&](int b, f32x16 (&Sx)[2]) {
     const uint16_t* Kb = (const uint16_t*)(smem + buf_off(L.K, b));
@@ -549,8 +572,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
   };
   f32x16 S[2];
   if (ntiles > 0) {
-    load_k(kbase);
-    load_v(kbase);
+    if constexpr (DT::kSplit) {
+      load_k(kbase);
+      load_v(kbase);
+    }
     store_k(0);
     store_v(0);
   }
