@@ -16,9 +16,9 @@ size_t chain_lds_bytes(int lam, int C, int d, bool f32) {
   return m;
 }
 
-template <class DT, int HD, int SPW>
+template <class DT, int HD, int SPW, bool XS>
 __global__ __launch_bounds__(chain_ns::kThreads) void chain_kernel(ChainArgs a) {
-  chain_body<DT, HD, SPW>(a, blockIdx.x);
+  chain_body<DT, HD, SPW, XS>(a, blockIdx.x);
 }
 
 // LDS layout of the candidate split (every workgroup holding all slabs)
@@ -26,15 +26,14 @@ size_t chain_split_lds_bytes(int lam, int C, int d, bool f32) {
   return chain_ns::chain_layout(lam, C, d / 32, f32, 1, true).total;
 }
 
-template <class DT, int HD, int SPW>
+template <class DT, int HD, int SPW, bool XS = false>
 static hipError_t launch_chain_t(const ChainArgs& a, int U, hipStream_t st) {
-  const bool xs = SPW == HD / 32 && a.xs && a.k > 1;
   const size_t lds =
-      chain_ns::chain_layout(a.vr.lam, a.C, SPW, DT::kSplit, chain_ns::kFoldBufs<HD, SPW>, xs).total;
-  const void* fn = (const void*)chain_kernel<DT, HD, SPW>;
+      chain_ns::chain_layout(a.vr.lam, a.C, SPW, DT::kSplit, chain_ns::kFoldBufs<HD, SPW>, XS).total;
+  const void* fn = (const void*)chain_kernel<DT, HD, SPW, XS>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((chain_kernel<DT, HD, SPW>), dim3(U * a.k), dim3(chain_ns::kThreads), lds, st, a);
+  hipLaunchKernelGGL((chain_kernel<DT, HD, SPW, XS>), dim3(U * a.k), dim3(chain_ns::kThreads), lds, st, a);
   return hipGetLastError();
 }
 
@@ -44,7 +43,7 @@ static hipError_t launch_chain_t(const ChainArgs& a, int U, hipStream_t st) {
 template <class DT, int HD>
 static hipError_t launch_chain_k(const ChainArgs& a, int U, hipStream_t st) {
   constexpr int NSLAB = HD / 32;
-  if (a.xs && a.k > 1) return launch_chain_t<DT, HD, NSLAB>(a, U, st);
+  if (a.xs && a.k > 1) return launch_chain_t<DT, HD, NSLAB, true>(a, U, st);
   if (a.k >= NSLAB) return launch_chain_t<DT, HD, 1>(a, U, st);   // k = NSLAB * CS
   if (a.k == 1) return launch_chain_t<DT, HD, NSLAB>(a, U, st);
   if constexpr (NSLAB == 4) {

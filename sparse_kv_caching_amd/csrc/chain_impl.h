@@ -145,8 +145,10 @@ __device__ __forceinline__ uint16_t half_of(u32x4 x, int e) {
 
 }  // namespace chain_ns
 
-// The chain of one workgroup (block index bid of the chain's grid).
-template <class DT, int HD, int SPW>
+// The chain of one workgroup (block index bid of the chain's grid).  XS: the
+// candidate split (the all-slab instance with k > 1), compiled separately so
+// that the other instances keep their registers.
+template <class DT, int HD, int SPW, bool XS = false>
 __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
   using namespace chain_ns;
   using T = typename DT::T;
@@ -158,7 +160,8 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
   // (the host launches SPW < NSLAB exactly when k > 1) or the candidates
   // (the candidate split: the all-slab instance with k > 1)
   constexpr bool kExch = SPW < NSLAB;
-  const bool xs = SPW == NSLAB && a.xs != 0 && a.k > 1;
+  static_assert(!XS || SPW == HD / 32, "the candidate split holds all slabs");
+  constexpr bool xs = XS;
   const bool xch = kExch || xs;
   const VirtRows vr = a.vr;
   const int lam = vr.lam, eta = vr.eta, k = a.k, CS = a.k / NG;

@@ -29,11 +29,11 @@ struct OverlapArgs {
 static_assert(chain_ns::kThreads == attn_ns::kThreads, "one block size for both roles");
 }  // namespace
 
-template <class DT, int HD, int SPW>
+template <class DT, int HD, int SPW, bool XS>
 __global__ __launch_bounds__(chain_ns::kThreads) void overlap_kernel(OverlapArgs o) {
   const int b = blockIdx.x;
   if (b < o.nchain) {
-    chain_body<DT, HD, SPW>(o.c, b);
+    chain_body<DT, HD, SPW, XS>(o.c, b);
     return;
   }
   const int w = b - o.nchain;
@@ -41,18 +41,17 @@ __global__ __launch_bounds__(chain_ns::kThreads) void overlap_kernel(OverlapArgs
   attn_body<DT, HD>(o.a, u, rest / o.nptile, rest % o.nptile);
 }
 
-template <class DT, int HD, int SPW>
+template <class DT, int HD, int SPW, bool XS = false>
 static hipError_t launch_overlap_t(const OverlapArgs& o, hipStream_t st) {
-  const bool xs = SPW == HD / 32 && o.c.xs && o.c.k > 1;
   const size_t lc =
-      chain_ns::chain_layout(o.c.vr.lam, o.c.C, SPW, DT::kSplit, chain_ns::kFoldBufs<HD, SPW>, xs).total;
+      chain_ns::chain_layout(o.c.vr.lam, o.c.C, SPW, DT::kSplit, chain_ns::kFoldBufs<HD, SPW>, XS).total;
   const size_t la = attn_ns::attn_layout(HD, o.a.vr.lam, o.a.vr.eta, o.a.C, DT::kSplit).total;
   const size_t lds = lc > la ? lc : la;
-  const void* fn = (const void*)overlap_kernel<DT, HD, SPW>;
+  const void* fn = (const void*)overlap_kernel<DT, HD, SPW, XS>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int nread = o.U * o.nptile * o.a.nch_launch;
-  hipLaunchKernelGGL((overlap_kernel<DT, HD, SPW>), dim3(o.nchain + nread), dim3(chain_ns::kThreads),
+  hipLaunchKernelGGL((overlap_kernel<DT, HD, SPW, XS>), dim3(o.nchain + nread), dim3(chain_ns::kThreads),
                      lds, st, o);
   return hipGetLastError();
 }
@@ -60,7 +59,7 @@ static hipError_t launch_overlap_t(const OverlapArgs& o, hipStream_t st) {
 template <class DT, int HD>
 static hipError_t launch_overlap_k(const OverlapArgs& o, hipStream_t st) {
   constexpr int NSLAB = HD / 32;
-  if (o.c.xs && o.c.k > 1) return launch_overlap_t<DT, HD, NSLAB>(o, st);
+  if (o.c.xs && o.c.k > 1) return launch_overlap_t<DT, HD, NSLAB, true>(o, st);
   if (o.c.k >= NSLAB) return launch_overlap_t<DT, HD, 1>(o, st);
   if (o.c.k == 1) return launch_overlap_t<DT, HD, NSLAB>(o, st);
   if constexpr (NSLAB == 4) {
