@@ -632,16 +632,13 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   }
   const int k_ovl = overlap_workgroups(st, T, C, nch);
   ca.k = k_ovl ? k_ovl : chain_workgroups(U, st->ncu, d, lam, C);
-  // k > 1: the candidate split where its LDS layout fits and (automatic
-  // choice) a workgroup scores >= 8 tiles of 32 candidates per step, so that
-  // staging the tiles once for all slabs pays for holding all of H (folds
-  // over all columns, a larger H^T rebuild).  Measured on MI355X, chain
-  // step at 2 workgroups per unit with 20 tiles: 34.8 -> 31.2 us; at 16
-  // with 72 tiles: 27.0 -> 27.3 us
-  ca.xs = ca.k > 1 && st->split != 0 && chain_split_lds_bytes(lam, C, d, st->f32) + 64 <= kMaxLds &&
-                  (st->split == 1 || (lam + C + 31) / 32 >= 8 * ca.k)
-              ? 1
-              : 0;
+  // k > 1: the candidate split where its LDS layout fits (staging the tiles
+  // once for all slabs pays for holding all of H: folds over all columns, a
+  // larger H^T rebuild).  Measured on MI355X, prefill call in the one-launch
+  // schedule, column split -> candidate split: T = 32768 3.30 -> 3.22 ms;
+  // 8 sequences of T = 8192 2.95 -> 2.81 ms; Llama-shaped T = 4096 0.684 ->
+  // 0.685 ms
+  ca.xs = ca.k > 1 && st->split != 0 && chain_split_lds_bytes(lam, C, d, st->f32) + 64 <= kMaxLds ? 1 : 0;
   ca.xcd_group = (U % 8 == 0) ? 1 : 0;
   ca.xbuf = (uint64_t*)(base + L.xbuf);
   ca.err = st->dev_err;
