@@ -358,8 +358,10 @@ int lola_state_positions(const lola_state* st, int64_t* out);
  *                             the work: 0 = column slabs of H times groups of
  *                             candidates; 1 = groups of candidates only, every
  *                             workgroup holding all of H (when its LDS layout
- *                             fits; otherwise as 0); -1 (default) = 1.  Both
- *                             give bitwise the same results.
+ *                             fits; otherwise as 0); -1 (default) = 1 when a
+ *                             workgroup scores >= 2 tiles of 32 candidates
+ *                             per step, else 0.  Both give bitwise the same
+ *                             results.
  * The first two exist to exercise the failure path: the chain sets its device
  * fault flag and ends, the later kernels of the call return untouched, and
  * lola_state_check() reports LOLA_ERR_STATE.

@@ -632,13 +632,17 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   }
   const int k_ovl = overlap_workgroups(st, T, C, nch);
   ca.k = k_ovl ? k_ovl : chain_workgroups(U, st->ncu, d, lam, C);
-  // k > 1: the candidate split where its LDS layout fits (staging the tiles
-  // once for all slabs pays for holding all of H: folds over all columns, a
-  // larger H^T rebuild).  Measured on MI355X, prefill call in the one-launch
-  // schedule, column split -> candidate split: T = 32768 3.30 -> 3.22 ms;
-  // 8 sequences of T = 8192 2.95 -> 2.81 ms; Llama-shaped T = 4096 0.684 ->
-  // 0.685 ms
-  ca.xs = ca.k > 1 && st->split != 0 && chain_split_lds_bytes(lam, C, d, st->f32) + 64 <= kMaxLds ? 1 : 0;
+  // k > 1: the candidate split where its LDS layout fits and (automatic
+  // choice) a workgroup scores >= 2 tiles of 32 candidates per step: staging
+  // the tiles once for all slabs then pays for holding all of H (folds over
+  // all columns, a larger H^T rebuild).  Measured on MI355X, prefill call in
+  // the one-launch schedule, column split -> candidate split: T = 32768
+  // (4.5 tiles per workgroup) 3.30 -> 3.13 ms; 8 sequences of T = 8192 (10)
+  // 2.95 -> 2.55 ms; Llama-shaped T = 4096 (0.6) 0.674 -> 0.705 ms
+  ca.xs = ca.k > 1 && st->split != 0 && chain_split_lds_bytes(lam, C, d, st->f32) + 64 <= kMaxLds &&
+                  (st->split == 1 || (lam + C + 31) / 32 >= 2 * ca.k)
+              ? 1
+              : 0;
   ca.xcd_group = (U % 8 == 0) ? 1 : 0;
   ca.xbuf = (uint64_t*)(base + L.xbuf);
   ca.err = st->dev_err;

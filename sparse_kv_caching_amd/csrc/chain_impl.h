@@ -791,7 +791,7 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
     constexpr int PER = 16 / (int)sizeof(T);             // V elements per 16-byte piece
     constexpr int VPR = 32 * SPW / PER;                  // V pieces of an own row
     constexpr int VL = (8 * VPR + 63) / 64;              // V pieces per lane
-    constexpr int GB = SPW == 1 ? 4 : 2;                 // blocks gathered together
+    constexpr int GB = SPW == 1 || (XS && !DT::kSplit) ? 4 : 2;   // blocks gathered together
     struct Gather {
       u32x4 x[4];
       u32x4 v[VL];
