@@ -362,12 +362,22 @@ int lola_state_positions(const lola_state* st, int64_t* out);
  *                             workgroup scores >= 2 tiles of 32 candidates
  *                             per step, else 0.  Both give bitwise the same
  *                             results.
+ *   LOLA_DEBUG_CHAIN_WORKGROUPS  the chain's workgroups per unit, k (1 .. 64;
+ *                             0, the default: automatic).  Taken where the
+ *                             whole chain grid fits the device (in the
+ *                             one-launch schedule: U * k < the compute units)
+ *                             and k suits the split (column split: k = 1, 2 or
+ *                             a multiple of d / 32; candidate split: k = 2 or
+ *                             k >= d / 32); otherwise the automatic count, or
+ *                             LOLA_ERR_INVALID_ARG from the prefill call when
+ *                             the one-launch schedule has taken it.  Results
+ *                             are bitwise the same for every k.
  * The first two exist to exercise the failure path: the chain sets its device
  * fault flag and ends, the later kernels of the call return untouched, and
  * lola_state_check() reports LOLA_ERR_STATE.
  * Errors: INVALID_ARG (NULL state, unknown key, value out of range). */
 enum { LOLA_DEBUG_SPIN_LIMIT = 0, LOLA_DEBUG_CHAIN_FAIL_AT = 1, LOLA_DEBUG_OVERLAP = 2,
-       LOLA_DEBUG_CHAIN_SPLIT = 3 };
+       LOLA_DEBUG_CHAIN_SPLIT = 3, LOLA_DEBUG_CHAIN_WORKGROUPS = 4 };
 int lola_debug_set(lola_state* st, int key, long long value);
 
 /* Text of a status code, and the last error detail of the calling thread. */

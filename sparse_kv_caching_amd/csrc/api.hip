@@ -54,6 +54,7 @@ struct lola_state {
   int fail_at;              // debug: exchange step at which the chain gives up (-1: never)
   int overlap;              // prefill schedule: -1 auto, 0 sequential, 1 concurrent read
   int split;                // chain work split (k > 1): -1 auto, 0 slabs x candidates, 1 candidates
+  int force_k;              // chain workgroups per unit (0: automatic)
   int ncu;                  // compute units of the device
   void* own_ws;
   size_t own_ws_bytes;
@@ -168,38 +169,46 @@ WsLayout ws_layout(const lola_state* st, int T, int C) {
 }
 
 // Workgroups per unit for the chain: the whole grid must be resident (one
-// workgroup per compute unit).  First split the columns into slabs (k = d / 32),
-// then split the candidate tiles into CS groups until a workgroup scores at
-// most two tiles per step (or the device is full): measured on the
-// Llama-shaped layer (8 units, 10 tiles per step), 8 / 16 / 32 workgroups
-// per unit take 633 / 573 / 552 us per call.
+// workgroup per compute unit, ncu of them available).  k = (d / 32) x CS:
+// the columns' slabs times CS candidate groups, the fewest groups in which
+// a workgroup scores at most two tiles of 32 candidates per step, as many
+// as fit.  Measured on the Llama-shaped layer (8 units, 10 tiles per step),
+// 8 / 16 / 32 workgroups per unit took 633 / 573 / 552 us per call.
 int chain_workgroups(int U, int ncu, int d, int lam, int C) {
   const int nslab = d / 32;
   const long long cap = ncu / std::max(U, 1);
   if (cap < 2) return 1;
   if (cap < nslab) return nslab >= 4 && cap >= 2 ? 2 : 1;
   const int tiles = (lam + C + 31) / 32;
-  int cs = 1;
-  while ((tiles + cs - 1) / cs > 2 && nslab * cs * 2 <= cap && cs < 32) cs *= 2;
+  const int cs = (int)std::min<long long>({cap / nslab, std::max(1, (tiles + 1) / 2), 32LL});
   return nslab * cs;
 }
 
 // Chain workgroups per unit when the read of finished chunks runs beside
-// the chain in one launch (the chain on half of the compute units), or 0
-// when the call runs the two one after the other.  The concurrent schedule
-// hides the read behind a chain that runs on fewer workgroups; the read is
-// latency-bound and loses much less than half of its speed on half of the
-// device.  Measured on MI355X (prefill call, ms, sequential -> concurrent):
-// T = 32768 single sequence 5.11 -> 3.72; 8 sequences of T = 8192 3.67 ->
-// 3.13; Llama-shaped T = 4096 0.679 -> 0.671.  The automatic choice takes it
-// whenever the chain fits half of the device and the call has >= 4 chunks.
+// the chain in one launch, or 0 when the call runs the two one after the
+// other.  The concurrent schedule hides the read behind a chain that runs on
+// fewer workgroups; the read is latency-bound and loses much less than half
+// of its speed on half of the device.  Measured on MI355X (prefill call,
+// ms, sequential -> concurrent): T = 32768 single sequence 5.11 -> 3.72; 8
+// sequences of T = 8192 3.67 -> 3.13; Llama-shaped T = 4096 0.679 -> 0.671.
+// The read keeps max(ncu / 8, R / 4) compute units, at most half, with R its
+// 64-key tiles per chunk over all units (a compute unit reads about four
+// such tiles in the time of a short chain step): the long and batched
+// workloads' reads take half of the device, the Llama-shaped one's 32 units
+// (its chain then runs on 20 workgroups per unit instead of 16: 0.678 ->
+// 0.653 ms).  The automatic choice takes the schedule whenever the chain
+// fits and the call has >= 4 chunks.
 int overlap_workgroups(const lola_state* st, int T, int C, int nch) {
   (void)T;
   if (st->overlap == 0 || nch < 2) return 0;
-  const int U = st->U, lam = st->cfg.cache;
-  const int half = st->ncu / 2;
-  const int k = chain_workgroups(U, half, st->d, lam, C);
-  if ((long long)U * k > half) return 0;
+  const int U = st->U, lam = st->cfg.cache, eta = st->cfg.window;
+  const int g = st->cfg.q_heads / st->cfg.kv_heads;
+  const long long nptile = (C + attn_positions_per_block(C, g) - 1) / attn_positions_per_block(C, g);
+  const long long R = (long long)U * nptile * ((lam + eta + C + 63) / 64);
+  const int keep = (int)std::min<long long>(st->ncu / 2, std::max<long long>(st->ncu / 8, R / 4));
+  const int chain_cus = st->ncu - keep;
+  const int k = st->force_k > 0 ? st->force_k : chain_workgroups(U, chain_cus, st->d, lam, C);
+  if ((long long)U * k > (st->force_k > 0 ? st->ncu - 1 : chain_cus)) return 0;
   if (st->overlap == 1) return k;
   return nch >= 4 ? k : 0;
 }
@@ -386,6 +395,7 @@ int lola_state_init(const lola_config* cfg, const void* W, void* stream, lola_st
   st->fail_at = -1;
   st->overlap = -1;
   st->split = -1;
+  st->force_k = 0;
   st->U = c.batch * c.kv_heads;
   st->g = g;
   st->d = c.head_dim;
@@ -631,7 +641,9 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
     if (e != hipSuccess) return hip_fail(st, e, "debug reset");
   }
   const int k_ovl = overlap_workgroups(st, T, C, nch);
-  ca.k = k_ovl ? k_ovl : chain_workgroups(U, st->ncu, d, lam, C);
+  ca.k = k_ovl                                                  ? k_ovl
+         : st->force_k > 0 && (long long)U * st->force_k <= st->ncu ? st->force_k
+                                                                 : chain_workgroups(U, st->ncu, d, lam, C);
   // k > 1: the candidate split where its LDS layout fits and (automatic
   // choice) a workgroup scores >= 2 tiles of 32 candidates per step: staging
   // the tiles once for all slabs then pays for holding all of H (folds over
@@ -639,10 +651,26 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   // the one-launch schedule, column split -> candidate split: T = 32768
   // (4.5 tiles per workgroup) 3.30 -> 3.13 ms; 8 sequences of T = 8192 (10)
   // 2.95 -> 2.55 ms; Llama-shaped T = 4096 (0.6) 0.674 -> 0.705 ms
-  ca.xs = ca.k > 1 && st->split != 0 && chain_split_lds_bytes(lam, C, d, st->f32) + 64 <= kMaxLds &&
-                  (st->split == 1 || (lam + C + 31) / 32 >= 2 * ca.k)
-              ? 1
-              : 0;
+  auto pick_split = [&]() {
+    ca.xs = ca.k > 1 && st->split != 0 && chain_split_lds_bytes(lam, C, d, st->f32) + 64 <= kMaxLds &&
+                    (st->split == 1 || (lam + C + 31) / 32 >= 2 * ca.k)
+                ? 1
+                : 0;
+  };
+  pick_split();
+  {
+    // a forced workgroup count the split cannot use: the automatic one (the
+    // snapshot's writers need k == 2 or k >= d / 32 with the candidate split,
+    // k a multiple of d / 32 (or 1, 2) with the column split)
+    const int nslab = d / 32, k = ca.k;
+    const bool ok = ca.xs ? (k == 2 || k >= nslab) : (k == 1 || (k == 2 && nslab == 4) || k % nslab == 0);
+    if (!ok && !k_ovl) {
+      ca.k = chain_workgroups(U, st->ncu, d, lam, C);
+      pick_split();
+    } else if (!ok) {
+      return fail(LOLA_ERR_INVALID_ARG, "chain workgroups per unit %d do not suit the work split", k);
+    }
+  }
   ca.xcd_group = (U % 8 == 0) ? 1 : 0;
   ca.xbuf = (uint64_t*)(base + L.xbuf);
   ca.err = st->dev_err;
@@ -674,7 +702,7 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   // writer workgroups per unit: one per slab group (d / 32 / SPW), or
   // min(k, d / 32) with the candidate split (the same counts)
   const int nslab = d / 32;
-  aa.ready_need = ca.k >= nslab ? nslab : (ca.k == 1 ? 1 : nslab / 2);
+  aa.ready_need = ca.xs ? std::min(ca.k, nslab) : (ca.k >= nslab ? nslab : (ca.k == 1 ? 1 : nslab / 2));
   aa.spin_limit = st->spin_limit;
 
   if (k_ovl) {
@@ -835,6 +863,11 @@ int lola_debug_set(lola_state* st, int key, long long value) {
       if (value < -1 || value > 1)
         return fail(LOLA_ERR_INVALID_ARG, "overlap %lld not in {-1, 0, 1}", value);
       st->overlap = (int)value;
+      return LOLA_OK;
+    case LOLA_DEBUG_CHAIN_WORKGROUPS:
+      if (value < 0 || value > 64)
+        return fail(LOLA_ERR_INVALID_ARG, "chain workgroups %lld not in [0, 64]", value);
+      st->force_k = (int)value;
       return LOLA_OK;
     case LOLA_DEBUG_CHAIN_SPLIT:
       if (value < -1 || value > 1)

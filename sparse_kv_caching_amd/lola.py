@@ -29,6 +29,7 @@ KERNELS = ("phi", "chain", "attn", "finalize", "decode", "overlap")
 READ_STATE, READ_CACHE, READ_WINDOW, READ_ALL = 1, 2, 4, 7   # lola_set_read_branches bits
 READ_BEFORE_UPDATE, READ_AFTER_UPDATE = 0, 1                 # lola_set_read_order
 DEBUG_SPIN_LIMIT, DEBUG_CHAIN_FAIL_AT, DEBUG_OVERLAP, DEBUG_CHAIN_SPLIT = 0, 1, 2, 3  # lola_debug_set keys
+DEBUG_CHAIN_WORKGROUPS = 4
 SCORE_SRE, SCORE_KERNEL_SQ, SCORE_KERNEL_ABS, SCORE_KERNEL_RATIO, SCORE_LOCAL_ATTN = range(5)
 
 EXPORTED = [
@@ -192,7 +193,8 @@ class LolaLayer:
         which the chain gives up; -1 = never), DEBUG_OVERLAP (prefill
         schedule: -1 auto, 0 chain then read, 1 read beside the chain) or
         DEBUG_CHAIN_SPLIT (the chain's workgroups: -1 auto, 0 column slabs x
-        candidate groups, 1 candidate groups holding all of H)."""
+        candidate groups, 1 candidate groups holding all of H) or
+        DEBUG_CHAIN_WORKGROUPS (the chain's workgroups per unit; 0 auto)."""
         _check(self.lib.lola_debug_set(self._st, int(key), int(value)), "lola_debug_set")
 
     def profile(self, enable: bool):

@@ -16,7 +16,8 @@ import numpy as np
 import pytest
 import torch
 
-from sparse_kv_caching_amd.lola import DEBUG_CHAIN_SPLIT, DEBUG_OVERLAP, DEBUG_SPIN_LIMIT, LolaError
+from sparse_kv_caching_amd.lola import (DEBUG_CHAIN_SPLIT, DEBUG_CHAIN_WORKGROUPS, DEBUG_OVERLAP,
+                                        DEBUG_SPIN_LIMIT, LolaError)
 from sparse_kv_caching_amd.workloads import WORKLOADS, make_inputs
 
 from lola_harness import dev, make_layer
@@ -24,11 +25,12 @@ from lola_harness import dev, make_layer
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, overlap, calls=1, split=-1):
+def _run(wl, overlap, calls=1, split=-1, k=0):
     inp = make_inputs(wl)
     layer = make_layer(wl, inp.W)
     layer.debug_set(DEBUG_OVERLAP, overlap)
     layer.debug_set(DEBUG_CHAIN_SPLIT, split)
+    layer.debug_set(DEBUG_CHAIN_WORKGROUPS, k)
     q, k, v = dev(wl, inp.q), dev(wl, inp.k), dev(wl, inp.v)
     outs, recs = [], []
     T = wl.T
@@ -44,9 +46,10 @@ def _run(wl, overlap, calls=1, split=-1):
     return outs, recs, st
 
 
-def _same(wl, calls=1, a_args=(0, -1), b_args=(1, -1)):
-    a = _run(wl, a_args[0], calls, a_args[1])
-    b = _run(wl, b_args[0], calls, b_args[1])
+def _same(wl, calls=1, a_args=(0, -1, 0), b_args=(1, -1, 0)):
+    """a_args / b_args: (schedule, work split, workgroups per unit; 0 auto)."""
+    a = _run(wl, a_args[0], calls, a_args[1], a_args[2])
+    b = _run(wl, b_args[0], calls, b_args[1], b_args[2])
     for ya, yb in zip(a[0], b[0]):
         assert torch.equal(ya, yb), "outputs differ between the schedules"
     for (spa, cka), (spb, ckb) in zip(a[1], b[1]):
@@ -66,14 +69,16 @@ def test_overlap_slab_per_workgroup():
 
 def test_overlap_two_slabs():
     """48 units: four workgroups per unit (one slab each) in the sequential
-    schedule, two (two slabs each) on half of the device."""
-    _same(WORKLOADS["llama8b_4k"].scaled(B=6, Hq=16, Hkv=8, T=256, eta=64, lam=64, C=32))
+    schedule, two (two slabs each, column split) in the one-launch one."""
+    _same(WORKLOADS["llama8b_4k"].scaled(B=6, Hq=16, Hkv=8, T=256, eta=64, lam=64, C=32),
+          b_args=(1, 0, 2))
 
 
 def test_overlap_one_workgroup_per_unit():
     """80 units of head dim 64: two workgroups per unit (one slab each)
-    sequentially, one (no exchange) on half of the device."""
-    _same(WORKLOADS["llama8b_4k"].scaled(B=10, Hq=8, Hkv=8, d=64, T=192, eta=32, lam=32, C=32))
+    sequentially, one (no exchange) in the one-launch schedule."""
+    _same(WORKLOADS["llama8b_4k"].scaled(B=10, Hq=8, Hkv=8, d=64, T=192, eta=32, lam=32, C=32),
+          b_args=(1, -1, 1))
 
 
 def test_overlap_fp32_and_gqa():
@@ -100,7 +105,17 @@ SPLIT_SHAPES = {
 @pytest.mark.parametrize("shape", list(SPLIT_SHAPES))
 @pytest.mark.parametrize("overlap", [0, 1])
 def test_chain_split_same(shape, overlap):
-    _same(SPLIT_SHAPES[shape], a_args=(overlap, 0), b_args=(overlap, 1))
+    _same(SPLIT_SHAPES[shape], a_args=(overlap, 0, 0), b_args=(overlap, 1, 0))
+
+
+def test_chain_workgroup_counts_same():
+    """Forced workgroups per unit (candidate groups not a power of two: 12 =
+    4 slabs x 3 groups with the column split; 6 and 2 with the candidate
+    split), bitwise the same as the automatic count."""
+    wl = SPLIT_SHAPES["k16"]
+    _same(wl, a_args=(0, -1, 0), b_args=(0, 0, 12))
+    _same(wl, a_args=(1, -1, 0), b_args=(1, 1, 6))
+    _same(wl, a_args=(1, -1, 0), b_args=(1, 1, 2))
 
 
 def test_overlap_read_gives_up():
