@@ -367,8 +367,8 @@ int lola_state_positions(const lola_state* st, int64_t* out);
  *                             whole chain grid fits the device (in the
  *                             one-launch schedule: U * k < the compute units)
  *                             and k suits the split (column split: k = 1, 2 or
- *                             a multiple of d / 32; candidate split: k = 2 or
- *                             k >= d / 32); otherwise the automatic count, or
+ *                             a multiple of d / 32; candidate split: any k >
+ *                             1); otherwise the automatic count, or
  *                             LOLA_ERR_INVALID_ARG from the prefill call when
  *                             the one-launch schedule has taken it.  Results
  *                             are bitwise the same for every k.

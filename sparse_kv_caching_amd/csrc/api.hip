@@ -660,10 +660,10 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   pick_split();
   {
     // a forced workgroup count the split cannot use: the automatic one (the
-    // snapshot's writers need k == 2 or k >= d / 32 with the candidate split,
-    // k a multiple of d / 32 (or 1, 2) with the column split)
+    // column split needs k = 1, 2 or a multiple of d / 32; the candidate
+    // split takes any k > 1)
     const int nslab = d / 32, k = ca.k;
-    const bool ok = ca.xs ? (k == 2 || k >= nslab) : (k == 1 || (k == 2 && nslab == 4) || k % nslab == 0);
+    const bool ok = ca.xs ? k > 1 : (k == 1 || (k == 2 && nslab == 4) || k % nslab == 0);
     if (!ok && !k_ovl) {
       ca.k = chain_workgroups(U, st->ncu, d, lam, C);
       pick_split();
@@ -702,7 +702,8 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   // writer workgroups per unit: one per slab group (d / 32 / SPW), or
   // min(k, d / 32) with the candidate split (the same counts)
   const int nslab = d / 32;
-  aa.ready_need = ca.xs ? std::min(ca.k, nslab) : (ca.k >= nslab ? nslab : (ca.k == 1 ? 1 : nslab / 2));
+  aa.ready_need = ca.xs ? (ca.k >= nslab ? nslab : (nslab % ca.k == 0 ? ca.k : 1))
+                        : (ca.k >= nslab ? nslab : (ca.k == 1 ? 1 : nslab / 2));
   aa.spin_limit = st->spin_limit;
 
   if (k_ovl) {

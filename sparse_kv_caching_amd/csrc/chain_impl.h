@@ -184,9 +184,9 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
   const int grp = rank % NG, ch = rank / NG;      // slab group, candidate group
   const int col0 = 32 * SPW * grp;                // first H column of this workgroup
   // snapshot writers: candidate group 0 of each slab group (its columns), or
-  // with the candidate split the first min(k, NSLAB) workgroups, a share of
-  // the columns each
-  const int nw = xs ? min(CS, NSLAB) : 1;
+  // with the candidate split the first nw workgroups, an equal share of the
+  // columns each (nw = NSLAB, or k where k divides NSLAB, else 1)
+  const int nw = xs ? (CS >= NSLAB ? NSLAB : (NSLAB % CS == 0 ? CS : 1)) : 1;
   const bool writer = ch < nw;
   const int wr0 = xs ? 32 * (NSLAB / nw) * ch : col0;   // first column written
   const int wrn = xs ? 32 * (NSLAB / nw) : 32 * SPW;    // columns written

@@ -110,11 +110,12 @@ def test_chain_split_same(shape, overlap):
 
 def test_chain_workgroup_counts_same():
     """Forced workgroups per unit (candidate groups not a power of two: 12 =
-    4 slabs x 3 groups with the column split; 6 and 2 with the candidate
-    split), bitwise the same as the automatic count."""
+    4 slabs x 3 groups with the column split; 6, 3 (one snapshot writer) and
+    2 with the candidate split), bitwise the same as the automatic count."""
     wl = SPLIT_SHAPES["k16"]
     _same(wl, a_args=(0, -1, 0), b_args=(0, 0, 12))
     _same(wl, a_args=(1, -1, 0), b_args=(1, 1, 6))
+    _same(wl, a_args=(1, -1, 0), b_args=(1, 1, 3))
     _same(wl, a_args=(1, -1, 0), b_args=(1, 1, 2))
 
 
