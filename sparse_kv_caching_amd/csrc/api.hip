@@ -170,17 +170,18 @@ WsLayout ws_layout(const lola_state* st, int T, int C) {
 
 // Workgroups per unit for the chain: the whole grid must be resident (one
 // workgroup per compute unit, ncu of them available).  k = (d / 32) x CS:
-// the columns' slabs times CS candidate groups, the fewest groups in which
-// a workgroup scores at most two tiles of 32 candidates per step, as many
-// as fit.  Measured on the Llama-shaped layer (8 units, 10 tiles per step),
-// 8 / 16 / 32 workgroups per unit took 633 / 573 / 552 us per call.
+// the columns' slabs times CS candidate groups, as many groups as fit, up to
+// one per tile of 32 candidates.  Measured on the Llama-shaped layer (8
+// units, 10 tiles per step), 8 / 16 / 32 workgroups per unit took 633 / 573
+// / 552 us per call (chain then read); in the one-launch schedule 16 / 20 /
+// 28 took 0.678 / 0.653 / 0.636 ms.
 int chain_workgroups(int U, int ncu, int d, int lam, int C) {
   const int nslab = d / 32;
   const long long cap = ncu / std::max(U, 1);
   if (cap < 2) return 1;
   if (cap < nslab) return nslab >= 4 && cap >= 2 ? 2 : 1;
   const int tiles = (lam + C + 31) / 32;
-  const int cs = (int)std::min<long long>({cap / nslab, std::max(1, (tiles + 1) / 2), 32LL});
+  const int cs = (int)std::min<long long>({cap / nslab, std::max(1, tiles), 32LL});
   return nslab * cs;
 }
 
@@ -195,8 +196,7 @@ int chain_workgroups(int U, int ncu, int d, int lam, int C) {
 // 64-key tiles per chunk over all units (a compute unit reads about four
 // such tiles in the time of a short chain step): the long and batched
 // workloads' reads take half of the device, the Llama-shaped one's 32 units
-// (its chain then runs on 20 workgroups per unit instead of 16: 0.678 ->
-// 0.653 ms).  The automatic choice takes the schedule whenever the chain
+// (its chain then runs on 28 workgroups per unit instead of 16).  The automatic choice takes the schedule whenever the chain
 // fits and the call has >= 4 chunks.
 int overlap_workgroups(const lola_state* st, int T, int C, int nch) {
   (void)T;

@@ -62,8 +62,8 @@ def _same(wl, calls=1, a_args=(0, -1, 0), b_args=(1, -1, 0)):
 
 
 def test_overlap_slab_per_workgroup():
-    """Two units, 16 workgroups each (one slab, four candidate groups) in
-    both schedules."""
+    """Two units, 32 workgroups each (one slab, eight candidate groups of one
+    tile) in both schedules."""
     _same(WORKLOADS["llama8b_4k"].scaled(B=1, Hq=8, Hkv=2, T=1024, eta=128, lam=192, C=64))
 
 
@@ -95,7 +95,7 @@ def test_overlap_second_call():
 # meet in LDS and whose phi tiles are staged there) give bitwise the same
 # results, in either schedule.
 SPLIT_SHAPES = {
-    "k16": WORKLOADS["llama8b_4k"].scaled(B=1, Hq=8, Hkv=2, T=1024, eta=128, lam=192, C=64),
+    "two_units": WORKLOADS["llama8b_4k"].scaled(B=1, Hq=8, Hkv=2, T=1024, eta=128, lam=192, C=64),
     "k2": WORKLOADS["llama8b_4k"].scaled(B=6, Hq=16, Hkv=8, T=256, eta=64, lam=64, C=32),
     "d64": WORKLOADS["llama8b_4k"].scaled(B=2, Hq=8, Hkv=4, d=64, T=640, eta=64, lam=96, C=64),
     "fp32": WORKLOADS["tiny_fp32"].scaled(B=2, Hq=4, Hkv=2, d=128, T=300, eta=32, lam=48, C=32),
@@ -112,7 +112,7 @@ def test_chain_workgroup_counts_same():
     """Forced workgroups per unit (candidate groups not a power of two: 12 =
     4 slabs x 3 groups with the column split; 6, 3 (one snapshot writer) and
     2 with the candidate split), bitwise the same as the automatic count."""
-    wl = SPLIT_SHAPES["k16"]
+    wl = SPLIT_SHAPES["two_units"]
     _same(wl, a_args=(0, -1, 0), b_args=(0, 0, 12))
     _same(wl, a_args=(1, -1, 0), b_args=(1, 1, 6))
     _same(wl, a_args=(1, -1, 0), b_args=(1, 1, 3))
