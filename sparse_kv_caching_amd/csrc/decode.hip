@@ -17,9 +17,9 @@
 //   * One workgroup of 4 waves per unit.  For bf16 state it needs at most
 //     80 KB of LDS and 256 registers per lane, so two workgroups share a CU.
 //   * The keys a query sees (cache 0..gs-1, window oldest first; the new pair
-//     apart) come in chunks of 128, 32 per wave, loaded straight into the
-//     registers of the wave's MFMA operands; the wave also loads its keys' V
-//     rows.  W^T, the queries, s and the leaving and new pairs go to LDS.
+//     apart) come in chunks of 128, 32 per wave (wave w: keys 16 w .. and
+//     64 + 16 w ..), loaded straight into the registers of the wave's MFMA
+//     operands; the wave also loads its keys' V rows.  W^T, the queries, s and the leaving and new pairs go to LDS.
 //     Only when those reads have arrived does the wave issue its slab of H,
 //     so that across the GPU the keys and values come back first and the
 //     logits and phi work overlaps the stream of H.
@@ -220,12 +220,37 @@ __device__ __forceinline__ void phi16(const f32x4 (&U)[4], float (&ph)[2][4][4])
 }
 
 // The wave's slab of H in the lane's operand positions: lane (n, q) holds
-// H[sigma(kb, q, j)][16 mb + n].  For bf16 state it is kept as an exact
-// three-way bf16 split (hi + mid + lo equals the fp32 value), split once: the
-// products use hi and mid (the 16-bit pair of the three-pass scheme), the
-// fold rebuilds the fp32 value.  fp32 state keeps fp32 and splits on use.
-template <class DT> struct HSlab;
-template <> struct HSlab<BF16> {
+// H[sigma(kb, q, j)][16 mb + n].  For bf16 state the products use the 16-bit
+// pair of the three-pass scheme, hi = bf16(x) and mid = bf16(x - hi), split
+// once; the fold needs the fp32 values, which the one-chunk instance keeps
+// as they are (fewer instructions) and the chunked one, short of registers,
+// as a third bf16 part lo = bf16(x - hi - mid) (hi + mid + lo is exactly x).
+// fp32 state keeps fp32 and splits on use.
+template <class DT, bool KEEP> struct HSlab;
+template <> struct HSlab<BF16, true> {
+  float v[2][4][8];
+  u32x4 hi[2][4], mid[2][4];
+  __device__ __forceinline__ void set(int mb, int kb, const float (&x)[8]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a0 = x[2 * j], a1 = x[2 * j + 1];
+      const uint32_t h = cvt_pk_bf16(a0, a1);
+      hi[mb][kb][j] = h;
+      mid[mb][kb][j] = cvt_pk_bf16(a0 - __uint_as_float(h << 16), a1 - __uint_as_float(h & 0xFFFF0000u));
+      v[mb][kb][2 * j] = a0;
+      v[mb][kb][2 * j + 1] = a1;
+    }
+  }
+  __device__ __forceinline__ void ops(int mb, int kb, u32x4& Ah, u32x4& Al) const {
+    Ah = hi[mb][kb];
+    Al = mid[mb][kb];
+  }
+  __device__ __forceinline__ void get(int mb, int kb, float (&x)[8]) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = v[mb][kb][j];
+  }
+};
+template <> struct HSlab<BF16, false> {
   u32x4 hi[2][4], mid[2][4], lo[2][4];
   __device__ __forceinline__ void set(int mb, int kb, const float (&x)[8]) {
 #pragma unroll
@@ -253,7 +278,7 @@ template <> struct HSlab<BF16> {
     }
   }
 };
-template <> struct HSlab<F32> {
+template <bool KEEP> struct HSlab<F32, KEEP> {
   float v[2][4][8];
   __device__ __forceinline__ void set(int mb, int kb, const float (&x)[8]) {
 #pragma unroll
@@ -312,8 +337,8 @@ __device__ __forceinline__ void phi_to_slot(const f32x4 (&U)[4], const float* s,
 // (H hi / lo from the slab, phi hi / lo from the slot) into the products of
 // the two halves, normalised by the row's meta.
 // Lane (n, q) gets P[mb][i] = P^T[16 mb + 4 q + i][row n] and z of row n.
-template <class DT>
-__device__ __forceinline__ void slab_prod(const u32x4* slot, const float* meta, const HSlab<DT>& Hs,
+template <class DT, class Slab>
+__device__ __forceinline__ void slab_prod(const u32x4* slot, const float* meta, const Slab& Hs,
                                           int lane, int n, f32x4 (&P)[2], float& z) {
   const DT dt{};
   f32x4 Pp[2], Pn[2];
@@ -541,29 +566,32 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
     }
     return val ? vin : kin;
   };
-  // The wave's keys of chunk k0 (keys k0 + 32 wave + 16 kt + n16, clamped to
-  // the chunk) as MFMA operands, and their V rows for P V: lane l takes the
-  // columns CPL l .. of every key (the weights of absent keys are 0).
+  // The wave's keys of chunk k0 (two 16-key blocks: keys k0 + kkey(kt, n16),
+  // clamped to the chunk) as MFMA operands, and their V rows for P V: lane l
+  // takes the columns CPL l .. of every key (the weights of absent keys are 0).
+  // Block kt of wave w is the chunk's keys 16 (4 kt + w) .. + 15, so that each
+  // wave holds one of the first four 16-row phi tiles (the cache rows).
+  auto kkey = [&](int kt, int r) { return 16 * (kWaves * kt + wave) + r; };
   KOp<DT> Kr[2][KB];
   typename VCols<DT, CPL>::W Vpv[32];
   auto load_keys = [&](int k0, int kn, int ln) {
-    if (32 * wave < kn) {
+    if (16 * wave < kn) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const T* kr = key_row(k0 + min(32 * wave + 16 * kt + (ln & 15), kn - 1), false) + 8 * (ln >> 4);
+        const T* kr = key_row(k0 + min(kkey(kt, ln & 15), kn - 1), false) + 8 * (ln >> 4);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) Kr[kt][kb].load(kr + 32 * kb);
       }
     }
   };
   auto load_vals = [&](int k0, int kn, int ln) {
-    if (32 * wave < kn) {
-      // lane j (< 32) finds the V row of key j once; load j takes that
+    if (16 * wave < kn) {
+      // lane j (< 32) finds the V row of the wave's key j once; load j takes that
       // address from lane j (a scalar base plus the lane's column offset)
       // (as a byte offset from the cache's V rows, so that the loads stay
       // global-memory loads)
       const char* vb = reinterpret_cast<const char*>(cv);
-      const uint64_t ra = reinterpret_cast<uintptr_t>(key_row(k0 + min(32 * wave + (ln & 31), kn - 1), true)) -
+      const uint64_t ra = reinterpret_cast<uintptr_t>(key_row(k0 + min(kkey((ln >> 4) & 1, ln & 15), kn - 1), true)) -
                           reinterpret_cast<uintptr_t>(vb);
       const uint32_t rlo = (uint32_t)ra, rhi = (uint32_t)(ra >> 32);
 #pragma unroll
@@ -634,6 +662,27 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   if (tid < np * PQ) *reinterpret_cast<u32x4*>(sm_pend + 4 * tid) = pbuf;
   for (int i = tid + kThreads; i < gs; i += kThreads) sm_cpos[i] = a.cache_pos[(size_t)u * lam + i];
   __syncthreads();
+  // The last phi tile of a one-chunk step holds at most one key row, the
+  // leaving pair's, which LDS holds too; its other rows are the new pair and
+  // the queries.  Its wave computes it here, from LDS, before issuing its
+  // second wave of reads, so that no wave has more than one tile in the phi
+  // phase (four tiles of cache rows and this one in the decode shapes).
+  int early = -1;
+  if constexpr (!MULTI) {
+    const int cno = max(0, min(kn0, ncand));        // as in the chunk loop (one chunk)
+    const int cn = cno + (ncand > nko ? 1 : 0);
+    const int t = (cn + g + 15) / 16 - 1;
+    // (cno <= gs + 1: the tile's only key row is gs, the leaving pair)
+    if (t >= 0 && 16 * t >= min(cno, gs)) early = t;
+    if (early >= 0 && (early & (kWaves - 1)) == wave) {
+      const int row = 16 * early + n16;
+      const T* xr = row < cno ? sm_lk : row < cn ? sm_nk : sm_q + min(max(row - cn, 0), g - 1) * RS;
+      f32x4 U[4];
+      pre16<DT, HD>([&](int kb, u32x4& hi, u32x4& lo) { xop(dt, xr + 32 * kb + 8 * q4, hi, lo); },
+                    sm_wt, n16, q4, U);
+      phi_to_slot<DT>(U, sm_s, lane, n16, q4, sm_slot + early * (8 * 64), sm_meta + early * 64);
+    }
+  }
   // ---- second wave, issued once every wave's first-wave LDS data has
   // arrived: the values of the wave's keys, the SRE values of the first phi
   // tiles, the H slab (lane (n16, q4) holds H[sigma(kb, q4, j)][32 wave +
@@ -664,7 +713,7 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
   float mrun[4], lrun[4];
 #pragma unroll
   for (int hd = 0; hd < 4; ++hd) { mrun[hd] = -INFINITY; lrun[hd] = 0.f; }
-  HSlab<DT> Hs;
+  HSlab<DT, !MULTI> Hs;
 
   // ---- key chunks (one for the decode shapes here)
   for (int c = 0; c < nch; ++c) {
@@ -687,9 +736,9 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
     float alpha[4] = {1.f, 1.f, 1.f, 1.f};         // rescale of the earlier chunks' partials
     {
       // logits of the wave's keys: S^T = K Q^T in two 16-key blocks, lane
-      // (n16, q4) = query n16, keys 32 wave + 16 kt + 4 q4 + i; softmax
-      // weights with the running max
-      if (32 * wave < kn) {
+      // (n16, q4) = query n16, keys kkey(kt, 4 q4 + i); softmax weights with
+      // the running max
+      if (16 * wave < kn) {
         // (queries past g read a valid row; never read back)
         const T* qrow = sm_q + min(n16, g - 1) * RS + 8 * q4;
         f32x4 St[2];
@@ -711,7 +760,7 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int j = 32 * wave + 16 * kt + 4 * q4 + i;
+            const int j = kkey(kt, 4 * q4 + i);
             const bool vis = j < kn && (k0 + j >= gs || (a.branches & LOLA_READ_CACHE));   // cache keys unless hidden
             S[kt][i] = vis ? St[kt][i] * scale2 : -INFINITY;
             mx = fmaxf(mx, S[kt][i]);
@@ -735,7 +784,7 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
           for (int i = 0; i < 4; ++i) {
             const float p = __builtin_amdgcn_exp2f(S[kt][i] - mr);
             ls += p;
-            if (n16 < 4) sm_logit[4 * (32 * wave + 16 * kt + 4 * q4 + i) + n16] = n16 < g ? p : 0.f;
+            if (n16 < 4) sm_logit[4 * kkey(kt, 4 * q4 + i) + n16] = n16 < g ? p : 0.f;
           }
         ls = qsum(ls);
 #pragma unroll
@@ -746,19 +795,19 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
 
     // phi rows of the chunk: its candidate keys (cno), the new pair when it is
     // a candidate (eta = 0), then (last chunk) the queries.  Tile t (rows
-    // 16 t ..) is computed by wave t / 2, whose key block t % 2 holds its key
-    // rows; tiles past the keys by the last wave.
+    // 16 t ..) is computed by wave t % 4, whose key block t / 4 holds its key
+    // rows (tiles past the keys: rows from LDS).
     const int cno = max(0, min(kn, ncand - k0));
     const int cn = cno + (last && ncand > nko ? 1 : 0);
     const int nr = cn + (last ? g : 0);
     const int nt = (nr + 15) / 16;
     for (int t = 0; t < nt; ++t) {
-      if (min(t >> 1, kWaves - 1) != wave) continue;
+      if ((t & (kWaves - 1)) != wave || t == early) continue;
       const int row = 16 * t + n16;
       // rows past the keys: the new pair, a query, else a copy of a query (never read back)
       const T* xr = row < cn ? sm_nk : sm_q + min(max(row - cn, 0), g - 1) * RS;
       const bool use = row < cno;
-      const bool odd = (t & 1) != 0;               // key block t % 2 (selected, not indexed)
+      const bool odd = ((t / kWaves) & 1) != 0;    // key block t / 4 (selected, not indexed)
       f32x4 U[4];
       pre16<DT, HD>([&](int kb, u32x4& hi, u32x4& lo) {
                       const KOp<DT> kr = KOp<DT>::pick(odd, Kr[0][kb], Kr[1][kb]);
@@ -775,12 +824,12 @@ __global__ __launch_bounds__(kThreads, DT::kSplit ? 1 : 2) void decode_kernel(De
       for (int hd = 0; hd < 4; ++hd)
 #pragma unroll
         for (int e = 0; e < CPL; ++e) acc[hd][e] = 0.f;
-      if (32 * wave < kn) {
+      if (16 * wave < kn) {
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");   // weights written above
         // lane l over the 32 keys, its CPL columns, four heads
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
-          const f32x4 p4 = *reinterpret_cast<const f32x4*>(sm_logit + 4 * (32 * wave + j));
+          const f32x4 p4 = *reinterpret_cast<const f32x4*>(sm_logit + 4 * kkey(j >> 4, j & 15));
           float v[CPL];
           VCols<DT, CPL>::cvt(Vpv[j], v);
 #pragma unroll

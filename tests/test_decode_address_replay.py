@@ -65,16 +65,18 @@ def run(B, Hkv, g, lam, eta, npos, phase, fails):
             chk('npos', b, 1, 'npos')
             # first wave: keys
             kn0 = min(kKC, nko)
+            def kkey(kt, r):                       # block kt of wave w: keys 16 (4 kt + w) ..
+                return 16 * (4 * kt + wave) + r
             def load_keys(k0, kn, ln):
-                if 32 * wave < kn:
+                if 16 * wave < kn:
                     for kt in range(2):
-                        buf, off = key_row(k0 + min(32 * wave + 16 * kt + (ln & 15), kn - 1), False)
+                        buf, off = key_row(k0 + min(kkey(kt, ln & 15), kn - 1), False)
                         off += 8 * (ln >> 4)
                         for kb in range(KB): chk(buf, off + 32 * kb, 8, 'keys')
             def load_vals(k0, kn, ln):
-                if 32 * wave < kn:
+                if 16 * wave < kn:
                     for j in range(32):
-                        buf, off = key_row(k0 + min(32 * wave + (j & 31), kn - 1), True)
+                        buf, off = key_row(k0 + min(kkey((j >> 4) & 1, j & 15), kn - 1), True)
                         chk(buf, off + CPL * ln, CPL, 'vals')
             def load_vs(row0, rr):
                 buf, off = key_row(min(row0 + rr, ncand - 1), True)
