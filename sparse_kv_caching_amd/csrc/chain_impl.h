@@ -64,7 +64,17 @@ namespace chain_ns {
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int HTP = kD + 8;   // padded LDS row of H^T (16-bit elements)
-constexpr int STP = 64 + 8;   // padded LDS row of fold staging tiles (64 tokens)
+// Fold staging: 64 tokens per block, token-major rows of 16-bit elements
+// (as gathered), read back as MFMA operands with transposing LDS reads.  A
+// row of P 16-byte pieces is stored unpadded with its pieces permuted (XOR
+// of the piece index with a function of the row), so that the four
+// consecutive rows one transposing read touches fall on distinct banks.
+template <int P>
+__device__ __forceinline__ int stg_off(int row, int col) {   // element offset, col % 4 == 0
+  static_assert(P == 4 || P == 8 || P == 16, "rows of 64, 128 or 256 bytes");
+  const int x = P == 16 ? 4 * (row & 3) : P == 8 ? 4 * ((row >> 1) & 1) : 0;
+  return row * (8 * P) + ((((col >> 3) ^ x)) << 3) + (col & 7);
+}
 // fold staging buffers: two where the workgroup holds fewer than all slabs
 // (the two then fit the LDS of the all-slab layout with one)
 template <int HD, int SPW> constexpr int kFoldBufs = SPW < HD / 32 ? 2 : 1;
@@ -76,7 +86,7 @@ template <int HD, int SPW> constexpr int kFoldBufs = SPW < HD / 32 ? 2 : 1;
 struct ChainLayout {
   uint32_t HT_hi, HT_lo, s32, spart, G, Gp, S, misc, kred;
   uint32_t E, part, keys, hist, stage;         // selection phase
-  uint32_t phT_hi, phT_lo, VT_hi, VT_lo;       // fold phase (same region)
+  uint32_t phS_hi, phS_lo, VS_hi, VS_lo;       // fold phase (same region)
   uint32_t total;
 };
 
@@ -112,10 +122,10 @@ __host__ __device__ inline ChainLayout chain_layout(int lam, int C, int spw, boo
   const uint32_t sel_end = off;
   off = region;
   const uint32_t nb = (uint32_t)nbuf;
-  L.phT_hi = take(nb * kD * STP * 2);      // [nbuf][kD][STP]
-  L.phT_lo = take(nb * kD * STP * 2);
-  L.VT_hi = take(nb * ncol * STP * 2);     // [nbuf][ncol][STP]
-  L.VT_lo = take(f32 ? nb * ncol * STP * 2 : 16);
+  L.phS_hi = take(nb * 64 * kD * 2);       // [nbuf][64][kD]
+  L.phS_lo = take(nb * 64 * kD * 2);
+  L.VS_hi = take(nb * 64 * ncol * 2);      // [nbuf][64][ncol]
+  L.VS_lo = take(f32 ? nb * 64 * ncol * 2 : 16);
   L.total = off > sel_end ? off : sel_end;
   return L;
 }
@@ -130,17 +140,23 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 
-// y[d] = x[(d + r) % 4] for a lane-dependent r in 0 .. 3 (two selects per
-// dword, no indexed registers).
-__device__ __forceinline__ u32x4 rot_dw(u32x4 x, int r) {
-  const bool r1 = r & 1, r2 = r & 2;
-  const u32x4 y = {r1 ? x[1] : x[0], r1 ? x[2] : x[1], r1 ? x[3] : x[2], r1 ? x[0] : x[3]};
-  return u32x4{r2 ? y[2] : y[0], r2 ? y[3] : y[1], r2 ? y[0] : y[2], r2 ? y[1] : y[3]};
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane i names 4 16-bit elements of row i / 4, columns 4 (i % 4) .. of a
+// 4 x 16 block, and receives column i of the block (its 4 rows, in order).
+__device__ __forceinline__ u32x2 ld_tr(const uint16_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s* lds_v4s;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)p));
 }
-
-// Halfword e (0 .. 7) of a 16-byte piece.
-__device__ __forceinline__ uint16_t half_of(u32x4 x, int e) {
-  return (uint16_t)((e & 1) ? x[e >> 1] >> 16 : x[e >> 1] & 0xFFFFu);
+// The 32 x 32 x 16 MFMA operand of a staged block: lane l gets column
+// c0 + l % 32 for rows k0 + 8 (l / 32) .. + 7 (k0: the k-block's first row, a
+// multiple of 8), as two transposing reads of 4 rows each.
+template <int P>
+__device__ __forceinline__ u32x4 ld_op_tr(const uint16_t* buf, int k0, int c0, int lane) {
+  const int row = k0 + 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const u32x2 a = ld_tr(buf + stg_off<P>(row, col)), b = ld_tr(buf + stg_off<P>(row + 4, col));
+  return u32x4{a[0], a[1], b[0], b[1]};
 }
 
 }  // namespace chain_ns
@@ -204,13 +220,13 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
     float* part;
     uint64_t* keys;
     int32_t* hist;
-    uint16_t *phT_hi, *phT_lo, *VT_hi, *VT_lo;
+    uint16_t *phS_hi, *phS_lo, *VS_hi, *VS_lo;
   } sm = {(uint16_t*)(smem + L.HT_hi), (uint16_t*)(smem + L.HT_lo), (float*)(smem + L.s32),
           (float*)(smem + L.spart), (int32_t*)(smem + L.G), (int32_t*)(smem + L.Gp),
           (int32_t*)(smem + L.S), (int32_t*)(smem + L.misc), (uint64_t*)(smem + L.kred),
           (int32_t*)(smem + L.E), (float*)(smem + L.part), (uint64_t*)(smem + L.keys),
-          (int32_t*)(smem + L.hist), (uint16_t*)(smem + L.phT_hi), (uint16_t*)(smem + L.phT_lo),
-          (uint16_t*)(smem + L.VT_hi), (uint16_t*)(smem + L.VT_lo)};
+          (int32_t*)(smem + L.hist), (uint16_t*)(smem + L.phS_hi), (uint16_t*)(smem + L.phS_lo),
+          (uint16_t*)(smem + L.VS_hi), (uint16_t*)(smem + L.VS_lo)};
 
   // ---- own H tiles: tile p = wave + kWaves * i (p < NTILE) -> slab p / 4, mt p % 4
   // (H is stored transposed, H^T [d][kD]: the lane's four consecutive
@@ -779,9 +795,9 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
     // with the rows one instruction touches): wave w loads plane w / 4 (hi,
     // lo) of feature quarter w % 4 for the block's 64 tokens (tokens
     // 16 i + lane / 4), and the own V columns of tokens 8 w .. 8 w + 7.  The
-    // tiles are written transposed (token-contiguous) for the MFMA operands;
-    // a lane writes its eight values starting at the one 2 (piece % 4) on, so
-    // that the lanes of one write hit distinct banks.  The gathers of up to
+    // pieces are staged as loaded, token-major (one 16-byte write each), and
+    // the MFMA operands (token-contiguous per feature or column) and the s
+    // sums are read back with transposing LDS reads.  The gathers of up to
     // GB blocks are issued together (they are latency-bound, and a later
     // block's loads then stay in flight while an earlier block is staged and
     // multiplied); values stay as loaded until they are staged.
@@ -827,36 +843,29 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
         // this block's staging buffer
         const int fb = NBUF == 2 ? (blk & 1) : 0;
         ++blk;
-        uint16_t* pTh = sm.phT_hi + fb * (kD * STP);
-        uint16_t* pTl = sm.phT_lo + fb * (kD * STP);
-        uint16_t* vTh = sm.VT_hi + fb * (32 * SPW * STP);
-        uint16_t* vTl = sm.VT_lo + (DT::kSplit ? fb * (32 * SPW * STP) : 0);
+        constexpr int PP = kD / 8, PV = 4 * SPW;           // 16-byte pieces per staged row
+        uint16_t* pSh = sm.phS_hi + fb * (64 * kD);
+        uint16_t* pSl = sm.phS_lo + fb * (64 * kD);
+        uint16_t* vSh = sm.VS_hi + fb * (64 * 32 * SPW);
+        uint16_t* vSl = sm.VS_lo + (DT::kSplit ? fb * (64 * 32 * SPW) : 0);
         {
-          uint16_t* dst = (wave < 4 ? pTh : pTl) + tq;
+          uint16_t* dst = wave < 4 ? pSh : pSl;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const u32x4 y = rot_dw(gb[b].x[i], pq);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dst[(fq + ((e + 2 * pq) & 7)) * STP + 16 * i] = half_of(y, e);
-          }
+          for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + stg_off<PP>(16 * i + tq, fq)) = gb[b].x[i];
         }
 #pragma unroll
         for (int m = 0; m < VL; ++m) {
           const int idx = lane + 64 * m, pc = idx % VPR, t = 8 * wave + idx / VPR;
           if (idx < 8 * VPR) {
-            const u32x4 y = rot_dw(gb[b].v[m], pc & 3);
             if constexpr (DT::kSplit) {
+              // four fp32 values: their 16-bit hi and lo parts, two per dword
+              uint32_t hi[4], lo[4];
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int c = PER * pc + ((e + (pc & 3)) & 3);
-                uint32_t hi, lo;
-                DT::split(__uint_as_float(y[e]), hi, lo);
-                vTh[c * STP + t] = (uint16_t)hi;
-                vTl[c * STP + t] = (uint16_t)lo;
-              }
+              for (int e = 0; e < 4; ++e) DT::split(__uint_as_float(gb[b].v[m][e]), hi[e], lo[e]);
+              *reinterpret_cast<u32x2*>(vSh + stg_off<PV>(t, PER * pc)) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+              *reinterpret_cast<u32x2*>(vSl + stg_off<PV>(t, PER * pc)) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
             } else {
-#pragma unroll
-              for (int e = 0; e < 8; ++e) vTh[(PER * pc + ((e + 2 * (pc & 3)) & 7)) * STP + t] = half_of(y, e);
+              *reinterpret_cast<u32x4*>(vSh + stg_off<PV>(t, PER * pc)) = gb[b].v[m];
             }
           }
         }
@@ -865,17 +874,20 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
         // its products of block b)
         lds_barrier();
         {
-          // s partial sums: feature F, 64 / NPART tokens per part, fixed order
+          // s partial sums: feature F, 64 / NPART tokens per part, fixed
+          // order; a transposing read gives the lane 4 tokens of its feature
           const int F = tid % kD, qt = tid / kD;
           constexpr int TPP = 64 / (kThreads / kD);
-          static_assert(TPP % 8 == 0, "parts are read as 8-token pieces");
+          static_assert(TPP % 4 == 0 && kD % 64 == 0, "parts are read as 4-token pieces");
+          const int foff = (F & ~15) + 4 * (lane & 3);     // the 16-feature block's column of the lane
           float part = 0.f;
 #pragma unroll
-          for (int q8 = 0; q8 < TPP / 8; ++q8) {
-            const u32x4 wh = ld16(pTh + F * STP + TPP * qt + 8 * q8);
-            const u32x4 wl = ld16(pTl + F * STP + TPP * qt + 8 * q8);
+          for (int q4 = 0; q4 < TPP / 4; ++q4) {
+            const int row = TPP * qt + 4 * q4 + ((lane & 15) >> 2);
+            const u32x2 wh = ld_tr(pSh + stg_off<PP>(row, foff));
+            const u32x2 wl = ld_tr(pSl + stg_off<PP>(row, foff));
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
+            for (int q = 0; q < 4; ++q) {
               const uint32_t bh = (q & 1) ? wh[q >> 1] >> 16 : wh[q >> 1] & 0xFFFFu;
               const uint32_t bl = (q & 1) ? wl[q >> 1] >> 16 : wl[q >> 1] & 0xFFFFu;
               part += DT::from_bits(bh) + DT::from_bits(bl);
@@ -887,18 +899,17 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
         }
         const int nkb = min(4, (nS - sb + 15) / 16);
         for (int kb = 0; kb < nkb; ++kb) {
-          const int k0 = 16 * kb + 8 * h;
 #pragma unroll
           for (int i = 0; i < NPW; ++i) {
             const int p = wave + kWaves * i, sw = p >> 2, mt = p & 3;
             if (p < NTILE) {
-              const u32x4 bv = ld16(vTh + (32 * sw + r) * STP + k0);
-              const u32x4 ah = ld16(pTh + (32 * mt + r) * STP + k0);
-              const u32x4 al = ld16(pTl + (32 * mt + r) * STP + k0);
+              const u32x4 bv = ld_op_tr<PV>(vSh, 16 * kb, 32 * sw, lane);
+              const u32x4 ah = ld_op_tr<PP>(pSh, 16 * kb, 32 * mt, lane);
+              const u32x4 al = ld_op_tr<PP>(pSl, 16 * kb, 32 * mt, lane);
               Hreg[i] = DT::mma(ah, bv, Hreg[i]);
               Hreg[i] = DT::mma(al, bv, Hreg[i]);
               if constexpr (DT::kSplit)
-                Hreg[i] = DT::mma(ah, ld16(vTl + (32 * sw + r) * STP + k0), Hreg[i]);
+                Hreg[i] = DT::mma(ah, ld_op_tr<PV>(vSl, 16 * kb, 32 * sw, lane), Hreg[i]);
             }
           }
         }
