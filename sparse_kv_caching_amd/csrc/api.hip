@@ -192,12 +192,17 @@ int chain_workgroups(int U, int ncu, int d, int lam, int C) {
 // of its speed on half of the device.  Measured on MI355X (prefill call,
 // ms, sequential -> concurrent): T = 32768 single sequence 5.11 -> 3.72; 8
 // sequences of T = 8192 3.67 -> 3.13; Llama-shaped T = 4096 0.679 -> 0.671.
-// The read keeps max(ncu / 8, R / 4) compute units, at most half, with R its
-// 64-key tiles per chunk over all units (a compute unit reads about four
-// such tiles in the time of a short chain step): the long and batched
-// workloads' reads take half of the device, the Llama-shaped one's 32 units
-// (its chain then runs on 28 workgroups per unit instead of 16).  The automatic choice takes the schedule whenever the chain
-// fits and the call has >= 4 chunks.
+// The read keeps max(ncu / 8, R / 4) compute units, at most 5/8 of them,
+// with R its 64-key tiles per chunk over all units (a compute unit reads about
+// four such tiles in the time of a short chain step), but leaves the chain
+// two workgroups per unit where half of the device allows (the candidate
+// split needs two): the long workload's read takes 160 units (its chain 12
+// workgroups per unit, six 32-candidate tiles each: 3.11 -> 2.99 ms per call
+// against 128 units and 16 workgroups, 3.19 at 11, 3.11 at 13 and 14), the
+// batched one's half of the device (2 per unit; 3.31 ms at 1), the
+// Llama-shaped one's 32 units (its chain then runs on 28 workgroups per unit).
+// The automatic choice takes the schedule whenever the chain fits and the
+// call has >= 4 chunks.
 int overlap_workgroups(const lola_state* st, int T, int C, int nch) {
   (void)T;
   if (st->overlap == 0 || nch < 2) return 0;
@@ -205,7 +210,8 @@ int overlap_workgroups(const lola_state* st, int T, int C, int nch) {
   const int g = st->cfg.q_heads / st->cfg.kv_heads;
   const long long nptile = (C + attn_positions_per_block(C, g) - 1) / attn_positions_per_block(C, g);
   const long long R = (long long)U * nptile * ((lam + eta + C + 63) / 64);
-  const int keep = (int)std::min<long long>(st->ncu / 2, std::max<long long>(st->ncu / 8, R / 4));
+  int keep = (int)std::min<long long>(st->ncu * 5 / 8, std::max<long long>(st->ncu / 8, R / 4));
+  if (st->ncu - keep < 2 * U && 2 * U <= st->ncu / 2) keep = st->ncu - 2 * U;
   const int chain_cus = st->ncu - keep;
   const int k = st->force_k > 0 ? st->force_k : chain_workgroups(U, chain_cus, st->d, lam, C);
   if ((long long)U * k > (st->force_k > 0 ? st->ncu - 1 : chain_cus)) return 0;
