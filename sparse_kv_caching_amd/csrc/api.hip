@@ -207,6 +207,7 @@ int overlap_workgroups(const lola_state* st, int T, int C, int nch) {
   (void)T;
   if (st->overlap == 0 || nch < 2) return 0;
   const int U = st->U, lam = st->cfg.cache, eta = st->cfg.window;
+  if (!attn_wide_table(st->d, lam, eta, C, st->f32)) return 0;
   const int g = st->cfg.q_heads / st->cfg.kv_heads;
   const long long nptile = (C + attn_positions_per_block(C, g) - 1) / attn_positions_per_block(C, g);
   const long long R = (long long)U * nptile * ((lam + eta + C + 63) / 64);

@@ -8,21 +8,31 @@ size_t attn_lds_bytes(int d, int lam, int eta, int C, bool f32) {
   return attn_ns::attn_layout(d, lam, eta, C, f32).total;
 }
 
-template <class DT, int HD>
+bool attn_wide_table(int d, int lam, int eta, int C, bool f32) {
+  return attn_ns::attn_layout(d, lam, eta, C, f32).wide;
+}
+
+template <class DT, int HD, bool WIDE>
 __global__ __launch_bounds__(attn_ns::kThreads) void attn_kernel(AttnArgs a) {
-  attn_body<DT, HD>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  attn_body<DT, HD, WIDE>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+}
+
+template <class DT, int HD, bool WIDE>
+static hipError_t launch_attn_w(const AttnArgs& a, int U, size_t lds, hipStream_t st) {
+  const int nptile = (a.C + a.ptile - 1) / a.ptile;
+  dim3 grid(U, a.nch_launch, nptile);
+  const void* fn = (const void*)attn_kernel<DT, HD, WIDE>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((attn_kernel<DT, HD, WIDE>), grid, dim3(attn_ns::kThreads), lds, st, a);
+  return hipGetLastError();
 }
 
 template <class DT, int HD>
 static hipError_t launch_attn_t(const AttnArgs& a, int U, hipStream_t st) {
-  const int nptile = (a.C + a.ptile - 1) / a.ptile;
-  dim3 grid(U, a.nch_launch, nptile);
-  const size_t lds = attn_lds_bytes(HD, a.vr.lam, a.vr.eta, a.C, DT::kSplit);
-  const void* fn = (const void*)attn_kernel<DT, HD>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_kernel<DT, HD>), grid, dim3(attn_ns::kThreads), lds, st, a);
-  return hipGetLastError();
+  const attn_ns::AttnLayout L = attn_ns::attn_layout(HD, a.vr.lam, a.vr.eta, a.C, DT::kSplit);
+  return L.wide ? launch_attn_w<DT, HD, true>(a, U, L.total, st)
+                : launch_attn_w<DT, HD, false>(a, U, L.total, st);
 }
 
 int attn_positions_per_block(int C, int g) {

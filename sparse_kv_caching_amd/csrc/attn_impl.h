@@ -47,7 +47,8 @@ constexpr int VTS = KT + 4;   // LDS row of the V^T tile (keys): 34 dwords, so t
 // Byte offsets of the LDS arrays; the key phase reuses the region of the
 // linear-read phase.
 struct AttnLayout {
-  uint32_t tab;                                // both phases: row of every key of the chunk
+  uint32_t tab, tabv;                          // both phases: the key table (below)
+  bool wide;
   uint32_t WT, HT_hi, HT_lo, s;                // linear-read phase
   uint32_t K[2], KL[2], VT[2], VTL[2];         // key phase, two buffers
   uint32_t total;
@@ -68,15 +69,22 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__host__ __device__ inline AttnLayout attn_layout(int d, int lam, int eta, int C, bool f32) {
+// LDS a workgroup may take (the device's 160 KB, less a margin)
+constexpr uint32_t kLdsCap = 160 * 1024 - 64;
+
+__host__ __device__ inline AttnLayout attn_layout_t(int d, int lam, int eta, int C, bool f32, bool wide) {
   AttnLayout L;
   uint32_t off = 0;
   auto take = [&](uint32_t b) { const uint32_t o = off; off = al16(off + b); return o; };
   const uint32_t esz = f32 ? 4 : 2;
   // the keys a chunk's queries see: the cache at chunk start, the window,
-  // the chunk's own positions; per key its source (cache, ring, input) and
-  // row, packed as (source << 30) | row
-  L.tab = take((uint32_t)(lam + eta + C) * 4);
+  // the chunk's own positions.  Wide: the byte addresses of every key's K
+  // row and V row (64-bit each); else per key its source (cache, ring,
+  // input) and row, packed as (source << 30) | row
+  const uint32_t nk = (uint32_t)(lam + eta + C);
+  L.wide = wide;
+  L.tab = take(nk * (wide ? 8u : 4u));
+  L.tabv = wide ? take(nk * 8u) : L.tab;
   const uint32_t base = off;
   L.WT = take((uint32_t)kM * (d + 8) * esz);          // [kM][d + 8] W^T, input dtype
   L.HT_hi = take((uint32_t)d * HTS * 2);               // [d][HTS]
@@ -92,6 +100,13 @@ __host__ __device__ inline AttnLayout attn_layout(int d, int lam, int eta, int C
   }
   L.total = phaseA > off ? phaseA : off;
   return L;
+}
+
+// The wide key table where it fits (a row address is then one LDS read),
+// else the packed one
+__host__ __device__ inline AttnLayout attn_layout(int d, int lam, int eta, int C, bool f32) {
+  const AttnLayout W = attn_layout_t(d, lam, eta, C, f32, true);
+  return W.total <= kLdsCap ? W : attn_layout_t(d, lam, eta, C, f32, false);
 }
 
 __device__ __forceinline__ u32x2 ld8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
@@ -136,7 +151,9 @@ __device__ __forceinline__ uint32_t f16_pair(float a, float b) {
 }  // namespace attn_ns
 
 // One workgroup of the read: unit u, chunk ch0 + jrel, position tile pt.
-template <class DT, int HD>
+// WIDE: the key table holds row addresses (the layout attn_layout picks
+// where it fits), else packed (source, row) words.
+template <class DT, int HD, bool WIDE>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, int pt_) {
   using namespace attn_ns;
   using T = typename DT::T;
@@ -201,8 +218,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
   const int n0e = eta > 0 ? (int)(n0 % eta) : 0;            // ring slot of position n0 - eta
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const AttnLayout L = attn_layout(HD, lam, eta, a.C, DT::kSplit);
+  const AttnLayout L = attn_layout_t(HD, lam, eta, a.C, DT::kSplit, WIDE);
   uint32_t* sm_tab = (uint32_t*)(smem + L.tab);
+  uint64_t* sm_tabk = (uint64_t*)(smem + L.tab);
+  uint64_t* sm_tabv = (uint64_t*)(smem + L.tabv);
   T* sm_WT = (T*)(smem + L.WT);
   uint16_t* sm_HT_hi = (uint16_t*)(smem + L.HT_hi);
   uint16_t* sm_HT_lo = (uint16_t*)(smem + L.HT_lo);
@@ -283,7 +302,15 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
 #pragma unroll
       for (int k = 0; k < GT; ++k) {
         const int i = i0 + k * kThreads + tid;
-        if (i < nkeys) sm_tab[i] = vsrc(i < gsj ? (int)(gv[k] < nv ? gv[k] : 0u) : vi_loc0 + (i - gsj));
+        if (i < nkeys) {
+          const uint32_t e = vsrc(i < gsj ? (int)(gv[k] < nv ? gv[k] : 0u) : vi_loc0 + (i - gsj));
+          if constexpr (WIDE) {
+            sm_tabk[i] = row_addr(e, bk, dk1, dk2);
+            sm_tabv[i] = row_addr(e, bv, dv1, dv2);
+          } else {
+            sm_tab[i] = e;
+          }
+        }
       }
     };
     uint32_t gv0[GT];
@@ -369,7 +396,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
     for (int q = 0; q < KPT; ++q) {
       const int pc = q * kThreads + tid, kl = pc / (HD / PER), c = (pc % (HD / PER)) * PER;
       const int kk = min(t0 + kl, nkeys - 1);
-      kreg[q] = ldg16(row_addr(sm_tab[kk], bk, dk1, dk2) + c * sizeof(T));
+      kreg[q] = ldg16((WIDE ? sm_tabk[kk] : row_addr(sm_tab[kk], bk, dk1, dk2)) + c * sizeof(T));
     }
   };
   auto load_v = [&](int t0) {
@@ -377,7 +404,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq) {
         const int kk = min(t0 + 2 * vpr + kq, nkeys - 1);
-        const uint64_t src = row_addr(sm_tab[kk], bv, dv1, dv2) + vcol * sizeof(T);
+        const uint64_t src = (WIDE ? sm_tabv[kk] : row_addr(sm_tab[kk], bv, dv1, dv2)) + vcol * sizeof(T);
 #pragma unroll
         for (int w = 0; w < VPC; ++w) vreg[kq][w] = ldg16(src + 16 * w);
       }

@@ -38,14 +38,18 @@ __global__ __launch_bounds__(chain_ns::kThreads) void overlap_kernel(OverlapArgs
   }
   const int w = b - o.nchain;
   const int u = w % o.U, rest = w / o.U;
-  attn_body<DT, HD>(o.a, u, rest / o.nptile, rest % o.nptile);
+  attn_body<DT, HD, true>(o.a, u, rest / o.nptile, rest % o.nptile);
 }
 
 template <class DT, int HD, int SPW, bool XS = false>
 static hipError_t launch_overlap_t(const OverlapArgs& o, hipStream_t st) {
   const size_t lc =
       chain_ns::chain_layout(o.c.vr.lam, o.c.C, SPW, DT::kSplit, chain_ns::kFoldBufs<HD, SPW>, XS).total;
-  const size_t la = attn_ns::attn_layout(HD, o.a.vr.lam, o.a.vr.eta, o.a.C, DT::kSplit).total;
+  // (the read's part: the wide key table; the library takes this schedule
+  // only where that layout fits)
+  const attn_ns::AttnLayout L = attn_ns::attn_layout(HD, o.a.vr.lam, o.a.vr.eta, o.a.C, DT::kSplit);
+  if (!L.wide) return hipErrorInvalidValue;
+  const size_t la = L.total;
   const size_t lds = lc > la ? lc : la;
   const void* fn = (const void*)overlap_kernel<DT, HD, SPW, XS>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

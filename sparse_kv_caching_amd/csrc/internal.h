@@ -244,6 +244,9 @@ hipError_t launch_score(const ScoreArgs& a, int U, bool f32, hipStream_t st);
 size_t score_lds_bytes(int d);
 hipError_t launch_score_writeback(const ScoreWriteArgs& a, int U, hipStream_t st);
 size_t attn_lds_bytes(int d, int lam, int eta, int C, bool f32);
+// the read's key table holds row addresses (the layout fits the LDS with
+// them); the one-launch schedule needs it
+bool attn_wide_table(int d, int lam, int eta, int C, bool f32);
 int attn_positions_per_block(int C, int g);
 hipError_t launch_finalize(const FinalizeArgs& a, int U, bool f32, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int U, bool f32, hipStream_t st);
