@@ -416,3 +416,14 @@ def test_invalid_arguments_leave_state_unchanged():
     L.prefill(q, k, v, 64)
     assert L.n == 64
     L.free()
+
+
+def test_wide_window_packed_key_table():
+    """A window too large for the read's table of row addresses (window 5000
+    + cache 64 + chunk 64 keys at d = 128: the address table would not fit
+    the LDS next to the linear-read staging), so the read takes its packed
+    (source, row) key table and the call the sequential schedule; 400
+    positions leave the window, so the cache and the linear state are read
+    too."""
+    wl = WORKLOADS["llama8b_4k"].scaled(B=1, Hq=4, Hkv=1, T=5400, eta=5000, lam=64, C=64)
+    run_lockstep(wl, check_continuous=True)
