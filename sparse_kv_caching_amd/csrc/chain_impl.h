@@ -897,22 +897,34 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
           // the last block's partial sums go out before its closing barrier
           if (sb + 64 >= nS) sm.spart[(tid / kD) * kD + tid % kD] = sacc;
         }
+        // The wave's tiles p = wave + kWaves i share the feature block
+        // mt = wave % 4, so the phi operands of a k-block are read once for
+        // all of them; the wave index is made uniform so that tiles past
+        // NTILE are skipped by a scalar branch.
         const int nkb = min(4, (nS - sb + 15) / 16);
-        for (int kb = 0; kb < nkb; ++kb) {
+        const int wv = __builtin_amdgcn_readfirstlane(wave), mt = wv & 3;
+        auto kblock = [&](int kb) {
+          const u32x4 ah = ld_op_tr<PP>(pSh, 16 * kb, 32 * mt, lane);
+          const u32x4 al = ld_op_tr<PP>(pSl, 16 * kb, 32 * mt, lane);
+          // (every wave holds NPW tiles unless there are fewer tiles than waves)
+          constexpr bool kAll = NTILE == NPW * kWaves;
+          u32x4 bv[NPW];
+#pragma unroll
+          for (int i = 0; i < NPW; ++i)
+            if (kAll || wv + kWaves * i < NTILE)
+              bv[i] = ld_op_tr<PV>(vSh, 16 * kb, 32 * ((wv + kWaves * i) >> 2), lane);
 #pragma unroll
           for (int i = 0; i < NPW; ++i) {
-            const int p = wave + kWaves * i, sw = p >> 2, mt = p & 3;
-            if (p < NTILE) {
-              const u32x4 bv = ld_op_tr<PV>(vSh, 16 * kb, 32 * sw, lane);
-              const u32x4 ah = ld_op_tr<PP>(pSh, 16 * kb, 32 * mt, lane);
-              const u32x4 al = ld_op_tr<PP>(pSl, 16 * kb, 32 * mt, lane);
-              Hreg[i] = DT::mma(ah, bv, Hreg[i]);
-              Hreg[i] = DT::mma(al, bv, Hreg[i]);
+            const int p = wv + kWaves * i, sw = p >> 2;
+            if (kAll || p < NTILE) {
+              Hreg[i] = DT::mma(ah, bv[i], Hreg[i]);
+              Hreg[i] = DT::mma(al, bv[i], Hreg[i]);
               if constexpr (DT::kSplit)
                 Hreg[i] = DT::mma(ah, ld_op_tr<PV>(vSl, 16 * kb, 32 * sw, lane), Hreg[i]);
             }
           }
-        }
+        };
+        for (int kb = 0; kb < nkb; ++kb) kblock(kb);
         if constexpr (NBUF == 1) lds_barrier();
       }
     }
