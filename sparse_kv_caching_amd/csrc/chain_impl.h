@@ -115,7 +115,9 @@ __host__ __device__ inline ChainLayout chain_layout(int lam, int C, int spw, boo
   L.kred = take(2 * kWaves * 8);           // per-wave key min / max
   const uint32_t region = off;
   L.E = take(le * 4);                      // candidates (virtual indices)
-  L.part = take(xs ? 2u * kWaves * 32 * 4 : (uint32_t)spw * le * 4);   // SRE parts
+  // SRE parts (candidate split: [2][kWaves][32] by round parity, then the
+  // z of the round's staged rows [kWaves][32])
+  L.part = take(xs ? 3u * kWaves * 32 * 4 : (uint32_t)spw * le * 4);
   L.keys = take(le * 8);
   L.hist = take(768 * 4);                  // three radix histograms
   L.stage = xs ? take((uint32_t)(kWaves / spw) * 2 * 32 * HTP * 2) : 0;   // [tile][plane][32][HTP]
@@ -377,12 +379,34 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
 #pragma unroll
       for (int c = 0; c < (int)sizeof(T); ++c) v[c] = *reinterpret_cast<const u32x4*>(vrow + 16 / sizeof(T) * c);
     };
+    // z = phi^T s of a candidate, with phi = hi + lo as the GEMM sees it,
+    // in a fixed order that does not depend on which threads hold the
+    // features: a partial per 16-byte piece (features 8 p .. 8 p + 7, an fma
+    // chain from 0 in feature order), then a pairwise tree over the 16
+    // pieces that pairs pieces differing in bit 1 of p, then bit 2, bit 3,
+    // and last bit 0 (every addition commutes, so the two holders of a pair
+    // form the same value)
+    auto zpiece = [&](const u32x4& bh, const u32x4& bl, const float* s8) {
+      const f32x4 s0 = *reinterpret_cast<const f32x4*>(s8);
+      const f32x4 s1 = *reinterpret_cast<const f32x4*>(s8 + 4);
+      float z = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t wh = bh[q], wl = bl[q];
+        const float f0 = DT::from_bits(wh & 0xFFFFu) + DT::from_bits(wl & 0xFFFFu);
+        const float f1 = DT::from_bits(wh >> 16) + DT::from_bits(wl >> 16);
+        z = fmaf(f0, q < 2 ? s0[2 * q] : s1[2 * q - 4], z);
+        z = fmaf(f1, q < 2 ? s0[2 * q + 1] : s1[2 * q - 3], z);
+      }
+      return z;
+    };
     // the part over slab sw of the candidate of lane row r (returned in
     // both lane halves), from its phi row's hi / lo pieces (get(kb, hi, lo):
-    // lane half h, features 16 kb + 8 h ..) and V values
-    // (merged: one pass over kb for z and the products, the operands read
-    // once each; else z first, as the register-held operands allow)
-    auto sre_tile = [&](auto merged, auto&& get, const u32x4 (&vw)[sizeof(T)], int sw, auto&& put) {
+    // lane half h, features 16 kb + 8 h ..: piece 2 kb + h) and V values.
+    // merged: z is given (zin) and one pass over kb reads the operands
+    // once each; else z first, as the register-held operands allow
+    auto sre_tile = [&](auto merged, auto&& get, const u32x4 (&vw)[sizeof(T)], int sw, float zin,
+                        auto&& put) {
       const uint16_t* Ahi = sm.HT_hi + (32 * sw + pr) * HTP + 8 * h;
       const uint16_t* Alo = sm.HT_lo + (32 * sw + pr) * HTP + 8 * h;
       float vv[16];
@@ -397,24 +421,11 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
             vv[4 * c + j] = __uint_as_float(vw[c][j]);
           }
         }
-      // z = phi^T s with phi = hi + lo, as the GEMM sees it, and P^T (this
-      // slab's 32 columns x 32 candidates) in two accumulators
-      float z = 0.f;
+      // z and P^T (this slab's 32 columns x 32 candidates) in two accumulators
+      float z = zin;
       f32x16 P0, P1;
 #pragma unroll
       for (int q = 0; q < 16; ++q) { P0[q] = 0.f; P1[q] = 0.f; }
-      auto zpart = [&](int kb, const u32x4& bh, const u32x4& bl) {
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(sm.s32 + 16 * kb + 8 * h);
-        const f32x4 s1 = *reinterpret_cast<const f32x4*>(sm.s32 + 16 * kb + 8 * h + 4);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t wh = bh[q], wl = bl[q];
-          const float f0 = DT::from_bits(wh & 0xFFFFu) + DT::from_bits(wl & 0xFFFFu);
-          const float f1 = DT::from_bits(wh >> 16) + DT::from_bits(wl >> 16);
-          z = fmaf(f0, q < 2 ? s0[2 * q] : s1[2 * q - 4], z);
-          z = fmaf(f1, q < 2 ? s0[2 * q + 1] : s1[2 * q - 3], z);
-        }
-      };
       auto prod = [&](int kb, const u32x4& bh, const u32x4& bl) {
         const u32x4 ah = ld16(Ahi + 16 * kb), al = ld16(Alo + 16 * kb);
         f32x16& P = (kb & 1) ? P1 : P0;
@@ -427,16 +438,20 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
         for (int kb = 0; kb < 8; ++kb) {
           u32x4 bh, bl;
           get(kb, bh, bl);
-          zpart(kb, bh, bl);
           prod(kb, bh, bl);
         }
       } else {
+        // pieces 2 kb + h: bits 1..3 of the piece are the bits of kb (in the
+        // lane), bit 0 the lane half
+        float zq[8];
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
           u32x4 bh, bl;
           get(kb, bh, bl);
-          zpart(kb, bh, bl);
+          zq[kb] = zpiece(bh, bl, sm.s32 + 16 * kb + 8 * h);
         }
+        z = ((zq[0] + zq[1]) + (zq[2] + zq[3])) + ((zq[4] + zq[5]) + (zq[6] + zq[7]));
+        z += xor32(z);
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
           u32x4 bh, bl;
@@ -444,7 +459,6 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
           prod(kb, bh, bl);
         }
       }
-      z += xor32(z);
       const float iz = z > 0.f ? 1.f / z : 0.f;   // z == 0: prediction 0
       float acc = 0.f;
 #pragma unroll
@@ -498,9 +512,22 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
         if (lt < ntile_own) load_v(vn, e < nE ? sm.E[e] : sm.E[0], sw);
       };
       if (nround > 0) stage_load(0);
+      float* zs = sm.part + 2 * kWaves * 32;         // [TPR][32]: z of the staged rows
       for (int ro = 0; ro < nround; ++ro) {
 #pragma unroll
         for (int m = 0; m < 2 * TPR; ++m) *reinterpret_cast<u32x4*>(sdst + m * 32 * HTP) = sg[m];
+        // z of the staged rows: this thread's piece, then the tree over the
+        // row's 16 pieces (lanes 16 (row % 4) + piece, pairs by lane xor 2,
+        // 4, 8, then 1)
+#pragma unroll
+        for (int tt = 0; tt < TPR; ++tt) {
+          float zp = zpiece(sg[2 * tt], sg[2 * tt + 1], sm.s32 + 8 * spc);
+          zp += __shfl_xor(zp, 2, 64);
+          zp += __shfl_xor(zp, 4, 64);
+          zp += __shfl_xor(zp, 8, 64);
+          zp += __shfl_xor(zp, 1, 64);
+          if (spc == 0) zs[tt * 32 + srow] = zp;
+        }
         u32x4 vc[sizeof(T)];
 #pragma unroll
         for (int c = 0; c < (int)sizeof(T); ++c) vc[c] = vn[c];
@@ -512,7 +539,7 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
           const uint16_t* sh = stg + ((ts * 2) * 32 + r) * HTP + 8 * h;
           const uint16_t* sl = sh + 32 * HTP;
           sre_tile(std::true_type{}, [&](int kb, u32x4& x, u32x4& y) { x = ld16(sh + 16 * kb); y = ld16(sl + 16 * kb); }, vc, sw,
-                   [&](float acc) { if (h == 0) rp[((ro & 1) * kWaves + wave) * 32 + r] = acc; });
+                   zs[ts * 32 + r], [&](float acc) { if (h == 0) rp[((ro & 1) * kWaves + wave) * 32 + r] = acc; });
         }
         lds_barrier();                               // the round's tiles are read
       }
@@ -532,7 +559,8 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) { bh[kb] = ld16(ph + 16 * kb); bl[kb] = ld16(pl + 16 * kb); }
         load_v(vw, vi, sw);
-        sre_tile(std::false_type{}, [&](int kb, u32x4& x, u32x4& y) { x = bh[kb]; y = bl[kb]; }, vw, sw, [&](float acc) {
+        sre_tile(std::false_type{}, [&](int kb, u32x4& x, u32x4& y) { x = bh[kb]; y = bl[kb]; }, vw, sw, 0.f,
+                 [&](float acc) {
           if (e < nE && h == 0) {
             if (!xch) sm.part[sw * LE + e] = acc;
             else __hip_atomic_store(xb + (size_t)(grp * SPW + sw) * LE + e,
