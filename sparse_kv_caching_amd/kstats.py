@@ -14,7 +14,10 @@ the whole run.
     python3 -m sparse_kv_caching_amd.kstats <dir>/run_kernel_trace.csv \
         --segments long_32k:12,batched_8k:12,llama8b_4k:12,decode_b64:1
 
-prints a Markdown table (calls, average / min / max in microseconds).
+prints a Markdown table (calls, average / min / max in microseconds).  With
+``--last N`` it adds, for the prefill kernels of each segment, the average of
+the segment's last N calls (``bench.py`` times its last N calls of a workload
+with HIP events, so that column is the one to set beside its figures).
 """
 
 from __future__ import annotations
@@ -39,6 +42,8 @@ def main():
     ap.add_argument("trace")
     ap.add_argument("--segments", required=True,
                     help="workload:calls,... in the order the prefill workloads ran")
+    ap.add_argument("--last", type=int, default=0,
+                    help="also average each segment's last N calls of a prefill kernel")
     args = ap.parse_args()
     segs = []
     for item in args.segments.split(","):
@@ -69,14 +74,24 @@ def main():
         short = name.split("(")[0].replace("void ", "")
         groups[(label, short)].append(us)
     order = ["before the first segment"] + [w for w, _ in segs] + ["whole run"]
-    print("| Workload | Kernel | Calls | Avg (us) | Min (us) | Max (us) |")
-    print("|---|---|---|---|---|---|")
+    n = args.last
+    if n:
+        print("| Workload | Kernel | Calls | Avg (us) | Avg of the last %d (us) | Min (us) | Max (us) |" % n)
+        print("|---|---|---|---|---|---|---|")
+    else:
+        print("| Workload | Kernel | Calls | Avg (us) | Min (us) | Max (us) |")
+        print("|---|---|---|---|---|---|")
     for label in order:
         items = sorted(((k, v) for k, v in groups.items() if k[0] == label),
                        key=lambda kv: -sum(kv[1]))
         for (lab, name), v in items:
-            print("| %s | `%s` | %d | %.1f | %.1f | %.1f |"
-                  % (lab, name, len(v), sum(v) / len(v), min(v), max(v)))
+            if n:
+                tail = "%.1f" % (sum(v[-n:]) / len(v[-n:])) if lab in dict(segs) and len(v) >= n else "-"
+                print("| %s | `%s` | %d | %.1f | %s | %.1f | %.1f |"
+                      % (lab, name, len(v), sum(v) / len(v), tail, min(v), max(v)))
+            else:
+                print("| %s | `%s` | %d | %.1f | %.1f | %.1f |"
+                      % (lab, name, len(v), sum(v) / len(v), min(v), max(v)))
 
 
 if __name__ == "__main__":

@@ -163,14 +163,16 @@ def _summarize(args):
     fb = sum(fv) / len(fv) * 1024.0 * f_fac
     wb = sum(wv) / len(wv) * 1024.0 * w_fac
     out = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (args.kernel, args.workload))
+    sched = "" if args.overlap is None else " --overlap %d" % args.overlap
     with open(out, "w") as fh:
-        fh.write("# HBM traffic of %s on the %s workload (rocprofv3 PMC, MI355X)\n"
-                 % (prefix, args.workload))
-        fh.write("# commands (repository root, one counter per run):\n")
+        fh.write("# HBM traffic of %s on the %s workload%s (rocprofv3 PMC, MI355X)\n"
+                 % (prefix, args.workload,
+                    ", sequential schedule (the kernel launched alone)" if args.overlap == 0 else ""))
+        fh.write("# commands (repository root = $REPO, on PYTHONPATH; one counter per run):\n")
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             fh.write("#   cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc %s "
                      "--output-format csv -d $REPO/gpurun_out/<dir> -o run -- python3 -m "
-                     "sparse_kv_caching_amd.traffic run --workload %s\n" % (c, args.workload))
+                     "sparse_kv_caching_amd.traffic run --workload %s%s\n" % (c, args.workload, sched))
         fh.write("#   python3 -m sparse_kv_caching_amd.traffic summarize --workload %s --kernel %s "
                  "--fetch <fetch dir> --write <write dir> --last %d\n"
                  % (args.workload, args.kernel, args.last))
@@ -244,6 +246,8 @@ def main():
     s.add_argument("--write", required=True)
     s.add_argument("--last", type=int, default=1)
     s.add_argument("--algorithmic", type=int, default=0)
+    s.add_argument("--overlap", type=int, default=None,
+                   help="the prefill schedule of the runs (recorded in the summary's commands)")
     c = sub.add_parser("counters")
     c.add_argument("--workload", required=True)
     c.add_argument("--kernel", required=True, choices=sorted(KERNELS))
