@@ -689,10 +689,6 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
   ca.vscore = vscore;
   ca.cscore = vscore ? st->cache_score[st->cur] : nullptr;
   ca.ready = k_ovl ? (int*)(base + L.ready) : nullptr;
-  if (ca.k > 1) {
-    e = launch_zero_u32((unsigned*)ca.xbuf, (size_t)U * 2 * (d / 32) * (lam + C) * 2, s);
-    if (e != hipSuccess) return hip_fail(st, e, "exchange reset");
-  }
 
   AttnArgs aa;
   aa.vr = vr; aa.q = q; aa.WT = st->WT;
@@ -713,9 +709,17 @@ static int prefill_impl(lola_state* st, const void* q, const void* k, const void
                         : (ca.k >= nslab ? nslab : (ca.k == 1 ? 1 : nslab / 2));
   aa.spin_limit = st->spin_limit;
 
+  {
+    // the exchange words (k > 1) and the published-snapshot counters (one
+    // launch): zero before the chain starts
+    FillSpan sp[2];
+    int nsp = 0;
+    if (ca.k > 1) sp[nsp++] = FillSpan{(uint32_t*)ca.xbuf, (size_t)U * 2 * (d / 32) * (lam + C) * 2, 0u};
+    if (k_ovl) sp[nsp++] = FillSpan{(uint32_t*)ca.ready, (size_t)U, 0u};
+    e = launch_fill_u32(sp, nsp, s);
+    if (e != hipSuccess) return hip_fail(st, e, "exchange reset");
+  }
   if (k_ovl) {
-    e = launch_zero_u32((unsigned*)ca.ready, (size_t)U, s);
-    if (e != hipSuccess) return hip_fail(st, e, "ready reset");
     { ProfScope ps(st, LOLA_KERNEL_OVERLAP, s); e = launch_overlap(ca, aa, U, st->f32, s); }
     if (e != hipSuccess) return hip_fail(st, e, "chain + read launch");
   } else {
@@ -891,12 +895,13 @@ int lola_state_reset(lola_state* st, void* stream) {
   if (!st) return fail(LOLA_ERR_INVALID_ARG, "state is NULL");
   hipStream_t s = (hipStream_t)stream;
   const size_t U = st->U, d = st->d, lam = st->cfg.cache;
-  hipError_t e = hipMemsetAsync(st->H, 0, U * kD * d * 4, s);
-  if (e == hipSuccess) e = hipMemsetAsync(st->s, 0, U * kD * 4, s);
-  for (int b = 0; b < 2 && e == hipSuccess; ++b)
-    e = hipMemsetAsync(st->cache_pos[b], 0xFF, U * (lam ? lam : 1) * 4, s);
-  if (e == hipSuccess) e = launch_zero_u32((unsigned*)st->dev_err, 1, s);
-  if (e == hipSuccess) e = launch_zero_u32((unsigned*)st->npend, U, s);
+  // H = 0, s = 0, both cache position buffers -1, the device flags and the
+  // held-back fold counts 0: one launch
+  const size_t cl = U * (lam ? lam : 1);
+  const FillSpan sp[] = {{(uint32_t*)st->H, U * kD * d, 0u}, {(uint32_t*)st->s, U * kD, 0u},
+                         {(uint32_t*)st->cache_pos[0], cl, ~0u}, {(uint32_t*)st->cache_pos[1], cl, ~0u},
+                         {(uint32_t*)st->dev_err, 1, 0u}, {(uint32_t*)st->npend, U, 0u}};
+  hipError_t e = launch_fill_u32(sp, 6, s);
   if (e != hipSuccess) return hip_fail(st, e, "reset");
   st->pend_maybe = false;
   set_uniform(st, 0);

@@ -267,6 +267,15 @@ size_t decode_lds_bytes(int lam, int eta, int d, int g, bool f32);
 void decode_plan(int lam, int eta, int d, int g, bool f32, int* kc);
 hipError_t launch_transpose_w(const void* W, void* WT, int Hkv, int d, bool f32, hipStream_t st);
 hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st);
+// Several spans of 32-bit words, each set to its value, in one launch
+// (empty spans are skipped; at most kMaxFill)
+constexpr int kMaxFill = 8;
+struct FillSpan {
+  uint32_t* p;
+  size_t n;
+  uint32_t v;
+};
+hipError_t launch_fill_u32(const FillSpan* spans, int n, hipStream_t st);
 // dst[b][c][r] = src[b][r][c] for b < batch, r < rows, c < cols (float32)
 hipError_t launch_transpose_f32(const float* src, float* dst, int batch, int rows, int cols,
                                 hipStream_t st);

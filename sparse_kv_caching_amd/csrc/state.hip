@@ -217,6 +217,44 @@ hipError_t launch_zero_u32(unsigned* p, size_t n, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Up to kMaxFill spans of 32-bit words, each set to its own value, in one
+// launch (row y of the grid: span y; 16-byte stores where the span allows)
+struct FillArgs {
+  FillSpan s[kMaxFill];
+};
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(FillArgs a) {
+  const FillSpan sp = a.s[blockIdx.y];
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if ((reinterpret_cast<uintptr_t>(sp.p) & 15) == 0) {
+    const size_t n4 = sp.n / 4;
+    const u32x4 v = u32x4{sp.v, sp.v, sp.v, sp.v};
+    for (size_t j = i; j < n4; j += stride) reinterpret_cast<u32x4*>(sp.p)[j] = v;
+    for (size_t j = 4 * n4 + i; j < sp.n; j += stride) sp.p[j] = sp.v;
+  } else {
+    for (; i < sp.n; i += stride) sp.p[i] = sp.v;
+  }
+}
+
+hipError_t launch_fill_u32(const FillSpan* spans, int n, hipStream_t st) {
+  if (n < 0 || n > kMaxFill) return hipErrorInvalidValue;
+  FillArgs a;
+  int m = 0;
+  size_t most = 0;
+  for (int i = 0; i < n; ++i) {
+    if (spans[i].n == 0) continue;
+    a.s[m++] = spans[i];
+    most = std::max(most, spans[i].n);
+  }
+  if (m == 0) return hipSuccess;
+  // 16-byte stores: a quarter of the words per thread pass; at most 1024
+  // blocks per span (grid-stride beyond)
+  const size_t blocks = std::min<size_t>(1024, (most / 4 + 255) / 256 + 1);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks, (unsigned)m), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 // dst[b][c][r] = src[b][r][c]: 32 x 32 tiles through LDS (export / import of
 // H, whose device layout is H^T)
 __global__ void transpose_f32_kernel(const float* src, float* dst, int rows, int cols) {
