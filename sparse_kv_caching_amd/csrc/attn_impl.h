@@ -169,7 +169,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
   // an XCD (blocks are dealt to the 8 XCDs round-robin) and its K/V rows,
   // re-read by every chunk, stay in that XCD's L2
   const int u = u_, j = a.ch0 + jrel, pt = pt_;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // (the wave index as a uniform value: scalar branches and address math)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
   const int kvh = u % a.Hkv;
   const long long n0 = vr.n0;

@@ -208,7 +208,8 @@ __device__ __forceinline__ void chain_body(const ChainArgs& a, int bid) {
   const bool writer = ch < nw;
   const int wr0 = xs ? 32 * (NSLAB / nw) * ch : col0;   // first column written
   const int wrn = xs ? 32 * (NSLAB / nw) : 32 * SPW;    // columns written
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // (the wave index as a uniform value: scalar branches and address math)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, r = lane & 31;
 
   extern __shared__ __align__(16) unsigned char smem[];
