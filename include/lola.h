@@ -348,9 +348,11 @@ int lola_state_positions(const lola_state* st, int64_t* out);
  *                             of the compute units and the read of each chunk
  *                             starts as soon as the chain has published that
  *                             chunk's state (when the chain fits half of the
- *                             compute units and the call has >= 2 chunks;
- *                             otherwise as 0); -1 (default) = 1 for calls of
- *                             >= 4 chunks, else 0.
+ *                             compute units, the call has >= 2 chunks and
+ *                             the read's table of key row addresses fits its
+ *                             LDS: window + cache + C up to about 4700 keys
+ *                             at d = 128; otherwise as 0); -1 (default) = 1
+ *                             for calls of >= 4 chunks, else 0.
  *                             Both schedules give bitwise the same results
  *                             (the chain's results do not depend on its
  *                             workgroup count).
