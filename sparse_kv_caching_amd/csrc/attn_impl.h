@@ -29,6 +29,8 @@
 // uses the hi/lo bf16 split on both phi(q) and H.  fp32 inputs split every
 // operand into hi/lo fp16 (three passes, ~2^-22 per product).
 #pragma once
+#include <type_traits>
+
 #include "internal.h"
 
 namespace lola {
@@ -598,7 +600,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
       }
     }
   };
-  f32x16 S[2];
+  // the scores of a tile and of the next one: two register sets whose roles
+  // alternate from tile to tile (16-bit inputs: the loop runs two tiles per
+  // iteration, so that the sets stay in fixed registers and are never copied)
+  f32x16 Sb[DT::kSplit ? 1 : 2][2];
   if (ntiles > 0) {
     if constexpr (DT::kSplit) {
       load_k(kbase);
@@ -614,10 +619,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
   }
   if (ntiles > 2) load_k(kbase + 2 * KT);   // staged in iteration 0
   __syncthreads();
-  if (ntiles > 0 && wactive && kbase <= wlast) scores(0, S);
+  if (ntiles > 0 && wactive && kbase <= wlast) scores(0, Sb[0]);
   // (iteration 0 overwrites K buffer 0 with tile 2: every wave has read it)
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  // tile t, its scores in Sb[P], the next tile's into Sb[P ^ 1]
+  auto tile_step = [&](int t, auto parity) {
+    // (fp32 inputs: the next tile's scores are taken after this tile's
+    // products, into the same registers; two sets would not fit)
+    constexpr int P = DT::kSplit ? 0 : decltype(parity)::value;
+    f32x16 (&S)[2] = Sb[P];
+    f32x16 (&Sn)[2] = Sb[DT::kSplit ? 0 : P ^ 1];
     const int t0 = kbase + t * KT, b = t & 1;
     // staged here: K of tile t + 2 into K buffer b, V of tile t + 1 into V
     // buffer b ^ 1; loaded here: K of tile t + 3, V of tile t + 2
@@ -697,7 +708,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
         // (fp32 inputs take three products per operand pair: the next
         // tile's scores come after this tile's products, in the same
         // registers, as two sets of them would not fit)
-        scores(b ^ 1, S);
+        scores(b ^ 1, Sn);
       } else {
         // The next tile's score products, one at a time, each followed by
         // EPC of this tile's weights (the exponentials, rounded to fp16 as
@@ -717,7 +728,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
         u32x4 ka[LA], va[LA];
 #pragma unroll
         for (int i = 0; i < LA; ++i) ka[i] = ld16(kaddr(i));
-        f32x16 Sn[2];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -760,8 +770,6 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
           if (c == 3 && ldv) load_v(t0 + 2 * KT);
           __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) S[kh] = Sn[kh];
       }
       rs = half_sum(rs);
       l += rs;
@@ -772,6 +780,16 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
       if (ldv) load_v(t0 + 2 * KT);
     }
     __syncthreads();
+  };
+  if constexpr (DT::kSplit) {
+    for (int t = 0; t < ntiles; ++t) tile_step(t, std::integral_constant<int, 0>{});
+  } else {
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      tile_step(t, std::integral_constant<int, 0>{});
+      tile_step(t + 1, std::integral_constant<int, 1>{});
+    }
+    if (t < ntiles) tile_step(t, std::integral_constant<int, 0>{});
   }
 
   // ---- y = O / l
