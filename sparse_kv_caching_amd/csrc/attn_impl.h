@@ -43,8 +43,6 @@ constexpr int KT = 64;        // keys per staged tile
 constexpr float kSlack = 8.f; // log2 headroom of the softmax weights over the running maximum
 constexpr int HTS = kD + 4;   // LDS row of H^T (16-bit elements): 66 dwords, so that the 32
                               // rows of a 64-bit operand read fall on distinct bank pairs
-constexpr int VTS = KT + 4;   // LDS row of the V^T tile (keys): 34 dwords, so that the 32 rows of a
-                              // 64-bit operand read fall on distinct bank pairs
 
 // Byte offsets of the LDS arrays; the key phase reuses the region of the
 // linear-read phase.
@@ -52,7 +50,7 @@ struct AttnLayout {
   uint32_t tab, tabv;                          // both phases: the key table (below)
   bool wide;
   uint32_t WT, HT_hi, HT_lo, s;                // linear-read phase
-  uint32_t K[2], KL[2], VT[2], VTL[2];         // key phase, two buffers
+  uint32_t K[2], KL[2], VT[2], VTL[2];         // key phase, two buffers (V: key-major rows)
   uint32_t total;
 };
 
@@ -97,8 +95,8 @@ __host__ __device__ inline AttnLayout attn_layout_t(int d, int lam, int eta, int
   for (int b = 0; b < 2; ++b) {
     L.K[b] = take((uint32_t)KT * (d + 8) * 2);         // [KT][d + 8] bf16 (fp32 inputs: fp16 hi)
     L.KL[b] = take(f32 ? (uint32_t)KT * (d + 8) * 2 : 16);   //                  fp16 lo
-    L.VT[b] = take((uint32_t)d * VTS * 2);             // [d][VTS] fp16 (fp32 inputs: hi)
-    L.VTL[b] = take(f32 ? (uint32_t)d * VTS * 2 : 16); //                       lo
+    L.VT[b] = take((uint32_t)KT * d * 2);              // [KT][d] fp16, pieces permuted (stg_off)
+    L.VTL[b] = take(f32 ? (uint32_t)KT * d * 2 : 16);  // (fp32 inputs: hi, lo)
   }
   L.total = phaseA > off ? phaseA : off;
   return L;
@@ -133,13 +131,21 @@ __device__ __forceinline__ u32x4 sigma_load(const uint16_t* row16, int h) {
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
-// First V column (of 8) of thread tid's item in the V^T staging: the two
-// half-waves take column groups 2 apart (V^T rows 16 apart, 544 dwords:
-// 32 banks apart), so that their 4-byte writes to one key-pair column fall on
-// all 64 banks
-__device__ __forceinline__ int vt_cols(int tid) {
-  const int w = tid >> 6, hh = (tid >> 5) & 1;
-  return 8 * (4 * (w >> 1) + (w & 1) + 2 * hh);
+// The A operand of O^T += V^T P^T (32 V columns x 16 keys of k-block kb,
+// columns 32 mo ..) from a V tile staged as key-major rows of P pieces
+// (stg_off<P>): lane l gets column 32 mo + l % 32 for the keys sigma_h of the
+// block (16 kb + 4 h .. + 3, then 16 kb + 8 + 4 h .. + 3; h = l / 32), as
+// two transposing reads of four rows each.  vt_off: the lane's element offset
+// for k-block 0 (rows 16 kb and 8 further keep the piece permutation, which
+// depends on the row mod 4, so they are plain offsets).
+template <int P>
+__device__ __forceinline__ int vt_off(int mo, int lane) {
+  return stg_off<P>(4 * (lane >> 5) + ((lane & 15) >> 2), 32 * mo + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+}
+template <int P>
+__device__ __forceinline__ u32x4 ld_vt(const uint16_t* buf, int kb, int off) {
+  const u32x2 a = ld_tr(buf + off + 16 * kb * 8 * P), b = ld_tr(buf + off + (16 * kb + 8) * 8 * P);
+  return u32x4{a[0], a[1], b[0], b[1]};
 }
 
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
@@ -164,7 +170,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
   constexpr int KRS = HD + 8;     // LDS row of a staged key (elements)
   constexpr int PER = 16 / (int)sizeof(T);       // input elements per 16-byte piece
   constexpr int KPT = KT * HD / PER / kThreads;  // key pieces per thread and tile
-  constexpr int VITEMS = (KT / 2) * (HD / 8);    // (key pair, 8 columns) items per tile
+  constexpr int VPT = KT * HD / PER / kThreads;  // V pieces per thread and tile (as K)
+  constexpr int VP = HD / 8;                     // 16-byte fp16 pieces of a staged V row
   const VirtRows vr = a.vr;
   const int lam = vr.lam, eta = vr.eta;
   // unit fastest: with the unit count a multiple of 8, a unit's chunks share
@@ -389,11 +396,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
   // past the last key are loaded from the last key's row (finite values
   // whose weights are exactly 0 after the mask), so the loads need no
   // branch.
-  constexpr int VPC = (int)sizeof(T) / 2;        // 16-byte pieces per 8 V columns
   u32x4 kreg[KPT];
-  u32x4 vreg[2][VPC];
-  const bool vthread = VITEMS >= kThreads || tid < VITEMS;   // (wave-uniform)
-  const int vpr = tid % (KT / 2), vcol = vt_cols(tid);        // this thread's V item
+  u32x4 vreg[VPT];
+  int vto[NMT];                                   // the lane's V operand offsets (ld_vt)
+#pragma unroll
+  for (int mo = 0; mo < NMT; ++mo) vto[mo] = vt_off<VP>(mo, lane);
   auto load_k = [&](int t0) {
 #pragma unroll
     for (int q = 0; q < KPT; ++q) {
@@ -403,14 +410,11 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
     }
   };
   auto load_v = [&](int t0) {
-    if (vthread) {
 #pragma unroll
-      for (int kq = 0; kq < 2; ++kq) {
-        const int kk = min(t0 + 2 * vpr + kq, nkeys - 1);
-        const uint64_t src = (WIDE ? sm_tabv[kk] : row_addr(sm_tab[kk], bv, dv1, dv2)) + vcol * sizeof(T);
-#pragma unroll
-        for (int w = 0; w < VPC; ++w) vreg[kq][w] = ldg16(src + 16 * w);
-      }
+    for (int q = 0; q < VPT; ++q) {
+      const int pc = q * kThreads + tid, kl = pc / (HD / PER), c = (pc % (HD / PER)) * PER;
+      const int kk = min(t0 + kl, nkeys - 1);
+      vreg[q] = ldg16((WIDE ? sm_tabv[kk] : row_addr(sm_tab[kk], bv, dv1, dv2)) + c * sizeof(T));
     }
   };
   // buffer b's arrays (selects, so that the offsets stay in registers)
@@ -434,36 +438,31 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
       }
     }
   };
-  // V column q (of the thread's 8) of its two keys into V^T buffer b
-  auto store_v_col = [&](int b, int q) {
+  // V piece q of the thread into buffer b: key-major fp16 row pieces (bf16
+  // inputs: 8 values to fp16, one 16-byte store; fp32 inputs: 4 values
+  // split into fp16 hi and lo, 8 bytes to each plane)
+  auto store_v_piece = [&](int b, int q) {
     uint16_t* VTb = (uint16_t*)(smem + buf_off(L.VT, b));
     uint16_t* VTLb = (uint16_t*)(smem + buf_off(L.VTL, b));
-    float vf[2];
-#pragma unroll
-    for (int kq = 0; kq < 2; ++kq) {
-      if constexpr (VPC == 1) {   // 8 bf16 in one piece
-        const uint32_t w = vreg[kq][0][q >> 1];
-        vf[kq] = __uint_as_float((q & 1) ? (w & 0xFFFF0000u) : (w << 16));
-      } else {                    // 8 fp32 in two pieces
-        vf[kq] = __uint_as_float(vreg[kq][q >> 2][q & 3]);
-      }
-    }
-    uint32_t* row = reinterpret_cast<uint32_t*>(VTb + (vcol + q) * VTS) + vpr;
+    const int pc = q * kThreads + tid, kl = pc / (HD / PER), c = (pc % (HD / PER)) * PER;
+    const int off = stg_off<VP>(kl, c);
     if constexpr (DT::kSplit) {
-      uint32_t h0, l0, h1, l1;
-      DT::split(vf[0], h0, l0);
-      DT::split(vf[1], h1, l1);
-      *row = h0 | (h1 << 16);
-      *(reinterpret_cast<uint32_t*>(VTLb + (vcol + q) * VTS) + vpr) = l0 | (l1 << 16);
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) DT::split(__uint_as_float(vreg[q][e]), hi[e], lo[e]);
+      *reinterpret_cast<u32x2*>(VTb + off) = u32x2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+      *reinterpret_cast<u32x2*>(VTLb + off) = u32x2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
     } else {
-      *row = f16_pair(vf[0], vf[1]);
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        w[j] = f16_pair(__uint_as_float(vreg[q][j] << 16), __uint_as_float(vreg[q][j] & 0xFFFF0000u));
+      *reinterpret_cast<u32x4*>(VTb + off) = w;
     }
   };
   auto store_v = [&](int b) {
-    if (vthread) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) store_v_col(b, q);
-    }
+    for (int q = 0; q < VPT; ++q) store_v_piece(b, q);
   };
   // cache keys hidden from the read: the key loop starts past them
   const int kbase = (a.branches & LOLA_READ_CACHE) ? 0 : gsj;
@@ -697,9 +696,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
           splitop<DT>(pv, ph8, pl8);
 #pragma unroll
           for (int mo = 0; mo < NMT; ++mo) {
-            const int row = 32 * mo + r;
-            const u32x4 vh = sigma_load(VTb + row * VTS + 16 * kb, h);
-            const u32x4 vl = sigma_load(VTLb + row * VTS + 16 * kb, h);
+            const u32x4 vh = ld_vt<VP>(VTb, kb, vto[mo]);
+            const u32x4 vl = ld_vt<VP>(VTLb, kb, vto[mo]);
             O[mo] = DT::mma(vh, ph8, O[mo]);
             O[mo] = DT::mma(vh, pl8, O[mo]);
             O[mo] = DT::mma(vl, ph8, O[mo]);
@@ -724,7 +722,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
         static_assert(NS >= 8 && NP >= 4, "staging and loads are spread over these steps");
         const uint16_t* Kn = (const uint16_t*)(smem + buf_off(L.K, b ^ 1));
         auto kaddr = [&](int c) { return Kn + (32 * (c & 1) + r) * KRS + 16 * (c >> 1) + 8 * h; };
-        auto vaddr = [&](int c) { return VTb + (32 * (c % NMT) + r) * VTS + 16 * (c / NMT); };
+        auto vop = [&](int c) { return ld_vt<VP>(VTb, c / NMT, vto[c % NMT]); };
         u32x4 ka[LA], va[LA];
 #pragma unroll
         for (int i = 0; i < LA; ++i) ka[i] = ld16(kaddr(i));
@@ -738,7 +736,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
           const int kh = c & 1, kb = c >> 1;
           const u32x4 ac = ka[c % LA];
           if (c + LA < NS) ka[c % LA] = ld16(kaddr(c + LA));
-          else va[(c + LA - NS) % LA] = sigma_load(vaddr(c + LA - NS), h);
+          else va[(c + LA - NS) % LA] = vop(c + LA - NS);
           Sn[kh] = DT::mma(ac, qh[kb], Sn[kh]);
 #pragma unroll
           for (int x = 0; x < EPC; ++x) {
@@ -747,7 +745,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
                 fmaf(S[kp >> 1][8 * (kp & 1) + q], scale2, -msub));
           }
           if (c == 0 && stk) store_k(b);
-          if (c < 8 && stv && vthread) store_v_col(b ^ 1, c);
+          if (c < VPT && stv) store_v_piece(b ^ 1, c);
           __builtin_amdgcn_sched_barrier(0);
         }
         // the value products, each with one step of the row sum (pairwise
@@ -759,7 +757,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
         for (int c = 0; c < NP; ++c) {
           const int kb = c / NMT, mo = c % NMT;
           const u32x4 vc = va[c % LA];
-          if (c + LA < NP) va[c % LA] = sigma_load(vaddr(c + LA), h);
+          if (c + LA < NP) va[c % LA] = vop(c + LA);
           O[mo] = mfma_f16(__builtin_bit_cast(f16x8, vc), p8[kb], O[mo]);
 #pragma unroll
           for (int x = 0; x < DPC; ++x) {

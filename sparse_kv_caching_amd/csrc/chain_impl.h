@@ -65,16 +65,8 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int HTP = kD + 8;   // padded LDS row of H^T (16-bit elements)
 // Fold staging: 64 tokens per block, token-major rows of 16-bit elements
-// (as gathered), read back as MFMA operands with transposing LDS reads.  A
-// row of P 16-byte pieces is stored unpadded with its pieces permuted (XOR
-// of the piece index with a function of the row), so that the four
-// consecutive rows one transposing read touches fall on distinct banks.
-template <int P>
-__device__ __forceinline__ int stg_off(int row, int col) {   // element offset, col % 4 == 0
-  static_assert(P == 4 || P == 8 || P == 16, "rows of 64, 128 or 256 bytes");
-  const int x = P == 16 ? 4 * (row & 3) : P == 8 ? 4 * ((row >> 1) & 1) : 0;
-  return row * (8 * P) + ((((col >> 3) ^ x)) << 3) + (col & 7);
-}
+// (as gathered, stg_off), read back as MFMA operands with transposing LDS
+// reads (ld_tr).
 // fold staging buffers: two where the workgroup holds fewer than all slabs
 // (the two then fit the LDS of the all-slab layout with one)
 template <int HD, int SPW> constexpr int kFoldBufs = SPW < HD / 32 ? 2 : 1;
@@ -142,14 +134,6 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 
-// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
-// lane i names 4 16-bit elements of row i / 4, columns 4 (i % 4) .. of a
-// 4 x 16 block, and receives column i of the block (its 4 rows, in order).
-__device__ __forceinline__ u32x2 ld_tr(const uint16_t* p) {
-  typedef short v4s __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) v4s* lds_v4s;
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)p));
-}
 // The 32 x 32 x 16 MFMA operand of a staged block: lane l gets column
 // c0 + l % 32 for rows k0 + 8 (l / 32) .. + 7 (k0: the k-block's first row, a
 // multiple of 8), as two transposing reads of 4 rows each.

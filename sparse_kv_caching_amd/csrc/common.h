@@ -218,4 +218,25 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
+// Staging of rows of 16-bit elements in LDS for transposing reads: a row of
+// P 16-byte pieces is stored unpadded with its pieces permuted (XOR of the
+// piece index with a function of the row), so that the four consecutive rows
+// one transposing read touches fall on distinct banks.  Element offset of
+// (row, col), col % 4 == 0.
+template <int P>
+__device__ __forceinline__ int stg_off(int row, int col) {
+  static_assert(P == 4 || P == 8 || P == 16, "rows of 64, 128 or 256 bytes");
+  const int x = P == 16 ? 4 * (row & 3) : P == 8 ? 4 * ((row >> 1) & 1) : 0;
+  return row * (8 * P) + ((((col >> 3) ^ x)) << 3) + (col & 7);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane i names 4 16-bit elements of row i / 4, columns 4 (i % 4) .. of a
+// 4 x 16 block, and receives column i of the block (its 4 rows, in order).
+__device__ __forceinline__ u32x2 ld_tr(const uint16_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s* lds_v4s;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)p));
+}
+
 }  // namespace lola
