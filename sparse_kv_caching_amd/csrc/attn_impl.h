@@ -16,8 +16,8 @@
 // transposed, S^T = K Q^T (32 keys x 32 queries per MFMA), so each lane owns
 // one query and softmax statistics need a single cross-half exchange; P then
 // feeds O^T += V^T P^T straight from registers (the K index of that MFMA is
-// permuted to match the result layout, see common.h), with V staged
-// transposed (key pairs packed per dword).
+// permuted to match the result layout, see common.h), with V staged as
+// key-major fp16 rows and its operand read back with transposing LDS reads.
 //
 // Exponentials are unshifted in Eq. (14); here they are shifted by a running
 // maximum m >= 0 (log2 domain) and the linear terms are scaled by the same
