@@ -631,8 +631,12 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
     const int t0 = kbase + t * KT, b = t & 1;
     // staged here: K of tile t + 2 into K buffer b, V of tile t + 1 into V
     // buffer b ^ 1; loaded here: K of tile t + 3, V of tile t + 2
-    const bool stk = t + 2 < ntiles, stv = t + 1 < ntiles;
-    const bool ldk = t + 3 < ntiles, ldv = t + 2 < ntiles;
+    // (16-bit inputs: always, past the last tile too: the rows are clamped to
+    // the last key, and a buffer staged past the end is one nobody reads in
+    // this iteration and whose products are never used; loads without a
+    // condition keep the staging registers free of copies)
+    const bool stk = !DT::kSplit || t + 2 < ntiles, stv = !DT::kSplit || t + 1 < ntiles;
+    const bool ldk = !DT::kSplit || t + 3 < ntiles, ldv = !DT::kSplit || t + 2 < ntiles;
     if (wactive && t0 <= wlast) {
       const uint16_t* VTb = (const uint16_t*)(smem + buf_off(L.VT, b));
       const uint16_t* VTLb = (const uint16_t*)(smem + buf_off(L.VTL, b));
