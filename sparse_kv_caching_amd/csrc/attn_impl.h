@@ -41,8 +41,8 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int KT = 64;        // keys per staged tile
 constexpr float kSlack = 8.f; // log2 headroom of the softmax weights over the running maximum
-constexpr int HTS = kD + 4;   // LDS row of H^T (16-bit elements): 66 dwords, so that the 32
-                              // rows of a 64-bit operand read fall on distinct bank pairs
+constexpr int HTS = kD + 8;   // LDS row of H^T (16-bit elements): 68 dwords, 16-byte aligned;
+                              // the 16 rows of a 16-byte read pass fall on distinct bank groups
 
 // Byte offsets of the LDS arrays; the key phase reuses the region of the
 // linear-read phase.
@@ -125,11 +125,6 @@ __device__ __forceinline__ u32x4 ldg16(uint64_t addr) {
   return *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(addr);
 }
 
-// operand with K-slots sigma_h: elements [4h, 4h+4) and [8+4h, 8+4h+4) of a 16-block
-__device__ __forceinline__ u32x4 sigma_load(const uint16_t* row16, int h) {
-  u32x2 a = ld8(row16 + 4 * h), b = ld8(row16 + 8 + 4 * h);
-  return u32x4{a[0], a[1], b[0], b[1]};
-}
 
 // The A operand of O^T += V^T P^T (32 V columns x 16 keys of k-block kb,
 // columns 32 mo ..) from a V tile staged as key-major rows of P pieces
@@ -367,10 +362,14 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
     for (int k = 0; k < HPT; ++k) {
       const int i = tid + k * kThreads, pl = i / HPIECES, rem = i % HPIECES;
       const int row = rem / (kD / 8), col = (rem % (kD / 8)) * 8;
-      // (rows are 8-byte aligned: two 8-byte stores)
-      uint16_t* dst = (pl ? sm_HT_lo : sm_HT_hi) + row * HTS + col;
+      // Each 16-element block of a row is stored with its middle quarters
+      // swapped (elements 0-3, 8-11, 4-7, 12-15), so that the K-slots sigma_h
+      // of an operand (elements 4h .. 4h + 3 and 8 + 4h .. 8 + 4h + 3) are 8
+      // contiguous elements at 8h: one 16-byte read.  A piece is half a
+      // block: its two 8-byte halves go to their places.
+      uint16_t* dst = (pl ? sm_HT_lo : sm_HT_hi) + row * HTS + (col & ~15) + ((col >> 3) & 1) * 4;
       *reinterpret_cast<u32x2*>(dst) = u32x2{hv[k][0], hv[k][1]};
-      *reinterpret_cast<u32x2*>(dst + 4) = u32x2{hv[k][2], hv[k][3]};
+      *reinterpret_cast<u32x2*>(dst + 8) = u32x2{hv[k][2], hv[k][3]};
     }
     if (tid < kD) sm_s[tid] = sv;
   }
@@ -549,8 +548,8 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int u_, int jrel, i
 #pragma unroll
       for (int mo = 0; mo < NMT; ++mo) {
         const int row = 32 * mo + r;
-        const u32x4 ah = sigma_load(sm_HT_hi + row * HTS + 16 * kb, h);
-        const u32x4 al = sigma_load(sm_HT_lo + row * HTS + 16 * kb, h);
+        const u32x4 ah = ld16(sm_HT_hi + row * HTS + 16 * kb + 8 * h);
+        const u32x4 al = ld16(sm_HT_lo + row * HTS + 16 * kb + 8 * h);
         O[mo] = DT::mma(ah, bh, O[mo]);
         O[mo] = DT::mma(ah, bl, O[mo]);
         O[mo] = DT::mma(al, bh, O[mo]);
